@@ -1,0 +1,139 @@
+"""Block selection: which query-key tiles run in FP16 (test infrastructure).
+
+ThriftAttention (abstract): "a heuristic rapidly selects a small number of
+important query-key block pairs for FP16 precision"; the error matters most
+for the most important query-key interactions.  HyQuant (summary, abstract):
+vertical-line tokens and a local sliding window are kept in full precision.
+The pages give no formula; the readings used here (R8-R11) are:
+
+* importance estimate s_ij = mean(Q over query tile i) . mean(K over key tile j)
+  (the logit of the tile means), fp32 with a fixed operation order;
+* forced tiles: key tiles j < sink_tiles (the sink column) and the local
+  window, i.e. the key tiles meeting rows [qs - (w-1)*Bk, qe] of the query
+  tile (its diagonal tiles plus w-1 tiles before them);
+* budget per query tile k_i = topk, or ceil(num*|V_i|/den) in integers,
+  capped at the number of non-forced candidates; candidates ordered by
+  descending score, ties to the lower tile index.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_bits_to_f32
+
+
+def tile_sets(n_valid, N, Bq, Bk, causal, sink_tiles, local_tiles):
+    """Per query tile i: (valid key tiles V_i, forced tiles F_i), as sorted lists.
+
+    Query tiles with qs >= n_valid get empty sets (their rows output 0)."""
+    n_qt, n_kt = N // Bq, N // Bk
+    out = []
+    for i in range(n_qt):
+        qs = i * Bq
+        if qs >= n_valid:
+            out.append(([], []))
+            continue
+        qe = min(qs + Bq, n_valid) - 1
+        valid = [j for j in range(n_kt) if j * Bk < n_valid and (not causal or j * Bk <= qe)]
+        lo = qs - (local_tiles - 1) * Bk
+        forced = []
+        for j in valid:
+            sink = j < sink_tiles
+            local = local_tiles >= 1 and (j + 1) * Bk - 1 >= lo and j * Bk <= qe
+            if sink or local:
+                forced.append(j)
+        out.append((valid, forced))
+    return out
+
+
+def _tile_means(x: np.ndarray, n_valid: int, T: int) -> np.ndarray:
+    """fp32 mean over each tile of T rows of x[N, D] (rows >= n_valid excluded):
+    sequential fp32 sum in ascending row order, then one fp32 division by the
+    row count.  Tiles with no valid row give zeros."""
+    N, D = x.shape
+    nt = N // T
+    xt = x.reshape(nt, T, D)
+    acc = np.zeros((nt, D), dtype=np.float32)
+    cnt = np.zeros(nt, dtype=np.float32)
+    rows = np.arange(N).reshape(nt, T)
+    for r in range(T):
+        ok = rows[:, r] < n_valid
+        acc = np.where(ok[:, None], (acc + xt[:, r, :]).astype(np.float32), acc)
+        cnt = cnt + ok.astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        mean = (acc / np.where(cnt == 0, np.float32(1), cnt)[:, None]).astype(np.float32)
+    return np.where(cnt[:, None] == 0, np.float32(0), mean)
+
+
+def pooled_means(q_bits, k_bits, n_valid, Bq, Bk):
+    """Tile means of Q per query head [B,Hq,n_qt,D] and of K per kv head
+    [B,Hkv,n_kt,D], float32 (reading R8)."""
+    q = bf16_bits_to_f32(q_bits)
+    k = bf16_bits_to_f32(k_bits)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    qm = np.stack([np.stack([_tile_means(q[b, h], n_valid, Bq) for h in range(Hq)]) for b in range(B)])
+    km = np.stack([np.stack([_tile_means(k[b, h], n_valid, Bk) for h in range(Hkv)]) for b in range(B)])
+    return qm, km
+
+
+def tile_scores(qm: np.ndarray, km: np.ndarray) -> np.ndarray:
+    """s[i, j] for one head: acc = fl32(acc + fl32(qm[i,d]*km[j,d])) for d
+    ascending, starting from +0 (no fused multiply-add)."""
+    n_qt, D = qm.shape
+    n_kt = km.shape[0]
+    acc = np.zeros((n_qt, n_kt), dtype=np.float32)
+    for d in range(D):
+        prod = (qm[:, d][:, None] * km[:, d][None, :]).astype(np.float32)
+        acc = (acc + prod).astype(np.float32)
+    return acc
+
+
+def budget(topk, ratio_num, ratio_den, n_valid_tiles, n_candidates):
+    """k_i (reading R9): topk if topk >= 0, else ceil(num*|V_i|/den) computed
+    in integers; never more than the number of candidates."""
+    if topk >= 0:
+        k = topk
+    else:
+        k = -((-ratio_num * n_valid_tiles) // ratio_den)
+    return min(k, n_candidates)
+
+
+def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, ratio_den,
+                  sink_tiles, local_tiles):
+    """Return (mask u32 [B,Hq,n_qt,ceil(n_kt/32)], n_fp16 i32 [B,Hq,n_qt],
+    scores f32 [B,Hq,n_qt,n_kt]).  Bit j%32 of word j//32 is set when key tile
+    j runs in FP16 for that query tile.  Scores are given for every tile pair
+    (also non-candidates) for inspection."""
+    B, Hq, N, D = q_bits.shape
+    Hkv = k_bits.shape[1]
+    G = Hq // Hkv
+    n_qt, n_kt = N // Bq, N // Bk
+    nw = (n_kt + 31) // 32
+    sets = tile_sets(n_valid, N, Bq, Bk, causal, sink_tiles, local_tiles)
+    qm, km = pooled_means(q_bits, k_bits, n_valid, Bq, Bk)
+    mask = np.zeros((B, Hq, n_qt, nw), dtype=np.uint32)
+    nfp = np.zeros((B, Hq, n_qt), dtype=np.int32)
+    scores = np.zeros((B, Hq, n_qt, n_kt), dtype=np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            s = tile_scores(qm[b, h], km[b, h // G])
+            scores[b, h] = s
+            for i in range(n_qt):
+                valid, forced = sets[i]
+                fset = set(forced)
+                cand = [j for j in valid if j not in fset]
+                k = budget(topk, ratio_num, ratio_den, len(valid), len(cand))
+                # descending score; equal scores keep ascending tile index (stable sort)
+                order = sorted(cand, key=lambda j: (-float(s[i, j]), j))
+                chosen = set(forced) | set(order[:k])
+                for j in chosen:
+                    mask[b, h, i, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+                nfp[b, h, i] = len(chosen)
+    return mask, nfp, scores
+
+
+def mask_to_sets(mask_row: np.ndarray, n_kt: int):
+    """Promoted tile indices of one mask row (u32 words)."""
+    return [j for j in range(n_kt) if (int(mask_row[j // 32]) >> (j % 32)) & 1]

@@ -1,0 +1,153 @@
+"""Pins for the oracle's block selection (CPU only)."""
+
+import os
+
+import numpy as np
+
+import mxq_inputs
+from oracle import select as S
+from oracle.formats import f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_counts():
+    out = {}
+    with open(os.path.join(GOLDEN, "tile_counts.txt")) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                name, *vals = line.split()
+                out[name] = tuple(int(v) for v in vals)
+    return out
+
+
+def _closed_form_counts(N, Bq, Bk, causal, n_valid, sink, w, topk, num, den):
+    """Independent count formulas (interval arithmetic, no set building)."""
+    n_qt = N // Bq
+    tv = tf = tk = 0
+    for i in range(n_qt):
+        qs = i * Bq
+        if qs >= n_valid:
+            continue
+        qe = min(qs + Bq, n_valid) - 1
+        last = (qe // Bk) if causal else (n_valid - 1) // Bk
+        nvalid = last + 1
+        ns = min(sink, nvalid)                      # sink tiles [0, ns)
+        if w >= 1:
+            lo_t = max(0, (qs - (w - 1) * Bk) // Bk)
+            hi_t = min(last, qe // Bk)
+            nloc = hi_t - lo_t + 1                  # window tiles [lo_t, hi_t]
+            both = max(0, min(hi_t, ns - 1) - lo_t + 1)
+            forced = nloc + ns - both
+        else:
+            forced = ns
+        k = topk if topk >= 0 else -((-num * nvalid) // den)
+        tv += nvalid
+        tf += forced
+        tk += min(k, nvalid - forced)
+    return tv, tf, tk, tf + tk
+
+
+def test_tile_count_closed_forms_match_golden():
+    gold = _golden_counts()
+    for name, cfg in mxq_inputs.PREFILL_CONFIGS.items():
+        got = _closed_form_counts(cfg["N"], cfg["Bq"], cfg["Bk"], cfg["causal"], cfg["n_valid"],
+                                  cfg["sink_tiles"], cfg["local_tiles"], cfg["topk"],
+                                  cfg["ratio_num"], cfg["ratio_den"])
+        assert got == gold[name], (name, got, gold[name])
+
+
+def test_oracle_selection_counts_match_closed_forms():
+    gold = _golden_counts()
+    rng = np.random.default_rng(0)
+    for name, cfg in mxq_inputs.PREFILL_CONFIGS.items():
+        N, D = cfg["N"], 32
+        q = f32_to_bf16_bits(rng.standard_normal((1, 1, N, D)).astype(np.float32))
+        k = f32_to_bf16_bits(rng.standard_normal((1, 1, N, D)).astype(np.float32))
+        sets = S.tile_sets(cfg["n_valid"], N, cfg["Bq"], cfg["Bk"], cfg["causal"],
+                           cfg["sink_tiles"], cfg["local_tiles"])
+        assert sum(len(v) for v, _ in sets) == gold[name][0]
+        assert sum(len(f) for _, f in sets) == gold[name][1]
+        mask, nfp, _ = S.select_blocks(q, k, cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                                       cfg["topk"], cfg["ratio_num"], cfg["ratio_den"],
+                                       cfg["sink_tiles"], cfg["local_tiles"])
+        assert int(nfp.sum()) == gold[name][3], name
+        bits = sum(bin(int(w)).count("1") for w in mask.ravel())
+        assert bits == gold[name][3]
+
+
+def test_local_window_is_w_tiles_when_square():
+    # Bq == Bk: the window is exactly the diagonal tile and the w-1 before it
+    sets = S.tile_sets(1024, 1024, 64, 64, True, 0, 3)
+    for i, (valid, forced) in enumerate(sets):
+        assert forced == list(range(max(0, i - 2), i + 1))
+    # Bq = 2*Bk, w = 1: both diagonal key tiles (the diagonal band)
+    sets = S.tile_sets(1024, 1024, 128, 64, True, 0, 1)
+    for i, (valid, forced) in enumerate(sets):
+        assert forced == [2 * i, 2 * i + 1]
+
+
+def test_tile_means_and_scores_against_float32_loops():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((256, 8)).astype(np.float32) * 5
+    xb = S.bf16_bits_to_f32(f32_to_bf16_bits(x))
+    m = S._tile_means(xb, 150, 64)   # tiles: 64 rows, 64 rows, 22 rows valid, 0 valid (pad to 256)
+    # plain loops, one element at a time in float32
+    for t in range(3):
+        for d in range(8):
+            acc = np.float32(0)
+            n = 0
+            for r in range(t * 64, min(t * 64 + 64, 150)):
+                acc = np.float32(acc + xb[r, d])
+                n += 1
+            assert m[t, d] == np.float32(acc / np.float32(n))
+    sc = S.tile_scores(m[:3], m[:3])
+    for i in range(3):
+        for j in range(3):
+            acc = np.float32(0)
+            for d in range(8):
+                acc = np.float32(acc + np.float32(m[i, d] * m[j, d]))
+            assert sc[i, j] == acc
+
+
+def _check_topk_property(scores_row, cand, chosen, k):
+    """Selected candidates dominate unselected ones: score strictly higher, or
+    equal score with a lower tile index (the tie rule)."""
+    assert len(chosen) == k
+    rest = [j for j in cand if j not in chosen]
+    for a in chosen:
+        for b in rest:
+            sa, sb = scores_row[a], scores_row[b]
+            assert sa > sb or (sa == sb and a < b)
+
+
+def test_topk_dominance_property_random_and_ties():
+    rng = np.random.default_rng(2)
+    N, D = 1024, 16
+    for trial in range(4):
+        qf = rng.standard_normal((1, 2, N, D)).astype(np.float32)
+        kf = rng.standard_normal((1, 1, N, D)).astype(np.float32)
+        if trial == 3:
+            kf[:] = np.round(kf)  # coarse values make equal scores likely
+            qf[:] = 1.0
+        q, k = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+        mask, nfp, scores = S.select_blocks(q, k, N, 64, 64, True, -1, 20, 100, 1, 1)
+        sets = S.tile_sets(N, N, 64, 64, True, 1, 1)
+        for h in range(2):
+            for i, (valid, forced) in enumerate(sets):
+                chosen = set(S.mask_to_sets(mask[0, h, i], N // 64))
+                assert set(forced) <= chosen
+                cand = [j for j in valid if j not in forced]
+                kk = S.budget(-1, 20, 100, len(valid), len(cand))
+                _check_topk_property(scores[0, h, i], cand, chosen - set(forced), kk)
+
+
+def test_zero_keys_pick_lowest_index_candidates():
+    N, D = 512, 16
+    rng = np.random.default_rng(3)
+    q = f32_to_bf16_bits(rng.standard_normal((1, 1, N, D)).astype(np.float32))
+    k = np.zeros((1, 1, N, D), dtype=np.uint16)
+    mask, _, scores = S.select_blocks(q, k, N, 64, 64, False, 2, 0, 1, 1, 0)
+    assert np.all(scores == 0)
+    for i in range(N // 64):
+        assert S.mask_to_sets(mask[0, 0, i], 8) == [0, 1, 2]   # sink 0 + lowest two candidates
