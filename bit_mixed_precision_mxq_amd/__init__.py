@@ -1,0 +1,294 @@
+"""Python binding of libmxq (mixed-precision block-scaled attention on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmxq.so, called through its C ABI (include/mxq.h).  torch provides device
+memory and the current HIP stream.  There is no CPU fallback: if the library
+is missing or no GPU is present, these functions raise.
+
+Entry points (same names as the C ABI):
+  mxq_quantize(x, fmt, axis, n_valid)         -> codes, scales[, zeros]
+  attn_select_blocks(q, k, shape, params)     -> mask, n_fp16, scores
+  attn_mixed_fwd(ops, mask, shape, ...)       -> out, lse
+  attn_quantkv_decode(q, cache, ...)          -> out
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxq.so")
+
+MXQ_OK, MXQ_EINVAL, MXQ_EUNSUPPORTED, MXQ_EHIP = 0, 1, 2, 3
+MXQ_MXFP4_E2M1, MXQ_MXFP8_E4M3, MXQ_INT4_ASYM_G32, MXQ_FP16 = 1, 2, 3, 4
+MXQ_AXIS_D, MXQ_AXIS_N = 0, 1
+MXQ_MIXED, MXQ_ALL_LOWBIT, MXQ_ALL_FP16 = 0, 1, 2
+MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
+
+EXPORTED = [
+    "mxq_quantize", "attn_select_blocks_workspace", "attn_select_blocks", "attn_mixed_fwd",
+    "attn_quantkv_decode_workspace", "attn_quantkv_decode", "mxq_status_string",
+    "mxq_last_error", "mxq_version",
+]
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "N", "n_valid", "D", "Bq", "Bk", "causal")]
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("topk", "ratio_num", "ratio_den", "sink_tiles", "local_tiles")]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
+        ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p),
+        ("seq_len", ctypes.c_void_p),
+        ("L_cap", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmxq.so and declare its signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m bit_mixed_precision_mxq_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mxq_quantize.argtypes = [vp, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.mxq_quantize.restype = i32
+    lib.attn_select_blocks_workspace.argtypes = [ctypes.POINTER(AttnShape)]
+    lib.attn_select_blocks_workspace.restype = sz
+    lib.attn_select_blocks.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(SelectParams),
+                                       vp, sz, vp, vp, vp, vp]
+    lib.attn_select_blocks.restype = i32
+    lib.attn_mixed_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AttnShape),
+                                   ctypes.c_float, i32, vp, i32, vp, vp]
+    lib.attn_mixed_fwd.restype = i32
+    lib.attn_quantkv_decode_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_quantkv_decode_workspace.restype = sz
+    lib.attn_quantkv_decode.argtypes = [vp, ctypes.POINTER(KVCache), i32, i32, i32, i32, i32,
+                                        ctypes.c_float, i32, vp, sz, vp, vp]
+    lib.attn_quantkv_decode.restype = i32
+    lib.mxq_status_string.argtypes = [i32]
+    lib.mxq_status_string.restype = ctypes.c_char_p
+    lib.mxq_last_error.argtypes = []
+    lib.mxq_last_error.restype = ctypes.c_char_p
+    lib.mxq_version.argtypes = []
+    lib.mxq_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != MXQ_OK:
+        lib = load_library()
+        raise MxqError(status, lib.mxq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+# ------------------------------------------------------------------ quantize
+def mxq_quantize(x: torch.Tensor, fmt: int, axis: int, n_valid: int | None = None):
+    """x: bf16 [B,H,N,D] on the GPU.  Returns (codes, scales, zeros) with the
+    layouts of include/mxq.h (scales/zeros None where the format has none)."""
+    _need_gpu(x)
+    assert x.dtype == torch.bfloat16 and x.dim() == 4
+    B, H, N, D = x.shape
+    nv = N if n_valid is None else int(n_valid)
+    dev = x.device
+    zeros = None
+    if fmt == MXQ_MXFP4_E2M1:
+        codes = torch.empty((B, H, N, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, N, D // 32), dtype=torch.uint8, device=dev)
+    elif fmt == MXQ_MXFP8_E4M3:
+        codes = torch.empty((B, H, D, N), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, D, N // 32), dtype=torch.uint8, device=dev)
+    elif fmt == MXQ_FP16:
+        shape = (B, H, N, D) if axis == MXQ_AXIS_D else (B, H, D, N)
+        codes = torch.empty(shape, dtype=torch.float16, device=dev)
+        scales = None
+    elif fmt == MXQ_INT4_ASYM_G32:
+        codes = torch.empty((B, H, N, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, N, D // 32), dtype=torch.float16, device=dev)
+        zeros = torch.empty((B, H, N, D // 32), dtype=torch.float16, device=dev)
+    else:
+        raise ValueError("unknown format")
+    lib = load_library()
+    _check(lib.mxq_quantize(_ptr(x), B, H, N, D, nv, fmt, axis, _ptr(codes), _ptr(scales), _ptr(zeros), _stream()))
+    return codes, scales, zeros
+
+
+# ------------------------------------------------------------------ select
+@dataclass
+class Shape:
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    n_valid: int
+    D: int
+    Bq: int
+    Bk: int
+    causal: bool
+
+    def c(self) -> AttnShape:
+        return AttnShape(self.B, self.Hq, self.Hkv, self.N, self.n_valid, self.D, self.Bq, self.Bk, int(self.causal))
+
+
+def select_workspace(shape: Shape, device) -> torch.Tensor:
+    n = load_library().attn_select_blocks_workspace(ctypes.byref(shape.c()))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0,
+                       want_scores=False, workspace=None):
+    """Returns (mask u32-as-int32 [B,Hq,n_qt,words], n_fp16 [B,Hq,n_qt], scores or None)."""
+    _need_gpu(q, k)
+    n_qt, n_kt = shape.N // shape.Bq, shape.N // shape.Bk
+    words = (n_kt + 31) // 32
+    dev = q.device
+    mask = torch.empty((shape.B, shape.Hq, n_qt, words), dtype=torch.int32, device=dev)
+    nfp = torch.empty((shape.B, shape.Hq, n_qt), dtype=torch.int32, device=dev)
+    scores = torch.empty((shape.B, shape.Hq, n_qt, n_kt), dtype=torch.float32, device=dev) if want_scores else None
+    ws = workspace if workspace is not None else select_workspace(shape, dev)
+    sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles))
+    cs = shape.c()
+    _check(load_library().attn_select_blocks(_ptr(q), _ptr(k), ctypes.byref(cs), ctypes.byref(sp), _ptr(ws),
+                                             ws.numel(), _ptr(mask), _ptr(nfp), _ptr(scores), _stream()))
+    return mask, nfp, scores
+
+
+# ------------------------------------------------------------------ attention
+@dataclass
+class PrefillOperands:
+    q_codes: torch.Tensor | None = None
+    q_scales: torch.Tensor | None = None
+    k_codes: torch.Tensor | None = None
+    k_scales: torch.Tensor | None = None
+    v_codes: torch.Tensor | None = None
+    v_scales: torch.Tensor | None = None
+    q_bf16: torch.Tensor | None = None
+    k_bf16: torch.Tensor | None = None
+    v_f16t: torch.Tensor | None = None
+
+
+def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED) -> PrefillOperands:
+    """Quantise Q/K (MXFP4), V (MXFP8 along keys) and make the fp16 V^T copy,
+    all on the GPU through mxq_quantize."""
+    ops = PrefillOperands(q_bf16=q, k_bf16=k)
+    if mode != MXQ_ALL_FP16:
+        ops.q_codes, ops.q_scales, _ = mxq_quantize(q, MXQ_MXFP4_E2M1, MXQ_AXIS_D, n_valid)
+        ops.k_codes, ops.k_scales, _ = mxq_quantize(k, MXQ_MXFP4_E2M1, MXQ_AXIS_D, n_valid)
+        ops.v_codes, ops.v_scales, _ = mxq_quantize(v, MXQ_MXFP8_E4M3, MXQ_AXIS_N, n_valid)
+    if mode != MXQ_ALL_LOWBIT:
+        ops.v_f16t, _, _ = mxq_quantize(v, MXQ_FP16, MXQ_AXIS_N, n_valid)
+    return ops
+
+
+def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, mode=MXQ_MIXED,
+                   out_dtype=MXQ_OUT_F32, want_lse=True, out=None, lse=None):
+    dev = (ops.q_bf16 if ops.q_bf16 is not None else ops.q_codes).device
+    if out is None:
+        out = torch.empty((shape.B, shape.Hq, shape.N, shape.D),
+                          dtype=torch.float32 if out_dtype == MXQ_OUT_F32 else torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.Hq, shape.N), dtype=torch.float32, device=dev)
+    cs = shape.c()
+    _check(load_library().attn_mixed_fwd(
+        _ptr(ops.q_codes), _ptr(ops.q_scales), _ptr(ops.k_codes), _ptr(ops.k_scales), _ptr(ops.v_codes),
+        _ptr(ops.v_scales), _ptr(ops.q_bf16), _ptr(ops.k_bf16), _ptr(ops.v_f16t), _ptr(mask),
+        ctypes.byref(cs), float(softmax_scale), int(mode), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
+    return out, lse
+
+
+# ------------------------------------------------------------------ decode
+@dataclass
+class QuantKVCache:
+    k_codes: torch.Tensor
+    v_codes: torch.Tensor
+    k_scale: torch.Tensor
+    k_zero: torch.Tensor
+    v_scale: torch.Tensor
+    v_zero: torch.Tensor
+    k_sink: torch.Tensor | None
+    v_sink: torch.Tensor | None
+    k_recent: torch.Tensor | None
+    v_recent: torch.Tensor | None
+    seq_len: torch.Tensor
+    n_sink: int
+    n_recent: int
+
+    def c(self) -> KVCache:
+        return KVCache(_ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.k_zero),
+                       _ptr(self.v_scale), _ptr(self.v_zero), _ptr(self.k_sink), _ptr(self.v_sink),
+                       _ptr(self.k_recent), _ptr(self.v_recent), _ptr(self.seq_len),
+                       int(self.k_codes.shape[2]), int(self.n_sink), int(self.n_recent))
+
+
+def build_quant_kv_cache(k, v, seq_len, n_sink, n_recent, k_recent=None, v_recent=None) -> QuantKVCache:
+    """k, v: bf16 [B,Hkv,L,D] on the GPU; seq_len int32 [B] on the GPU.  The
+    INT4 arrays cover all L positions; the sink copy is tokens 0..n_sink-1 and
+    the recent copy (bf16 [B,Hkv,n_recent,D], given by the caller, who knows
+    each sequence's last tokens) is converted to fp16."""
+    kc, ks, kz = mxq_quantize(k, MXQ_INT4_ASYM_G32, MXQ_AXIS_D)
+    vc, vs, vz = mxq_quantize(v, MXQ_INT4_ASYM_G32, MXQ_AXIS_D)
+    k_sink = v_sink = k_rec = v_rec = None
+    if n_sink > 0:
+        k_sink, _, _ = mxq_quantize(k[:, :, :n_sink].contiguous(), MXQ_FP16, MXQ_AXIS_D)
+        v_sink, _, _ = mxq_quantize(v[:, :, :n_sink].contiguous(), MXQ_FP16, MXQ_AXIS_D)
+    if n_recent > 0:
+        k_rec, _, _ = mxq_quantize(k_recent.contiguous(), MXQ_FP16, MXQ_AXIS_D)
+        v_rec, _, _ = mxq_quantize(v_recent.contiguous(), MXQ_FP16, MXQ_AXIS_D)
+    return QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, seq_len, n_sink, n_recent)
+
+
+def decode_workspace(B, Hq, D, num_splits, max_seq_len, device) -> torch.Tensor:
+    n = load_library().attn_quantkv_decode_workspace(B, Hq, D, num_splits, max_seq_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def attn_quantkv_decode(q, cache: QuantKVCache, Hkv, max_seq_len, softmax_scale=0.0, num_splits=0,
+                        workspace=None, out=None):
+    """q: bf16 [B,Hq,D] on the GPU.  Returns out f32 [B,Hq,D]."""
+    _need_gpu(q)
+    B, Hq, D = q.shape
+    ws = workspace if workspace is not None else decode_workspace(B, Hq, D, num_splits, max_seq_len, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    kv = cache.c()
+    _check(load_library().attn_quantkv_decode(_ptr(q), ctypes.byref(kv), B, Hq, Hkv, D, int(max_seq_len),
+                                              float(softmax_scale), int(num_splits), _ptr(ws), ws.numel(),
+                                              _ptr(out), _stream()))
+    return out

@@ -1,0 +1,245 @@
+// mxq_quantize: MXFP4 / MXFP8 / INT4-G32 / fp16 conversion of bf16 tensors.
+//
+// Block-scaled quantisation (ThriftAttention abstract; OCP MX rules for the
+// shared E8M0 exponent).  All four conversions are memory-bound: one pass that
+// reads each bf16 once and writes the codes once.  Rounding is done with
+// compares and integer bit operations so that every code is the exact
+// round-half-even of the exactly scaled input.
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+// ---- MXFP4 along D: one thread per 32-element block ---------------------------
+// x [rows][D] bf16 -> codes [rows][D/2], scales [rows][D/32].  Consecutive
+// threads take consecutive blocks, so a wave reads 4 KB of contiguous input.
+__global__ void __launch_bounds__(256) k_quant_mxfp4_d(const uint16_t* __restrict__ x,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales,
+                                                       int64_t n_blocks, int64_t blocks_per_row,
+                                                       int64_t N, int64_t n_valid) {
+  int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blk >= n_blocks) return;
+  int64_t row = blk / blocks_per_row;
+  bool live = (row % N) < n_valid;
+  const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 v = live ? src[i] : make_uint4(0, 0, 0, 0);
+    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+  }
+  int e = shared_exponent(amax, 2);
+  uint32_t packed[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t b = h ? (w[i] & 0xFFFF0000u) : (w[i] << 16);
+      float v = __builtin_ldexpf(__uint_as_float(b), -e);
+      uint32_t c = e2m1_mag_code(fabsf(v)) | ((b >> 28) & 8u);
+      int el = 2 * i + h;  // element index within the block
+      packed[el / 8] |= c << (4 * (el % 8));
+    }
+  }
+  reinterpret_cast<uint4*>(codes)[blk] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scales[blk] = static_cast<uint8_t>(e + 127);
+}
+
+// ---- MXFP8 along N (V): x [BH][N][D] -> codes [BH][D][N], scales [BH][D][N/32]
+// One thread per (bh, 32-row block, d).  Lanes run over d, so each of the 32
+// column loads is a contiguous 128-byte read across the wave.
+__global__ void __launch_bounds__(256) k_quant_mxfp8_n(const uint16_t* __restrict__ x,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int64_t BH,
+                                                       int64_t N, int64_t D, int64_t n_valid) {
+  int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  int64_t nb = N / 32;
+  int64_t total = BH * nb * D;
+  if (t >= total) return;
+  int64_t d = t % D;
+  int64_t rest = t / D;
+  int64_t blk = rest % nb;
+  int64_t bh = rest / nb;
+  const uint16_t* col = x + (bh * N + blk * 32) * D + d;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    bool live = blk * 32 + r < n_valid;
+    v[r] = live ? bf16_to_f32(col[static_cast<int64_t>(r) * D]) : 0.0f;
+    amax = fmaxf(amax, fabsf(v[r]));
+  }
+  int e = shared_exponent(amax, 8);
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w |= e4m3_code(__builtin_ldexpf(v[4 * i + j], -e)) << (8 * j);
+    out[i] = w;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + (bh * D + d) * N + blk * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[(bh * D + d) * nb + blk] = static_cast<uint8_t>(e + 127);
+}
+
+// ---- fp16, same layout: one thread per 8 elements -----------------------------
+__global__ void __launch_bounds__(256) k_to_f16_d(const uint16_t* __restrict__ x,
+                                                  uint16_t* __restrict__ y, int64_t n8, int64_t D,
+                                                  int64_t N, int64_t n_valid) {
+  int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= n8) return;
+  int64_t row = (t * 8) / D;
+  bool live = (row % N) < n_valid;
+  uint4 v = live ? reinterpret_cast<const uint4*>(x)[t] : make_uint4(0, 0, 0, 0);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    _Float16 lo = static_cast<_Float16>(__uint_as_float(w[i] << 16));
+    _Float16 hi = static_cast<_Float16>(__uint_as_float(w[i] & 0xFFFF0000u));
+    o[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+  }
+  reinterpret_cast<uint4*>(y)[t] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---- fp16 transposed: x [BH][N][D] -> y [BH][D][N], 32x32 tiles via LDS --------
+__global__ void __launch_bounds__(256) k_to_f16_n(const uint16_t* __restrict__ x,
+                                                  uint16_t* __restrict__ y, int64_t N, int64_t D,
+                                                  int64_t n_valid) {
+  __shared__ uint16_t tile[32][33];
+  int64_t bh = blockIdx.z;
+  int64_t n0 = static_cast<int64_t>(blockIdx.x) * 32;
+  int64_t d0 = static_cast<int64_t>(blockIdx.y) * 32;
+  int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 8 rows of 32 per pass
+  for (int r = ty; r < 32; r += 8) {
+    int64_t n = n0 + r;
+    float f = n < n_valid ? bf16_to_f32(x[(bh * N + n) * D + d0 + tx]) : 0.0f;
+    tile[r][tx] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) y[(bh * D + d0 + r) * N + n0 + tx] = tile[tx][r];
+}
+
+// ---- INT4 asymmetric, groups of 32 along D: one thread per group ----------------
+__global__ void __launch_bounds__(256) k_quant_int4_d(const uint16_t* __restrict__ x,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint16_t* __restrict__ scales,
+                                                      uint16_t* __restrict__ zeros,
+                                                      int64_t n_groups, int64_t groups_per_row,
+                                                      int64_t N, int64_t n_valid) {
+  int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= n_groups) return;
+  int64_t row = g / groups_per_row;
+  bool live = (row % N) < n_valid;
+  const uint4* src = reinterpret_cast<const uint4*>(x + g * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 q = live ? src[i] : make_uint4(0, 0, 0, 0);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+  float s32 = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+  _Float16 sh = static_cast<_Float16>(s32);
+  _Float16 zh = static_cast<_Float16>(mn);
+  float s = static_cast<float>(sh), z = static_cast<float>(zh);
+  uint32_t packed[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t c = 0;
+    if (s != 0.0f) {
+      float q = __builtin_rintf(__fdiv_rn(__fsub_rn(v[i], z), s));
+      q = fminf(fmaxf(q, 0.0f), 15.0f);
+      c = static_cast<uint32_t>(q);
+    }
+    packed[i / 8] |= c << (4 * (i % 8));
+  }
+  reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scales[g] = __builtin_bit_cast(uint16_t, sh);
+  zeros[g] = __builtin_bit_cast(uint16_t, zh);
+}
+
+inline unsigned grid_for(int64_t n, int threads) {
+  return static_cast<unsigned>(ceil_div(n, threads));
+}
+
+}  // namespace
+}  // namespace mxq
+
+using namespace mxq;
+
+extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int64_t N, int64_t D,
+                                   int64_t n_valid, mxq_format fmt, mxq_axis axis, void* codes,
+                                   void* scales, uint16_t* zeros, mxq_stream_t stream) {
+  MXQ_REQUIRE(x != nullptr && codes != nullptr, MXQ_EINVAL, "mxq_quantize: null input or codes");
+  MXQ_REQUIRE(B >= 0 && H >= 0 && N >= 0 && D > 0, MXQ_EINVAL, "mxq_quantize: negative shape");
+  MXQ_REQUIRE(n_valid >= 0 && n_valid <= N, MXQ_EINVAL, "mxq_quantize: n_valid must be in [0, N]");
+  MXQ_REQUIRE(D % 32 == 0, MXQ_EUNSUPPORTED, "mxq_quantize: D must be a multiple of 32");
+  MXQ_REQUIRE(axis == MXQ_AXIS_D || axis == MXQ_AXIS_N, MXQ_EINVAL, "mxq_quantize: bad axis");
+  MXQ_REQUIRE(axis == MXQ_AXIS_D || N % 32 == 0, MXQ_EUNSUPPORTED,
+              "mxq_quantize: AXIS_N needs N to be a multiple of 32");
+  hipStream_t st = as_stream(stream);
+  const int64_t BH = B * H;
+  const int64_t rows = BH * N;
+  if (rows == 0) return MXQ_OK;
+  if (fmt == MXQ_MXFP4_E2M1 && axis == MXQ_AXIS_D) {
+    MXQ_REQUIRE(scales != nullptr && zeros == nullptr, MXQ_EINVAL,
+                "mxq_quantize MXFP4: scales required, zeros must be NULL");
+    int64_t nb = rows * (D / 32);
+    hipLaunchKernelGGL(k_quant_mxfp4_d, dim3(grid_for(nb, 256)), dim3(256), 0, st, x,
+                       static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), nb, D / 32, N,
+                       n_valid);
+    return check_launch("k_quant_mxfp4_d");
+  }
+  if (fmt == MXQ_MXFP8_E4M3 && axis == MXQ_AXIS_N) {
+    MXQ_REQUIRE(scales != nullptr && zeros == nullptr, MXQ_EINVAL,
+                "mxq_quantize MXFP8: scales required, zeros must be NULL");
+    MXQ_REQUIRE(N % 128 == 0, MXQ_EUNSUPPORTED, "mxq_quantize MXFP8 AXIS_N: N must be a multiple of 128");
+    int64_t total = BH * (N / 32) * D;
+    hipLaunchKernelGGL(k_quant_mxfp8_n, dim3(grid_for(total, 256)), dim3(256), 0, st, x,
+                       static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), BH, N, D, n_valid);
+    return check_launch("k_quant_mxfp8_n");
+  }
+  if (fmt == MXQ_FP16) {
+    MXQ_REQUIRE(scales == nullptr && zeros == nullptr, MXQ_EINVAL,
+                "mxq_quantize FP16: scales and zeros must be NULL");
+    if (axis == MXQ_AXIS_D) {
+      int64_t n8 = rows * D / 8;
+      hipLaunchKernelGGL(k_to_f16_d, dim3(grid_for(n8, 256)), dim3(256), 0, st, x,
+                         static_cast<uint16_t*>(codes), n8, D, N, n_valid);
+      return check_launch("k_to_f16_d");
+    }
+    MXQ_REQUIRE(BH <= 65535, MXQ_EUNSUPPORTED, "mxq_quantize FP16 AXIS_N: B*H must be <= 65535");
+    hipLaunchKernelGGL(k_to_f16_n, dim3(static_cast<unsigned>(N / 32), static_cast<unsigned>(D / 32),
+                                        static_cast<unsigned>(BH)),
+                       dim3(256), 0, st, x, static_cast<uint16_t*>(codes), N, D, n_valid);
+    return check_launch("k_to_f16_n");
+  }
+  if (fmt == MXQ_INT4_ASYM_G32 && axis == MXQ_AXIS_D) {
+    MXQ_REQUIRE(scales != nullptr && zeros != nullptr, MXQ_EINVAL,
+                "mxq_quantize INT4: scales and zeros required");
+    int64_t ng = rows * (D / 32);
+    hipLaunchKernelGGL(k_quant_int4_d, dim3(grid_for(ng, 256)), dim3(256), 0, st, x,
+                       static_cast<uint8_t*>(codes), static_cast<uint16_t*>(scales), zeros, ng,
+                       D / 32, N, n_valid);
+    return check_launch("k_quant_int4_d");
+  }
+  return fail(MXQ_EUNSUPPORTED, "mxq_quantize: unsupported (format, axis) pair");
+}

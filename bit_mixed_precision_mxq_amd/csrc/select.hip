@@ -1,0 +1,184 @@
+// attn_select_blocks: stage 1 of ThriftAttention (abstract) -- a cheap
+// heuristic picks the query-key tiles that run in FP16; HyQuant (abstract)
+// adds the sink column and the local window as always-high-precision tiles.
+//
+// Two kernels:
+//  k_tile_means : fp32 mean of every query tile (per query head) and key tile
+//                 (per kv head); one thread per (tile, d), rows summed in
+//                 ascending order, then one correctly rounded division.
+//  k_select     : one workgroup per (b, query head, query tile): scores of all
+//                 key tiles against the tile mean (sequential over d, rounded
+//                 product then rounded sum, never fused), forced tiles, and the
+//                 top-k by rank counting with ties to the lower index.
+// The fixed operation order makes the result bit-identical to a plain CPU
+// evaluation of the same formula.
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+constexpr int kMaxKeyTiles = 2048;
+
+__global__ void k_tile_means(const uint16_t* __restrict__ x, float* __restrict__ mean, int N,
+                             int D, int T, int n_valid, int n_tiles) {
+  int d = threadIdx.x;
+  int tile = blockIdx.x;
+  int64_t bh = blockIdx.y;
+  if (d >= D) return;
+  const uint16_t* base = x + (bh * N + static_cast<int64_t>(tile) * T) * D + d;
+  float acc = 0.0f;
+  int cnt = 0;
+  for (int r = 0; r < T; ++r) {
+    if (tile * T + r < n_valid) {
+      acc = __fadd_rn(acc, bf16_to_f32(base[static_cast<int64_t>(r) * D]));
+      ++cnt;
+    }
+  }
+  float m = cnt > 0 ? __fdiv_rn(acc, static_cast<float>(cnt)) : 0.0f;
+  mean[(bh * n_tiles + tile) * D + d] = m;
+}
+
+struct SelectArgs {
+  const float* qmean;  // [B*Hq][n_qt][D]
+  const float* kmean;  // [B*Hkv][n_kt][D]
+  uint32_t* mask;      // [B*Hq][n_qt][words]
+  int32_t* n_fp16;     // [B*Hq][n_qt] or null
+  float* scores;       // [B*Hq][n_qt][n_kt] or null
+  int Hq, Hkv, N, n_valid, D, Bq, Bk, causal, n_qt, n_kt, words;
+  int topk, ratio_num, ratio_den, sink_tiles, local_tiles;
+};
+
+__global__ void __launch_bounds__(256) k_select(SelectArgs a) {
+  __shared__ float s_score[kMaxKeyTiles];
+  __shared__ float s_q[256];
+  __shared__ uint32_t s_mask[kMaxKeyTiles / 32];
+  __shared__ int s_count;
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
+  const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + h / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x;
+
+  for (int d = tid; d < a.D; d += blockDim.x) s_q[d] = a.qmean[(bhq * a.n_qt + i) * a.D + d];
+  for (int w = tid; w < a.words; w += blockDim.x) s_mask[w] = 0u;
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+
+  // scores of every key tile (also invalid ones, for inspection)
+  for (int j = tid; j < a.n_kt; j += blockDim.x) {
+    const float* km = a.kmean + (bhk * a.n_kt + j) * a.D;
+    float acc = 0.0f;
+    for (int d = 0; d < a.D; ++d) acc = __fadd_rn(acc, __fmul_rn(s_q[d], km[d]));
+    s_score[j] = acc;
+    if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+  }
+  __syncthreads();
+
+  const int qs = i * a.Bq;
+  if (qs < a.n_valid) {
+    const int qe = min(qs + a.Bq, a.n_valid) - 1;
+    int last = (a.n_valid - 1) / a.Bk;
+    if (a.causal) last = min(last, qe / a.Bk);
+    const int nvt = last + 1;
+    const int lo = qs - (a.local_tiles - 1) * a.Bk;
+    auto forced = [&](int j) {
+      bool sink = j < a.sink_tiles;
+      bool local = a.local_tiles >= 1 && (j + 1) * a.Bk - 1 >= lo && j * a.Bk <= qe;
+      return sink || local;
+    };
+    int n_forced = 0;
+    for (int j = 0; j < nvt; ++j) n_forced += forced(j) ? 1 : 0;
+    const int n_cand = nvt - n_forced;
+    int64_t k;
+    if (a.topk >= 0) k = a.topk;
+    else k = (static_cast<int64_t>(a.ratio_num) * nvt + a.ratio_den - 1) / a.ratio_den;
+    if (k > n_cand) k = n_cand;
+    for (int j = tid; j < nvt; j += blockDim.x) {
+      bool take = forced(j);
+      if (!take && k > 0) {
+        const float sj = s_score[j];
+        int rank = 0;
+        for (int jj = 0; jj < nvt; ++jj) {
+          if (jj == j || forced(jj)) continue;
+          const float so = s_score[jj];
+          rank += (so > sj || (so == sj && jj < j)) ? 1 : 0;
+        }
+        take = rank < k;
+      }
+      if (take) {
+        atomicOr(&s_mask[j / 32], 1u << (j % 32));
+        atomicAdd(&s_count, 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int w = tid; w < a.words; w += blockDim.x) a.mask[(bhq * a.n_qt + i) * a.words + w] = s_mask[w];
+  if (tid == 0 && a.n_fp16) a.n_fp16[bhq * a.n_qt + i] = s_count;
+}
+
+mxq_status validate_shape(const mxq_attn_shape* s) {
+  MXQ_REQUIRE(s != nullptr, MXQ_EINVAL, "shape is NULL");
+  MXQ_REQUIRE(s->B >= 1 && s->Hq >= 1 && s->Hkv >= 1 && s->N >= 1, MXQ_EINVAL,
+              "shape: B, Hq, Hkv, N must be >= 1");
+  MXQ_REQUIRE(s->Hq % s->Hkv == 0, MXQ_EINVAL, "shape: Hq must be a multiple of Hkv");
+  MXQ_REQUIRE(s->n_valid >= 1 && s->n_valid <= s->N, MXQ_EINVAL, "shape: n_valid must be in [1, N]");
+  MXQ_REQUIRE(s->D == 64 || s->D == 128, MXQ_EUNSUPPORTED, "shape: D must be 64 or 128");
+  MXQ_REQUIRE(s->Bk == 64, MXQ_EUNSUPPORTED, "shape: Bk must be 64");
+  MXQ_REQUIRE(s->Bq == 64 || s->Bq == 128, MXQ_EUNSUPPORTED, "shape: Bq must be 64 or 128");
+  MXQ_REQUIRE(s->N % 128 == 0, MXQ_EUNSUPPORTED, "shape: N must be a multiple of 128");
+  MXQ_REQUIRE(s->N / s->Bk <= kMaxKeyTiles, MXQ_EUNSUPPORTED, "shape: at most 2048 key tiles");
+  MXQ_REQUIRE(s->B <= 65535 && s->Hq <= 65535, MXQ_EUNSUPPORTED, "shape: B and Hq must be <= 65535");
+  MXQ_REQUIRE(s->causal == 0 || s->causal == 1, MXQ_EINVAL, "shape: causal must be 0 or 1");
+  return MXQ_OK;
+}
+
+}  // namespace
+
+mxq_status validate_attn_shape(const mxq_attn_shape* s) { return validate_shape(s); }
+
+}  // namespace mxq
+
+using namespace mxq;
+
+extern "C" size_t attn_select_blocks_workspace(const mxq_attn_shape* s) {
+  if (s == nullptr || s->Bq <= 0 || s->Bk <= 0) return 0;
+  size_t n_qt = static_cast<size_t>(s->N / s->Bq), n_kt = static_cast<size_t>(s->N / s->Bk);
+  return (static_cast<size_t>(s->B) * s->Hq * n_qt + static_cast<size_t>(s->B) * s->Hkv * n_kt) *
+         static_cast<size_t>(s->D) * sizeof(float);
+}
+
+extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
+                                         const mxq_attn_shape* s, const mxq_select_params* p,
+                                         void* workspace, size_t ws_bytes, uint32_t* mask,
+                                         int32_t* n_fp16, float* scores, mxq_stream_t stream) {
+  mxq_status st = validate_shape(s);
+  if (st != MXQ_OK) return st;
+  MXQ_REQUIRE(p != nullptr, MXQ_EINVAL, "attn_select_blocks: params is NULL");
+  MXQ_REQUIRE(q != nullptr && k != nullptr && mask != nullptr, MXQ_EINVAL,
+              "attn_select_blocks: q, k and mask are required");
+  MXQ_REQUIRE(p->topk >= 0 || (p->ratio_num >= 0 && p->ratio_den > 0), MXQ_EINVAL,
+              "attn_select_blocks: need topk >= 0 or ratio_num >= 0 and ratio_den > 0");
+  MXQ_REQUIRE(p->sink_tiles >= 0 && p->local_tiles >= 0, MXQ_EINVAL,
+              "attn_select_blocks: sink_tiles and local_tiles must be >= 0");
+  MXQ_REQUIRE(workspace != nullptr && ws_bytes >= attn_select_blocks_workspace(s), MXQ_EINVAL,
+              "attn_select_blocks: workspace too small");
+  hipStream_t strm = as_stream(stream);
+  const int n_qt = s->N / s->Bq, n_kt = s->N / s->Bk;
+  float* qmean = static_cast<float*>(workspace);
+  float* kmean = qmean + static_cast<size_t>(s->B) * s->Hq * n_qt * s->D;
+  hipLaunchKernelGGL(k_tile_means, dim3(n_qt, s->B * s->Hq), dim3(s->D), 0, strm, q, qmean, s->N,
+                     s->D, s->Bq, s->n_valid, n_qt);
+  if ((st = check_launch("k_tile_means(q)")) != MXQ_OK) return st;
+  hipLaunchKernelGGL(k_tile_means, dim3(n_kt, s->B * s->Hkv), dim3(s->D), 0, strm, k, kmean, s->N,
+                     s->D, s->Bk, s->n_valid, n_kt);
+  if ((st = check_launch("k_tile_means(k)")) != MXQ_OK) return st;
+  SelectArgs a;
+  a.qmean = qmean; a.kmean = kmean; a.mask = mask; a.n_fp16 = n_fp16; a.scores = scores;
+  a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.D = s->D; a.Bq = s->Bq;
+  a.Bk = s->Bk; a.causal = s->causal; a.n_qt = n_qt; a.n_kt = n_kt; a.words = (n_kt + 31) / 32;
+  a.topk = p->topk; a.ratio_num = p->ratio_num; a.ratio_den = p->ratio_den;
+  a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
+  hipLaunchKernelGGL(k_select, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
+  return check_launch("k_select");
+}

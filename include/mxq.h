@@ -1,0 +1,213 @@
+/*
+ * mxq.h -- block-scaled low-bit attention with selective mixed precision on
+ * AMD Instinct MI355X (gfx950).  C ABI of libmxq.so.
+ *
+ * The method (what each call computes) comes from these pages:
+ *  - ThriftAttention: Selective Mixed Precision for Long-Context FP4 Attention
+ *    (abstract): stage 1, a cheap heuristic picks a few important query-key
+ *    block pairs for FP16; stage 2 computes those blocks in FP16 and the rest
+ *    in FP4 and merges both through one online softmax.
+ *  - HyQuant: Hybrid-Precision Quantization for LLM Attention (summary and
+ *    abstract): vertical-line (sink) tokens and a local window stay in high
+ *    precision; decode compresses the KV cache and fuses dequantisation into
+ *    attention.
+ *  - "Attention Quantization" topic page (overview): block-scaled FP8/FP4 and
+ *    integer formats; softmax stays in full precision.
+ *  - NOVA-KV abstract (third page): decode reads the whole KV cache every step,
+ *    so it is bandwidth-bound.
+ * Formats follow the OCP Microscaling v1.0 rules (E2M1 / E4M3 elements with an
+ * E8M0 shared exponent per 32 elements).  Points the pages leave open are the
+ * numbered readings listed in the design doc; each call below names its readings.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays that
+ *    the caller allocates and owns.  The library never keeps them after the
+ *    call returns (work is enqueued on `stream` and runs asynchronously).
+ *  - bf16 and fp16 values travel as uint16_t bit patterns; E2M1, E4M3 and
+ *    E8M0 as uint8_t.  Two E2M1 codes share a byte: element 2k in bits 0-3,
+ *    element 2k+1 in bits 4-7.  An E8M0 byte e means 2^(e-127).
+ *  - `stream` is a hipStream_t (NULL = the default stream).
+ *  - All arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is written.  MXQ_EINVAL: bad argument (null pointer,
+ *    inconsistent shape, too-small workspace).  MXQ_EUNSUPPORTED: valid but
+ *    not implemented (head_dim other than 64/128, tile sizes, format/axis
+ *    pairs).  MXQ_EHIP: a HIP launch error; mxq_last_error() has the text.
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give the same bits.
+ *  - Calls are reentrant and hold no state between calls.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* mxq_stream_t; /* a hipStream_t */
+
+typedef enum { MXQ_OK = 0, MXQ_EINVAL = 1, MXQ_EUNSUPPORTED = 2, MXQ_EHIP = 3 } mxq_status;
+
+typedef enum {
+  MXQ_MXFP4_E2M1 = 1,   /* E2M1 codes + one E8M0 scale per 32 elements      */
+  MXQ_MXFP8_E4M3 = 2,   /* E4M3 codes + one E8M0 scale per 32 elements      */
+  MXQ_INT4_ASYM_G32 = 3,/* 4-bit codes + fp16 scale and zero per 32 elements */
+  MXQ_FP16 = 4          /* plain fp16 copy                                  */
+} mxq_format;
+
+typedef enum {
+  MXQ_AXIS_D = 0, /* blocks run along head_dim; output keeps [.., N, D]         */
+  MXQ_AXIS_N = 1  /* blocks run along the sequence; output is [.., D, N]        */
+} mxq_axis;
+
+typedef enum { MXQ_MIXED = 0, MXQ_ALL_LOWBIT = 1, MXQ_ALL_FP16 = 2 } mxq_mode;
+typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_dtype;
+
+/* Attention problem.  Q is [B][Hq][N][D], K and V are [B][Hkv][N][D].
+ * N: padded length (multiple of 128); n_valid <= N: rows >= n_valid are
+ * padding (never attended to, output 0).  D in {64, 128}.  Hq % Hkv == 0; query
+ * head h uses kv head h / (Hq/Hkv).  Tiles: Bq in {64, 128} query rows by
+ * Bk = 64 keys.  causal: key index <= query index (aligned self-attention). */
+typedef struct {
+  int32_t B, Hq, Hkv, N, n_valid, D, Bq, Bk, causal;
+} mxq_attn_shape;
+
+/* Selection parameters (readings R8-R11).  Per query tile i the FP16 set is
+ * the forced tiles (key tiles j < sink_tiles, and the local window: key tiles
+ * meeting rows [i*Bq - (local_tiles-1)*Bk, last row of tile i]; none when
+ * local_tiles == 0) plus the k_i best-scoring other valid tiles, where
+ * k_i = topk if topk >= 0, else ceil(ratio_num * |valid tiles of i| / ratio_den)
+ * (integer arithmetic), capped at the number of candidates.  Ties in score go
+ * to the lower tile index. */
+typedef struct {
+  int32_t topk, ratio_num, ratio_den, sink_tiles, local_tiles;
+} mxq_select_params;
+
+/* ---------------------------------------------------------------------------
+ * mxq_quantize -- block-scaled quantisation of a bf16 tensor x [B][H][N][D].
+ * ThriftAttention abstract (block-scaled quantisation moves attention to 4-bit);
+ * readings R2-R6 (MX rules), R19 (INT4).  Rows n >= n_valid are treated as 0.
+ * Supported (fmt, axis) pairs and outputs:
+ *  MXFP4_E2M1, AXIS_D: codes u8 [B][H][N][D/2], scales u8 [B][H][N][D/32].
+ *     e = floor(log2 amax) - 2 (clamped to [-127,127]; amax 0 -> -127),
+ *     code = round-half-even of x*2^-e onto {0,.5,1,1.5,2,3,4,6} (saturating),
+ *     sign bit copies the sign of x.
+ *  MXFP8_E4M3, AXIS_N: codes u8 [B][H][D][N], scales u8 [B][H][D][N/32]
+ *     (blocks of 32 consecutive rows n per column d).  e = floor(log2 amax)-8,
+ *     code = OCP E4M3 round-half-even of x*2^-e, saturating at 448.
+ *  FP16, AXIS_D: codes u16 [B][H][N][D];  FP16, AXIS_N: codes u16 [B][H][D][N].
+ *  INT4_ASYM_G32, AXIS_D: codes u8 [B][H][N][D/2]; scales (fp16) and zeros
+ *     (fp16) [B][H][N][D/32]:  s = fp16(fl32(max-min)/15), z = fp16(min),
+ *     code = clamp(rint(fl32(x-z)/s), 0, 15), 0 when s == 0.
+ * `zeros` must be NULL except for INT4.  N must be a multiple of 32 (128 for
+ * AXIS_N); D a multiple of 32.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t B, int64_t H, int64_t N, int64_t D,
+                        int64_t n_valid, mxq_format fmt, mxq_axis axis, void* codes, void* scales,
+                        uint16_t* zeros, mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_select_blocks -- stage 1 of ThriftAttention (abstract): choose the
+ * query-key tiles that run in FP16.  Importance estimate (reading R8): the
+ * score of tile pair (i, j) is mean(Q rows of tile i) . mean(K rows of tile j)
+ * over the bf16 inputs, per query head, with a fixed fp32 operation order
+ * (sequential sums over rows, one division by the row count, then a sequential
+ * sum over d of rounded products, no fused multiply-add), so results are
+ * bit-identical to a plain CPU evaluation.
+ * Outputs: mask u32 [B][Hq][N/Bq][ceil((N/Bk)/32)] (bit j%32 of word j/32 set
+ * when key tile j is FP16 for that query tile); n_fp16 i32 [B][Hq][N/Bq] or
+ * NULL; scores f32 [B][Hq][N/Bq][N/Bk] or NULL (every pair, for inspection).
+ * workspace: device memory of at least attn_select_blocks_workspace(shape)
+ * bytes, caller-owned, contents undefined after the call.
+ * ------------------------------------------------------------------------- */
+size_t attn_select_blocks_workspace(const mxq_attn_shape* shape);
+mxq_status attn_select_blocks(const uint16_t* q_bf16, const uint16_t* k_bf16,
+                              const mxq_attn_shape* shape, const mxq_select_params* params,
+                              void* workspace, size_t ws_bytes, uint32_t* mask, int32_t* n_fp16,
+                              float* scores, mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_mixed_fwd -- stage 2 of ThriftAttention (abstract): one fused pass over
+ * the key tiles of each query tile, ascending; selected tiles in FP16, the
+ * rest low-bit, merged through one online softmax.  Readings R7, R12-R18:
+ *  low-bit tile: S = Q_mxfp4 . K_mxfp4 (exactly rounded fp32 whenever the
+ *    per-pair spread of block exponents is <= 18), P = E4M3(2^xq) * 2^-8 with
+ *    xq = fl32(S*c + 6152 - m) - 6144 (the exponent on a 2^-11 grid),
+ *    V from the MXFP8 copy;
+ *  FP16 tile: S = Q_bf16 . K_bf16 (fp32 accumulate), P = fp16(2^(S*c - m)),
+ *    V from the fp16 copy;
+ *  c = fl32(scale * log2 e); m = running max over tiles so far of
+ *  ceil(fl32(rowmax(S_tile) * c)); O and l (the sum of the same quantised P)
+ *  are rescaled by 2^(m_old - m_new); out = O / l, lse = ln2 * (m + log2 l).
+ * Inputs (from mxq_quantize): q_codes/q_scales and k_codes/k_scales MXFP4
+ * AXIS_D; v_codes/v_scales MXFP8 AXIS_N; q_bf16, k_bf16 the original bf16
+ * [..][N][D]; v_f16t fp16 AXIS_N ([..][D][N]).  The bf16/fp16 operands may be
+ * NULL in MXQ_ALL_LOWBIT mode; the low-bit operands may be NULL in
+ * MXQ_ALL_FP16 mode.  mask (from attn_select_blocks) is needed in MXQ_MIXED
+ * mode only.  softmax_scale <= 0 means 1/sqrt(D).
+ * out: [B][Hq][N][D] fp32 or bf16; lse: f32 [B][Hq][N] or NULL (natural log).
+ * Rows >= n_valid: out 0, lse -inf.
+ * ------------------------------------------------------------------------- */
+mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
+                          const uint8_t* k_codes, const uint8_t* k_scales,
+                          const uint8_t* v_codes, const uint8_t* v_scales,
+                          const uint16_t* q_bf16, const uint16_t* k_bf16, const uint16_t* v_f16t,
+                          const uint32_t* mask, const mxq_attn_shape* shape, float softmax_scale,
+                          mxq_mode mode, void* out, mxq_out_dtype out_dtype, float* lse,
+                          mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Quantised KV cache for decode (HyQuant summary/abstract; readings R19, R20).
+ * Sequence b has seq_len[b] tokens (device array, 1 <= seq_len[b] <=
+ * max_seq_len <= L_cap).  Token t of kv head h is read from
+ *   - k_sink/v_sink   fp16 [B][Hkv][n_sink][D]      when t < n_sink,
+ *   - k_recent/v_recent fp16 [B][Hkv][n_recent][D]  when t >= seq_len[b]-n_recent
+ *     (row r holds token seq_len[b]-n_recent+r),
+ *   - otherwise the INT4 arrays: codes u8 [B][Hkv][L_cap][D/2], scale and zero
+ *     fp16 [B][Hkv][L_cap][D/32] (mxq_quantize INT4_ASYM_G32 layout), with
+ *     x = fl32(code*s + z).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint16_t* v_scale;
+  const uint16_t* v_zero;
+  const uint16_t* k_sink;
+  const uint16_t* v_sink;
+  const uint16_t* k_recent;
+  const uint16_t* v_recent;
+  const int32_t* seq_len;
+  int32_t L_cap, n_sink, n_recent;
+} mxq_kv_cache;
+
+/* ---------------------------------------------------------------------------
+ * attn_quantkv_decode -- one decode step: for each sequence b and query head
+ * h, softmax(q . k * scale) . v over the cache (fp32 softmax and accumulation,
+ * P not quantised), with dequantisation fused into the attention (HyQuant
+ * abstract).  The keys of each (b, kv head) are split into num_splits ranges
+ * processed independently and merged in ascending split order (reading R23);
+ * num_splits 0 picks a value.  q: bf16 [B][Hq][D]; out: f32 [B][Hq][D].
+ * workspace: at least attn_quantkv_decode_workspace(...) bytes (caller-owned).
+ * D must be 128 (or 64); Hq / Hkv must be <= 16.
+ * ------------------------------------------------------------------------- */
+size_t attn_quantkv_decode_workspace(int32_t B, int32_t Hq, int32_t D, int32_t num_splits,
+                                     int32_t max_seq_len);
+mxq_status attn_quantkv_decode(const uint16_t* q_bf16, const mxq_kv_cache* cache, int32_t B,
+                               int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
+                               float softmax_scale, int32_t num_splits, void* workspace,
+                               size_t ws_bytes, float* out, mxq_stream_t stream);
+
+/* Status text, and the message of the last failing call on this thread. */
+const char* mxq_status_string(mxq_status s);
+const char* mxq_last_error(void);
+/* Library version string. */
+const char* mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

@@ -1,0 +1,54 @@
+"""Shared helpers for the GPU parity tests (not a test module)."""
+
+import numpy as np
+import pytest
+
+try:
+    import torch
+except Exception:  # pragma: no cover
+    torch = None
+
+
+def gpu_or_skip():
+    if torch is None or not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_mixed_precision_mxq_amd as mxq
+
+    mxq.load_library()  # raises if the library is missing: no silent fallback
+    return mxq
+
+
+def bf16_dev(bits: np.ndarray):
+    """uint16 bf16 bit patterns -> torch.bfloat16 tensor on cuda:0 (bit copy)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to("cuda:0")
+
+
+def u8(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint8)
+
+
+def u16(t) -> np.ndarray:
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u32(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def random_bf16(shape, seed, scale=1.0, specials=True):
+    """N(0,1)*scale bf16 bits, with some special values mixed in: zeros,
+    negative zeros, subnormals, large and tiny magnitudes, exact E2M1 grid
+    points and exact midpoints."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    if specials:
+        flat = x.reshape(-1)
+        n = flat.size
+        idx = rng.choice(n, size=max(1, n // 50), replace=False)
+        pool = np.array([0.0, -0.0, 1e-40, -3e-39, 6.0, 5.0, -2.5, 0.75, 1.25, 3.5, 448.0, 464.0,
+                         1e30, -7e-20, 0.25, -0.25, 1.75], dtype=np.float32)
+        flat[idx] = pool[rng.integers(0, len(pool), size=len(idx))]
+    b = x.view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)

@@ -1,0 +1,93 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mxq.h declares, sizes workspaces, and rejects bad arguments on the
+host before anything is launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+LIB = os.path.join(ROOT, "bit_mixed_precision_mxq_amd", "libmxq.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*((?:mxq|attn)_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmxq.so is not built (run __graft_entry__.build())")
+    import bit_mixed_precision_mxq_amd as mxq
+
+    return mxq, mxq.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert {"mxq_quantize", "attn_select_blocks", "attn_mixed_fwd", "attn_quantkv_decode"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = declared - exported
+    assert not missing, missing
+    mxq, so = lib
+    for name in declared:
+        assert hasattr(so, name)
+    assert set(mxq.EXPORTED) == declared
+
+
+def test_status_strings_and_version(lib):
+    mxq, so = lib
+    assert so.mxq_status_string(0) == b"MXQ_OK"
+    assert b"EINVAL" in so.mxq_status_string(1)
+    assert b"gfx950" in so.mxq_version()
+
+
+def test_workspace_sizes(lib):
+    mxq, so = lib
+    s = mxq.AttnShape(1, 32, 8, 8192, 8192, 128, 128, 64, 1)
+    n = so.attn_select_blocks_workspace(ctypes.byref(s))
+    assert n == (1 * 32 * 64 + 1 * 8 * 128) * 128 * 4
+    assert so.attn_quantkv_decode_workspace(64, 32, 128, 16, 32768) == 64 * 32 * 16 * 130 * 4
+    assert so.attn_quantkv_decode_workspace(64, 32, 128, 0, 32768) == 64 * 32 * 16 * 130 * 4
+
+
+def test_host_validation_rejects_before_launch(lib):
+    mxq, so = lib
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    st = so.mxq_quantize(None, 1, 1, 64, 64, 64, mxq.MXQ_MXFP4_E2M1, mxq.MXQ_AXIS_D, fake, fake, None, None)
+    assert st == mxq.MXQ_EINVAL and b"null" in so.mxq_last_error()
+    st = so.mxq_quantize(fake, 1, 1, 64, 48, 64, mxq.MXQ_MXFP4_E2M1, mxq.MXQ_AXIS_D, fake, fake, None, None)
+    assert st == mxq.MXQ_EUNSUPPORTED
+    st = so.mxq_quantize(fake, 1, 1, 64, 64, 65, mxq.MXQ_MXFP4_E2M1, mxq.MXQ_AXIS_D, fake, fake, None, None)
+    assert st == mxq.MXQ_EINVAL
+    st = so.mxq_quantize(fake, 1, 1, 64, 64, 64, mxq.MXQ_MXFP8_E4M3, mxq.MXQ_AXIS_D, fake, fake, None, None)
+    assert st == mxq.MXQ_EUNSUPPORTED
+    bad_d = mxq.AttnShape(1, 2, 2, 256, 256, 96, 64, 64, 0)
+    p = mxq.SelectParams(1, 0, 1, 0, 0)
+    st = so.attn_select_blocks(fake, fake, ctypes.byref(bad_d), ctypes.byref(p), fake, 1 << 20, fake, None, None, None)
+    assert st == mxq.MXQ_EUNSUPPORTED
+    gqa = mxq.AttnShape(1, 3, 2, 256, 256, 64, 64, 64, 0)
+    st = so.attn_select_blocks(fake, fake, ctypes.byref(gqa), ctypes.byref(p), fake, 1 << 20, fake, None, None, None)
+    assert st == mxq.MXQ_EINVAL
+    ok = mxq.AttnShape(1, 2, 2, 256, 256, 64, 64, 64, 0)
+    st = so.attn_select_blocks(fake, fake, ctypes.byref(ok), ctypes.byref(p), fake, 16, fake, None, None, None)
+    assert st == mxq.MXQ_EINVAL and b"workspace" in so.mxq_last_error()
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, ctypes.byref(ok), 0.0,
+                           mxq.MXQ_MIXED, fake, 0, None, None)
+    assert st == mxq.MXQ_EINVAL and b"mask" in so.mxq_last_error()
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, fake, ctypes.byref(ok), 0.0,
+                           mxq.MXQ_ALL_FP16, fake, 0, None, None)
+    assert st == mxq.MXQ_EINVAL
+    kv = mxq.KVCache()
+    st = so.attn_quantkv_decode(fake, ctypes.byref(kv), 1, 8, 2, 128, 64, 0.0, 0, fake, 1 << 20, fake, None)
+    assert st == mxq.MXQ_EINVAL
+    st = so.attn_quantkv_decode(fake, ctypes.byref(kv), 1, 8, 2, 64, 64, 0.0, 0, fake, 1 << 20, fake, None)
+    assert st == mxq.MXQ_EUNSUPPORTED

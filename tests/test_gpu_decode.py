@@ -1,0 +1,102 @@
+"""GPU parity: attn_quantkv_decode against the oracle (max-abs <= 5e-3)."""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import bf16_dev, gpu_or_skip
+import mxq_inputs
+from oracle import decode as Dm
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+def _run(mxq, d, n_sink, n_recent, num_splits=0):
+    import torch
+
+    k, v, q = bf16_dev(d["k"]), bf16_dev(d["v"]), bf16_dev(d["q"])
+    lens = d["seq_len"]
+    B = len(lens)
+    if n_recent > 0:
+        krec = torch.stack([k[b, :, lens[b] - n_recent:lens[b]] for b in range(B)])
+        vrec = torch.stack([v[b, :, lens[b] - n_recent:lens[b]] for b in range(B)])
+    else:
+        krec = vrec = None
+    cache = mxq.build_quant_kv_cache(k, v, torch.from_numpy(lens).to("cuda:0"), n_sink, n_recent, krec, vrec)
+    out = mxq.attn_quantkv_decode(q, cache, d["Hkv"], int(lens.max()), num_splits=num_splits)
+    return out.cpu().numpy(), cache
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 16])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_small_ragged(num_splits, G):
+    mxq = gpu_or_skip()
+    Hkv = 2
+    lens = [1000, 257, 193, 64 + 128 + 5]
+    d = mxq_inputs.make_decode(dict(B=4, L=1024, Hq=Hkv * G, Hkv=Hkv, D=128, n_sink=64, n_recent=128, seed=9,
+                                    seq_len=lens), threads=4)
+    out, _ = _run(mxq, d, 64, 128, num_splits)
+    ref = Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 64, 128),
+                             d["seq_len"], 64, 128)
+    err = np.abs(out - ref).max()
+    assert err <= TOL, err
+    assert err <= 1e-4, f"fp32 path should be far below the tolerance: {err}"
+
+
+def test_all_fp16_and_no_fp16_regions():
+    mxq = gpu_or_skip()
+    d = mxq_inputs.make_decode(dict(B=2, L=256, Hq=8, Hkv=2, D=128, n_sink=64, n_recent=128, seed=3,
+                                    seq_len=[150, 192]), threads=2)
+    out, _ = _run(mxq, d, 64, 128)      # every token in the fp16 copies
+    ref = Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 64, 128), d["seq_len"], 64, 128)
+    assert np.abs(out - ref).max() <= 1e-4
+    out0, _ = _run(mxq, d, 0, 0)         # every token INT4
+    ref0 = Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 0, 0), d["seq_len"], 0, 0)
+    assert np.abs(out0 - ref0).max() <= 1e-4
+
+
+def test_cache_build_matches_oracle():
+    mxq = gpu_or_skip()
+    from gpu_helpers import u8, u16
+    from oracle.formats import pack_nibbles
+
+    d = mxq_inputs.make_decode(dict(B=2, L=512, Hq=8, Hkv=2, D=128, n_sink=64, n_recent=128, seed=5,
+                                    seq_len=[512, 400]), threads=2)
+    _, cache = _run(mxq, d, 64, 128)
+    ref = Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 64, 128)
+    assert np.array_equal(u8(cache.k_codes), pack_nibbles(ref["k_codes"]))
+    assert np.array_equal(u8(cache.v_codes), pack_nibbles(ref["v_codes"]))
+    assert np.array_equal(u16(cache.k_scale), ref["k_scale"].view(np.uint16))
+    assert np.array_equal(u16(cache.v_zero), ref["v_zero"].view(np.uint16))
+    assert np.array_equal(u16(cache.k_sink), ref["k_sink"].view(np.uint16))
+    assert np.array_equal(u16(cache.v_recent), ref["v_recent"].view(np.uint16))
+
+
+def test_decode_workload_shape_sampled():
+    """The decode workload's per-sequence shape (32768 cached tokens, Hq=32,
+    Hkv=8, D=128) for 4 sequences; the oracle checks 2 of them."""
+    mxq = gpu_or_skip()
+    d = mxq_inputs.make_decode("decode", seqs=range(4), B=4)
+    out, _ = _run(mxq, d, 64, 128)
+    sub = dict(d, k=d["k"][:2], v=d["v"][:2])
+    ref = Dm.attn_decode_ref(d["q"][:2], Dm.build_kv_cache_ref(sub["k"], sub["v"], d["seq_len"][:2], 64, 128),
+                             d["seq_len"][:2], 64, 128)
+    err = np.abs(out[:2] - ref).max()
+    assert err <= TOL, err
+    print(f"decode full-length max-abs {err:.3e}")
+
+
+def test_error_paths():
+    mxq = gpu_or_skip()
+    import torch
+
+    d = mxq_inputs.make_decode(dict(B=1, L=256, Hq=16, Hkv=2, D=128, n_sink=0, n_recent=0, seed=1), threads=1)
+    k, v, q = bf16_dev(d["k"]), bf16_dev(d["v"]), bf16_dev(d["q"])
+    cache = mxq.build_quant_kv_cache(k, v, torch.tensor([256], dtype=torch.int32, device="cuda:0"), 0, 0)
+    with pytest.raises(mxq.MxqError) as ei:        # G = 8 is not built
+        mxq.attn_quantkv_decode(q, cache, 2, 256)
+    assert ei.value.status == mxq.MXQ_EUNSUPPORTED
+    with pytest.raises(mxq.MxqError) as ei:        # max_seq_len above the cache capacity
+        mxq.attn_quantkv_decode(q[:, :8].contiguous(), cache, 4, 4096)
+    assert ei.value.status == mxq.MXQ_EINVAL

@@ -1,0 +1,78 @@
+"""GPU parity: attn_select_blocks masks, counts and scores are bit-exact."""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import bf16_dev, gpu_or_skip, u32
+import mxq_inputs
+from oracle import select as S
+from oracle.formats import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(mxq, cfg, want_scores=True):
+    shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"],
+                      cfg["Bk"], cfg["causal"])
+    mask, nfp, sc = mxq.attn_select_blocks(bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), shape, topk=cfg["topk"],
+                                           ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                                           sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
+                                           want_scores=want_scores)
+    return u32(mask), nfp.cpu().numpy(), (sc.cpu().numpy() if sc is not None else None)
+
+
+def _ref(cfg):
+    return S.select_blocks(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"], cfg["topk"],
+                           cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"], cfg["local_tiles"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "vit"])
+def test_configured_workloads_bit_exact(name):
+    mxq = gpu_or_skip()
+    # vit: a 16-image batch of the same recipe (images are independent)
+    cfg = mxq_inputs.make_prefill(name, **({"B": 16} if name == "vit" else {}))
+    mask, nfp, sc = _run(mxq, cfg)
+    rm, rn, rs = _ref(cfg)
+    assert np.array_equal(sc.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(mask, rm)
+    assert np.array_equal(nfp, rn)
+
+
+def test_long32k_counts_and_sampled_rows():
+    mxq = gpu_or_skip()
+    cfg = mxq_inputs.make_prefill("long32k")
+    mask, nfp, _ = _run(mxq, cfg, want_scores=False)
+    assert int(nfp.sum()) == 32 * 4933
+    # full oracle on 4 of the 32 heads (one per kv group pair)
+    for h in (0, 9, 18, 31):
+        sub = dict(cfg, q=cfg["q"][:, h:h + 1], k=cfg["k"][:, h // 4:h // 4 + 1], Hq=1, Hkv=1)
+        rm, rn, _ = _ref(sub)
+        assert np.array_equal(mask[:, h:h + 1], rm)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_gqa_and_constructed_ties(causal):
+    mxq = gpu_or_skip()
+    rng = np.random.default_rng(4)
+    N, D = 1024, 64
+    q = rng.standard_normal((2, 4, N, D)).astype(np.float32)
+    k = rng.standard_normal((2, 2, N, D)).astype(np.float32)
+    k[:, :, 256:512] = k[:, :, 0:256]          # repeated key tiles -> equal scores
+    k[1] = np.round(k[1])                       # coarse values -> more ties
+    q[1] = 1.0
+    cfg = dict(B=2, Hq=4, Hkv=2, N=N, n_valid=1000, D=D, Bq=128, Bk=64, causal=causal, topk=-1,
+               ratio_num=30, ratio_den=100, sink_tiles=1, local_tiles=2,
+               q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k))
+    mask, nfp, sc = _run(mxq, cfg)
+    rm, rn, rs = _ref(cfg)
+    assert np.array_equal(sc.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(mask, rm)
+    assert np.array_equal(nfp, rn)
+
+
+def test_deterministic():
+    mxq = gpu_or_skip()
+    cfg = mxq_inputs.make_prefill("llama8b")
+    a = _run(mxq, cfg)
+    b = _run(mxq, cfg)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
