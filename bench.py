@@ -1,0 +1,321 @@
+"""Benchmark of the mixed-precision block-scaled attention hot path on one MI355X.
+
+One step = the whole prefill path on one batch: MXFP4 quantisation of Q and K,
+MXFP8 quantisation of V (blocks along keys) and its fp16 copy, block selection
+(5% of tiles plus the sink column and local window), and the fused
+mixed-precision attention pass.  Inputs are bf16 tensors already resident in
+HBM when the timed region starts.
+
+The JSON line reports effective attention TFLOP/s (4*D per valid query-key
+pair per head, divided by the step time), the roofline of the dominant kernel
+(attn_mixed_fwd) against the precision-weighted MFMA peak, the CPU oracle timed
+on a bounded sample, and the decode path (quantised-KV decode, KV-read GB/s
+against HBM peak).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--no-decode] [--only prefill|decode]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Published MI355X dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_FP16 = 2516.6
+PEAK_FP8 = 5033.2
+PEAK_FP4 = 10066.4
+PEAK_HBM = 8000.0
+METRIC = "effective attention TFLOPS @5% FP16 tiles (prefill); KV-read GB/s (decode)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _bf16(t_np, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(t_np).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def pair_counts(cfg, mask_np):
+    """Valid (query, key) pairs per head summed over heads, and how many of them
+    fall in FP16 tiles (read back from the selection mask)."""
+    import numpy as np
+
+    N, nv, Bq, Bk, causal = cfg["N"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"]
+    n_qt, n_kt = N // Bq, N // Bk
+    # pairs[i, j]: valid pairs inside tile (i, j)
+    q = np.arange(nv)
+    pairs = np.zeros((n_qt, n_kt), dtype=np.int64)
+    for i in range(n_qt):
+        rows = q[(q >= i * Bq) & (q < (i + 1) * Bq)]
+        if rows.size == 0:
+            continue
+        for j in range(n_kt):
+            k0, k1 = j * Bk, min((j + 1) * Bk, nv)
+            if k0 >= nv:
+                break
+            if causal:
+                cnt = np.clip(rows + 1 - k0, 0, k1 - k0).sum()
+            else:
+                cnt = rows.size * (k1 - k0)
+            pairs[i, j] = cnt
+    bits = np.unpackbits(mask_np.view(np.uint8).reshape(mask_np.shape[:-1] + (-1,)), axis=-1, bitorder="little")
+    bits = bits[..., :n_kt].astype(bool)  # [B, Hq, n_qt, n_kt]
+    heads = mask_np.shape[0] * mask_np.shape[1]
+    total = int(pairs.sum()) * heads
+    fp16 = int((bits * pairs[None, None]).sum())
+    return total, fp16
+
+
+def roofline_peak(D, total_pairs, fp16_pairs):
+    """Precision-weighted MFMA peak: FP16 pairs at the FP16 peak; low-bit pairs
+    split evenly between the FP4 QK^T and the FP8 PV contractions."""
+    f_all = 4.0 * D * total_pairs
+    f16 = 4.0 * D * fp16_pairs
+    flow = f_all - f16
+    t_roof = f16 / (PEAK_FP16 * 1e12) + flow * (0.5 / (PEAK_FP4 * 1e12) + 0.5 / (PEAK_FP8 * 1e12))
+    return f_all / t_roof / 1e12, t_roof
+
+
+def bench_prefill(args, dev):
+    import numpy as np
+    import torch
+
+    import bit_mixed_precision_mxq_amd as mxq
+    import mxq_inputs
+
+    cfg = mxq_inputs.make_prefill(args.workload)
+    q, k, v = _bf16(cfg["q"], dev), _bf16(cfg["k"], dev), _bf16(cfg["v"], dev)
+    shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
+                      cfg["causal"])
+    ws = mxq.select_workspace(shape, dev)
+    out = torch.empty((cfg["B"], cfg["Hq"], cfg["N"], cfg["D"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg["B"], cfg["Hq"], cfg["N"]), dtype=torch.float32, device=dev)
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"])
+        mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                                            sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
+                                            workspace=ws)
+        if i is not None:
+            ev_a0[i].record()
+        mxq.attn_mixed_fwd(ops, mask, shape, out_dtype=mxq.MXQ_OUT_BF16, out=out, lse=lse)
+        if i is not None:
+            ev_a1[i].record()
+        return mask
+
+    for _ in range(args.warmup):
+        mask = step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mask = step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)) / args.steps
+    mask_np = mask.cpu().numpy().view(np.uint32)
+    total, fp16 = pair_counts(cfg, mask_np)
+    flops = 4.0 * cfg["D"] * total
+    peak_eff, t_roof = roofline_peak(cfg["D"], total, fp16)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    res = dict(
+        cfg=cfg, ms_step=ms_step, attn_ms=attn_ms, flops=flops, total_pairs=total, fp16_pairs=fp16,
+        tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_attn=achieved, peak_eff=peak_eff,
+        t_roof_ms=t_roof * 1e3, mask=mask_np,
+    )
+    log(f"prefill {args.workload}: step {ms_step:.3f} ms, attn {attn_ms:.3f} ms, "
+        f"{res['tflops_step']:.1f} TFLOP/s step, {achieved:.1f} TFLOP/s attn, "
+        f"fp16 pairs {fp16 / total:.4f}, roofline {t_roof * 1e3:.3f} ms ({peak_eff:.0f} TFLOP/s eff peak)")
+    return res
+
+
+def bench_decode(args, dev):
+    import numpy as np
+    import torch
+
+    import bit_mixed_precision_mxq_amd as mxq
+    import mxq_inputs
+
+    t_gen = time.perf_counter()
+    d = mxq_inputs.make_decode("decode")
+    log(f"decode inputs generated in {time.perf_counter() - t_gen:.1f} s")
+    B, Hq, Hkv, D, L = d["B"], d["Hq"], d["Hkv"], d["D"], d["L"]
+    n_sink, n_recent = d["n_sink"], d["n_recent"]
+    lens = d["seq_len"]
+    # build the cache on the GPU one sequence at a time (bounded device memory)
+    kc = torch.empty((B, Hkv, L, D // 2), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((B, Hkv, L, D // 32), dtype=torch.float16, device=dev)
+    kz, vs, vz = torch.empty_like(ks), torch.empty_like(ks), torch.empty_like(ks)
+    k_sink = torch.empty((B, Hkv, n_sink, D), dtype=torch.float16, device=dev)
+    v_sink = torch.empty_like(k_sink)
+    k_rec = torch.empty((B, Hkv, n_recent, D), dtype=torch.float16, device=dev)
+    v_rec = torch.empty_like(k_rec)
+    for b in range(B):
+        kb = _bf16(d["k"][b:b + 1], dev)
+        vb = _bf16(d["v"][b:b + 1], dev)
+        c = mxq.build_quant_kv_cache(kb, vb, torch.tensor([int(lens[b])], dtype=torch.int32, device=dev), n_sink,
+                                     n_recent, kb[:, :, lens[b] - n_recent:lens[b]], vb[:, :, lens[b] - n_recent:lens[b]])
+        kc[b], vc[b], ks[b], kz[b], vs[b], vz[b] = c.k_codes[0], c.v_codes[0], c.k_scale[0], c.k_zero[0], c.v_scale[0], c.v_zero[0]
+        k_sink[b], v_sink[b], k_rec[b], v_rec[b] = c.k_sink[0], c.v_sink[0], c.k_recent[0], c.v_recent[0]
+    del d["k"], d["v"]
+    cache = mxq.QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec,
+                             torch.from_numpy(lens).to(dev), n_sink, n_recent)
+    q = _bf16(d["q"], dev)
+    ws = mxq.decode_workspace(B, Hq, D, 0, int(lens.max()), dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        mxq.attn_quantkv_decode(q, cache, Hkv, int(lens.max()), workspace=ws, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        mxq.attn_quantkv_decode(q, cache, Hkv, int(lens.max()), workspace=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # bytes the step must read: INT4 codes + fp16 scale/zero for the quantised
+    # tokens, fp16 rows for the sink/recent tokens, q, and the output written
+    n_fp = n_sink + n_recent
+    n_q = lens.astype(np.int64) - n_fp
+    per_tok_q = 2 * (D // 2 + 2 * 2 * (D // 32))
+    per_tok_f = 2 * D * 2
+    byts = int((n_q * per_tok_q + n_fp * per_tok_f).sum()) * Hkv + B * Hq * D * 2 + B * Hq * D * 4
+    gbs = byts / (ms * 1e-3) / 1e9
+    log(f"decode: {ms:.4f} ms/step, {byts / 1e9:.4f} GB, {gbs:.0f} GB/s ({gbs / PEAK_HBM:.3f} of HBM peak)")
+    return dict(ms=ms, bytes=byts, gbs=gbs)
+
+
+def cpu_baseline(args, pre):
+    """The oracle (test infrastructure) timed on the host on a bounded sample of
+    the same workload: the selection of one query head plus the mixed attention
+    of query tiles of that head until about 15 s of CPU work."""
+    import numpy as np
+
+    import oracle
+    from oracle import attention as A
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cfg = pre["cfg"]
+    h = 0
+    G = cfg["Hq"] // cfg["Hkv"]
+    sub = dict(q=cfg["q"][:1, h:h + 1], k=cfg["k"][:1, h // G:h // G + 1], v=cfg["v"][:1, h // G:h // G + 1])
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"], cfg["topk"],
+                             cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"], cfg["local_tiles"])
+        ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
+        n_qt = cfg["N"] // cfg["Bq"]
+        order = list(range(n_qt - 1, -1, -1))  # heavy causal tiles first; spread over the key range
+        order = order[::7] + [i for i in order if i % 7 != (n_qt - 1) % 7]
+        done, pairs = [], 0
+        mask = pre["mask"][:1, h:h + 1]
+        while order and time.perf_counter() - t0 < args.cpu_seconds:
+            i = order.pop(0)
+            A.attn_mixed_ref(sub["q"], sub["k"], sub["v"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                             mask=mask, qtiles=[i], ops=ops)
+            done.append(i)
+            r = np.arange(i * cfg["Bq"], min((i + 1) * cfg["Bq"], cfg["n_valid"]))
+            pairs += int(np.clip(r + 1, 0, cfg["n_valid"]).sum()) if cfg["causal"] else r.size * cfg["n_valid"]
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    flops = 4.0 * cfg["D"] * pairs
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"selection of query head 0 plus mixed attention of {len(done)} of its {n_qt} query tiles "
+                       f"({pairs} valid pairs), {dt:.1f} s on 1 host thread, same inputs")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "long32k", "vit"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; each (batch, kv head) is independent, so more GPUs "
+              "would shard heads with no communication, but that path is not built. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    import bit_mixed_precision_mxq_amd as mxq
+
+    mxq.load_library()
+    pre = dec = None
+    if args.only != "decode":
+        pre = bench_prefill(args, dev)
+    if args.only != "prefill" and not args.no_decode:
+        dec = bench_decode(args, dev)
+    cpu = None
+    if pre is not None and not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, pre)
+        log(f"cpu baseline: {cpu['value']:.6f} TFLOP/s ({cpu['sample']})")
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded N(0,1) bf16; outlier channels and "
+            "sink key as in the workload recipe)"}
+    if pre is not None:
+        cfg = pre["cfg"]
+        line.update(value=round(pre["tflops_step"], 3), unit="TFLOP/s", ms_per_step=round(pre["ms_step"], 4),
+                    dtype="mxfp4 QK^T + fp8 PV, fp16 on selected tiles, fp32 accumulate")
+        line["config"] = {
+            "workload": f"{args.workload}: B={cfg['B']} Hq={cfg['Hq']} Hkv={cfg['Hkv']} N={cfg['N']} "
+                        f"n_valid={cfg['n_valid']} D={cfg['D']} {'causal' if cfg['causal'] else 'non-causal'}, "
+                        f"{cfg['Bq']}x{cfg['Bk']} tiles, FP16 = top "
+                        f"{('k=' + str(cfg['topk'])) if cfg['topk'] >= 0 else str(cfg['ratio_num']) + '%'}"
+                        f" + sink {cfg['sink_tiles']} + window {cfg['local_tiles']}",
+            "step": "quantize Q,K (MXFP4), V (MXFP8 + fp16 copy) -> select -> fused mixed attention",
+            "fp16_pair_fraction": round(pre["fp16_pairs"] / pre["total_pairs"], 5),
+            "attn_ms": round(pre["attn_ms"], 4),
+            "attn_tflops": round(pre["tflops_attn"], 2),
+        }
+        line["roofline"] = {
+            "bound": "mfma", "kernel": "attn_mixed_fwd",
+            "achieved": round(pre["tflops_attn"], 2), "peak": round(pre["peak_eff"], 1), "unit": "TFLOP/s",
+            "frac": round(pre["tflops_attn"] / pre["peak_eff"], 4), "traffic": None,
+            "peak_note": "precision-weighted: FP16 pairs at 2516.6, low-bit pairs half at FP4 10066.4 (QK^T) "
+                         "and half at FP8 5033.2 (PV)",
+        }
+    if dec is not None:
+        dline = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 5),
+                 "workload": "decode: 64 seqs x 32768 cached tokens, Hq=32 Hkv=8 D=128, INT4-G32 KV + fp16 "
+                             "first 64 / last 128 tokens",
+                 "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": PEAK_HBM, "unit": "GB/s",
+                              "frac": round(dec["gbs"] / PEAK_HBM, 4), "traffic": None}}
+        line["decode"] = dline
+        if pre is None:
+            line.update(value=dline["value"], unit="GB/s", ms_per_step=dline["ms_per_step"], dtype="int4 KV, fp32",
+                        config={"workload": dline["workload"]}, roofline=dline["roofline"])
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,6 +32,10 @@
 // global memory.
 #include "mxq_internal.h"
 
+// Products and sums round on their own unless written as __builtin_fmaf: the
+// reference exponent ceil(fl32(rowmax * c)) must be one rounded product.
+#pragma clang fp contract(off)
+
 namespace mxq {
 mxq_status validate_attn_shape(const mxq_attn_shape* s);
 
@@ -234,8 +238,8 @@ __global__ void __launch_bounds__(BQ * 4) k_attn_mixed(AttnArgs a) {
       for (int i = 0; i < 4; ++i) mx1 = fmaxf(mx1, S[beta][i]);
     mx0 = wave_rowmax(mx0);
     mx1 = wave_rowmax(mx1);
-    const float t0 = ceilf(__fmul_rn(mx0, c));
-    const float t1 = ceilf(__fmul_rn(mx1, c));
+    const float t0 = ceilf(mx0 * c);
+    const float t1 = ceilf(mx1 * c);
     const float m0 = fmaxf(m_run, t0);
     const float m1 = fmaxf(m0, t1);
     if (__any(m1 != m_run)) {

@@ -7,6 +7,12 @@
 // round-half-even of the exactly scaled input.
 #include "mxq_internal.h"
 
+// Every product and sum in this file is rounded on its own, as written: with
+// contraction off the compiler may not fuse a*b+c into one FMA.  (HIP's
+// __fmul_rn/__fadd_rn are plain * and + defined in a header, so they would
+// still be fused; plain operators under this pragma are not.)
+#pragma clang fp contract(off)
+
 namespace mxq {
 namespace {
 
@@ -156,7 +162,7 @@ __global__ void __launch_bounds__(256) k_quant_int4_d(const uint16_t* __restrict
   float mn = v[0], mx = v[0];
 #pragma unroll
   for (int i = 1; i < 32; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-  float s32 = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+  float s32 = (mx - mn) / 15.0f;
   _Float16 sh = static_cast<_Float16>(s32);
   _Float16 zh = static_cast<_Float16>(mn);
   float s = static_cast<float>(sh), z = static_cast<float>(zh);
@@ -165,7 +171,7 @@ __global__ void __launch_bounds__(256) k_quant_int4_d(const uint16_t* __restrict
   for (int i = 0; i < 32; ++i) {
     uint32_t c = 0;
     if (s != 0.0f) {
-      float q = __builtin_rintf(__fdiv_rn(__fsub_rn(v[i], z), s));
+      float q = __builtin_rintf((v[i] - z) / s);
       q = fminf(fmaxf(q, 0.0f), 15.0f);
       c = static_cast<uint32_t>(q);
     }

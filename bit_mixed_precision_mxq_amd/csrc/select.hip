@@ -14,6 +14,12 @@
 // evaluation of the same formula.
 #include "mxq_internal.h"
 
+// Every product and sum in this file is rounded on its own, as written: with
+// contraction off the compiler may not fuse a*b+c into one FMA.  (HIP's
+// __fmul_rn/__fadd_rn are plain * and + defined in a header, so they would
+// still be fused; plain operators under this pragma are not.)
+#pragma clang fp contract(off)
+
 namespace mxq {
 namespace {
 
@@ -30,11 +36,11 @@ __global__ void k_tile_means(const uint16_t* __restrict__ x, float* __restrict__
   int cnt = 0;
   for (int r = 0; r < T; ++r) {
     if (tile * T + r < n_valid) {
-      acc = __fadd_rn(acc, bf16_to_f32(base[static_cast<int64_t>(r) * D]));
+      acc = acc + bf16_to_f32(base[static_cast<int64_t>(r) * D]);
       ++cnt;
     }
   }
-  float m = cnt > 0 ? __fdiv_rn(acc, static_cast<float>(cnt)) : 0.0f;
+  float m = cnt > 0 ? acc / static_cast<float>(cnt) : 0.0f;  // correctly rounded division
   mean[(bh * n_tiles + tile) * D + d] = m;
 }
 
@@ -69,7 +75,7 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
   for (int j = tid; j < a.n_kt; j += blockDim.x) {
     const float* km = a.kmean + (bhk * a.n_kt + j) * a.D;
     float acc = 0.0f;
-    for (int d = 0; d < a.D; ++d) acc = __fadd_rn(acc, __fmul_rn(s_q[d], km[d]));
+    for (int d = 0; d < a.D; ++d) acc = acc + s_q[d] * km[d];  // two roundings: contraction is off here
     s_score[j] = acc;
     if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
   }
