@@ -55,12 +55,14 @@ struct AttnArgs {
   void* out;
   float* lse;
   int Hq, Hkv, N, n_valid, n_qt, words, causal, mode, out_bf16;
+  int sel_bq;  // query rows per selection tile (mask row = query row / sel_bq)
   float c;  // fl32(softmax_scale * log2(e))
 };
 
 constexpr float kGridMagic = 6144.0f;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^13)
 constexpr float kExpOffset = 8.0f;     // P is stored as E4M3(2^(x + 8)) * 2^-8
 constexpr int kPScale = 119;           // E8M0 code of 2^-8
+constexpr float kMaxLag = 64.0f;       // largest gap kept between O's reference and the running one
 
 // Key (within the 128-key chunk) that A-operand row r of S-block beta holds.
 __device__ __forceinline__ int chunk_key(int beta, int r) {
@@ -73,18 +75,79 @@ __device__ __forceinline__ float wave_rowmax(float v) {
   return v;
 }
 
-template <int D, int BQ>
-__global__ void __launch_bounds__(BQ * 4) k_attn_mixed(AttnArgs a) {
-  constexpr int NW = BQ / 16;    // waves per workgroup
-  constexpr int NT = NW * 64;    // threads
-  constexpr int KROW = D / 2;    // bytes of one FP4 K row
+// max of three scores.  This file is compiled with NaNs not honoured and the
+// IEEE mode bit off (scores are finite or -inf, never NaN), so fmaxf needs no
+// canonicalising moves and maps to one v_max3_f32.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Row maximum over the 4 lane groups (lanes col, col+16, col+32, col+48) with
+// two cross-row swaps (v_permlane16_swap / v_permlane32_swap), no LDS traffic.
+__device__ __forceinline__ float rowmax4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m1 = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const uint32_t u1 = __float_as_uint(m1);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u1, u1, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+// LDS layouts.
+//  Low-bit chunk (128 keys, two buffers):
+//   K codes: FP4 rows of D/2 bytes (D/32 chunks of 16 bytes), the chunk index
+//     XOR-swizzled with key bits so the 16 rows one MFMA operand read touches
+//     fall in distinct banks (for D = 64 rows also swap 4 apart);
+//   K scales: byte [g][col][beta] = scale of block g of the key that S block
+//     beta's row col holds, so one 8-byte read per lane serves all 8 QK MFMAs
+//     (op_sel picks the byte);
+//   V codes: FP8 V^T rows (one per head_dim element, 128 keys) padded to 144 B;
+//   V scales: byte [g][col][db] = scale of key block g of row 16*db+col.
+//  FP16 tile (64 keys, one buffer): bf16 K rows of 2*D bytes with the 16-byte
+//  chunk index XOR-swizzled by 4 key bits; fp16 V^T rows padded to 144 bytes.
+template <int D>
+struct Lds {
+  static constexpr int KROW = D / 2;
+  static constexpr int NSB = D / 32;
+  static constexpr int VSTRIDE = 144;
+  static constexpr int K_OFF = 0;
+  static constexpr int KS_OFF = K_OFF + 128 * KROW;
+  static constexpr int V_OFF = KS_OFF + 512;
+  static constexpr int VS_OFF = V_OFF + D * VSTRIDE;
+  static constexpr int LO_BYTES = VS_OFF + 512;
+  static constexpr int HK_OFF = 2 * LO_BYTES;             // bf16 K tile
+  static constexpr int HV_OFF = HK_OFF + 64 * 2 * D;      // fp16 V^T tile
+  static constexpr int ONES_OFF = HV_OFF + D * VSTRIDE;   // 32 B of E4M3 1.0, 16 B of fp16 1.0
+  static constexpr int BYTES = ONES_OFF + 48;
+  __device__ static __forceinline__ int k_off(int key, int g) {
+    if constexpr (D == 128) {
+      return K_OFF + key * KROW + 16 * (g ^ ((key >> 4) & 3));
+    } else {
+      const int row = key ^ ((key >> 2) & 4);
+      return K_OFF + row * KROW + 16 * (g ^ ((key >> 5) & 1));
+    }
+  }
+  __device__ static __forceinline__ int hk_off(int key, int cidx) {  // key in [0,64)
+    int f;
+    if constexpr (D == 128) f = (key & 3) | ((key >> 2) & 12);
+    else f = ((key >> 1) & 1) | ((key >> 3) & 6);
+    return HK_OFF + key * 2 * D + 16 * (cidx ^ f);
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
+  using LY = Lds<D>;
+  constexpr int BQ = 128;        // query rows per workgroup
+  constexpr int NT = 512;        // 8 waves of 16 rows
+  constexpr int KROW = D / 2;
   constexpr int NDB = D / 16;    // 16-row head_dim blocks of O^T
   constexpr int NSB = D / 32;    // MX blocks per row, and K=32 steps of the bf16 MFMA
+  constexpr int KUNITS = 128 * KROW / 16;   // 16-byte K-code units per chunk
+  constexpr int KU = (KUNITS + NT - 1) / NT;
+  constexpr int VU = D * 8 / NT;            // 16-byte V-code units per thread
+  static_assert(D * 8 % NT == 0, "V units must divide evenly");
+  constexpr float NEG_INF = -__builtin_inff();
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_kc[128 * KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t s_ks[128 * NSB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vc[D * 128];
-  __shared__ __attribute__((aligned(16))) uint32_t s_vs[D];
+  __shared__ __attribute__((aligned(16))) uint8_t sm[LY::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -100,236 +163,378 @@ __global__ void __launch_bounds__(BQ * 4) k_attn_mixed(AttnArgs a) {
   const int qs = it * BQ;
   const int q = qs + wave * 16 + col;  // this lane's query row
 
-  // ---------------------------------------------------------------- epilogue for padding tiles
-  if (qs >= a.n_valid) {
+  if (qs >= a.n_valid) {  // a tile of padding rows: output 0, lse -inf
     for (int idx = tid; idx < BQ * D; idx += NT) {
       int64_t o = (bhq * a.N + qs) * D + idx;
       if (a.out_bf16) static_cast<uint16_t*>(a.out)[o] = 0;
       else static_cast<float*>(a.out)[o] = 0.0f;
     }
     if (a.lse)
-      for (int r = tid; r < BQ; r += NT) a.lse[bhq * a.N + qs + r] = -__builtin_inff();
+      for (int r = tid; r < BQ; r += NT) a.lse[bhq * a.N + qs + r] = NEG_INF;
     return;
   }
   const int qe = min(qs + BQ, a.n_valid) - 1;
   int last_tile = (a.n_valid - 1) / 64;
   if (a.causal) last_tile = min(last_tile, qe / 64);
   const int n_chunks = (last_tile + 2) / 2;
+  const int wq_lo = qs + wave * 16;                 // this wave's first row
+  const bool wave_live = wq_lo < a.n_valid;
 
-  // ---------------------------------------------------------------- Q fragments (registers)
+  // FP4 Q fragment (B operand of S^T = K Q^T), held for the whole pass
   v8i qf4 = {0, 0, 0, 0, 0, 0, 0, 0};
   int qsc = 127;
   if (a.mode != MXQ_ALL_FP16 && g < NSB) {
-    const uint4 w = *reinterpret_cast<const uint4*>(a.q_codes + (bhq * a.N + q) * KROW + 16 * g);
-    qf4[0] = w.x; qf4[1] = w.y; qf4[2] = w.z; qf4[3] = w.w;
+    const v4i w = *reinterpret_cast<const v4i*>(a.q_codes + (bhq * a.N + q) * KROW + 16 * g);
+    qf4[0] = w[0]; qf4[1] = w[1]; qf4[2] = w[2]; qf4[3] = w[3];
     qsc = a.q_scales[(bhq * a.N + q) * NSB + g];
   }
-  v8bf qbf[NSB];
-  if (a.mode != MXQ_ALL_LOWBIT) {
-#pragma unroll
-    for (int s = 0; s < NSB; ++s)
-      qbf[s] = *reinterpret_cast<const v8bf*>(a.q_bf16 + (bhq * a.N + q) * D + 32 * s + 8 * g);
-  }
+  const uint16_t* qrow_bf16 = a.q_bf16 ? a.q_bf16 + (bhq * a.N + q) * D : nullptr;
 
   v4f O[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) O[i] = v4f{0.f, 0.f, 0.f, 0.f};
   v4f L = {0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
+  float m_run = NEG_INF;   // running integer reference (log2 units)
+  float m_o = NEG_INF;     // reference O and L are currently expressed in
   const float c = a.c;
-  const uint32_t* mrow = a.mask ? a.mask + (bhq * a.n_qt + it) * a.words : nullptr;
 
-  v8i ones8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones8[i] = 0x38383838;  // E4M3 1.0
-  v8h ones16;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones16[i] = static_cast<_Float16>(1.0f);
-
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const int kc = ch * 128;
+  // Promotion flags.  The workgroup's 128 rows may span two selection tiles
+  // (64-row tiles): each wave reads the mask row of its own rows, and staging
+  // uses the union (FP16 data some wave needs) and the intersection (low-bit
+  // data is needed unless every wave promotes the tile).
+  const int64_t mbase = bhq * (a.N / a.sel_bq);
+  const uint32_t* mrow_w = a.mask ? a.mask + (mbase + wq_lo / a.sel_bq) * a.words : nullptr;
+  const uint32_t* mrow_a = a.mask ? a.mask + (mbase + qs / a.sel_bq) * a.words : nullptr;
+  const uint32_t* mrow_b = a.mask ? a.mask + (mbase + (qs + BQ - 1) / a.sel_bq) * a.words : nullptr;
+  auto row_flags = [&](const uint32_t* mr, int ch) -> int {  // bit t: tile t of chunk ch is FP16
     const int j0 = 2 * ch;
     const bool valid1 = j0 + 1 <= last_tile;
-    bool prom0, prom1;
-    if (a.mode == MXQ_ALL_FP16) {
-      prom0 = true; prom1 = valid1;
-    } else if (a.mode == MXQ_ALL_LOWBIT) {
-      prom0 = false; prom1 = false;
-    } else {
-      const uint32_t wbits = mrow[j0 >> 5];
-      prom0 = (wbits >> (j0 & 31)) & 1u;
-      prom1 = valid1 && ((wbits >> ((j0 + 1) & 31)) & 1u);
-    }
-    const bool low0 = !prom0;
-    const bool low1 = valid1 && !prom1;
-    const bool need_low = low0 || low1;
-
-    // ------------------------------------------------------------ stage low-bit K, V in LDS
-    __syncthreads();
-    if (need_low) {
-      const uint4* kg = reinterpret_cast<const uint4*>(a.k_codes + (bhk * a.N + kc) * KROW);
-      for (int u = tid; u < 128 * KROW / 16; u += NT) reinterpret_cast<uint4*>(s_kc)[u] = kg[u];
-      const uint4* ksg = reinterpret_cast<const uint4*>(a.k_scales + (bhk * a.N + kc) * NSB);
-      for (int u = tid; u < 128 * NSB / 16; u += NT) reinterpret_cast<uint4*>(s_ks)[u] = ksg[u];
-      for (int u = tid; u < D * 8; u += NT) {
-        const int d = u >> 3, part = u & 7;
-        reinterpret_cast<uint4*>(s_vc)[u] =
-            *reinterpret_cast<const uint4*>(a.v_codes + (bhk * D + d) * a.N + kc + 16 * part);
-      }
-      for (int d = tid; d < D; d += NT)
-        s_vs[d] = *reinterpret_cast<const uint32_t*>(a.v_scales + (bhk * D + d) * (a.N / 32) + kc / 32);
-    }
-    __syncthreads();
-
-    // ------------------------------------------------------------ S^T blocks
-    v4f S[8];
-#pragma unroll
-    for (int beta = 0; beta < 8; ++beta) {
-      const int t = beta >> 2;
-      const bool valid_t = t == 0 ? true : valid1;
-      const bool prom_t = t == 0 ? prom0 : prom1;
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const int key = chunk_key(beta, col);  // A-operand row of this lane
-      if (!valid_t) {
-        acc = v4f{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-      } else if (prom_t) {
-        const uint16_t* krow = a.k_bf16 + (bhk * a.N + kc + key) * D;
-#pragma unroll
-        for (int s = 0; s < NSB; ++s) {
-          const v8bf ka = *reinterpret_cast<const v8bf*>(krow + 32 * s + 8 * g);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbf[s], acc, 0, 0, 0);
-        }
-      } else {
-        v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-        int ksc = 127;
-        if (g < NSB) {
-          const uint4 w = *reinterpret_cast<const uint4*>(s_kc + key * KROW + 16 * g);
-          ka[0] = w.x; ka[1] = w.y; ka[2] = w.z; ka[3] = w.w;
-          ksc = s_ks[key * NSB + g];
-        }
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, acc, 4, 4, 0, ksc, 0, qsc);
-      }
-      S[beta] = acc;
-    }
-
-    // ------------------------------------------------------------ masking
-    const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > qs) || (qe < qs + BQ - 1);
-    if (need_mask) {
-#pragma unroll
-      for (int beta = 0; beta < 8; ++beta) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kc + 64 * (beta >> 2) + 16 * g + 4 * (beta & 3) + i;
-          const bool ok = key < a.n_valid && q < a.n_valid && (!a.causal || key <= q);
-          if (!ok) S[beta][i] = -__builtin_inff();
-        }
-      }
-    }
-
-    // ------------------------------------------------------------ running reference per tile
-    float mx0 = -__builtin_inff(), mx1 = -__builtin_inff();
-#pragma unroll
-    for (int beta = 0; beta < 4; ++beta)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx0 = fmaxf(mx0, S[beta][i]);
-#pragma unroll
-    for (int beta = 4; beta < 8; ++beta)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx1 = fmaxf(mx1, S[beta][i]);
-    mx0 = wave_rowmax(mx0);
-    mx1 = wave_rowmax(mx1);
-    const float t0 = ceilf(mx0 * c);
-    const float t1 = ceilf(mx1 * c);
-    const float m0 = fmaxf(m_run, t0);
-    const float m1 = fmaxf(m0, t1);
-    if (__any(m1 != m_run)) {
+    if (a.mode == MXQ_ALL_FP16) return 1 | (valid1 ? 2 : 0);
+    if (a.mode == MXQ_ALL_LOWBIT) return 0;
+    const uint32_t wbits = mr[j0 >> 5];
+    return static_cast<int>((wbits >> (j0 & 31)) & 1u) |
+           (valid1 ? static_cast<int>(((wbits >> ((j0 + 1) & 31)) & 1u) << 1) : 0);
+  };
+  // packed: bits 0-1 this wave, 2-3 any wave, 4-5 every wave
+  auto chunk_flags = [&](int ch) -> int {
+    const int fw = row_flags(mrow_w, ch);
+    const int fa = row_flags(mrow_a, ch);
+    const int fb = row_flags(mrow_b, ch);
+    return fw | ((fa | fb) << 2) | ((fa & fb) << 4);
+  };
+  auto needs_low = [&](int ch, int fl) -> bool {
+    const int all = (fl >> 4) & 3;
+    return !(all & 1) || ((2 * ch + 1 <= last_tile) && !(all & 2));
+  };
+  auto rebase = [&](float m) {  // rescale O and L from m_o to m >= m_o (powers of two)
+    if (__any(m != m_o)) {
       float f = 1.0f;
-      if (m_run != -__builtin_inff() && m1 != m_run)
-        f = __builtin_ldexpf(1.0f, static_cast<int>(fmaxf(m_run - m1, -256.0f)));
+      if (m_o != NEG_INF && m != m_o) f = __builtin_ldexpf(1.0f, static_cast<int>(fmaxf(m_o - m, -256.0f)));
 #pragma unroll
       for (int i = 0; i < NDB; ++i) O[i] *= f;
       L *= f;
     }
-    m_run = m1;
+    m_o = m;
+  };
 
-    // ------------------------------------------------------------ low-bit P and PV
-    if (need_low) {
-      v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (low0) {
-        const float off = kGridMagic + kExpOffset - (m0 == -__builtin_inff() ? 0.0f : m0);
+  // ---- staging registers for one chunk of low-bit K and V
+  v4i pk[KU], pv[VU];
+  uint32_t pks = 0, pvs = 0;
+  auto stage_load = [&](int ch) {
+    const int kc = ch * 128;
+    const v4i* kg = reinterpret_cast<const v4i*>(a.k_codes + (bhk * a.N + kc) * KROW);
 #pragma unroll
-        for (int beta = 0; beta < 4; ++beta) {
-          float y[4];
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + i * NT;
+      if (u < KUNITS) pk[i] = kg[u];
+    }
+    if (tid < 128 * NSB) pks = a.k_scales[(bhk * a.N + kc) * NSB + tid];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[beta][i], c, off) - kGridMagic);
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-          pb[beta] = w;
+    for (int i = 0; i < VU; ++i) {
+      const int u = tid + i * NT;
+      pv[i] = *reinterpret_cast<const v4i*>(a.v_codes + (bhk * D + (u >> 3)) * a.N + kc + 16 * (u & 7));
+    }
+    if (tid < D) pvs = *reinterpret_cast<const uint32_t*>(a.v_scales + (bhk * D + tid) * (a.N / 32) + kc / 32);
+  };
+  auto stage_store = [&](int buf) {
+    uint8_t* sb = sm + buf * LY::LO_BYTES;
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + i * NT;
+      if (u < KUNITS) *reinterpret_cast<v4i*>(sb + LY::k_off(u / NSB, u % NSB)) = pk[i];
+    }
+    if (tid < 128 * NSB) {  // K scale of (key, block kg) -> [kg][col][beta]
+      const int key = tid / NSB, kg = tid % NSB;
+      const int kcol = 4 * ((key >> 4) & 3) + (key & 3);
+      const int kbeta = 4 * (key >> 6) + ((key >> 2) & 3);
+      sb[LY::KS_OFF + (kg * 16 + kcol) * 8 + kbeta] = static_cast<uint8_t>(pks);
+    }
+#pragma unroll
+    for (int i = 0; i < VU; ++i) {
+      const int u = tid + i * NT;
+      *reinterpret_cast<v4i*>(sb + LY::V_OFF + (u >> 3) * LY::VSTRIDE + 16 * (u & 7)) = pv[i];
+    }
+    if (tid < D) {  // V scales of row d for key blocks 0..3 -> [block][d%16][d/16]
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        sb[LY::VS_OFF + (kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(pvs >> (8 * kb));
+    }
+  };
+  auto stage_fp16_tile = [&](int kt0) {
+    constexpr int HKU = 64 * 2 * D / 16;  // 16-byte units of the bf16 K tile
+    v4i hk[(HKU + NT - 1) / NT], hv[(D * 8 + NT - 1) / NT];
+#pragma unroll
+    for (int i = 0; i < (HKU + NT - 1) / NT; ++i) {
+      const int u = tid + i * NT;
+      if (u < HKU) hk[i] = reinterpret_cast<const v4i*>(a.k_bf16 + (bhk * a.N + kt0 + u / (D / 8)) * D)[u % (D / 8)];
+    }
+#pragma unroll
+    for (int i = 0; i < (D * 8 + NT - 1) / NT; ++i) {
+      const int u = tid + i * NT;
+      if (u < D * 8) hv[i] = *reinterpret_cast<const v4i*>(a.v_f16t + (bhk * D + (u >> 3)) * a.N + kt0 + 8 * (u & 7));
+    }
+#pragma unroll
+    for (int i = 0; i < (HKU + NT - 1) / NT; ++i) {
+      const int u = tid + i * NT;
+      if (u < HKU) *reinterpret_cast<v4i*>(sm + LY::hk_off(u / (D / 8), u % (D / 8))) = hk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < (D * 8 + NT - 1) / NT; ++i) {
+      const int u = tid + i * NT;
+      if (u < D * 8) *reinterpret_cast<v4i*>(sm + LY::HV_OFF + (u >> 3) * LY::VSTRIDE + 16 * (u & 7)) = hv[i];
+    }
+  };
+
+  if (tid < 12) reinterpret_cast<uint32_t*>(sm + LY::ONES_OFF)[tid] = tid < 8 ? 0x38383838u : 0x3C003C00u;
+  if constexpr (NSB < 4) {
+    // lane groups g >= D/32 carry no head_dim data: their K scale bytes must be
+    // a finite E8M0 (0xFF would be NaN), so set them to 127 (= 1.0) once
+    constexpr int PAD = (4 - NSB) * 16 * 8;
+    for (int i = tid; i < 2 * PAD; i += NT)
+      sm[(i / PAD) * LY::LO_BYTES + LY::KS_OFF + NSB * 16 * 8 + i % PAD] = 127;
+  }
+
+  // per-lane LDS byte offsets (constant over the pass)
+  int koff[8];
+#pragma unroll
+  for (int beta = 0; beta < 8; ++beta) koff[beta] = LY::k_off(chunk_key(beta, col), g);
+  const int ksoff = LY::KS_OFF + (g * 16 + col) * 8;
+  const int voff = LY::V_OFF + col * LY::VSTRIDE + 16 * g;
+  const int vsoff = LY::VS_OFF + (g * 16 + col) * 8;
+
+  int flags = chunk_flags(0);
+  bool have_next = false;
+  if (needs_low(0, flags)) {
+    stage_load(0);
+    have_next = true;
+  }
+
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int kc = ch * 128;
+    const bool valid1 = 2 * ch + 1 <= last_tile;
+    const bool need_low = needs_low(ch, flags);
+    const uint8_t* sb = sm + (ch & 1) * LY::LO_BYTES;
+    // ---- publish this chunk (loaded one chunk ahead), prefetch the next one
+    __syncthreads();  // every wave is done with the buffer about to be written
+    if (have_next) stage_store(ch & 1);
+    int next_flags = 0;
+    have_next = false;
+    if (ch + 1 < n_chunks) {
+      next_flags = chunk_flags(ch + 1);
+      if (needs_low(ch + 1, next_flags)) {
+        stage_load(ch + 1);
+        have_next = true;
+      }
+    }
+    if (need_low) __syncthreads();
+
+    const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
+    const bool any_hi = (flags >> 2) & 3;
+    if (!any_hi && valid1 && !need_mask) {
+      // ================= hot path: both tiles low-bit for every wave, no masks
+      const uint32_t* ksw = reinterpret_cast<const uint32_t*>(sb + ksoff);
+      const uint32_t ksc0 = ksw[0], ksc1 = ksw[1];
+      v4f S[8];
+#pragma unroll
+      for (int beta = 0; beta < 8; ++beta) {
+        v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
+        const v4i w = *reinterpret_cast<const v4i*>(sb + koff[beta]);
+        ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
+        const int sc = beta < 4 ? static_cast<int>(ksc0) : static_cast<int>(ksc1);
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+        switch (beta & 3) {
+          case 0: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 0, sc, 0, qsc); break;
+          case 1: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 1, sc, 0, qsc); break;
+          case 2: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 2, sc, 0, qsc); break;
+          default: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 3, sc, 0, qsc); break;
         }
       }
-      if (low1) {
-        const float off = kGridMagic + kExpOffset - (m1 == -__builtin_inff() ? 0.0f : m1);
+      float mx0 = max3f(S[0][0], S[0][1], S[0][2]);
+      float mx1 = max3f(S[4][0], S[4][1], S[4][2]);
+      mx0 = max3f(mx0, S[0][3], S[1][0]);
+      mx1 = max3f(mx1, S[4][3], S[5][0]);
 #pragma unroll
-        for (int beta = 4; beta < 8; ++beta) {
-          float y[4];
+      for (int e = 5; e < 16; e += 2) {  // remaining 11 values of each tile, two per v_max3
+        const float a0 = S[e >> 2][e & 3], b0 = e + 1 < 16 ? S[(e + 1) >> 2][(e + 1) & 3] : a0;
+        const float a1 = S[4 + (e >> 2)][e & 3], b1 = e + 1 < 16 ? S[4 + ((e + 1) >> 2)][(e + 1) & 3] : a1;
+        mx0 = max3f(mx0, a0, b0);
+        mx1 = max3f(mx1, a1, b1);
+      }
+      mx0 = rowmax4(mx0);
+      mx1 = rowmax4(mx1);
+      const float m0 = fmaxf(m_run, ceilf(mx0 * c));
+      const float m1 = fmaxf(m0, ceilf(mx1 * c));
+      m_run = m1;
+      // O and L stay expressed against a lagging reference m_o <= m0: each
+      // tile's contribution is scaled by 2^(m_t - m_o) through the E8M0 scale
+      // of its P blocks, so O is only rescaled when the gap grows large
+      if (m_o == NEG_INF) m_o = m0;
+      if (__any(m1 - m_o > kMaxLag)) rebase(m1);
+      const float off0 = kGridMagic + kExpOffset - m0;  // m0 is finite: key 0.. are valid
+      const float off1 = kGridMagic + kExpOffset - m1;
+      v8i pb;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[beta][i], c, off) - kGridMagic);
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-          pb[beta] = w;
-        }
+      for (int beta = 0; beta < 8; ++beta) {
+        const float off = beta < 4 ? off0 : off1;
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[beta][i], c, off) - kGridMagic);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        pb[beta] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
       }
-      // K blocks 0,1 (lane groups 0,1) carry the first tile, blocks 2,3 the second.
-      int psc = kPScale;
-      if (g < 2) {
-        // the first tile's P was formed against m0 <= m1: scale it by 2^-(m1-m0)
-        const float gap = m1 - m0;
-        psc = (m0 == -__builtin_inff() || gap >= static_cast<float>(kPScale))
-                  ? 0
-                  : kPScale - static_cast<int>(gap);
-      }
+      // 2^-8 * 2^(m_t - m_o); below 2^-127 (after a forced rebase) the tile adds nothing visible
+      const int psc = static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + ((g < 2 ? m0 : m1) - m_o), 0.0f), 254.0f));
+      const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
+      const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint8_t* vrow = s_vc + (16 * db + col) * 128;
-        const uint4 w0 = *reinterpret_cast<const uint4*>(vrow + 16 * g);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(vrow + 64 + 16 * g);
-        const v8i va = {static_cast<int>(w0.x), static_cast<int>(w0.y), static_cast<int>(w0.z),
-                        static_cast<int>(w0.w), static_cast<int>(w1.x), static_cast<int>(w1.y),
-                        static_cast<int>(w1.z), static_cast<int>(w1.w)};
-        const int vsc = (s_vs[16 * db + col] >> (8 * g)) & 0xFF;
-        O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vsc, 0, psc);
-      }
-      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
-    }
-
-    // ------------------------------------------------------------ FP16 tiles
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bool prom_t = t == 0 ? prom0 : prom1;
-      if (!prom_t) continue;
-      const float negm = -(m1 == -__builtin_inff() ? 0.0f : m1);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        v8h ph;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int beta = 4 * t + 2 * s + (e >> 2);
-          ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(S[beta][e & 3], c, negm)));
+        const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
+        const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
+        const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
+        const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
+        switch (db & 3) {
+          case 0: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vs, 0, psc); break;
+          case 1: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 1, vs, 0, psc); break;
+          case 2: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 2, vs, 0, psc); break;
+          default: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 3, vs, 0, psc); break;
         }
-        const int key0 = kc + 64 * t + 16 * g + 8 * s;
+      }
+      const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
+      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+    } else {
+      // ================= general path: masks, FP16 tiles, a lone last tile
+      const bool low_w = !(flags & 1) || (valid1 && !(flags & 2));  // this wave runs FP8 PV
+      v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};
+      float m_tile0 = NEG_INF;
+#pragma unroll 1
+      for (int t = 0; t < 2; ++t) {
+        if (t == 1 && !valid1) break;
+        const bool prom = (flags >> t) & 1;            // this wave's tile t is FP16
+        const bool stage_hi = (flags >> (2 + t)) & 1;  // some wave's tile t is FP16
+        if (stage_hi) {
+          __syncthreads();  // previous users of the FP16 stage are done
+          stage_fp16_tile(kc + 64 * t);
+          __syncthreads();
+        }
+        v4f S[4];
+        if (prom) {
+          const uint16_t* qp16 = qrow_bf16;
+          asm volatile("" : "+v"(qp16));  // re-read the bf16 Q fragment, do not hoist it
+#pragma unroll
+          for (int st = 0; st < NSB; ++st) {
+            const v8bf qb = *reinterpret_cast<const v8bf*>(qp16 + 32 * st + 8 * g);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              const int key = 16 * (col >> 2) + 4 * bb + (col & 3);
+              const v8bf ka = *reinterpret_cast<const v8bf*>(sm + LY::hk_off(key, 4 * st + g));
+              S[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : S[bb], 0, 0, 0);
+            }
+          }
+        } else {
+          const uint32_t kscw = reinterpret_cast<const uint32_t*>(sb + ksoff)[t];
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
+            const v4i w = *reinterpret_cast<const v4i*>(sb + koff[4 * t + bb]);
+            ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
+            const int sc = static_cast<int>(kscw >> (8 * bb)) & 0xFF;
+            S[bb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                       sc, 0, qsc);
+          }
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kc + 64 * t + 16 * g + 4 * bb + i;
+              const bool ok = key < a.n_valid && q < a.n_valid && (!a.causal || key <= q);
+              if (!ok) S[bb][i] = NEG_INF;
+            }
+        }
+        float mx = NEG_INF;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) mx = fmaxf(fmaxf(mx, fmaxf(S[bb][0], S[bb][1])), fmaxf(S[bb][2], S[bb][3]));
+        mx = rowmax4(mx);
+        const float m_t = fmaxf(m_run, ceilf(mx * c));
+        m_run = m_t;
+        if (t == 0) m_tile0 = m_t;
+        const float m_safe = m_t == NEG_INF ? 0.0f : m_t;
+        if (prom) {
+          rebase(m_t);
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            v8h ph;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * st + (e >> 2)][e & 3], c, -m_safe)));
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const v8h va = *reinterpret_cast<const v8h*>(sm + LY::HV_OFF + (16 * db + col) * LY::VSTRIDE + 32 * g + 16 * st);
+              O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
+            }
+            const v8h ones16 = *reinterpret_cast<const v8h*>(sm + LY::ONES_OFF + 32);
+            L = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones16, ph, L, 0, 0, 0);
+          }
+        } else {
+          const float off = kGridMagic + kExpOffset - m_safe;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[bb][i], c, off) - kGridMagic);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            pb[4 * t + bb] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+          }
+        }
+      }
+      if (low_w) {
+        rebase(m_run);
+        int psc = kPScale;
+        if (g < 2) {
+          const float gap = m_run - m_tile0;
+          psc = (m_tile0 == NEG_INF || gap >= static_cast<float>(kPScale)) ? 0 : kPScale - static_cast<int>(gap);
+        }
+        const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const v8h va = *reinterpret_cast<const v8h*>(a.v_f16t + (bhk * D + 16 * db + col) * a.N + key0);
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
+          const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
+          const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
+          const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
+          const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+          const int vs = static_cast<int>(vsw[db >> 2] >> (8 * (db & 3))) & 0xFF;
+          O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vs, 0, psc);
         }
-        L = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones16, ph, L, 0, 0, 0);
+        const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
+        L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
       }
     }
+    flags = next_flags;
   }
 
   // ---------------------------------------------------------------- epilogue
+  // out = O / l is independent of the reference; lse uses O's reference m_o
   const bool row_ok = q < a.n_valid;
   const float l = L[0];
   const float inv = row_ok ? 1.0f / l : 0.0f;
@@ -343,20 +548,21 @@ __global__ void __launch_bounds__(BQ * 4) k_attn_mixed(AttnArgs a) {
         uint32_t u = __float_as_uint(x);
         return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
       };
-      uint2 pk = make_uint2(bf(o0) | (bf(o1) << 16), bf(o2) | (bf(o3) << 16));
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) = pk;
+      uint2 pk2 = make_uint2(bf(o0) | (bf(o1) << 16), bf(o2) | (bf(o3) << 16));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) = pk2;
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(o0, o1, o2, o3);
     }
   }
   if (a.lse && g == 0) {
-    a.lse[bhq * a.N + q] = row_ok ? (m_run + __log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+    a.lse[bhq * a.N + q] = row_ok ? (m_o + __log2f(l)) * 0.69314718055994531f : NEG_INF;
   }
+  (void)wave_live;
 }
 
-template <int D, int BQ>
+template <int D>
 mxq_status launch(const AttnArgs& a, int n_qt, int Hq, int B, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_mixed<D, BQ>), dim3(n_qt, Hq, B), dim3(BQ * 4), 0, st, a);
+  hipLaunchKernelGGL((k_attn_mixed<D>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
   return check_launch("k_attn_mixed");
 }
 
@@ -396,11 +602,13 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
   a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.n_qt = s->N / s->Bq;
   a.words = (s->N / s->Bk + 31) / 32; a.causal = s->causal; a.mode = mode;
   a.out_bf16 = out_dtype == MXQ_OUT_BF16;
+  a.sel_bq = s->Bq;
   a.c = static_cast<float>(sc * 1.4426950408889634);
   hipStream_t strm = as_stream(stream);
-  const int n_qt = s->N / s->Bq;
-  if (s->D == 128 && s->Bq == 128) return launch<128, 128>(a, n_qt, s->Hq, s->B, strm);
-  if (s->D == 128 && s->Bq == 64) return launch<128, 64>(a, n_qt, s->Hq, s->B, strm);
-  if (s->D == 64 && s->Bq == 128) return launch<64, 128>(a, n_qt, s->Hq, s->B, strm);
-  return launch<64, 64>(a, n_qt, s->Hq, s->B, strm);
+  // 128-row workgroups of 8 waves whatever the selection tile height (the
+  // mask row is looked up per row block); two workgroups share a CU.
+  const int n_qt = s->N / 128;
+  a.n_qt = n_qt;
+  if (s->D == 128) return launch<128>(a, n_qt, s->Hq, s->B, strm);
+  return launch<64>(a, n_qt, s->Hq, s->B, strm);
 }
