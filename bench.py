@@ -36,6 +36,22 @@ PEAK_HBM = 8000.0
 METRIC = "effective attention TFLOPS @5% FP16 tiles (prefill); KV-read GB/s (decode)"
 
 
+def recorded_traffic(kernel):
+    """HBM bytes per launch recorded by rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    (profiles/hbm_traffic.json), or None when the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -202,8 +218,9 @@ def bench_decode(args, dev):
 
 def cpu_baseline(args, pre):
     """The oracle (test infrastructure) timed on the host on a bounded sample of
-    the same workload: the selection of one query head plus the mixed attention
-    of query tiles of that head until about 15 s of CPU work."""
+    the same workload: per query head in turn, its block selection and the mixed
+    attention of its query tiles (heavy causal tiles first), until about
+    ``--cpu-seconds`` of CPU work."""
     import numpy as np
 
     import oracle
@@ -214,37 +231,56 @@ def cpu_baseline(args, pre):
     except Exception:  # pragma: no cover
         threadpool_limits = None
     cfg = pre["cfg"]
-    h = 0
     G = cfg["Hq"] // cfg["Hkv"]
-    sub = dict(q=cfg["q"][:1, h:h + 1], k=cfg["k"][:1, h // G:h // G + 1], v=cfg["v"][:1, h // G:h // G + 1])
+    n_qt = cfg["N"] // cfg["Bq"]
     ctx = threadpool_limits(1) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
+    tiles, pairs, heads = 0, 0, 0
     try:
         t0 = time.perf_counter()
-        oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"], cfg["topk"],
-                             cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"], cfg["local_tiles"])
-        ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
-        n_qt = cfg["N"] // cfg["Bq"]
-        order = list(range(n_qt - 1, -1, -1))  # heavy causal tiles first; spread over the key range
-        order = order[::7] + [i for i in order if i % 7 != (n_qt - 1) % 7]
-        done, pairs = [], 0
-        mask = pre["mask"][:1, h:h + 1]
-        while order and time.perf_counter() - t0 < args.cpu_seconds:
-            i = order.pop(0)
-            A.attn_mixed_ref(sub["q"], sub["k"], sub["v"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
-                             mask=mask, qtiles=[i], ops=ops)
-            done.append(i)
-            r = np.arange(i * cfg["Bq"], min((i + 1) * cfg["Bq"], cfg["n_valid"]))
-            pairs += int(np.clip(r + 1, 0, cfg["n_valid"]).sum()) if cfg["causal"] else r.size * cfg["n_valid"]
+        for h in range(cfg["Hq"]):
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+            sub = dict(q=cfg["q"][:1, h:h + 1], k=cfg["k"][:1, h // G:h // G + 1], v=cfg["v"][:1, h // G:h // G + 1])
+            oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                                 cfg["topk"], cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"],
+                                 cfg["local_tiles"])
+            ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
+            mask = pre["mask"][:1, h:h + 1]
+            heads += 1
+            for i in range(n_qt - 1, -1, -1):
+                if time.perf_counter() - t0 >= args.cpu_seconds:
+                    break
+                A.attn_mixed_ref(sub["q"], sub["k"], sub["v"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                                 mask=mask, qtiles=[i], ops=ops)
+                tiles += 1
+                r = np.arange(i * cfg["Bq"], min((i + 1) * cfg["Bq"], cfg["n_valid"]))
+                pairs += int(np.clip(r + 1, 0, cfg["n_valid"]).sum()) if cfg["causal"] else r.size * cfg["n_valid"]
         dt = time.perf_counter() - t0
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
     flops = 4.0 * cfg["D"] * pairs
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"selection of query head 0 plus mixed attention of {len(done)} of its {n_qt} query tiles "
-                       f"({pairs} valid pairs), {dt:.1f} s on 1 host thread, same inputs")
+                sample=f"selection plus mixed attention of {tiles} query tiles over {heads} of {cfg['Hq']} query "
+                       f"heads ({pairs} valid pairs of {pre['total_pairs']}), {dt:.1f} s on 1 host thread, "
+                       f"same inputs")
+
+
+def copy_calibration(dev, mib=256, reps=3):
+    """A plain device-to-device copy of `mib` MiB, the known-size reference that
+    scales hardware byte counters (FETCH_SIZE, WRITE_SIZE) to HBM bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[-4:], src[-4:])
+    print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}), flush=True)
 
 
 def main():
@@ -255,7 +291,8 @@ def main():
     ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "long32k", "vit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="copy: a plain device copy of a known size, the reference for HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -268,6 +305,9 @@ def main():
     dev = torch.device("cuda:0")
     import bit_mixed_precision_mxq_amd as mxq
 
+    if args.only == "copy":
+        copy_calibration(dev)
+        return
     mxq.load_library()
     pre = dec = None
     if args.only != "decode":
@@ -299,7 +339,8 @@ def main():
         line["roofline"] = {
             "bound": "mfma", "kernel": "attn_mixed_fwd",
             "achieved": round(pre["tflops_attn"], 2), "peak": round(pre["peak_eff"], 1), "unit": "TFLOP/s",
-            "frac": round(pre["tflops_attn"] / pre["peak_eff"], 4), "traffic": None,
+            "frac": round(pre["tflops_attn"] / pre["peak_eff"], 4),
+            "traffic": recorded_traffic("attn_mixed_fwd") if args.workload == "llama8b" else None,
             "peak_note": "precision-weighted: FP16 pairs at 2516.6, low-bit pairs half at FP4 10066.4 (QK^T) "
                          "and half at FP8 5033.2 (PV)",
         }
@@ -308,7 +349,8 @@ def main():
                  "workload": "decode: 64 seqs x 32768 cached tokens, Hq=32 Hkv=8 D=128, INT4-G32 KV + fp16 "
                              "first 64 / last 128 tokens",
                  "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": PEAK_HBM, "unit": "GB/s",
-                              "frac": round(dec["gbs"] / PEAK_HBM, 4), "traffic": None}}
+                              "frac": round(dec["gbs"] / PEAK_HBM, 4),
+                              "traffic": recorded_traffic("attn_quantkv_decode")}}
         line["decode"] = dline
         if pre is None:
             line.update(value=dline["value"], unit="GB/s", ms_per_step=dline["ms_per_step"], dtype="int4 KV, fp32",

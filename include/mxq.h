@@ -16,8 +16,9 @@
  *  - NOVA-KV abstract (third page): decode reads the whole KV cache every step,
  *    so it is bandwidth-bound.
  * Formats follow the OCP Microscaling v1.0 rules (E2M1 / E4M3 elements with an
- * E8M0 shared exponent per 32 elements).  Points the pages leave open are the
- * numbered readings listed in the design doc; each call below names its readings.
+ * E8M0 shared exponent per 32 elements).  Points the pages leave open are
+ * settled by numbered readings (R1-R24); each call below states the readings
+ * it follows.
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays that

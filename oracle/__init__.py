@@ -25,8 +25,8 @@ What it follows (the pages and the readings of them):
 
 Element formats follow the public OCP Microscaling (MX) v1.0 rules (E2M1 and
 E4M3 elements with an E8M0 shared exponent per 32 elements), which is what
-"MX-style" means.  Every point the pages leave open is a numbered reading in
-the design doc; the functions below name the reading they implement.
+"MX-style" means.  Every point the pages leave open is settled by a numbered
+reading (R1-R24); the functions below state the reading they implement.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against closed forms, brute force, exhaustive

@@ -5,7 +5,7 @@ and the remaining blocks in FP4, and both paths are merged through online
 softmax into a single output.  The "Attention Quantization" topic page
 (overview) notes that softmax amplifies small quantisation errors, so the
 softmax itself stays in full precision and only the matmul operands are
-quantised.  Readings R7 and R12-R18 of the design doc fix the open points:
+quantised.  Readings R7 and R12-R18 fix the open points:
 
 * low-bit tiles: S = fl32(exact q_hat . k_hat) over MXFP4-dequantised Q and K;
   FP16 tiles: S = fl32(exact q . k) over the bf16 inputs (bf16 -> fp16 is exact);

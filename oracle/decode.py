@@ -4,7 +4,7 @@ HyQuant (summary, abstract): in decode the same hybrid principle is applied to
 KV-cache compression, and KV dequantisation is fused with the attention
 computation.  The NOVA-KV abstract (third page) states why this path is
 bandwidth-bound: each decode step reads the whole KV cache, and loading it
-takes longer than computing attention over it.  Readings (DESIGN.md R19, R20,
+takes longer than computing attention over it.  Readings (R19, R20,
 R23): keys/values are stored as asymmetric 4-bit codes with an fp16 scale and
 zero per 32 elements of head_dim; the first ``n_sink`` tokens and the last
 ``n_recent`` tokens of each sequence stay in fp16 (the high-precision

@@ -6,7 +6,8 @@ Sources: the ThriftAttention abstract (block-scaled quantisation moves
 attention to 4-bit; selected blocks stay FP16), the "Attention Quantization"
 topic page overview (block-scaled FP8/FP4 and integer formats), and the
 public OCP Microscaling v1.0 rules for E2M1, E4M3 and the E8M0 shared scale.
-Readings R2-R5, R7, R15, R17 and R19 of the design doc are implemented here.
+Readings R2-R5, R7, R15, R17 and R19 are implemented here; each function
+states the rule it follows.
 """
 
 from __future__ import annotations

@@ -4,7 +4,7 @@ ThriftAttention (abstract): "a heuristic rapidly selects a small number of
 important query-key block pairs for FP16 precision"; the error matters most
 for the most important query-key interactions.  HyQuant (summary, abstract):
 vertical-line tokens and a local sliding window are kept in full precision.
-The pages give no formula; the readings used here (DESIGN.md R8-R11) are:
+The pages give no formula; the readings used here (R8-R11) are:
 
 * importance estimate s_ij = mean(Q over query tile i) . mean(K over key tile j)
   (the logit of the tile means), fp32 with a fixed operation order;
