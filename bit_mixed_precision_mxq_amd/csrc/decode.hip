@@ -110,24 +110,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region(const void* base, int64
                                            bytes, 0x00020000);
 }
 
-// One INT4 block's loads for one lane.
-struct Blk {
-  u4v kc[2];           // K codes of token t0 + 16*set + (lane%16), group lane/16
-  uint32_t sz[4];      // dword `lane` of the block's 256-byte row span of each scale/zero array
-  uint32_t vc[8];      // V codes, dword lane%16 of rows t0 + 8*(lane/16) + r
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-wave LDS slot of one INT4 block: its V codes [32 rows][64 B].  Four
+// slots per wave rotate with the blocks in flight.
+constexpr int kSlotBytes = kBlk * (kD / 2);  // 2048
+constexpr int kInFlight = 3;                 // blocks whose loads are in flight while one is computed
+constexpr int kVmemPerBlk = 8;               // vector-memory instructions issue_blk issues
+
+// Register part of one block: K codes of token t0 + 16*set + (lane%16), group
+// lane/16, and dword `lane` of the block's 256-byte span of each scale/zero
+// array (token lane/2, half lane%2).
+struct KBlk {
+  u4v kc[2];
+  uint32_t sz[4];
 };
 
-// offk: lane's byte offset of its K code chunk at t0 = 0; offs: 4 * lane;
-// offv: its V code dword (row 8*(lane/16)).
-__device__ __forceinline__ void load_blk(Blk& x, const Rsrc& r, int t0, int offk, int offs, int offv) {
-  const int ok = offk + t0 * (kD / 2), os = offs + t0 * 8, ov = offv + t0 * (kD / 2);
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-    x.kc[st] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, ok + 16 * (kD / 2) * st, 0, 0);
+// Issue one block's loads (kVmemPerBlk vector-memory instructions): K codes
+// and scale/zero spans into registers, the V codes straight into the wave's
+// LDS slot (the 16 bytes of lane l land at byte 16 l of each 1 KB half).
+__device__ __forceinline__ void issue_blk(KBlk& x, const Rsrc& r, int t0, int offk, int lane, lds_char* slot) {
+  const int ok = offk + t0 * (kD / 2);
+  x.kc[0] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, ok, 0, 0);
+  x.kc[1] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, ok + 16 * (kD / 2), 0, 0);
+  const int ov = lane * 16 + t0 * (kD / 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)slot, 16, ov, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)(slot + 1024), 16, ov + 1024, 0, 0, 0);
+  const int os = lane * 4 + t0 * 8;
 #pragma unroll
   for (int a = 0; a < 4; ++a) x.sz[a] = __builtin_amdgcn_raw_buffer_load_b32(r.sz[a], os, 0, 0);
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) x.vc[rr] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, ov + (kD / 2) * rr, 0, 0);
+  // keep the block's loads together, ahead of the computation that follows,
+  // so that waits for the block being computed never cover these loads
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // 32 codes (16 bytes) -> 32 E4M3 bytes: low nibbles (even head_dim elements)
@@ -223,31 +238,41 @@ struct Ctx {
   int end, tl, hl;
   lds_s4* rd0;
   lds_s4* rd1;
-  uint2* wr;      // this wave's [32 tokens][4 heads] fp16x4 staging of p*s
-  uint32_t* sw;   // this wave's [32 tokens][4 arrays][2 dwords] scale/zero rows
+  uint2* wr;   // this wave's [16 tokens][4 heads] fp16x4 staging of p*s, tokens 0..15
+  uint2* wr2;  // tokens 16..31
   int lane;
 };
 
+// The LDS pointers are restrict parameters: after inlining, their accesses
+// carry alias scopes, which lets the compiler's wait insertion see that reads
+// of this block's slot do not depend on loads still landing in other slots.
 template <int G>
-__device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const Blk& x, int t0) {
+__device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const KBlk& x,
+                                            const lds_char* __restrict__ slot, u2v* __restrict__ szw,
+                                            uint2* __restrict__ wr, uint2* __restrict__ wr2,
+                                            lds_s4* __restrict__ rd0, lds_s4* __restrict__ rd1, int t0) {
+  // this block's V codes have landed once only the later blocks' loads may
+  // still be in flight (vector-memory loads complete in order); the compiler
+  // does not track loads that write LDS directly
+  __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");  // kInFlight * kVmemPerBlk
   const int tl = cx.tl, hl = cx.hl;
-  // fp16 scale/zero rows of the block's tokens through LDS: lane l holds
-  // dword l of each array's 32-token span (token l/2, half l%2); rows of
-  // tokens past the range are zeroed so that 0 * garbage cannot make a NaN
+  // scale/zero rows: lane l holds dword l of each array's span; share them
+  // through LDS ([array][32 tokens] of 8-byte rows) so that each lane has the
+  // four rows of its own tokens
   {
-    const bool wvalid = t0 + (cx.lane >> 1) < cx.end;
-    uint32_t* w = cx.sw + (cx.lane >> 1) * 8 + (cx.lane & 1);
+    uint32_t* w = reinterpret_cast<uint32_t*>(szw) + cx.lane;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) w[2 * a] = wvalid ? x.sz[a] : 0u;
+    for (int a = 0; a < 4; ++a) w[64 * a] = x.sz[a];
   }
   __asm__ volatile("" ::: "memory");
   u2v sz[2][4];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    const u4v* rr = reinterpret_cast<const u4v*>(cx.sw + (16 * st + tl) * 8);
-    const u4v s01 = rr[0], s23 = rr[1];
-    sz[st][0] = u2v{s01[0], s01[1]}; sz[st][1] = u2v{s01[2], s01[3]};
-    sz[st][2] = u2v{s23[0], s23[1]}; sz[st][3] = u2v{s23[2], s23[3]};
+#pragma unroll
+    for (int a = 0; a < 4; ++a) sz[st][a] = szw[32 * a + 16 * st + tl];
+    // V scale and zero rows of tokens past the range are zeroed, so that the
+    // zero weight of such a token cannot meet garbage from beyond the sequence
+    if (t0 + 16 * st + tl >= cx.end) { sz[st][2] = u2v{0u, 0u}; sz[st][3] = u2v{0u, 0u}; }
   }
   // scores of tokens t0 + 16*st + tl for head hl
   float xs[2];
@@ -294,24 +319,29 @@ __device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const Blk& 
     const uint32_t vs01 = sz[st][2][0], vs23 = sz[st][2][1];
     const h2 p01 = pp * __builtin_bit_cast(h2, vs01);
     const h2 p23 = pp * __builtin_bit_cast(h2, vs23);
-    cx.wr[(16 * st + tl) * 4 + hl] = uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+    (st == 0 ? wr : wr2)[tl * 4 + hl] = uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
   }
   __asm__ volatile("" ::: "memory");
-  const s4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(cx.rd0);
-  const s4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(cx.rd1);
+  const s4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(rd0);
+  const s4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(rd1);
   __asm__ volatile("" ::: "memory");
-  // A operand: row 4h+g, tokens 8*(lane/16) + e
+  // A operand: row 4h+g, K slot e = token 4e + lane/16
   const v4i pai = __builtin_shufflevector(__builtin_bit_cast(v2i_t, ra), __builtin_bit_cast(v2i_t, rb), 0, 1, 2, 3);
   const v8h pA = __builtin_bit_cast(v8h, pai);
-  // B operand of head_dim column 8*(lane%16) + dd, tokens 8*(lane/16) + e:
+  // B operand of head_dim column 8*(lane%16) + dd, tokens 4e + lane/16:
   // byte kb of the lane's code dword holds columns 2kb (low nibble) and 2kb+1
   // (high nibble); each code becomes the fp16 subnormal 16*code*2^-24, i.e.
   // the nibble moved to bits 4..7 of a zero-extended byte
+  // rows 4e + (lane/16), e = 0..7, dword lane%16 (K slot e of the B operand
+  // is token 4e + lane/16; the A operand above uses the same order)
+  typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+  lds_u32* vb = (lds_u32*)slot + 16 * hl + tl;
   uint32_t hiR[8], loR[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    hiR[r] = x.vc[r] & 0xF0F0F0F0u;
-    loR[r] = (x.vc[r] << 4) & 0xF0F0F0F0u;
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t v = vb[64 * e];
+    hiR[e] = v & 0xF0F0F0F0u;
+    loR[e] = (v << 4) & 0xF0F0F0F0u;
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -328,11 +358,19 @@ __device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const Blk& 
 }
 
 template <int G>
-__global__ void __launch_bounds__(256, 2) k_decode_split(DecodeArgs a) {
+__global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
   __shared__ float s_o[kWaves][4][kD];
   __shared__ float s_ml[kWaves][4][2];
-  __shared__ uint2 s_p[kWaves][kBlk][4];  // fp16 p*s_v of (token, head), 4 groups each
-  __shared__ uint32_t s_sz[kWaves][kBlk * 8];  // scale/zero rows of the current block
+  // fp16 p*s_v of (token, head), 4 groups each: tokens 0..15, then 16..31
+  __shared__ uint2 s_p[kWaves][kBlk / 2][4];
+  __shared__ uint2 s_p2[kWaves][kBlk / 2][4];
+  // INT4 blocks in flight, one array per slot (separate objects, so that
+  // reads of one slot never wait for loads still landing in another)
+  __shared__ __align__(16) char s_blk0[kWaves][kSlotBytes];
+  __shared__ __align__(16) char s_blk1[kWaves][kSlotBytes];
+  __shared__ __align__(16) char s_blk2[kWaves][kSlotBytes];
+  __shared__ __align__(16) char s_blk3[kWaves][kSlotBytes];
+  __shared__ u2v s_sz[kWaves][4 * kBlk];  // scale/zero rows of the block being computed
   const int s = blockIdx.x;
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
@@ -421,12 +459,12 @@ __global__ void __launch_bounds__(256, 2) k_decode_split(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) cx.qs[g] = qs[g];
     cx.c = a.c; cx.end = end; cx.tl = tl; cx.hl = hl;
-    // transposed-read addresses of this lane: token 8*(lane/16) + 4r + (lane/4)%4, head lane%4
+    // transposed-read addresses of this lane: token 4(4r + (lane/4)%4) + lane/16, head lane%4
     const int rq = lane >> 4, rk = (lane >> 2) & 3, rh = lane & 3;
-    cx.rd0 = (lds_s4*)(&s_p[wave][8 * rq + rk][rh]);
-    cx.rd1 = (lds_s4*)(&s_p[wave][8 * rq + 4 + rk][rh]);
+    cx.rd0 = (lds_s4*)(&s_p[wave][4 * rk + rq][rh]);
+    cx.rd1 = (lds_s4*)(&s_p2[wave][4 * rk + rq][rh]);
     cx.wr = &s_p[wave][0][0];
-    cx.sw = &s_sz[wave][0];
+    cx.wr2 = &s_p2[wave][0][0];
     cx.lane = lane;
 
     const int L = a.kv.L_cap;
@@ -438,30 +476,46 @@ __global__ void __launch_bounds__(256, 2) k_decode_split(DecodeArgs a) {
     rs.sz[2] = region(a.kv.v_scale, bh * L * 8, L * 8);
     rs.sz[3] = region(a.kv.v_zero, bh * L * 8, L * 8);
     const int offk = tl * (kD / 2) + 16 * jg;
-    const int offv = 8 * jg * (kD / 2) + 4 * tl;
     constexpr int kStep = kBlk * kWaves;
     int t0 = beg + kBlk * wave;
+    lds_char* sl0 = (lds_char*)&s_blk0[wave][0];
+    lds_char* sl1 = (lds_char*)&s_blk1[wave][0];
+    lds_char* sl2 = (lds_char*)&s_blk2[wave][0];
+    lds_char* sl3 = (lds_char*)&s_blk3[wave][0];
+    u2v* szw = &s_sz[wave][0];
     if (t0 < end) {
-      // three register buffers in turn: two blocks' loads are in flight while
-      // the third is computed; past the end the current block is loaded again
-      // (cache hits) so that every iteration issues the same loads
-      Blk b0, b1, b2;
-      load_blk(b0, rs, t0, offk, 4 * lane, offv);
-      load_blk(b1, rs, t0 + kStep < end ? t0 + kStep : t0, offk, 4 * lane, offv);
-      for (;;) {
-        load_blk(b2, rs, t0 + 2 * kStep < end ? t0 + 2 * kStep : t0, offk, 4 * lane, offv);
-        process_blk<G>(st_, cx, b0, t0);
-        if (t0 + kStep >= end) break;
+      // four blocks rotate through registers and LDS slots: a block is
+      // computed while the next three blocks' loads are in flight, and its
+      // registers and slot are refilled with the block four ahead right after.
+      // The loop runs whole groups of four steps with one exit: a step past
+      // the range computes nothing (all its tokens are masked), and loads past
+      // the range re-read the current block (cache hits), so every step
+      // issues the same loads and the wait count in process_blk holds.
+      const int n_steps = (end - t0 + kStep - 1) / kStep;
+      const int n_groups = (n_steps + 3) / 4;
+      KBlk k0, k1, k2, k3;
+#define MXQ_AT(d) (t0 + (d) * kStep < end ? t0 + (d) * kStep : t0)
+      issue_blk(k0, rs, t0, offk, lane, sl0);
+      issue_blk(k1, rs, MXQ_AT(1), offk, lane, sl1);
+      issue_blk(k2, rs, MXQ_AT(2), offk, lane, sl2);
+      issue_blk(k3, rs, MXQ_AT(3), offk, lane, sl3);
+      for (int grp = 0; grp < n_groups; ++grp) {
+        process_blk<G>(st_, cx, k0, sl0, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        issue_blk(k0, rs, MXQ_AT(4), offk, lane, sl0);
         t0 += kStep;
-        load_blk(b0, rs, t0 + 2 * kStep < end ? t0 + 2 * kStep : t0, offk, 4 * lane, offv);
-        process_blk<G>(st_, cx, b1, t0);
-        if (t0 + kStep >= end) break;
+        process_blk<G>(st_, cx, k1, sl1, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        issue_blk(k1, rs, MXQ_AT(4), offk, lane, sl1);
         t0 += kStep;
-        load_blk(b1, rs, t0 + 2 * kStep < end ? t0 + 2 * kStep : t0, offk, 4 * lane, offv);
-        process_blk<G>(st_, cx, b2, t0);
-        if (t0 + kStep >= end) break;
+        process_blk<G>(st_, cx, k2, sl2, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        issue_blk(k2, rs, MXQ_AT(4), offk, lane, sl2);
+        t0 += kStep;
+        process_blk<G>(st_, cx, k3, sl3, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        issue_blk(k3, rs, MXQ_AT(4), offk, lane, sl3);
         t0 += kStep;
       }
+#undef MXQ_AT
+      // the re-issued loads past the end still write LDS: let them land
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     const float m_run = st_.m_run, l_run = st_.l_run;
     float Z[4];
@@ -547,7 +601,7 @@ __global__ void __launch_bounds__(kD) k_decode_merge(const float* __restrict__ w
 
 int pick_splits(int max_seq_len, int num_splits) {
   if (num_splits > 0) return num_splits;
-  int s = (max_seq_len + 2047) / 2048;
+  int s = (max_seq_len + 4095) / 4096;
   return s < 1 ? 1 : (s > 64 ? 64 : s);
 }
 
