@@ -55,9 +55,10 @@ def test_workspace_sizes(lib):
     s = mxq.AttnShape(1, 32, 8, 8192, 8192, 128, 128, 64, 1)
     n = so.attn_select_blocks_workspace(ctypes.byref(s))
     assert n == (1 * 32 * 64 + 1 * 8 * 128) * 128 * 4
-    # 16 INT4 splits plus one for the fp16 sink and recent tokens
+    # INT4 splits plus one for the fp16 sink and recent tokens; the default is
+    # one split per 4096 cached tokens
     assert so.attn_quantkv_decode_workspace(64, 32, 128, 16, 32768) == 64 * 32 * 17 * 130 * 4
-    assert so.attn_quantkv_decode_workspace(64, 32, 128, 0, 32768) == 64 * 32 * 17 * 130 * 4
+    assert so.attn_quantkv_decode_workspace(64, 32, 128, 0, 32768) == 64 * 32 * 9 * 130 * 4
 
 
 def test_host_validation_rejects_before_launch(lib):
