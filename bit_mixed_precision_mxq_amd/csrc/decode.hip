@@ -637,6 +637,9 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
               "attn_quantkv_decode: recent arrays missing");
   MXQ_REQUIRE(max_seq_len >= 1 && max_seq_len <= kv->L_cap, MXQ_EINVAL,
               "attn_quantkv_decode: need 1 <= max_seq_len <= L_cap");
+  // each (sequence, kv head) region of the code arrays is addressed with
+  // 32-bit byte offsets (L_cap * 64 bytes)
+  MXQ_REQUIRE(kv->L_cap <= (1 << 25), MXQ_EUNSUPPORTED, "attn_quantkv_decode: L_cap must be <= 2^25");
   MXQ_REQUIRE(num_splits >= 0 && num_splits <= 4096, MXQ_EINVAL, "attn_quantkv_decode: num_splits out of range");
   MXQ_REQUIRE(B <= 65535 && Hkv <= 65535, MXQ_EUNSUPPORTED, "attn_quantkv_decode: B, Hkv must be <= 65535");
   MXQ_REQUIRE(!(softmax_scale != softmax_scale), MXQ_EINVAL, "attn_quantkv_decode: softmax_scale is NaN");

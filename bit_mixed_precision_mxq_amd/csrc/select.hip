@@ -25,28 +25,38 @@ namespace {
 
 constexpr int kMaxKeyTiles = 2048;
 
-__global__ void k_tile_means(const uint16_t* __restrict__ x, float* __restrict__ mean, int N,
-                             int D, int T, int n_valid, int n_tiles) {
-  int d = threadIdx.x;
-  int tile = blockIdx.x;
-  int64_t bh = blockIdx.y;
+// mean of rows [tile*T, tile*T + T) of x (capped at n_valid), column d.  The
+// row loads are issued 16 at a time; the sum is taken in ascending row order.
+// transposed == 0 writes mean[(bh*n_tiles + tile)*D + d], else
+// mean[(bh*D + d)*n_tiles + tile] (so that a thread per key tile reads a
+// column of means with consecutive threads at consecutive addresses).
+__global__ void __launch_bounds__(128) k_tile_means(const uint16_t* __restrict__ x, float* __restrict__ mean,
+                                                    int N, int D, int T, int n_valid, int n_tiles,
+                                                    int transposed) {
+  const int d = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int64_t bh = blockIdx.y;
   if (d >= D) return;
   const uint16_t* base = x + (bh * N + static_cast<int64_t>(tile) * T) * D + d;
+  const int rows = max(0, min(T, n_valid - tile * T));
   float acc = 0.0f;
-  int cnt = 0;
-  for (int r = 0; r < T; ++r) {
-    if (tile * T + r < n_valid) {
-      acc = acc + bf16_to_f32(base[static_cast<int64_t>(r) * D]);
-      ++cnt;
-    }
+  int r = 0;
+  for (; r + 16 <= rows; r += 16) {
+    uint16_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = base[static_cast<int64_t>(r + u) * D];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc = acc + bf16_to_f32(v[u]);
   }
-  float m = cnt > 0 ? acc / static_cast<float>(cnt) : 0.0f;  // correctly rounded division
-  mean[(bh * n_tiles + tile) * D + d] = m;
+  for (; r < rows; ++r) acc = acc + bf16_to_f32(base[static_cast<int64_t>(r) * D]);
+  const float m = rows > 0 ? acc / static_cast<float>(rows) : 0.0f;  // correctly rounded division
+  if (transposed) mean[(bh * D + d) * n_tiles + tile] = m;
+  else mean[(bh * n_tiles + tile) * D + d] = m;
 }
 
 struct SelectArgs {
   const float* qmean;  // [B*Hq][n_qt][D]
-  const float* kmean;  // [B*Hkv][n_kt][D]
+  const float* kmean;  // [B*Hkv][D][n_kt] (transposed)
   uint32_t* mask;      // [B*Hq][n_qt][words]
   int32_t* n_fp16;     // [B*Hq][n_qt] or null
   float* scores;       // [B*Hq][n_qt][n_kt] or null
@@ -73,9 +83,10 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
 
   // scores of every key tile (also invalid ones, for inspection)
   for (int j = tid; j < a.n_kt; j += blockDim.x) {
-    const float* km = a.kmean + (bhk * a.n_kt + j) * a.D;
+    const float* km = a.kmean + bhk * a.D * a.n_kt + j;
     float acc = 0.0f;
-    for (int d = 0; d < a.D; ++d) acc = acc + s_q[d] * km[d];  // two roundings: contraction is off here
+#pragma unroll 16
+    for (int d = 0; d < a.D; ++d) acc = acc + s_q[d] * km[static_cast<int64_t>(d) * a.n_kt];  // two roundings: contraction is off here
     s_score[j] = acc;
     if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
   }
@@ -174,10 +185,10 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
   float* qmean = static_cast<float*>(workspace);
   float* kmean = qmean + static_cast<size_t>(s->B) * s->Hq * n_qt * s->D;
   hipLaunchKernelGGL(k_tile_means, dim3(n_qt, s->B * s->Hq), dim3(s->D), 0, strm, q, qmean, s->N,
-                     s->D, s->Bq, s->n_valid, n_qt);
+                     s->D, s->Bq, s->n_valid, n_qt, 0);
   if ((st = check_launch("k_tile_means(q)")) != MXQ_OK) return st;
   hipLaunchKernelGGL(k_tile_means, dim3(n_kt, s->B * s->Hkv), dim3(s->D), 0, strm, k, kmean, s->N,
-                     s->D, s->Bk, s->n_valid, n_kt);
+                     s->D, s->Bk, s->n_valid, n_kt, 1);
   if ((st = check_launch("k_tile_means(k)")) != MXQ_OK) return st;
   SelectArgs a;
   a.qmean = qmean; a.kmean = kmean; a.mask = mask; a.n_fp16 = n_fp16; a.scores = scores;

@@ -192,8 +192,13 @@ typedef struct {
  * abstract).  The keys of each (b, kv head) are split into num_splits ranges
  * processed independently and merged in ascending split order (reading R23);
  * num_splits 0 picks a value.  q: bf16 [B][Hq][D]; out: f32 [B][Hq][D].
- * workspace: at least attn_quantkv_decode_workspace(...) bytes (caller-owned).
- * D must be 128 (or 64); Hq / Hkv must be <= 16.
+ * workspace: at least attn_quantkv_decode_workspace(...) bytes (caller-owned,
+ * contents undefined after the call).  Supported: D = 128; Hq / Hkv in
+ * {1, 2, 4}; L_cap <= 2^25.  MXQ_EUNSUPPORTED otherwise.
+ * Rounding: scores and the fp32 softmax follow the reference arithmetic up to
+ * fp32 accumulation order; the weights p * scale enter the value product in
+ * fp16 (relative rounding 2^-11 each), so outputs differ from an all-fp32
+ * evaluation by about 1e-4 at unit-variance values.
  * ------------------------------------------------------------------------- */
 size_t attn_quantkv_decode_workspace(int32_t B, int32_t Hq, int32_t D, int32_t num_splits,
                                      int32_t max_seq_len);
