@@ -154,8 +154,15 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
   const int lane = tid & 63;
   const int col = lane & 15;   // query column within the wave's 16 rows
   const int g = lane >> 4;     // lane group 0..3
-  const int it = a.n_qt - 1 - static_cast<int>(blockIdx.x);  // longest causal tiles first
-  const int h = blockIdx.y;
+  // Work order: workgroups are dispatched in linear id order, round-robin
+  // over the 8 XCDs.  Linear id L takes query tile n_qt-1 - L/Hq (longest
+  // causal tiles of every head first, then shorter ones fill in) and, when Hq
+  // is a multiple of 8, head (Hq/8)*(L%8) + (L%Hq)/8, so that each XCD (and
+  // its L2) serves a contiguous block of query heads, i.e. whole kv groups.
+  const int lin = static_cast<int>(blockIdx.x) + a.n_qt * static_cast<int>(blockIdx.y);
+  const int it = a.n_qt - 1 - lin / a.Hq;
+  const int hr = lin % a.Hq;
+  const int h = (a.Hq % 8 == 0) ? (a.Hq / 8) * (hr % 8) + hr / 8 : hr;
   const int b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
