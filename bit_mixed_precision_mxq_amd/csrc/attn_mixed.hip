@@ -63,6 +63,7 @@ constexpr float kGridMagic = 6144.0f;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^
 constexpr float kExpOffset = 8.0f;     // P is stored as E4M3(2^(x + 8)) * 2^-8
 constexpr int kPScale = 119;           // E8M0 code of 2^-8
 constexpr float kMaxLag = 64.0f;       // largest gap kept between O's reference and the running one
+constexpr int kMaxChunks = 1024;       // 128-key chunks: 2048 key tiles of 64
 
 // Key (within the 128-key chunk) that A-operand row r of S-block beta holds.
 __device__ __forceinline__ int chunk_key(int beta, int r) {
@@ -92,7 +93,7 @@ __device__ __forceinline__ float rowmax4(float v) {
 }
 
 // LDS layouts.
-//  Low-bit chunk (128 keys, two buffers):
+//  Low-bit chunk (128 keys, a ring of three buffers):
 //   K codes: FP4 rows of D/2 bytes (D/32 chunks of 16 bytes), the chunk index
 //     XOR-swizzled with key bits so the 16 rows one MFMA operand read touches
 //     fall in distinct banks (for D = 64 rows also swap 4 apart);
@@ -103,6 +104,7 @@ __device__ __forceinline__ float rowmax4(float v) {
 //   V scales: byte [g][col][db] = scale of key block g of row 16*db+col.
 //  FP16 tile (64 keys, one buffer): bf16 K rows of 2*D bytes with the 16-byte
 //  chunk index XOR-swizzled by 4 key bits; fp16 V^T rows padded to 144 bytes.
+//  bf16 Q of the workgroup's 128 rows (read by the FP16 tiles' QK), loaded once.
 template <int D>
 struct Lds {
   static constexpr int KROW = D / 2;
@@ -113,10 +115,16 @@ struct Lds {
   static constexpr int V_OFF = KS_OFF + 512;
   static constexpr int VS_OFF = V_OFF + D * VSTRIDE;
   static constexpr int LO_BYTES = VS_OFF + 512;
-  static constexpr int HK_OFF = 2 * LO_BYTES;             // bf16 K tile
+  static constexpr int RING = 3;                          // low-bit chunk buffers
+  static constexpr int HK_OFF = RING * LO_BYTES;          // bf16 K tile
   static constexpr int HV_OFF = HK_OFF + 64 * 2 * D;      // fp16 V^T tile
   static constexpr int ONES_OFF = HV_OFF + D * VSTRIDE;   // 32 B of E4M3 1.0, 16 B of fp16 1.0
-  static constexpr int BYTES = ONES_OFF + 48;
+  static constexpr int Q_OFF = ONES_OFF + 48;             // bf16 Q tile of the workgroup
+  static constexpr int BYTES = Q_OFF + 128 * 2 * D;
+  // bf16 Q row r, 16-byte unit u (8 head_dim elements), XOR-swizzled by the row
+  __device__ static __forceinline__ int q_off(int r, int u) {
+    return Q_OFF + r * 2 * D + 16 * (u ^ (r & (D / 8 - 1)));
+  }
   __device__ static __forceinline__ int k_off(int key, int g) {
     if constexpr (D == 128) {
       return K_OFF + key * KROW + 16 * (g ^ ((key >> 4) & 3));
@@ -133,8 +141,16 @@ struct Lds {
   }
 };
 
+
+// One FP4 x FP4 QK block: S^T[16 keys x 16 queries] over the whole head_dim.
+// The key's scale byte is selected from the packed word by op_sel (beta & 3).
+#define MXQ_QK_BLOCK(OPSEL) \
+  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, OPSEL, sc, 0, qsc)
+#define MXQ_PV_BLOCK(OPSEL) \
+  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, o, 0, 0, OPSEL, vs, 0, psc)
+
 template <int D>
-__global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
+__global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   using LY = Lds<D>;
   constexpr int BQ = 128;        // query rows per workgroup
   constexpr int NT = 512;        // 8 waves of 16 rows
@@ -150,7 +166,7 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sm[LY::BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;   // query column within the wave's 16 rows
   const int g = lane >> 4;     // lane group 0..3
@@ -195,7 +211,6 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
     qf4[0] = w[0]; qf4[1] = w[1]; qf4[2] = w[2]; qf4[3] = w[3];
     qsc = a.q_scales[(bhq * a.N + q) * NSB + g];
   }
-  const uint16_t* qrow_bf16 = a.q_bf16 ? a.q_bf16 + (bhq * a.N + q) * D : nullptr;
 
   v4f O[NDB];
 #pragma unroll
@@ -205,14 +220,16 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
   float m_o = NEG_INF;     // reference O and L are currently expressed in
   const float c = a.c;
 
-  // Promotion flags.  The workgroup's 128 rows may span two selection tiles
-  // (64-row tiles): each wave reads the mask row of its own rows, and staging
+  // Promotion flags.  Selection tiles are 64 or 128 rows high, so the
+  // workgroup's 128 rows lie in one or two mask rows (ra, rb) and each wave's
+  // 16 rows in one of them.  Each wave uses the flags of its own row; staging
   // uses the union (FP16 data some wave needs) and the intersection (low-bit
-  // data is needed unless every wave promotes the tile).
+  // data is needed unless every wave promotes the tile).  The two rows' bits
+  // are unpacked once per workgroup into one byte per chunk in LDS.
   const int64_t mbase = bhq * (a.N / a.sel_bq);
-  const uint32_t* mrow_w = a.mask ? a.mask + (mbase + wq_lo / a.sel_bq) * a.words : nullptr;
   const uint32_t* mrow_a = a.mask ? a.mask + (mbase + qs / a.sel_bq) * a.words : nullptr;
   const uint32_t* mrow_b = a.mask ? a.mask + (mbase + (qs + BQ - 1) / a.sel_bq) * a.words : nullptr;
+  const bool w_in_b = wq_lo / a.sel_bq != qs / a.sel_bq;
   auto row_flags = [&](const uint32_t* mr, int ch) -> int {  // bit t: tile t of chunk ch is FP16
     const int j0 = 2 * ch;
     const bool valid1 = j0 + 1 <= last_tile;
@@ -222,12 +239,14 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
     return static_cast<int>((wbits >> (j0 & 31)) & 1u) |
            (valid1 ? static_cast<int>(((wbits >> ((j0 + 1) & 31)) & 1u) << 1) : 0);
   };
+  __shared__ uint8_t s_fl[kMaxChunks];  // per chunk: bits 0-1 row ra, bits 2-3 row rb
+  for (int ch = tid; ch < n_chunks; ch += NT)
+    s_fl[ch] = static_cast<uint8_t>(row_flags(mrow_a, ch) | (row_flags(mrow_b, ch) << 2));
   // packed: bits 0-1 this wave, 2-3 any wave, 4-5 every wave
   auto chunk_flags = [&](int ch) -> int {
-    const int fw = row_flags(mrow_w, ch);
-    const int fa = row_flags(mrow_a, ch);
-    const int fb = row_flags(mrow_b, ch);
-    return fw | ((fa | fb) << 2) | ((fa & fb) << 4);
+    const int v = __builtin_amdgcn_readfirstlane(static_cast<int>(s_fl[ch]));
+    const int fa = v & 3, fb = v >> 2;
+    return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4);
   };
   auto needs_low = [&](int ch, int fl) -> bool {
     const int all = (fl >> 4) & 3;
@@ -263,8 +282,7 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
     }
     if (tid < D) pvs = *reinterpret_cast<const uint32_t*>(a.v_scales + (bhk * D + tid) * (a.N / 32) + kc / 32);
   };
-  auto stage_store = [&](int buf) {
-    uint8_t* sb = sm + buf * LY::LO_BYTES;
+  auto stage_store = [&](uint8_t* sb) {
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
       const int u = tid + i * NT;
@@ -287,26 +305,29 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
         sb[LY::VS_OFF + (kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(pvs >> (8 * kb));
     }
   };
-  auto stage_fp16_tile = [&](int kt0) {
-    constexpr int HKU = 64 * 2 * D / 16;  // 16-byte units of the bf16 K tile
-    v4i hk[(HKU + NT - 1) / NT], hv[(D * 8 + NT - 1) / NT];
+  // FP16 tile staging: global loads into registers, then LDS stores
+  constexpr int HKU = 64 * 2 * D / 16;  // 16-byte units of the bf16 K tile
+  constexpr int HKR = (HKU + NT - 1) / NT, HVR = (D * 8 + NT - 1) / NT;
+  auto fp16_tile_load = [&](int kt0, v4i (&hk)[HKR], v4i (&hv)[HVR]) {
 #pragma unroll
-    for (int i = 0; i < (HKU + NT - 1) / NT; ++i) {
+    for (int i = 0; i < HKR; ++i) {
       const int u = tid + i * NT;
       if (u < HKU) hk[i] = reinterpret_cast<const v4i*>(a.k_bf16 + (bhk * a.N + kt0 + u / (D / 8)) * D)[u % (D / 8)];
     }
 #pragma unroll
-    for (int i = 0; i < (D * 8 + NT - 1) / NT; ++i) {
+    for (int i = 0; i < HVR; ++i) {
       const int u = tid + i * NT;
       if (u < D * 8) hv[i] = *reinterpret_cast<const v4i*>(a.v_f16t + (bhk * D + (u >> 3)) * a.N + kt0 + 8 * (u & 7));
     }
+  };
+  auto fp16_tile_store = [&](const v4i (&hk)[HKR], const v4i (&hv)[HVR]) {
 #pragma unroll
-    for (int i = 0; i < (HKU + NT - 1) / NT; ++i) {
+    for (int i = 0; i < HKR; ++i) {
       const int u = tid + i * NT;
       if (u < HKU) *reinterpret_cast<v4i*>(sm + LY::hk_off(u / (D / 8), u % (D / 8))) = hk[i];
     }
 #pragma unroll
-    for (int i = 0; i < (D * 8 + NT - 1) / NT; ++i) {
+    for (int i = 0; i < HVR; ++i) {
       const int u = tid + i * NT;
       if (u < D * 8) *reinterpret_cast<v4i*>(sm + LY::HV_OFF + (u >> 3) * LY::VSTRIDE + 16 * (u & 7)) = hv[i];
     }
@@ -317,145 +338,303 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
     // lane groups g >= D/32 carry no head_dim data: their K scale bytes must be
     // a finite E8M0 (0xFF would be NaN), so set them to 127 (= 1.0) once
     constexpr int PAD = (4 - NSB) * 16 * 8;
-    for (int i = tid; i < 2 * PAD; i += NT)
+    for (int i = tid; i < LY::RING * PAD; i += NT)
       sm[(i / PAD) * LY::LO_BYTES + LY::KS_OFF + NSB * 16 * 8 + i % PAD] = 127;
   }
 
   // per-lane LDS byte offsets (constant over the pass)
-  int koff[8];
-#pragma unroll
-  for (int beta = 0; beta < 8; ++beta) koff[beta] = LY::k_off(chunk_key(beta, col), g);
+  // K fragment of S block beta: a per-lane base plus a constant per block
+  // (lane bits and block bits of chunk_key() do not interact in k_off()); no
+  // array, so nothing is indexed at run time
+  const int kbase0 = LY::k_off(chunk_key(0, col), g);
+  const int kbase1 = LY::k_off(chunk_key(1, col), g);
+  auto koff = [&](int beta) -> int {
+    if constexpr (D == 128) {
+      return kbase0 + LY::KROW * (64 * (beta >> 2) + 4 * (beta & 3));
+    } else {  // the row swizzle flips key bit 2, i.e. block bit 0
+      return (beta & 1 ? kbase1 : kbase0) + LY::KROW * (64 * (beta >> 2) + 4 * (beta & 2));
+    }
+  };
   const int ksoff = LY::KS_OFF + (g * 16 + col) * 8;
+  auto qk_block = [&](const v8i& ka, int sc, int beta) -> v4f {
+    switch (beta & 3) {
+      case 0: return MXQ_QK_BLOCK(0);
+      case 1: return MXQ_QK_BLOCK(1);
+      case 2: return MXQ_QK_BLOCK(2);
+      default: return MXQ_QK_BLOCK(3);
+    }
+  };
+  auto pv_block = [&](const v8i& va, const v8i& pb, const v4f& o, int vs, int psc, int db) -> v4f {
+    switch (db & 3) {
+      case 0: return MXQ_PV_BLOCK(0);
+      case 1: return MXQ_PV_BLOCK(1);
+      case 2: return MXQ_PV_BLOCK(2);
+      default: return MXQ_PV_BLOCK(3);
+    }
+  };
   const int voff = LY::V_OFF + col * LY::VSTRIDE + 16 * g;
   const int vsoff = LY::VS_OFF + (g * 16 + col) * 8;
 
-  int flags = chunk_flags(0);
-  bool have_next = false;
-  if (needs_low(0, flags)) {
+  // ---- low-bit building blocks (chunk staged in LDS at sb)
+  // S^T blocks of the chunk's 128 keys: one FP4 x FP4 MFMA per 16 keys
+  auto qk_lowbit = [&](const uint8_t* sb, v4f (&S)[8]) {
+    const uint32_t* ksw = reinterpret_cast<const uint32_t*>(sb + ksoff);
+    const uint32_t ksc0 = ksw[0], ksc1 = ksw[1];
+#pragma unroll
+    for (int beta = 0; beta < 8; ++beta) {
+      v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
+      const v4i w = *reinterpret_cast<const v4i*>(sb + koff(beta));
+      ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
+      const int sc = beta < 4 ? static_cast<int>(ksc0) : static_cast<int>(ksc1);
+      S[beta] = qk_block(ka, sc, beta);
+    }
+  };
+  // running reference after an unmasked low-bit chunk: integer per-tile
+  // references m0 <= m1 and, when O's reference lags too far, a rebase
+  auto chunk_max = [&](const v4f (&S)[8], float& m0, float& m1) {
+    float mx0 = max3f(S[0][0], S[0][1], S[0][2]);
+    float mx1 = max3f(S[4][0], S[4][1], S[4][2]);
+    mx0 = max3f(mx0, S[0][3], S[1][0]);
+    mx1 = max3f(mx1, S[4][3], S[5][0]);
+#pragma unroll
+    for (int e = 5; e < 16; e += 2) {  // remaining 11 values of each tile, two per v_max3
+      const float a0 = S[e >> 2][e & 3], b0 = e + 1 < 16 ? S[(e + 1) >> 2][(e + 1) & 3] : a0;
+      const float a1 = S[4 + (e >> 2)][e & 3], b1 = e + 1 < 16 ? S[4 + ((e + 1) >> 2)][(e + 1) & 3] : a1;
+      mx0 = max3f(mx0, a0, b0);
+      mx1 = max3f(mx1, a1, b1);
+    }
+    mx0 = rowmax4(mx0);
+    mx1 = rowmax4(mx1);
+    m0 = fmaxf(m_run, ceilf(mx0 * c));
+    m1 = fmaxf(m0, ceilf(mx1 * c));
+    m_run = m1;
+  };
+  auto chunk_lag = [&](float m0, float m1) {
+    // O and L stay expressed against a lagging reference m_o <= m0: each
+    // tile's contribution is scaled by 2^(m_t - m_o) through the E8M0 scale
+    // of its P blocks, so O is only rescaled when the gap grows large
+    if (m_o == NEG_INF) m_o = m0;
+    if (__any(m1 - m_o > kMaxLag)) rebase(m1);
+  };
+  auto chunk_refs = [&](const v4f (&S)[8], float& m0, float& m1) {
+    chunk_max(S, m0, m1);
+    chunk_lag(m0, m1);
+  };
+  // P = E4M3(2^xq) of one S block (4 scores per lane -> 4 bytes)
+  auto p_block = [&](const v4f& s4, float off) -> int {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s4[i], c, off) - kGridMagic);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+  };
+  // O^T += V^T P^T (FP8 x FP8) and L += sum(P) for a staged chunk
+  auto pv_lowbit = [&](const uint8_t* sb, const v8i& pb, int psc) {
+    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
+    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
+      const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
+      const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
+      const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
+      O[db] = pv_block(va, pb, O[db], vs, psc, db);
+    }
+    const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
+    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+  };
+
+  // ---- main loop over 128-key chunks.
+  // Ring protocol: chunk ch+1's low-bit data (loaded into registers during
+  // iteration ch-1) is written to its ring buffer at the top of iteration ch,
+  // the loads for chunk ch+2 are issued, then one barrier.  After it, chunks ch
+  // and ch+1 are both visible, and ring buffer (ch+2)%3 may be overwritten in
+  // the next iteration (its previous chunk, ch-1, was finished by every wave
+  // before this barrier).
+  // Software pipeline for runs of unmasked all-low-bit chunks: while the
+  // exponentials of chunk ch are computed, the FP4 QK MFMAs of chunk ch+1 are
+  // issued into the score registers just consumed, and the row maxima of chunk
+  // ch+1 are taken while the PV MFMAs of chunk ch run.
+  v4f S[8];
+  float hm0 = 0.0f, hm1 = 0.0f;   // tile references of the chunk whose scores S holds
+  bool s_ready = false;           // S already holds the scores of chunk ch
+  auto is_hot = [&](int ch, int fl) -> bool {
+    const int kc = ch * 128;
+    const bool valid1 = 2 * ch + 1 <= last_tile;
+    const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
+    return !((fl >> 2) & 3) && valid1 && !need_mask;
+  };
+  // P blocks of the chunk held in S (references hm0, hm1)
+  auto p_scale = [&]() -> int {
+    // 2^-8 * 2^(m_t - m_o); below 2^-127 (after a forced rebase) the tile adds nothing visible
+    return static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + ((g < 2 ? hm0 : hm1) - m_o), 0.0f), 254.0f));
+  };
+  // last chunk of a run: exponentials and PV only
+  auto hot_chunk = [&](const uint8_t* sb) {
+    const float off0 = kGridMagic + kExpOffset - hm0;  // hm0 is finite: key 0.. are valid
+    const float off1 = kGridMagic + kExpOffset - hm1;
+    v8i pb;
+#pragma unroll
+    for (int beta = 0; beta < 8; ++beta) pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
+    pv_lowbit(sb, pb, p_scale());
+  };
+  // chunk ch (scores in S) followed by another hot chunk at sbn.  Issue order,
+  // fixed with scheduling barriers: the next chunk's K fragments; per S block
+  // its exponentials and then the FP4 QK MFMA of the next chunk into the same
+  // registers (the vector ALU and the matrix core work side by side); per
+  // head_dim block the V fragments two blocks ahead, one PV MFMA and a slice of
+  // the next chunk's row maxima.
+  auto hot_chunk_next = [&](const uint8_t* sb, const uint8_t* sbn) {
+    const float off0 = kGridMagic + kExpOffset - hm0;
+    const float off1 = kGridMagic + kExpOffset - hm1;
+    const uint32_t* ksw = reinterpret_cast<const uint32_t*>(sbn + ksoff);
+    const uint32_t nks0 = ksw[0], nks1 = ksw[1];
+    constexpr int KAHEAD = 3;  // K fragments in flight ahead of their MFMA
+    v4i kn[8];
+#pragma unroll
+    for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(sbn + koff(beta));
+    __builtin_amdgcn_sched_barrier(0);
+    v8i pb;
+#pragma unroll
+    for (int beta = 0; beta < 8; ++beta) {
+      if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(sbn + koff(beta + KAHEAD));
+      pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
+      const v8i ka = {kn[beta][0], kn[beta][1], kn[beta][2], kn[beta][3], 0, 0, 0, 0};
+      S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int psc = p_scale();
+    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
+    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
+    auto vload = [&](int db) -> v8i {
+      const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
+      const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
+      const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
+      return v8i{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    };
+    v8i va[NDB];
+    va[0] = vload(0);
+    va[1] = vload(1);
+    constexpr int SPB = 8 / NDB;  // S blocks reduced per PV step
+    float mx0 = NEG_INF, mx1 = NEG_INF;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (db + 2 < NDB) va[db + 2] = vload(db + 2);
+      O[db] = pv_block(va[db], pb, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), psc, db);
+#pragma unroll
+      for (int j = 0; j < SPB; ++j) {
+        const int beta = db * SPB + j;
+        float& mx = beta < 4 ? mx0 : mx1;
+        mx = max3f(mx, S[beta][0], S[beta][1]);
+        mx = max3f(mx, S[beta][2], S[beta][3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
+    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+    mx0 = rowmax4(mx0);
+    mx1 = rowmax4(mx1);
+    hm0 = fmaxf(m_run, ceilf(mx0 * c));
+    hm1 = fmaxf(hm0, ceilf(mx1 * c));
+    m_run = hm1;
+    chunk_lag(hm0, hm1);
+  };
+
+  if (a.mode != MXQ_ALL_LOWBIT) {  // bf16 Q rows of the workgroup -> LDS (rows past N are never read)
+    constexpr int QU = 128 * D / 8;  // 16-byte units
+#pragma unroll
+    for (int i = 0; i < (QU + NT - 1) / NT; ++i) {
+      const int u = tid + i * NT;
+      if (u < QU) {
+        const int r = u / (D / 8), cu = u % (D / 8);
+        *reinterpret_cast<v4i*>(sm + LY::q_off(r, cu)) =
+            *reinterpret_cast<const v4i*>(a.q_bf16 + (bhq * a.N + qs + r) * D + 8 * cu);
+      }
+    }
+  }
+  // the Q fragment is used in every chunk: wait for it here, once
+  asm volatile("" ::"v"(qsc), "v"(qf4[0]), "v"(qf4[1]), "v"(qf4[2]), "v"(qf4[3]));
+  __syncthreads();  // s_fl and the constant LDS words are written
+  int f_cur = chunk_flags(0);
+  int f_nxt = n_chunks > 1 ? chunk_flags(1) : 0;
+  if (needs_low(0, f_cur)) {  // chunk 0 is published before the first barrier
     stage_load(0);
+    stage_store(sm);
+  }
+  bool have_next = false;
+  if (n_chunks > 1 && needs_low(1, f_nxt)) {
+    stage_load(1);
     have_next = true;
   }
+  int slot = 0;  // ring buffer of chunk ch
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int kc = ch * 128;
     const bool valid1 = 2 * ch + 1 <= last_tile;
-    const bool need_low = needs_low(ch, flags);
-    const uint8_t* sb = sm + (ch & 1) * LY::LO_BYTES;
-    // ---- publish this chunk (loaded one chunk ahead), prefetch the next one
-    __syncthreads();  // every wave is done with the buffer about to be written
-    if (have_next) stage_store(ch & 1);
-    int next_flags = 0;
+    const int slot1 = slot == LY::RING - 1 ? 0 : slot + 1;
+    const uint8_t* sb = sm + slot * LY::LO_BYTES;
+    uint8_t* sbn = sm + slot1 * LY::LO_BYTES;
+    if (have_next) stage_store(sbn);
     have_next = false;
-    if (ch + 1 < n_chunks) {
-      next_flags = chunk_flags(ch + 1);
-      if (needs_low(ch + 1, next_flags)) {
-        stage_load(ch + 1);
+    int f_nn = 0;
+    if (ch + 2 < n_chunks) {
+      f_nn = chunk_flags(ch + 2);
+      if (needs_low(ch + 2, f_nn)) {
+        stage_load(ch + 2);
         have_next = true;
       }
     }
-    if (need_low) __syncthreads();
+    // A general chunk with FP16 tiles: the first such tile's K and V and this
+    // wave's bf16 Q fragment are fetched before the barrier, so their latency
+    // overlaps the wait.
+    const bool hot = is_hot(ch, f_cur);
+    const int t_first = (f_cur & 4) ? 0 : 1;  // first tile some wave promotes
+    v4i hk[HKR], hv[HVR];
+    v8bf qb[NSB];
+    __syncthreads();
 
-    const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
-    const bool any_hi = (flags >> 2) & 3;
-    if (!any_hi && valid1 && !need_mask) {
+    if (hot) {
       // ================= hot path: both tiles low-bit for every wave, no masks
-      const uint32_t* ksw = reinterpret_cast<const uint32_t*>(sb + ksoff);
-      const uint32_t ksc0 = ksw[0], ksc1 = ksw[1];
-      v4f S[8];
-#pragma unroll
-      for (int beta = 0; beta < 8; ++beta) {
-        v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-        const v4i w = *reinterpret_cast<const v4i*>(sb + koff[beta]);
-        ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
-        const int sc = beta < 4 ? static_cast<int>(ksc0) : static_cast<int>(ksc1);
-        const v4f z = {0.f, 0.f, 0.f, 0.f};
-        switch (beta & 3) {
-          case 0: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 0, sc, 0, qsc); break;
-          case 1: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 1, sc, 0, qsc); break;
-          case 2: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 2, sc, 0, qsc); break;
-          default: S[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, z, 4, 4, 3, sc, 0, qsc); break;
-        }
+      if (!s_ready) {
+        qk_lowbit(sb, S);
+        chunk_refs(S, hm0, hm1);
       }
-      float mx0 = max3f(S[0][0], S[0][1], S[0][2]);
-      float mx1 = max3f(S[4][0], S[4][1], S[4][2]);
-      mx0 = max3f(mx0, S[0][3], S[1][0]);
-      mx1 = max3f(mx1, S[4][3], S[5][0]);
-#pragma unroll
-      for (int e = 5; e < 16; e += 2) {  // remaining 11 values of each tile, two per v_max3
-        const float a0 = S[e >> 2][e & 3], b0 = e + 1 < 16 ? S[(e + 1) >> 2][(e + 1) & 3] : a0;
-        const float a1 = S[4 + (e >> 2)][e & 3], b1 = e + 1 < 16 ? S[4 + ((e + 1) >> 2)][(e + 1) & 3] : a1;
-        mx0 = max3f(mx0, a0, b0);
-        mx1 = max3f(mx1, a1, b1);
-      }
-      mx0 = rowmax4(mx0);
-      mx1 = rowmax4(mx1);
-      const float m0 = fmaxf(m_run, ceilf(mx0 * c));
-      const float m1 = fmaxf(m0, ceilf(mx1 * c));
-      m_run = m1;
-      // O and L stay expressed against a lagging reference m_o <= m0: each
-      // tile's contribution is scaled by 2^(m_t - m_o) through the E8M0 scale
-      // of its P blocks, so O is only rescaled when the gap grows large
-      if (m_o == NEG_INF) m_o = m0;
-      if (__any(m1 - m_o > kMaxLag)) rebase(m1);
-      const float off0 = kGridMagic + kExpOffset - m0;  // m0 is finite: key 0.. are valid
-      const float off1 = kGridMagic + kExpOffset - m1;
-      v8i pb;
-#pragma unroll
-      for (int beta = 0; beta < 8; ++beta) {
-        const float off = beta < 4 ? off0 : off1;
-        float y[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[beta][i], c, off) - kGridMagic);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        pb[beta] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-      }
-      // 2^-8 * 2^(m_t - m_o); below 2^-127 (after a forced rebase) the tile adds nothing visible
-      const int psc = static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + ((g < 2 ? m0 : m1) - m_o), 0.0f), 254.0f));
-      const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
-      const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
-        const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
-        const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
-        const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
-        switch (db & 3) {
-          case 0: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vs, 0, psc); break;
-          case 1: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 1, vs, 0, psc); break;
-          case 2: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 2, vs, 0, psc); break;
-          default: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 3, vs, 0, psc); break;
-        }
-      }
-      const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
-      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+      const bool hot_next = ch + 1 < n_chunks && is_hot(ch + 1, f_nxt);
+      if (hot_next) hot_chunk_next(sb, sbn);
+      else hot_chunk(sb);
+      s_ready = hot_next;
     } else {
+      s_ready = false;
+      const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
       // ================= general path: masks, FP16 tiles, a lone last tile
-      const bool low_w = !(flags & 1) || (valid1 && !(flags & 2));  // this wave runs FP8 PV
+      const bool low_w = !(f_cur & 1) || (valid1 && !(f_cur & 2));  // this wave runs FP8 PV
       v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};
       float m_tile0 = NEG_INF;
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (t == 1 && !valid1) break;
-        const bool prom = (flags >> t) & 1;            // this wave's tile t is FP16
-        const bool stage_hi = (flags >> (2 + t)) & 1;  // some wave's tile t is FP16
+        const bool prom = (f_cur >> t) & 1;            // this wave's tile t is FP16
+        const bool stage_hi = (f_cur >> (2 + t)) & 1;  // some wave's tile t is FP16
         if (stage_hi) {
-          __syncthreads();  // previous users of the FP16 stage are done
-          stage_fp16_tile(kc + 64 * t);
+          // the stage's previous users finished before the chunk barrier,
+          // unless it holds this chunk's tile 0
+          if (t != t_first) __syncthreads();
+          fp16_tile_load(kc + 64 * t, hk, hv);
+          fp16_tile_store(hk, hv);
           __syncthreads();
         }
         v4f S[4];
         if (prom) {
-          const uint16_t* qp16 = qrow_bf16;
-          asm volatile("" : "+v"(qp16));  // re-read the bf16 Q fragment, do not hoist it
+#pragma unroll
+          for (int st = 0; st < NSB; ++st) qb[st] = *reinterpret_cast<const v8bf*>(sm + LY::q_off(wave * 16 + col, 4 * st + g));
 #pragma unroll
           for (int st = 0; st < NSB; ++st) {
-            const v8bf qb = *reinterpret_cast<const v8bf*>(qp16 + 32 * st + 8 * g);
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
               const int key = 16 * (col >> 2) + 4 * bb + (col & 3);
               const v8bf ka = *reinterpret_cast<const v8bf*>(sm + LY::hk_off(key, 4 * st + g));
-              S[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : S[bb], 0, 0, 0);
+              S[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : S[bb], 0, 0, 0);
             }
           }
         } else {
@@ -463,7 +642,7 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-            const v4i w = *reinterpret_cast<const v4i*>(sb + koff[4 * t + bb]);
+            const v4i w = *reinterpret_cast<const v4i*>(sb + (t ? koff(4 + bb) : koff(bb)));
             ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
             const int sc = static_cast<int>(kscw >> (8 * bb)) & 0xFF;
             S[bb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
@@ -537,7 +716,9 @@ __global__ void __launch_bounds__(512, 2) k_attn_mixed(AttnArgs a) {
         L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
       }
     }
-    flags = next_flags;
+    f_cur = f_nxt;
+    f_nxt = f_nn;
+    slot = slot1;
   }
 
   // ---------------------------------------------------------------- epilogue
