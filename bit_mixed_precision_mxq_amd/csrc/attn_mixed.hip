@@ -92,52 +92,59 @@ __device__ __forceinline__ float rowmax4(float v) {
   return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
-// LDS layouts.
-//  Low-bit chunk (128 keys, a ring of three buffers):
-//   K codes: FP4 rows of D/2 bytes (D/32 chunks of 16 bytes), the chunk index
-//     XOR-swizzled with key bits so the 16 rows one MFMA operand read touches
-//     fall in distinct banks (for D = 64 rows also swap 4 apart);
-//   K scales: byte [g][col][beta] = scale of block g of the key that S block
-//     beta's row col holds, so one 8-byte read per lane serves all 8 QK MFMAs
-//     (op_sel picks the byte);
-//   V codes: FP8 V^T rows (one per head_dim element, 128 keys) padded to 144 B;
-//   V scales: byte [g][col][db] = scale of key block g of row 16*db+col.
-//  FP16 tile (64 keys, one buffer): bf16 K rows of 2*D bytes with the 16-byte
-//  chunk index XOR-swizzled by 4 key bits; fp16 V^T rows padded to 144 bytes.
+// LDS layouts.  Low-bit chunks (128 keys) live in two rings: K (four
+// buffers) and V (three buffers); the FP16 tile stage, the workgroup's bf16 Q
+// rows and constants follow.  Codes and FP16 tiles are written by direct
+// global-to-LDS loads, 1 KB (64 lanes x 16 B) per wave instruction, so every
+// layout is a permutation of 16-byte units inside contiguous rows.
+//  K buffer: FP4 K rows of D/2 bytes, the 16-byte unit index XOR-swizzled with
+//    key bits so that the 16 rows one MFMA operand read touches fall in
+//    distinct banks (for D = 64 rows 4 apart are also swapped); then the K
+//    scales, byte [g][col][beta] = scale of block g of the key that S block
+//    beta's row col holds (one 8-byte read per lane serves all 8 QK MFMAs,
+//    op_sel picks the byte).
+//  V buffer: FP8 V^T rows (one per head_dim element, 128 keys = 8 units), unit u
+//    of row d stored at u ^ ((d >> 1) & 7); then the V scales, byte
+//    [g][col][db] = scale of key block g of row 16*db+col.
+//  FP16 tile (64 keys): bf16 K rows of 2*D bytes, unit index XOR-swizzled by 4
+//    key bits; fp16 V^T rows of 128 bytes swizzled like the FP8 V rows.
 //  bf16 Q of the workgroup's 128 rows (read by the FP16 tiles' QK), loaded once.
 template <int D>
 struct Lds {
   static constexpr int KROW = D / 2;
   static constexpr int NSB = D / 32;
-  static constexpr int VSTRIDE = 144;
+  static constexpr int RK = 4, RV = 3;           // ring buffers
+  static constexpr int KS_IN = 128 * KROW;       // K scales inside a K buffer
+  static constexpr int K_BYTES = KS_IN + 512;
+  static constexpr int VS_IN = D * 128;          // V scales inside a V buffer
+  static constexpr int V_BYTES = VS_IN + 512;
   static constexpr int K_OFF = 0;
-  static constexpr int KS_OFF = K_OFF + 128 * KROW;
-  static constexpr int V_OFF = KS_OFF + 512;
-  static constexpr int VS_OFF = V_OFF + D * VSTRIDE;
-  static constexpr int LO_BYTES = VS_OFF + 512;
-  static constexpr int RING = 3;                          // low-bit chunk buffers
-  static constexpr int HK_OFF = RING * LO_BYTES;          // bf16 K tile
+  static constexpr int V_OFF = K_OFF + RK * K_BYTES;
+  static constexpr int HK_OFF = V_OFF + RV * V_BYTES;     // bf16 K tile
   static constexpr int HV_OFF = HK_OFF + 64 * 2 * D;      // fp16 V^T tile
-  static constexpr int ONES_OFF = HV_OFF + D * VSTRIDE;   // 32 B of E4M3 1.0, 16 B of fp16 1.0
-  static constexpr int Q_OFF = ONES_OFF + 48;             // bf16 Q tile of the workgroup
+  static constexpr int Q_OFF = HV_OFF + D * 128;          // bf16 Q tile of the workgroup
   static constexpr int BYTES = Q_OFF + 128 * 2 * D;
+  // K codes of (key, 16-byte unit g) inside a K buffer
+  __device__ static __forceinline__ int k_off(int key, int g) {
+    if constexpr (D == 128) {
+      return key * KROW + 16 * (g ^ ((key >> 4) & 3));
+    } else {
+      const int row = key ^ ((key >> 2) & 4);
+      return row * KROW + 16 * (g ^ ((key >> 5) & 1));
+    }
+  }
+  // 128-byte row d, 16-byte unit u (FP8 V^T of 128 keys or fp16 V^T of 64)
+  __device__ static __forceinline__ int vrow_off(int d, int u) { return d * 128 + 16 * (u ^ ((d >> 1) & 7)); }
+  __device__ static __forceinline__ int hk_swz(int key) {
+    if constexpr (D == 128) return (key & 3) | ((key >> 2) & 12);
+    else return ((key >> 1) & 1) | ((key >> 3) & 6);
+  }
+  __device__ static __forceinline__ int hk_off(int key, int cidx) {  // key in [0,64)
+    return HK_OFF + key * 2 * D + 16 * (cidx ^ hk_swz(key));
+  }
   // bf16 Q row r, 16-byte unit u (8 head_dim elements), XOR-swizzled by the row
   __device__ static __forceinline__ int q_off(int r, int u) {
     return Q_OFF + r * 2 * D + 16 * (u ^ (r & (D / 8 - 1)));
-  }
-  __device__ static __forceinline__ int k_off(int key, int g) {
-    if constexpr (D == 128) {
-      return K_OFF + key * KROW + 16 * (g ^ ((key >> 4) & 3));
-    } else {
-      const int row = key ^ ((key >> 2) & 4);
-      return K_OFF + row * KROW + 16 * (g ^ ((key >> 5) & 1));
-    }
-  }
-  __device__ static __forceinline__ int hk_off(int key, int cidx) {  // key in [0,64)
-    int f;
-    if constexpr (D == 128) f = (key & 3) | ((key >> 2) & 12);
-    else f = ((key >> 1) & 1) | ((key >> 3) & 6);
-    return HK_OFF + key * 2 * D + 16 * (cidx ^ f);
   }
 };
 
@@ -248,10 +255,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     const int fa = v & 3, fb = v >> 2;
     return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4);
   };
-  auto needs_low = [&](int ch, int fl) -> bool {
-    const int all = (fl >> 4) & 3;
-    return !(all & 1) || ((2 * ch + 1 <= last_tile) && !(all & 2));
-  };
+
   auto rebase = [&](float m) {  // rescale O and L from m_o to m >= m_o (powers of two)
     if (__any(m != m_o)) {
       float f = 1.0f;
@@ -263,83 +267,120 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     m_o = m;
   };
 
-  // ---- staging registers for one chunk of low-bit K and V
-  v4i pk[KU], pv[VU];
-  uint32_t pks = 0, pvs = 0;
-  auto stage_load = [&](int ch) {
-    const int kc = ch * 128;
-    const v4i* kg = reinterpret_cast<const v4i*>(a.k_codes + (bhk * a.N + kc) * KROW);
-#pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NT;
-      if (u < KUNITS) pk[i] = kg[u];
-    }
-    if (tid < 128 * NSB) pks = a.k_scales[(bhk * a.N + kc) * NSB + tid];
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + i * NT;
-      pv[i] = *reinterpret_cast<const v4i*>(a.v_codes + (bhk * D + (u >> 3)) * a.N + kc + 16 * (u & 7));
-    }
-    if (tid < D) pvs = *reinterpret_cast<const uint32_t*>(a.v_scales + (bhk * D + tid) * (a.N / 32) + kc / 32);
+  // ---- staging.  Buffer resources over this (batch, kv head)'s slices:
+  // reads past a slice return zeros instead of faulting.
+  // (base, size) pass through readfirstlane so that the resource is built in
+  // scalar registers even where its offset arithmetic ran on the vector ALU
+  auto rsrc = [](const void* base, int64_t off_bytes, int64_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base) + (base ? off_bytes : 0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(base ? bytes : 0));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, n,
+                                             0x00020000);
   };
-  auto stage_store = [&](uint8_t* sb) {
-#pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NT;
-      if (u < KUNITS) *reinterpret_cast<v4i*>(sb + LY::k_off(u / NSB, u % NSB)) = pk[i];
+  const bool lowbit = a.mode != MXQ_ALL_FP16;  // low-bit operands exist
+  const bool hibit = a.mode != MXQ_ALL_LOWBIT;  // FP16 operands exist
+  const auto r_kc = rsrc(a.k_codes, bhk * a.N * KROW, static_cast<int64_t>(a.N) * KROW);
+  const auto r_ks = rsrc(a.k_scales, bhk * a.N * NSB, static_cast<int64_t>(a.N) * NSB);
+  const auto r_vc = rsrc(a.v_codes, bhk * D * a.N, static_cast<int64_t>(D) * a.N);
+  const auto r_vs = rsrc(a.v_scales, bhk * D * (a.N / 32), static_cast<int64_t>(D) * (a.N / 32));
+  const auto r_hk = rsrc(a.k_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2);
+  const auto r_hv = rsrc(a.v_f16t, bhk * D * a.N * 2, static_cast<int64_t>(D) * a.N * 2);
+  uint8_t* const kring = sm + LY::K_OFF;
+  uint8_t* const vring = sm + LY::V_OFF;
+  // One wave's share of a direct global -> LDS copy: 64 lanes x 16 B land
+  // contiguously at dst (a wave-uniform LDS address).
+  auto dma16 = [](const __amdgpu_buffer_rsrc_t& r, uint8_t* dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+  };
+  // Per iteration every wave issues the same vector-memory instructions in
+  // the same order: the scale loads (registers), one K-code copy and D/64
+  // V-code copies.  kRegOps is the fewest of them any wave issues.
+  constexpr int kRegOps = D == 128 ? 4 : 2;
+  // keeps the compiler from moving memory operations across it: the wait
+  // counts rely on the order in which the copies are issued
+  auto issue_fence = []() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // K codes of chunk ch -> K buffer kb: wave w fills rows 16w..16w+15
+  auto k_dma = [&](int ch, uint8_t* kb) {
+    const int kc = ch * 128;
+    if constexpr (D == 128) {
+      const int key = 16 * wave + (lane >> 2);
+      const int gu = (lane & 3) ^ (wave & 3);
+      dma16(r_kc, kb + 1024 * wave, (kc + key) * KROW + 16 * gu);
+    } else {
+      if (lane < 32) {
+        const int row = 16 * wave + (lane >> 1);
+        const int key = row ^ ((row >> 2) & 4);
+        const int gu = (lane & 1) ^ ((key >> 5) & 1);
+        dma16(r_kc, kb + 512 * wave, (kc + key) * KROW + 16 * gu);
+      }
     }
-    if (tid < 128 * NSB) {  // K scale of (key, block kg) -> [kg][col][beta]
+  };
+  // V^T codes of chunk ch -> V buffer vb: 8 rows per 1 KB
+  auto v_dma = [&](int ch, uint8_t* vb) {
+    const int kc = ch * 128;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int blk = i * 8 + wave;
+      const int d = blk * 8 + (lane >> 3);
+      const int u = (lane & 7) ^ ((d >> 1) & 7);
+      dma16(r_vc, vb + 1024 * blk, d * a.N + kc + 16 * u);
+    }
+  };
+  uint32_t pks = 0, pvs = 0;  // scales in flight (one iteration)
+  auto ks_load = [&](int ch) {
+    if (tid < 128 * NSB) pks = __builtin_amdgcn_raw_buffer_load_b8(r_ks, ch * 128 * NSB + tid, 0, 0);
+  };
+  auto vs_load = [&](int ch) {
+    if (tid < D) pvs = __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32) + ch * 4, 0, 0);
+  };
+  auto ks_store = [&](uint8_t* kb) {  // K scale of (key, block kg) -> [kg][col][beta]
+    if (tid < 128 * NSB) {
       const int key = tid / NSB, kg = tid % NSB;
       const int kcol = 4 * ((key >> 4) & 3) + (key & 3);
       const int kbeta = 4 * (key >> 6) + ((key >> 2) & 3);
-      sb[LY::KS_OFF + (kg * 16 + kcol) * 8 + kbeta] = static_cast<uint8_t>(pks);
+      kb[LY::KS_IN + (kg * 16 + kcol) * 8 + kbeta] = static_cast<uint8_t>(pks);
     }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + i * NT;
-      *reinterpret_cast<v4i*>(sb + LY::V_OFF + (u >> 3) * LY::VSTRIDE + 16 * (u & 7)) = pv[i];
-    }
-    if (tid < D) {  // V scales of row d for key blocks 0..3 -> [block][d%16][d/16]
+  };
+  auto vs_store = [&](uint8_t* vb) {  // V scales of row d for key blocks 0..3 -> [block][d%16][d/16]
+    if (tid < D) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        sb[LY::VS_OFF + (kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(pvs >> (8 * kb));
+        vb[LY::VS_IN + (kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(pvs >> (8 * kb));
     }
   };
-  // FP16 tile staging: global loads into registers, then LDS stores
-  constexpr int HKU = 64 * 2 * D / 16;  // 16-byte units of the bf16 K tile
-  constexpr int HKR = (HKU + NT - 1) / NT, HVR = (D * 8 + NT - 1) / NT;
-  auto fp16_tile_load = [&](int kt0, v4i (&hk)[HKR], v4i (&hv)[HVR]) {
+  // FP16 tile (64 keys from kt0) -> the stage: bf16 K rows and fp16 V^T rows
+  auto fp16_dma = [&](int kt0) {
 #pragma unroll
-    for (int i = 0; i < HKR; ++i) {
-      const int u = tid + i * NT;
-      if (u < HKU) hk[i] = reinterpret_cast<const v4i*>(a.k_bf16 + (bhk * a.N + kt0 + u / (D / 8)) * D)[u % (D / 8)];
+    for (int i = 0; i < D / 64; ++i) {  // bf16 K: 2*D bytes per key
+      const int blk = i * 8 + wave;
+      const int o = blk * 1024 + 16 * lane;
+      const int key = o / (2 * D), cu = (o % (2 * D)) / 16;
+      dma16(r_hk, sm + LY::HK_OFF + 1024 * blk, (kt0 + key) * 2 * D + 16 * (cu ^ LY::hk_swz(key)));
     }
 #pragma unroll
-    for (int i = 0; i < HVR; ++i) {
-      const int u = tid + i * NT;
-      if (u < D * 8) hv[i] = *reinterpret_cast<const v4i*>(a.v_f16t + (bhk * D + (u >> 3)) * a.N + kt0 + 8 * (u & 7));
-    }
-  };
-  auto fp16_tile_store = [&](const v4i (&hk)[HKR], const v4i (&hv)[HVR]) {
-#pragma unroll
-    for (int i = 0; i < HKR; ++i) {
-      const int u = tid + i * NT;
-      if (u < HKU) *reinterpret_cast<v4i*>(sm + LY::hk_off(u / (D / 8), u % (D / 8))) = hk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < HVR; ++i) {
-      const int u = tid + i * NT;
-      if (u < D * 8) *reinterpret_cast<v4i*>(sm + LY::HV_OFF + (u >> 3) * LY::VSTRIDE + 16 * (u & 7)) = hv[i];
+    for (int i = 0; i < D / 64; ++i) {  // fp16 V^T: 128 bytes per row
+      const int blk = i * 8 + wave;
+      const int d = blk * 8 + (lane >> 3);
+      const int u = (lane & 7) ^ ((d >> 1) & 7);
+      dma16(r_hv, sm + LY::HV_OFF + 1024 * blk, d * a.N * 2 + kt0 * 2 + 16 * u);
     }
   };
 
-  if (tid < 12) reinterpret_cast<uint32_t*>(sm + LY::ONES_OFF)[tid] = tid < 8 ? 0x38383838u : 0x3C003C00u;
+  // all-ones MFMA operands for the row sums (E4M3 1.0 and fp16 1.0), kept in
+  // registers: an LDS read here would be made to wait for copies in flight
+  constexpr int kOne8 = 0x38383838, kOne16 = 0x3C003C00;
+  const v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
   if constexpr (NSB < 4) {
     // lane groups g >= D/32 carry no head_dim data: their K scale bytes must be
     // a finite E8M0 (0xFF would be NaN), so set them to 127 (= 1.0) once
     constexpr int PAD = (4 - NSB) * 16 * 8;
-    for (int i = tid; i < LY::RING * PAD; i += NT)
-      sm[(i / PAD) * LY::LO_BYTES + LY::KS_OFF + NSB * 16 * 8 + i % PAD] = 127;
+    for (int i = tid; i < LY::RK * PAD; i += NT)
+      sm[LY::K_OFF + (i / PAD) * LY::K_BYTES + LY::KS_IN + NSB * 16 * 8 + i % PAD] = 127;
   }
 
   // per-lane LDS byte offsets (constant over the pass)
@@ -355,7 +396,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       return (beta & 1 ? kbase1 : kbase0) + LY::KROW * (64 * (beta >> 2) + 4 * (beta & 2));
     }
   };
-  const int ksoff = LY::KS_OFF + (g * 16 + col) * 8;
+  const int ksoff = LY::KS_IN + (g * 16 + col) * 8;  // inside a K buffer
   auto qk_block = [&](const v8i& ka, int sc, int beta) -> v4f {
     switch (beta & 3) {
       case 0: return MXQ_QK_BLOCK(0);
@@ -372,18 +413,26 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       default: return MXQ_PV_BLOCK(3);
     }
   };
-  const int voff = LY::V_OFF + col * LY::VSTRIDE + 16 * g;
-  const int vsoff = LY::VS_OFF + (g * 16 + col) * 8;
+  // V fragment of head_dim block db: row 16*db+col, units g and g+4 (keys
+  // 16g.. and 64+16g..); the row swizzle depends on col only, and unit g+4
+  // sits 64 bytes from unit g's slot (bit 6 flipped)
+  const int voff = LY::vrow_off(col, g);  // + 2048*db inside a V buffer
+  const int vsoff = LY::VS_IN + (g * 16 + col) * 8;
+  auto vfrag = [&](const uint8_t* vb, int db) -> v8i {
+    const v4i w0 = *reinterpret_cast<const v4i*>(vb + 2048 * db + voff);
+    const v4i w1 = *reinterpret_cast<const v4i*>(vb + 2048 * db + (voff ^ 64));
+    return v8i{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  };
 
-  // ---- low-bit building blocks (chunk staged in LDS at sb)
+  // ---- low-bit building blocks (chunk staged in K buffer kb, V buffer vb)
   // S^T blocks of the chunk's 128 keys: one FP4 x FP4 MFMA per 16 keys
-  auto qk_lowbit = [&](const uint8_t* sb, v4f (&S)[8]) {
-    const uint32_t* ksw = reinterpret_cast<const uint32_t*>(sb + ksoff);
+  auto qk_lowbit = [&](const uint8_t* kb, v4f (&S)[8]) {
+    const uint32_t* ksw = reinterpret_cast<const uint32_t*>(kb + ksoff);
     const uint32_t ksc0 = ksw[0], ksc1 = ksw[1];
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) {
       v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-      const v4i w = *reinterpret_cast<const v4i*>(sb + koff(beta));
+      const v4i w = *reinterpret_cast<const v4i*>(kb + koff(beta));
       ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
       const int sc = beta < 4 ? static_cast<int>(ksc0) : static_cast<int>(ksc1);
       S[beta] = qk_block(ka, sc, beta);
@@ -429,19 +478,15 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
   };
   // O^T += V^T P^T (FP8 x FP8) and L += sum(P) for a staged chunk
-  auto pv_lowbit = [&](const uint8_t* sb, const v8i& pb, int psc) {
-    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
+  auto pv_lowbit = [&](const uint8_t* vb, const v8i& pb, int psc) {
+    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
     const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
-      const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
-      const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
-      const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      const v8i va = vfrag(vb, db);
       const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
       O[db] = pv_block(va, pb, O[db], vs, psc, db);
     }
-    const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
     L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
   };
 
@@ -471,56 +516,50 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     return static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + ((g < 2 ? hm0 : hm1) - m_o), 0.0f), 254.0f));
   };
   // last chunk of a run: exponentials and PV only
-  auto hot_chunk = [&](const uint8_t* sb) {
+  auto hot_chunk = [&](const uint8_t* vb) {
     const float off0 = kGridMagic + kExpOffset - hm0;  // hm0 is finite: key 0.. are valid
     const float off1 = kGridMagic + kExpOffset - hm1;
     v8i pb;
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
-    pv_lowbit(sb, pb, p_scale());
+    pv_lowbit(vb, pb, p_scale());
   };
-  // chunk ch (scores in S) followed by another hot chunk at sbn.  Issue order,
+  // chunk ch (scores in S, V in vb) followed by another hot chunk (K in kbn).  Issue order,
   // fixed with scheduling barriers: the next chunk's K fragments; per S block
   // its exponentials and then the FP4 QK MFMA of the next chunk into the same
   // registers (the vector ALU and the matrix core work side by side); per
   // head_dim block the V fragments two blocks ahead, one PV MFMA and a slice of
   // the next chunk's row maxima.
-  auto hot_chunk_next = [&](const uint8_t* sb, const uint8_t* sbn) {
+  auto hot_chunk_next = [&](const uint8_t* vb, const uint8_t* kbn) {
     const float off0 = kGridMagic + kExpOffset - hm0;
     const float off1 = kGridMagic + kExpOffset - hm1;
-    const uint32_t* ksw = reinterpret_cast<const uint32_t*>(sbn + ksoff);
+    const uint32_t* ksw = reinterpret_cast<const uint32_t*>(kbn + ksoff);
     const uint32_t nks0 = ksw[0], nks1 = ksw[1];
     constexpr int KAHEAD = 3;  // K fragments in flight ahead of their MFMA
     v4i kn[8];
 #pragma unroll
-    for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(sbn + koff(beta));
+    for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(kbn + koff(beta));
     __builtin_amdgcn_sched_barrier(0);
     v8i pb;
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) {
-      if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(sbn + koff(beta + KAHEAD));
+      if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
       pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
       const v8i ka = {kn[beta][0], kn[beta][1], kn[beta][2], kn[beta][3], 0, 0, 0, 0};
       S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
       __builtin_amdgcn_sched_barrier(0);
     }
     const int psc = p_scale();
-    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
+    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
     const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
-    auto vload = [&](int db) -> v8i {
-      const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
-      const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
-      const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
-      return v8i{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-    };
     v8i va[NDB];
-    va[0] = vload(0);
-    va[1] = vload(1);
+    va[0] = vfrag(vb, 0);
+    va[1] = vfrag(vb, 1);
     constexpr int SPB = 8 / NDB;  // S blocks reduced per PV step
     float mx0 = NEG_INF, mx1 = NEG_INF;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      if (db + 2 < NDB) va[db + 2] = vload(db + 2);
+      if (db + 2 < NDB) va[db + 2] = vfrag(vb, db + 2);
       O[db] = pv_block(va[db], pb, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), psc, db);
 #pragma unroll
       for (int j = 0; j < SPB; ++j) {
@@ -531,7 +570,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
     L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
     mx0 = rowmax4(mx0);
     mx1 = rowmax4(mx1);
@@ -558,51 +596,106 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   __syncthreads();  // s_fl and the constant LDS words are written
   int f_cur = chunk_flags(0);
   int f_nxt = n_chunks > 1 ? chunk_flags(1) : 0;
-  if (needs_low(0, f_cur)) {  // chunk 0 is published before the first barrier
-    stage_load(0);
-    stage_store(sm);
+
+  // Staging schedule (K ring of 4, V ring of 3, one barrier per chunk).
+  // Iteration ch, after its barrier, issues (in this order): the FP16 tile of
+  // chunk ch or ch+1 when one is due (below), the K and V scale loads into
+  // registers, the K codes of chunk ch+3 and the V codes of chunk ch+2.  At the
+  // top of iteration ch+1 the scales are written to LDS and each wave waits
+  // until at most kRegOps of its loads are in flight, i.e. everything issued
+  // before iteration ch's scale loads has landed: the K codes of chunk ch+2,
+  // the V codes of chunk ch+1 and any FP16 tile issued in iteration ch.  The
+  // barrier then publishes them to all waves.  A K buffer is rewritten three
+  // iterations after its chunk was last read, a V buffer two, both after a
+  // barrier that every reader has passed.
+  auto kbuf = [&](int ch) { return kring + (ch & (LY::RK - 1)) * LY::K_BYTES; };
+  // Workgroup barrier without the memory fence __syncthreads() carries (that
+  // fence waits for every load in flight, copies for later chunks included):
+  // this wave's LDS writes are complete, then s_barrier.  Copies are waited
+  // for explicitly before it.
+  auto lds_barrier = []() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto vbuf = [&](int vslot) { return vring + vslot * LY::V_BYTES; };
+  if (lowbit) {  // chunks 0, 1 (K) and 0 (V) in full, as iterations -3 and -2 would have
+    ks_load(0);
+    ks_store(kbuf(0));
+    ks_load(1);
+    ks_store(kbuf(1));
+    vs_load(0);
+    vs_store(vbuf(0));
+    k_dma(0, kbuf(0));
+    k_dma(1, kbuf(1));
+    v_dma(0, vbuf(0));
   }
-  bool have_next = false;
-  if (n_chunks > 1 && needs_low(1, f_nxt)) {
-    stage_load(1);
-    have_next = true;
+  // FP16 tile of chunk 0, then iteration -1's regular loads
+  bool hi_ready = false;  // the FP16 stage holds chunk ch's first promoted tile
+  issue_fence();
+  if (hibit && ((f_cur >> 2) & 3)) {
+    fp16_dma(64 * ((f_cur & 4) ? 0 : 1));
+    hi_ready = true;
   }
-  int slot = 0;  // ring buffer of chunk ch
+  issue_fence();
+  if (lowbit) {
+    ks_load(2);
+    vs_load(1);
+    k_dma(2, kbuf(2));
+    v_dma(1, vbuf(1));
+  }
+  int vslot = 0;  // V buffer of chunk ch
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int kc = ch * 128;
     const bool valid1 = 2 * ch + 1 <= last_tile;
-    const int slot1 = slot == LY::RING - 1 ? 0 : slot + 1;
-    const uint8_t* sb = sm + slot * LY::LO_BYTES;
-    uint8_t* sbn = sm + slot1 * LY::LO_BYTES;
-    if (have_next) stage_store(sbn);
-    have_next = false;
-    int f_nn = 0;
-    if (ch + 2 < n_chunks) {
-      f_nn = chunk_flags(ch + 2);
-      if (needs_low(ch + 2, f_nn)) {
-        stage_load(ch + 2);
-        have_next = true;
-      }
+    const int vslot1 = vslot == LY::RV - 1 ? 0 : vslot + 1;
+    const int vslot2 = vslot1 == LY::RV - 1 ? 0 : vslot1 + 1;
+    const uint8_t* kb = kbuf(ch);
+    const uint8_t* vb = vbuf(vslot);
+    const int f_nn = ch + 2 < n_chunks ? chunk_flags(ch + 2) : 0;
+    if (lowbit) {
+      ks_store(kbuf(ch + 2));
+      vs_store(vbuf(vslot1));
+      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
+    } else {
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // A general chunk with FP16 tiles: the first such tile's K and V and this
-    // wave's bf16 Q fragment are fetched before the barrier, so their latency
-    // overlaps the wait.
+    lds_barrier();
+    // FP16 tile issue: chunk ch's first promoted tile if it is not staged yet
+    // (the stage's previous users finished before this barrier), else chunk
+    // ch+1's when chunk ch leaves the stage alone
+    const bool hi_cur = (f_cur >> 2) & 3;
+    const bool hi_nxt = ch + 1 < n_chunks && ((f_nxt >> 2) & 3);
+    bool hi_next_ready = false;
+    if (hibit && hi_cur && !hi_ready) {
+      fp16_dma(kc + 64 * ((f_cur & 4) ? 0 : 1));
+    } else if (hibit && !hi_cur && hi_nxt) {
+      fp16_dma(kc + 128 + 64 * ((f_nxt & 4) ? 0 : 1));
+      hi_next_ready = true;
+    }
+    const bool hi_wait = hibit && hi_cur && !hi_ready;  // issued just now
+    issue_fence();
+    if (lowbit) {
+      ks_load(ch + 3);
+      vs_load(ch + 2);
+      k_dma(ch + 3, kbuf(ch + 3));
+      v_dma(ch + 2, vbuf(vslot2));
+    }
+    issue_fence();
     const bool hot = is_hot(ch, f_cur);
     const int t_first = (f_cur & 4) ? 0 : 1;  // first tile some wave promotes
-    v4i hk[HKR], hv[HVR];
-    v8bf qb[NSB];
-    __syncthreads();
 
     if (hot) {
       // ================= hot path: both tiles low-bit for every wave, no masks
       if (!s_ready) {
-        qk_lowbit(sb, S);
+        qk_lowbit(kb, S);
         chunk_refs(S, hm0, hm1);
       }
       const bool hot_next = ch + 1 < n_chunks && is_hot(ch + 1, f_nxt);
-      if (hot_next) hot_chunk_next(sb, sbn);
-      else hot_chunk(sb);
+      if (hot_next) hot_chunk_next(vb, kbuf(ch + 1));
+      else hot_chunk(vb);
       s_ready = hot_next;
     } else {
       s_ready = false;
@@ -617,15 +710,22 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         const bool prom = (f_cur >> t) & 1;            // this wave's tile t is FP16
         const bool stage_hi = (f_cur >> (2 + t)) & 1;  // some wave's tile t is FP16
         if (stage_hi) {
-          // the stage's previous users finished before the chunk barrier,
-          // unless it holds this chunk's tile 0
-          if (t != t_first) __syncthreads();
-          fp16_tile_load(kc + 64 * t, hk, hv);
-          fp16_tile_store(hk, hv);
-          __syncthreads();
+          if (t == t_first) {
+            if (hi_wait) {  // issued after this chunk's barrier: let it land, then publish
+              if (lowbit) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
+              else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+              lds_barrier();
+            }
+          } else {  // the second promoted tile: every wave is done with the first
+            lds_barrier();
+            fp16_dma(kc + 64 * t);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+          }
         }
         v4f S[4];
         if (prom) {
+          v8bf qb[NSB];
 #pragma unroll
           for (int st = 0; st < NSB; ++st) qb[st] = *reinterpret_cast<const v8bf*>(sm + LY::q_off(wave * 16 + col, 4 * st + g));
 #pragma unroll
@@ -638,11 +738,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
             }
           }
         } else {
-          const uint32_t kscw = reinterpret_cast<const uint32_t*>(sb + ksoff)[t];
+          const uint32_t kscw = reinterpret_cast<const uint32_t*>(kb + ksoff)[t];
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-            const v4i w = *reinterpret_cast<const v4i*>(sb + (t ? koff(4 + bb) : koff(bb)));
+            const v4i w = *reinterpret_cast<const v4i*>(kb + (t ? koff(4 + bb) : koff(bb)));
             ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
             const int sc = static_cast<int>(kscw >> (8 * bb)) & 0xFF;
             S[bb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
@@ -677,10 +777,10 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
               ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * st + (e >> 2)][e & 3], c, -m_safe)));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              const v8h va = *reinterpret_cast<const v8h*>(sm + LY::HV_OFF + (16 * db + col) * LY::VSTRIDE + 32 * g + 16 * st);
+              const v8h va = *reinterpret_cast<const v8h*>(sm + LY::HV_OFF + LY::vrow_off(16 * db + col, 2 * g + st));
               O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
             }
-            const v8h ones16 = *reinterpret_cast<const v8h*>(sm + LY::ONES_OFF + 32);
+            const v8h ones16 = __builtin_bit_cast(v8h, v4i{kOne16, kOne16, kOne16, kOne16});
             L = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones16, ph, L, 0, 0, 0);
           }
         } else {
@@ -702,24 +802,23 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
           const float gap = m_run - m_tile0;
           psc = (m_tile0 == NEG_INF || gap >= static_cast<float>(kPScale)) ? 0 : kPScale - static_cast<int>(gap);
         }
-        const uint32_t* vsw = reinterpret_cast<const uint32_t*>(sb + vsoff);
+        const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const uint8_t* vrow = sb + voff + 16 * db * LY::VSTRIDE;
-          const v4i w0 = *reinterpret_cast<const v4i*>(vrow);
-          const v4i w1 = *reinterpret_cast<const v4i*>(vrow + 64);
-          const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+          const v8i va = vfrag(vb, db);
           const int vs = static_cast<int>(vsw[db >> 2] >> (8 * (db & 3))) & 0xFF;
           O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vs, 0, psc);
         }
-        const v8i ones8 = *reinterpret_cast<const v8i*>(sm + LY::ONES_OFF);
-        L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+            L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
       }
     }
     f_cur = f_nxt;
     f_nxt = f_nn;
-    slot = slot1;
+    vslot = vslot1;
+    hi_ready = hi_next_ready;
   }
+  // no copy may still be landing when the workgroup's LDS is handed on
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
   // out = O / l is independent of the reference; lse uses O's reference m_o
