@@ -63,6 +63,7 @@ constexpr float kGridMagic = 6144.0f;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^
 constexpr float kExpOffset = 8.0f;     // P is stored as E4M3(2^(x + 8)) * 2^-8
 constexpr int kPScale = 119;           // E8M0 code of 2^-8
 constexpr float kMaxLag = 64.0f;       // largest gap kept between O's reference and the running one
+constexpr float kMaxLag16 = 15.0f;     // the same for FP16 tiles, whose P must stay below 2^16
 constexpr int kMaxChunks = 1024;       // 128-key chunks: 2048 key tiles of 64
 
 // Key (within the 128-key chunk) that A-operand row r of S-block beta holds.
@@ -768,13 +769,18 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         if (t == 0) m_tile0 = m_t;
         const float m_safe = m_t == NEG_INF ? 0.0f : m_t;
         if (prom) {
-          rebase(m_t);
+          // P relative to O's reference m_o <= m_t: the same fp16 values scaled
+          // by 2^(m_t - m_o) (exact while normal), so O needs no rescale unless
+          // the largest one, 2^(m_t - m_o), would leave fp16's range
+          if (m_o == NEG_INF) m_o = m_t;
+          else if (__any(m_t - m_o > kMaxLag16)) rebase(m_t);
+          const float m_ref = m_o == NEG_INF ? 0.0f : m_o;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             v8h ph;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * st + (e >> 2)][e & 3], c, -m_safe)));
+              ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * st + (e >> 2)][e & 3], c, -m_ref)));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
               const v8h va = *reinterpret_cast<const v8h*>(sm + LY::HV_OFF + LY::vrow_off(16 * db + col, 2 * g + st));
@@ -796,12 +802,14 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         }
       }
       if (low_w) {
-        rebase(m_run);
-        int psc = kPScale;
-        if (g < 2) {
-          const float gap = m_run - m_tile0;
-          psc = (m_tile0 == NEG_INF || gap >= static_cast<float>(kPScale)) ? 0 : kPScale - static_cast<int>(gap);
-        }
+        // as in the hot path: each tile's P enters through the E8M0 scale
+        // 2^-8 * 2^(m_t - m_o); O is rescaled only when the lag grows large
+        if (m_o == NEG_INF) m_o = m_run;
+        else if (__any(m_run - m_o > kMaxLag)) rebase(m_run);
+        const float mt = g < 2 ? m_tile0 : m_run;
+        int psc = 0;  // a tile with no valid key for this row adds nothing
+        if (mt != NEG_INF && m_o != NEG_INF)
+          psc = static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + (mt - m_o), 0.0f), 254.0f));
         const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
