@@ -207,8 +207,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   const int qe = min(qs + BQ, a.n_valid) - 1;
   int last_tile = (a.n_valid - 1) / 64;
   if (a.causal) last_tile = min(last_tile, qe / 64);
+  last_tile = __builtin_amdgcn_readfirstlane(last_tile);
   const int n_chunks = (last_tile + 2) / 2;
-  const int wq_lo = qs + wave * 16;                 // this wave's first row
+  const int wq_lo = __builtin_amdgcn_readfirstlane(qs + wave * 16);  // this wave's first row
   const bool wave_live = wq_lo < a.n_valid;
 
   // FP4 Q fragment (B operand of S^T = K Q^T), held for the whole pass
@@ -237,7 +238,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   const int64_t mbase = bhq * (a.N / a.sel_bq);
   const uint32_t* mrow_a = a.mask ? a.mask + (mbase + qs / a.sel_bq) * a.words : nullptr;
   const uint32_t* mrow_b = a.mask ? a.mask + (mbase + (qs + BQ - 1) / a.sel_bq) * a.words : nullptr;
-  const bool w_in_b = wq_lo / a.sel_bq != qs / a.sel_bq;
+  const bool w_in_b = __builtin_amdgcn_readfirstlane(static_cast<int>(wq_lo / a.sel_bq != qs / a.sel_bq)) != 0;
   auto row_flags = [&](const uint32_t* mr, int ch) -> int {  // bit t: tile t of chunk ch is FP16
     const int j0 = 2 * ch;
     const bool valid1 = j0 + 1 <= last_tile;
@@ -471,11 +472,15 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     chunk_lag(m0, m1);
   };
   // P = E4M3(2^xq) of one S block (4 scores per lane -> 4 bytes)
+  // (the two conversions write the low and the high half of the word, so its
+  // previous contents do not matter: an opaque register spares a zeroing move)
   auto p_block = [&](const v4f& s4, float off) -> int {
     float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s4[i], c, off) - kGridMagic);
-    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    int w;
+    __asm__ volatile("" : "=v"(w));
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
   };
   // O^T += V^T P^T (FP8 x FP8) and L += sum(P) for a staged chunk
