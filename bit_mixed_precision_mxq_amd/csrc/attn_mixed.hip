@@ -4,7 +4,8 @@
 // tiles are among the high-precision ones (the selection mask carries them).
 //
 // Work decomposition (gfx950, wave64):
-//   workgroup = (batch, query head, query tile of BQ rows), BQ/16 waves;
+//   workgroup = (batch, query head, query tile of 128 rows), 8 waves, one per
+//               CU (two waves per SIMD);
 //   wave      = 16 query rows; the wave walks the key axis in chunks of 128
 //               keys (two 64-key selection tiles) in ascending order.
 // Per chunk and wave:
@@ -19,17 +20,25 @@
 //   16g..16g+15) ends up holding, for its query column, keys {16g+j} of the
 //   first tile and {64+16g+j} of the second: exactly the K-operand layout of
 //   the 16x16x128 FP8 MFMA used for PV, so P never leaves the registers.
-//   Softmax: row max over lanes (2 shuffles), integer-snapped running
-//   reference per tile, P = E4M3(2^xq) with xq on the 2^-11 grid (one FMA,
-//   one subtraction, v_exp_f32, v_cvt_pk_fp8_f32), FP16 tiles fp16(2^x).
+//   Softmax: row max within a lane (v_max3) and across the 4 lane groups
+//   (permlane swaps), integer-snapped running reference per tile,
+//   P = E4M3(2^xq) with xq on the 2^-11 grid (one FMA, one subtraction,
+//   v_exp_f32, v_cvt_pk_fp8_f32), FP16 tiles fp16(2^x).
 //   O^T[d x 16 queries] += V^T . P^T: v_mfma_scale_f32_16x16x128_f8f6f4 (FP8 x
 //   FP8) per 16 head_dim rows; each 64-key tile's reference enters through
-//   the E8M0 scale of its K blocks (2^-8 minus the reference gap), and one
-//   more MFMA with an all-ones A operand accumulates l = sum(P).  FP16 tiles
-//   add their contribution with v_mfma_f32_16x16x32_f16.
-// K and V of the low-bit tiles are staged once per chunk in LDS and shared by
-// the BQ/16 waves; the FP16 tiles' operands (few) are read straight from
-// global memory.
+//   the E8M0 scale of its P blocks (2^-8 times 2^(tile reference - O's
+//   reference)), so O is rescaled only when that gap grows large; one more
+//   MFMA with an all-ones A operand accumulates l = sum(P).  FP16 tiles add
+//   their contribution with v_mfma_f32_16x16x32_f16.
+// Runs of unmasked all-low-bit chunks are software-pipelined inside each wave:
+// the QK MFMAs of chunk c+1 are issued between the exponentials of chunk c,
+// and the row maxima of chunk c+1 between its PV MFMAs.  Masked chunks (the
+// causal diagonal, padding) and chunks holding FP16 tiles take a general path.
+// Staging: the workgroup's K and V chunks arrive in LDS by direct
+// global-to-LDS copies, K two chunks and V one chunk before they are needed
+// (rings of four and three buffers, one barrier per chunk); a promoted tile's
+// bf16 K and fp16 V^T are copied into a stage one chunk ahead when the stage
+// is free; the bf16 Q rows of the workgroup sit in LDS for the FP16 tiles.
 #include "mxq_internal.h"
 
 // Products and sums round on their own unless written as __builtin_fmaf: the
