@@ -194,7 +194,9 @@ def bench_decode(args, dev):
     q = _bf16(d["q"], dev)
     ws = mxq.decode_workspace(B, Hq, D, 0, int(lens.max()), dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
+    # the cache build above keeps the GPU idle for seconds: warm the decode
+    # step to steady clocks (at least 50 steps, about 25 ms) before timing
+    for _ in range(max(args.warmup, 50)):
         mxq.attn_quantkv_decode(q, cache, Hkv, int(lens.max()), workspace=ws, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -287,7 +289,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 50 untimed steps (about 35 ms of prefill): fewer leave the GPU clocks
+    # short of their steady state and read a few percent slow
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "long32k", "vit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")

@@ -35,7 +35,7 @@
 //          zero-point term sum_t p_t z_t,g is accumulated on the side.
 //  Loads for the next block are issued before the current one is computed.
 // k_decode_merge: (sequence, query head): merge the S+1 partials in ascending
-// split order.
+// split order, 16 at a time.
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -576,17 +576,20 @@ __global__ void __launch_bounds__(kD) k_decode_merge(const float* __restrict__ w
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const float* base = ws + (static_cast<int64_t>(b) * Hq + h) * S1 * (kD + 2);
   float M = -__builtin_inff(), lt = 0.0f, ot = 0.0f;
-  for (int s0 = 0; s0 < S1; s0 += 8) {
-    float ms[8], ls[8], os[8];
+  // 16 partials per round (one round for the default split counts): all loads
+  // of a round are in flight together
+  constexpr int R = 16;
+  for (int s0 = 0; s0 < S1; s0 += R) {
+    float ms[R], ls[R], os[R];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < R; ++j) {
       const float* part = base + min(s0 + j, S1 - 1) * (kD + 2);
       ms[j] = s0 + j < S1 ? part[kD] : -__builtin_inff();
       ls[j] = part[kD + 1];
       os[j] = part[d];
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < R; ++j) {
       if (ms[j] == -__builtin_inff()) continue;
       const float mn = fmaxf(M, ms[j]);
       const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
