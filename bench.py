@@ -13,7 +13,7 @@ on a bounded sample, and the decode path (quantised-KV decode, KV-read GB/s
 against HBM peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-decode] [--only prefill|decode]
+                       [--no-cpu-baseline] [--no-decode] [--only prefill|decode|copy|quality]
 """
 
 from __future__ import annotations
@@ -159,6 +159,96 @@ def bench_prefill(args, dev):
     return res
 
 
+def quality_sweep(args, dev):
+    """Synthetic quality/speed curve of the promotion fraction.
+
+    For the Llama-8B-shaped shapes at N = 8K, 16K and 32K, under three input
+    recipes (the workload's: outlier channels x20 and a sink key x8; the sink
+    key alone; plain N(0,1)), and FP16 fractions from none (all low-bit) through the forced
+    sink and window tiles alone, 1, 2, 5, 10 and 20% (plus the forced tiles),
+    to all FP16: the error of attn_mixed_fwd (fp32 output) against exact
+    softmax attention computed in float64 by torch on sampled query rows, the
+    kernel time, and the share of the all-low-bit-to-all-FP16 error gap each
+    fraction recovers, (e_lowbit - e) / (e_lowbit - e_fp16).  The pages report
+    this quantity on real models and benchmarks; here it is measured on
+    seeded synthetic inputs only."""
+    import numpy as np
+    import torch
+
+    import bit_mixed_precision_mxq_amd as mxq
+    import mxq_inputs
+
+    sizes = [int(x) for x in args.quality_n.split(",")]
+    recipes = {"outliers+sink": {}, "sink": dict(outliers=False), "plain": dict(outliers=False, sink=None)}
+    fracs = [("lowbit", None), ("forced", 0), ("1%", 1), ("2%", 2), ("5%", 5), ("10%", 10), ("20%", 20), ("fp16", None)]
+    rows_per_head = 16
+    results = []
+    for recipe, N in [(r, n) for r in recipes for n in sizes]:
+        base = "llama8b" if N <= 8192 else "long32k"
+        cfg = mxq_inputs.make_prefill(base, N=N, n_valid=N, **recipes[recipe])
+        B, Hq, Hkv, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+        G = Hq // Hkv
+        q, k, v = _bf16(cfg["q"], dev), _bf16(cfg["k"], dev), _bf16(cfg["v"], dev)
+        shape = mxq.Shape(B, Hq, Hkv, N, N, D, cfg["Bq"], cfg["Bk"], cfg["causal"])
+        # sampled rows: evenly spread over the sequence, the last row included
+        rows = torch.linspace(N - 1, N / rows_per_head, rows_per_head, device=dev).round().long().flip(0)
+        scale = 1.0 / math.sqrt(D)
+        exact = []
+        for h in range(Hq):
+            qd = q[0, h, rows].double()
+            kd, vd = k[0, h // G].double(), v[0, h // G].double()
+            sc = (qd @ kd.T) * scale
+            if cfg["causal"]:
+                sc = sc.masked_fill(torch.arange(N, device=dev)[None, :] > rows[:, None], float("-inf"))
+            exact.append(torch.softmax(sc, dim=-1) @ vd)
+        exact = torch.stack(exact)  # [Hq, rows, D]
+        ops_mixed = mxq.prepare_prefill(q, k, v, N, mode=mxq.MXQ_MIXED)
+        ws = mxq.select_workspace(shape, dev)
+        errs = {}
+        for label, pct in fracs:
+            mode = mxq.MXQ_ALL_LOWBIT if label == "lowbit" else mxq.MXQ_ALL_FP16 if label == "fp16" else mxq.MXQ_MIXED
+            mask = None
+            fp16_frac = 0.0 if label == "lowbit" else 1.0
+            if mode == mxq.MXQ_MIXED:
+                mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(pct, 100),
+                                                    sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
+                                                    workspace=ws)
+                total, fp16 = pair_counts(cfg, mask.cpu().numpy().view(np.uint32))
+                fp16_frac = fp16 / total
+            out = torch.empty((B, Hq, N, D), dtype=torch.float32, device=dev)
+            call = lambda: mxq.attn_mixed_fwd(ops_mixed, mask, shape, mode=mode, out_dtype=mxq.MXQ_OUT_F32,
+                                              out=out, want_lse=False)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            got = out[0][:, rows].double()
+            diff = got - exact
+            rel = float(diff.norm() / exact.norm())
+            mabs = float(diff.abs().max())
+            errs[label] = rel
+            results.append(dict(recipe=recipe, N=N, fp16=label, fp16_pair_fraction=round(fp16_frac, 5), rel_l2=rel, max_abs=mabs,
+                                attn_ms=round(ms, 4)))
+            log(f"quality {recipe} N={N} {label:7s} fp16 pairs {fp16_frac:.4f}: rel L2 {rel:.3e}, max abs {mabs:.3e}, "
+                f"attn {ms:.3f} ms")
+        gap = errs["lowbit"] - errs["fp16"]
+        for r in results:
+            if r["N"] == N and r["recipe"] == recipe:
+                r["gap_recovered"] = round((errs["lowbit"] - r["rel_l2"]) / gap, 4) if gap > 0 else None
+        del q, k, v, ops_mixed, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"quality_sweep": results, "rows_sampled_per_head": rows_per_head,
+                      "reference": "float64 softmax attention (torch) on the sampled rows",
+                      "data": "synthetic (seeded N(0,1) bf16; outlier channels and sink key as in the recipe)"}),
+          flush=True)
+
+
 def bench_decode(args, dev):
     import numpy as np
     import torch
@@ -295,8 +385,10 @@ def main():
     ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "long32k", "vit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
-                    help="copy: a plain device copy of a known size, the reference for HBM byte counters")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "quality"], default=None,
+                    help="copy: a plain device copy of a known size, the reference for HBM byte counters; "
+                         "quality: the synthetic error/speed curve over the FP16 fraction")
+    ap.add_argument("--quality-n", default="8192,16384,32768", help="sequence lengths of the quality sweep")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -313,6 +405,9 @@ def main():
         copy_calibration(dev)
         return
     mxq.load_library()
+    if args.only == "quality":
+        quality_sweep(args, dev)
+        return
     pre = dec = None
     if args.only != "decode":
         pre = bench_prefill(args, dev)
