@@ -136,6 +136,98 @@ __global__ void __launch_bounds__(256) k_to_f16_n(const uint16_t* __restrict__ x
   for (int r = ty; r < 32; r += 8) y[(bh * D + d0 + r) * N + n0 + tx] = tile[tx][r];
 }
 
+// ---- V^T conversions through an LDS transpose (D <= 256) ---------------------
+// x [BH][N][D] bf16 -> fp16 V^T [BH][D][N], or MXFP8 codes [BH][D][N] with
+// scales [BH][D][N/32] (blocks of 32 keys).  One workgroup per (bh, KB keys):
+// the block's KB rows of D elements are contiguous in x, so they are read in
+// one coalesced sweep of 16-byte units; each unit's 8 elements are scattered
+// into 8 rows of the transposed tile tt[d][key] (row stride KB + 8 halves,
+// 16-byte aligned), and the writers read contiguous keys of one row and store
+// 16 bytes at a time.  The arithmetic is that of the per-element kernels
+// above, so codes, scales and fp16 values are identical.
+template <int KB, bool FP8>
+__global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, void* __restrict__ out,
+                                              uint8_t* __restrict__ scales, int64_t N, int D,
+                                              int64_t n_valid, int64_t n_kb) {
+  constexpr int S = KB + 8;
+  extern __shared__ __attribute__((aligned(16))) uint16_t tt[];  // [D][S]
+  const int64_t bh = blockIdx.x / n_kb;
+  const int64_t n0 = (blockIdx.x % n_kb) * KB;
+  const uint4* src = reinterpret_cast<const uint4*>(x + (bh * N + n0) * D);
+  const int cpr = D / 8;  // 16-byte units per key row
+  for (int u = threadIdx.x; u < KB * cpr; u += 256) {
+    const int key = u / cpr, c = u % cpr;
+    const uint4 v = n0 + key < n_valid ? src[u] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tt[(8 * c + 2 * i) * S + key] = static_cast<uint16_t>(w[i] & 0xFFFFu);
+      tt[(8 * c + 2 * i + 1) * S + key] = static_cast<uint16_t>(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  if constexpr (!FP8) {
+    uint16_t* y = static_cast<uint16_t*>(out);
+    for (int t = threadIdx.x; t < D * (KB / 8); t += 256) {
+      const int d = t / (KB / 8), c = t % (KB / 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(tt + d * S + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 lo = static_cast<_Float16>(__uint_as_float(w[i] << 16));
+        const _Float16 hi = static_cast<_Float16>(__uint_as_float(w[i] & 0xFFFF0000u));
+        o[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(y + (bh * D + d) * N + n0 + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    uint8_t* codes = static_cast<uint8_t*>(out);
+    for (int t = threadIdx.x; t < D * (KB / 32); t += 256) {
+      const int d = t / (KB / 32), b = t % (KB / 32);
+      const uint4* r = reinterpret_cast<const uint4*>(tt + d * S + 32 * b);
+      float v[32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 q = r[i];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int r2 = 0; r2 < 32; ++r2) amax = fmaxf(amax, fabsf(v[r2]));
+      const int e = shared_exponent(amax, 8);
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w |= e4m3_code(__builtin_ldexpf(v[4 * i + j], -e)) << (8 * j);
+        o[i] = w;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(codes + (bh * D + d) * N + n0 + 32 * b);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      scales[(bh * D + d) * (N / 32) + n0 / 32 + b] = static_cast<uint8_t>(e + 127);
+    }
+  }
+}
+
+template <int KB, bool FP8>
+mxq_status launch_vt_n(const uint16_t* x, void* out, uint8_t* scales, int64_t BH, int64_t N, int64_t D,
+                       int64_t n_valid, hipStream_t st) {
+  const int64_t n_kb = N / KB;
+  const size_t lds = static_cast<size_t>(D) * (KB + 8) * sizeof(uint16_t);
+  hipLaunchKernelGGL((k_vt_n<KB, FP8>), dim3(static_cast<unsigned>(BH * n_kb)), dim3(256), lds, st, x, out,
+                     scales, N, static_cast<int>(D), n_valid, n_kb);
+  return check_launch(FP8 ? "k_vt_n<fp8>" : "k_vt_n<fp16>");
+}
+
 // ---- INT4 asymmetric, groups of 32 along D: one thread per group ----------------
 __global__ void __launch_bounds__(256) k_quant_int4_d(const uint16_t* __restrict__ x,
                                                       uint8_t* __restrict__ codes,
@@ -218,6 +310,8 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
     MXQ_REQUIRE(scales != nullptr && zeros == nullptr, MXQ_EINVAL,
                 "mxq_quantize MXFP8: scales required, zeros must be NULL");
     MXQ_REQUIRE(N % 128 == 0, MXQ_EUNSUPPORTED, "mxq_quantize MXFP8 AXIS_N: N must be a multiple of 128");
+    if (D <= 256 && BH * (N / 64) <= 0x7FFFFFFF)
+      return launch_vt_n<64, true>(x, codes, static_cast<uint8_t*>(scales), BH, N, D, n_valid, st);
     int64_t total = BH * (N / 32) * D;
     hipLaunchKernelGGL(k_quant_mxfp8_n, dim3(grid_for(total, 256)), dim3(256), 0, st, x,
                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), BH, N, D, n_valid);
@@ -231,6 +325,10 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
       hipLaunchKernelGGL(k_to_f16_d, dim3(grid_for(n8, 256)), dim3(256), 0, st, x,
                          static_cast<uint16_t*>(codes), n8, D, N, n_valid);
       return check_launch("k_to_f16_d");
+    }
+    if (D <= 256 && BH * (N / 32) <= 0x7FFFFFFF) {
+      if (N % 64 == 0) return launch_vt_n<64, false>(x, codes, nullptr, BH, N, D, n_valid, st);
+      return launch_vt_n<32, false>(x, codes, nullptr, BH, N, D, n_valid, st);
     }
     MXQ_REQUIRE(BH <= 65535, MXQ_EUNSUPPORTED, "mxq_quantize FP16 AXIS_N: B*H must be <= 65535");
     hipLaunchKernelGGL(k_to_f16_n, dim3(static_cast<unsigned>(N / 32), static_cast<unsigned>(D / 32),

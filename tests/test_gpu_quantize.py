@@ -55,6 +55,32 @@ def test_fp16_copy_bit_exact(axis):
     assert np.array_equal(u16(out), ref.view(np.uint16))
 
 
+# V^T layouts along N: the LDS-transpose path (D <= 256, blocks of 64 keys, or
+# 32 when N is not a multiple of 64) and the per-tile path (D > 256).
+VT_SHAPES = [
+    (2, 3, 96, 64, 77),         # fp16 only: N % 64 != 0
+    (1, 2, 192, 256, 192),      # widest head dim of the transpose path
+    (1, 1, 128, 288, 100),      # per-tile path
+    (4, 6, 256, 64, 200),       # many (b, h) pairs, ragged
+]
+
+
+@pytest.mark.parametrize("shape", VT_SHAPES)
+def test_vt_layouts_bit_exact(shape):
+    mxq = gpu_or_skip()
+    B, H, N, D, nv = shape
+    bits = random_bf16((B, H, N, D), seed=3 * N + D, scale=5.0)
+    x32 = _zero_pad(F.bf16_bits_to_f32(bits), nv)
+    out, _, _ = mxq.mxq_quantize(bf16_dev(bits), mxq.MXQ_FP16, mxq.MXQ_AXIS_N, nv)
+    ref = np.ascontiguousarray(np.swapaxes(x32.astype(np.float16), -1, -2))
+    assert np.array_equal(u16(out), ref.view(np.uint16))
+    if N % 128 == 0:
+        codes, scales, _ = mxq.mxq_quantize(bf16_dev(bits), mxq.MXQ_MXFP8_E4M3, mxq.MXQ_AXIS_N, nv)
+        rc, rs = F.quantize_mxfp8_keys(x32)
+        assert np.array_equal(u8(codes), rc)
+        assert np.array_equal(u8(scales), rs)
+
+
 def test_int4_g32_bit_exact():
     mxq = gpu_or_skip()
     bits = random_bf16((2, 2, 320, 128), seed=13, scale=1.5)
