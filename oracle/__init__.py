@@ -13,9 +13,10 @@ What it follows (the pages and the readings of them):
   for FP16, then the picked blocks run in FP16 and the rest in FP4, and both
   are merged through one online softmax.
 * HyQuant: Hybrid-Precision Quantization for LLM Attention (summary and
-  abstract): vertical-line tokens (here: the attention-sink key tiles) and a
-  local window stay in high precision; in decode the KV cache is compressed
-  and dequantisation is fused into attention.
+  abstract): vertical-line tokens (single key positions: the attention sink or
+  CLS token and the keys a head's probe query scores highest) and a local
+  window stay in high precision; in decode the KV cache is compressed and
+  dequantisation is fused into attention.
 * The "Attention Quantization" topic page (overview): block-scaled FP8/FP4
   formats; softmax amplifies small quantisation errors, so softmax runs in
   full precision.
@@ -26,7 +27,7 @@ What it follows (the pages and the readings of them):
 Element formats follow the public OCP Microscaling (MX) v1.0 rules (E2M1 and
 E4M3 elements with an E8M0 shared exponent per 32 elements), which is what
 "MX-style" means.  Every point the pages leave open is settled by a numbered
-reading (R1-R24); the functions below state the reading they implement.
+reading (R1-R31); the functions below state the reading they implement.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against closed forms, brute force, exhaustive
@@ -57,7 +58,9 @@ from .formats import (  # noqa: F401
     p_exponent_grid,
     p_e4m3_code,
 )
-from .select import tile_sets, pooled_means, tile_scores, select_blocks  # noqa: F401
+from .select import (  # noqa: F401
+    tile_sets, pooled_means, tile_scores, select_blocks, select_lines, used_lines,
+)
 from .attention import (  # noqa: F401
     attn_mixed_ref,
     attn_exact_ref,

@@ -17,7 +17,11 @@ quantised.  Readings R7 and R12-R18 fix the open points:
 * row sum l accumulates the same quantised P that multiplies V, so each output
   row is a convex combination of its V rows;
 * O and l are rescaled by 2**(m_old - m_new) (exact) whenever m grows;
-  out = O / l, lse = ln2 * (m + log2 l).
+  out = O / l, lse = ln2 * (m + log2 l);
+* vertical-line tokens (HyQuant, summary and abstract; readings R29, R30): the
+  keys of a line list form one more FP16 tile that comes first in the
+  reference order, and they are left out of every key tile, so each key is
+  counted once, at FP16 if it is a line.
 
 "Two-pass" here means: pass 1 computes every tile's running reference m_j,
 pass 2 computes every tile's P against its own m_j and sums the rescaled
@@ -42,7 +46,7 @@ from .formats import (
     p_exponent_grid,
     p_e4m3_code,
 )
-from .select import tile_sets, mask_to_sets
+from .select import tile_sets, mask_to_sets, used_lines
 
 LOG2E = 1.4426950408889634  # log2(e) in double precision
 
@@ -98,11 +102,12 @@ def _exact_lowbit_scores(q_hat, k_hat, q_exp, k_exp):
 
 def attn_mixed_ref(q_bits, k_bits, v_bits, n_valid, Bq, Bk, causal, mask=None,
                    mode=MODE_MIXED, softmax_scale=None, heads=None, qtiles=None,
-                   ops=None):
+                   ops=None, lines=None):
     """Reference mixed-precision attention.
 
     q_bits [B,Hq,N,D], k_bits/v_bits [B,Hkv,N,D] (bf16 bit patterns); mask u32
-    [B,Hq,n_qt,ceil(n_kt/32)] (MIXED mode).  ``heads`` (list of (b, hq)) and
+    [B,Hq,n_qt,ceil(n_kt/32)] (MIXED mode); lines int32 [B,Hq,n_lines] or None
+    (vertical-line keys, in every mode).  ``heads`` (list of (b, hq)) and
     ``qtiles`` (list of query-tile indices) restrict the work to a sample; rows
     not computed are NaN.  Returns (out f32 [B,Hq,N,D], lse f32 [B,Hq,N]).
     """
@@ -145,10 +150,25 @@ def attn_mixed_ref(q_bits, k_bits, v_bits, n_valid, Bq, Bk, causal, mask=None,
             if causal:
                 ok = ok & (keys[None, :nk] <= rows[:, None])
             ok = ok & (rows[:, None] < n_valid)
-            # ---- pass 1: running integer reference per tile (ascending j)
+            lk = used_lines(lines[b, h], n_valid) if lines is not None else []
+            lk = np.asarray(lk, dtype=np.int64)
+            ok_line = (rows[:, None] < n_valid) & np.ones((Bq, lk.size), dtype=bool)
+            if causal:
+                ok_line = ok_line & (lk[None, :] <= rows[:, None])
+            ok[:, lk[lk < nk]] = False  # a line key leaves its tile
+            # ---- pass 1: running integer reference per tile (ascending j),
+            # the line tile first
             m_run = np.full(Bq, -np.inf, dtype=np.float32)
             m_tile = {}
             s_tile = {}
+            if lk.size:
+                s = (ops["q"][b, h, rows] @ ops["k"][b, kv, lk].T).astype(np.float32)
+                s = np.where(ok_line, s, np.float32(-np.inf)).astype(np.float32)
+                with np.errstate(invalid="ignore", over="ignore"):
+                    t = np.ceil((s.max(axis=1).astype(np.float64) * np.float64(c)).astype(np.float32))
+                m_run = np.maximum(m_run, t).astype(np.float32)
+                m_tile["lines"] = m_run.copy()
+                s_tile["lines"] = s
             for j in valid_tiles:
                 cols = slice(j * Bk, (j + 1) * Bk)
                 s = np.where(j in promoted, s_hi[:, cols], s_low[:, cols])
@@ -163,16 +183,16 @@ def attn_mixed_ref(q_bits, k_bits, v_bits, n_valid, Bq, Bk, causal, mask=None,
             # ---- pass 2: P per tile against its own reference, rescaled sums
             O = np.zeros((Bq, D))
             L = np.zeros(Bq)
-            for j in valid_tiles:
+            for j in list(m_tile):  # the line tile (if any), then key tiles ascending
                 s = s_tile[j]
                 m = m_tile[j]
                 live = np.isfinite(m)
                 m_safe = np.where(live, m, np.float32(0))
-                if j in promoted:
+                if j == "lines" or j in promoted:
                     x = fma_f32(s, c, -m_safe[:, None])
                     with np.errstate(over="ignore"):
                         p = np.exp2(x.astype(np.float64)).astype(np.float16).astype(np.float64)
-                    vv = ops["v16"][b, kv, j * Bk:(j + 1) * Bk]
+                    vv = ops["v16"][b, kv, lk] if j == "lines" else ops["v16"][b, kv, j * Bk:(j + 1) * Bk]
                 else:
                     xq = p_exponent_grid(s, c, m_safe[:, None])
                     p = e4m3_value(p_e4m3_code(xq)) * 2.0 ** -8

@@ -137,3 +137,88 @@ def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, rati
 def mask_to_sets(mask_row: np.ndarray, n_kt: int):
     """Promoted tile indices of one mask row (u32 words)."""
     return [j for j in range(n_kt) if (int(mask_row[j // 32]) >> (j % 32)) & 1]
+
+
+# ---------------------------------------------------------------- vertical lines
+# HyQuant (summary and abstract): besides a local window, a small set of
+# "vertical-line" tokens -- key positions that queries across the whole
+# sequence attend to -- stays in full precision, found from cheap
+# attention-pattern signals.  The pages give no formula; the readings are:
+#
+# * probe vector of a head (R28): the mean of its valid query tiles' means,
+#   i.e. sum over query tiles i ascending (tiles with a valid row) of the fp32
+#   tile mean, one fp32 division by the tile count.  With group sharing (R31)
+#   the sum runs over the G query heads of the kv group (head ascending, then
+#   tile ascending) and is divided once by G times the tile count;
+# * line score of key j: v_j = probe . k_j with the arithmetic of the tile
+#   scores (fl32 product, fl32 sum, d ascending, from +0);
+# * lines: the first min(sink_tokens, n_valid) keys (attention sink / CLS
+#   token), then the top (n_lines - sinks) remaining valid keys by descending
+#   score, ties to the lower index; listed ascending, padded with -1.
+
+
+def line_probe(qm_heads: np.ndarray, n_valid: int, Bq: int) -> np.ndarray:
+    """qm_heads: tile means [G', n_qt, D] of the heads that share the probe."""
+    n_vt = -(-n_valid // Bq)  # query tiles holding at least one valid row
+    acc = np.zeros(qm_heads.shape[-1], dtype=np.float32)
+    for h in range(qm_heads.shape[0]):
+        for i in range(n_vt):
+            acc = (acc + qm_heads[h, i]).astype(np.float32)
+    return (acc / np.float32(qm_heads.shape[0] * n_vt)).astype(np.float32)
+
+
+def line_scores(probe: np.ndarray, k_rows: np.ndarray) -> np.ndarray:
+    """v_j for every row of k_rows [N, D] (fp32): sequential, never fused."""
+    acc = np.zeros(k_rows.shape[0], dtype=np.float32)
+    for d in range(k_rows.shape[1]):
+        acc = (acc + (k_rows[:, d] * probe[d]).astype(np.float32)).astype(np.float32)
+    return acc
+
+
+def choose_lines(v: np.ndarray, n_valid: int, n_lines: int, sink_tokens: int) -> np.ndarray:
+    """Ascending line list (int32 [n_lines], -1 padded) from scores v [N]."""
+    s = min(sink_tokens, n_valid, n_lines)
+    cand = list(range(s, n_valid))
+    k = min(n_lines - s, len(cand))
+    order = sorted(cand, key=lambda j: (-float(v[j]), j))
+    chosen = sorted(list(range(s)) + order[:k])
+    out = np.full(n_lines, -1, dtype=np.int32)
+    out[:len(chosen)] = chosen
+    return out
+
+
+def select_lines(q_bits, k_bits, n_valid, Bq, n_lines, sink_tokens, group_shared=False):
+    """Return (lines int32 [B,Hq,n_lines], scores f32 [B,Hq,N]); scores of keys
+    j >= n_valid are -inf (they are never lines)."""
+    B, Hq, N, D = q_bits.shape
+    Hkv = k_bits.shape[1]
+    G = Hq // Hkv
+    q = bf16_bits_to_f32(q_bits)
+    k = bf16_bits_to_f32(k_bits)
+    lines = np.full((B, Hq, n_lines), -1, dtype=np.int32)
+    scores = np.full((B, Hq, N), -np.inf, dtype=np.float32)
+    for b in range(B):
+        qm = np.stack([_tile_means(q[b, h], n_valid, Bq) for h in range(Hq)])
+        for h in range(Hq):
+            kv = h // G
+            heads = qm[kv * G:(kv + 1) * G] if group_shared else qm[h:h + 1]
+            probe = line_probe(heads, n_valid, Bq)
+            kr = k[b, kv].copy()
+            kr[n_valid:] = 0.0
+            v = line_scores(probe, kr)
+            v[n_valid:] = -np.inf
+            scores[b, h] = v
+            lines[b, h] = choose_lines(v, n_valid, n_lines, sink_tokens)
+    return lines, scores
+
+
+def used_lines(row: np.ndarray, n_valid: int):
+    """Keys of one line list that take part (reading R30): an entry counts when
+    0 <= key < n_valid and it exceeds every earlier entry; anything else (the
+    -1 padding, duplicates, out-of-order or out-of-range values) is ignored."""
+    out, top = [], -1
+    for key in (int(x) for x in row):
+        if 0 <= key < n_valid and key > top:
+            out.append(key)
+        top = max(top, key)
+    return out
