@@ -63,9 +63,10 @@ def _bf16(t_np, dev):
     return torch.from_numpy(np.ascontiguousarray(t_np).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def pair_counts(cfg, mask_np):
+def pair_counts(cfg, mask_np, lines_np=None):
     """Valid (query, key) pairs per head summed over heads, and how many of them
-    fall in FP16 tiles (read back from the selection mask)."""
+    run in FP16: those in FP16 tiles (read back from the selection mask) plus
+    those of vertical-line keys that sit in low-bit tiles."""
     import numpy as np
 
     N, nv, Bq, Bk, causal = cfg["N"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"]
@@ -91,6 +92,20 @@ def pair_counts(cfg, mask_np):
     heads = mask_np.shape[0] * mask_np.shape[1]
     total = int(pairs.sum()) * heads
     fp16 = int((bits * pairs[None, None]).sum())
+    if lines_np is not None:
+        for b in range(lines_np.shape[0]):
+            for h in range(lines_np.shape[1]):
+                top = -1
+                for key in (int(x) for x in lines_np[b, h]):
+                    used = 0 <= key < nv and key > top
+                    top = max(top, key)
+                    if not used:
+                        continue
+                    j = key // Bk
+                    for i in range(n_qt):
+                        rows = q[(q >= i * Bq) & (q < (i + 1) * Bq)]
+                        if rows.size and not bits[b, h, i, j]:
+                            fp16 += int((rows >= key).sum()) if causal else int(rows.size)
     return total, fp16
 
 
@@ -116,42 +131,48 @@ def bench_prefill(args, dev):
     shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
                       cfg["causal"])
     ws = mxq.select_workspace(shape, dev)
+    n_lines = cfg.get("n_lines", 0)
+    lws = mxq.lines_workspace(shape, dev) if n_lines else None
     out = torch.empty((cfg["B"], cfg["Hq"], cfg["N"], cfg["D"]), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((cfg["B"], cfg["Hq"], cfg["N"]), dtype=torch.float32, device=dev)
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
     def step(i=None):
-        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"])
+        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], lines=bool(n_lines))
         mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
                                             sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
                                             workspace=ws)
+        lines = None
+        if n_lines:
+            lines, _ = mxq.attn_select_lines(q, k, shape, n_lines, cfg["sink_tokens"], workspace=lws)
         if i is not None:
             ev_a0[i].record()
-        mxq.attn_mixed_fwd(ops, mask, shape, out_dtype=mxq.MXQ_OUT_BF16, out=out, lse=lse)
+        mxq.attn_mixed_fwd(ops, mask, shape, out_dtype=mxq.MXQ_OUT_BF16, out=out, lse=lse, lines=lines)
         if i is not None:
             ev_a1[i].record()
-        return mask
+        return mask, lines
 
     for _ in range(args.warmup):
-        mask = step()
+        mask, lines = step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        mask = step(i)
+        mask, lines = step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     attn_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)) / args.steps
     mask_np = mask.cpu().numpy().view(np.uint32)
-    total, fp16 = pair_counts(cfg, mask_np)
+    lines_np = lines.cpu().numpy() if lines is not None else None
+    total, fp16 = pair_counts(cfg, mask_np, lines_np)
     flops = 4.0 * cfg["D"] * total
     peak_eff, t_roof = roofline_peak(cfg["D"], total, fp16)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     res = dict(
         cfg=cfg, ms_step=ms_step, attn_ms=attn_ms, flops=flops, total_pairs=total, fp16_pairs=fp16,
         tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_attn=achieved, peak_eff=peak_eff,
-        t_roof_ms=t_roof * 1e3, mask=mask_np,
+        t_roof_ms=t_roof * 1e3, mask=mask_np, lines=lines_np,
     )
     log(f"prefill {args.workload}: step {ms_step:.3f} ms, attn {attn_ms:.3f} ms, "
         f"{res['tflops_step']:.1f} TFLOP/s step, {achieved:.1f} TFLOP/s attn, "
@@ -338,6 +359,11 @@ def cpu_baseline(args, pre):
             oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
                                  cfg["topk"], cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"],
                                  cfg["local_tiles"])
+            lines = None
+            if cfg.get("n_lines", 0):
+                oracle.select_lines(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["n_lines"],
+                                    cfg["sink_tokens"])
+                lines = pre["lines"][:1, h:h + 1]
             ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
             mask = pre["mask"][:1, h:h + 1]
             heads += 1
@@ -345,7 +371,7 @@ def cpu_baseline(args, pre):
                 if time.perf_counter() - t0 >= args.cpu_seconds:
                     break
                 A.attn_mixed_ref(sub["q"], sub["k"], sub["v"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
-                                 mask=mask, qtiles=[i], ops=ops)
+                                 mask=mask, qtiles=[i], ops=ops, lines=lines)
                 tiles += 1
                 r = np.arange(i * cfg["Bq"], min((i + 1) * cfg["Bq"], cfg["n_valid"]))
                 pairs += int(np.clip(r + 1, 0, cfg["n_valid"]).sum()) if cfg["causal"] else r.size * cfg["n_valid"]
@@ -429,8 +455,11 @@ def main():
                         f"n_valid={cfg['n_valid']} D={cfg['D']} {'causal' if cfg['causal'] else 'non-causal'}, "
                         f"{cfg['Bq']}x{cfg['Bk']} tiles, FP16 = top "
                         f"{('k=' + str(cfg['topk'])) if cfg['topk'] >= 0 else str(cfg['ratio_num']) + '%'}"
-                        f" + sink {cfg['sink_tiles']} + window {cfg['local_tiles']}",
-            "step": "quantize Q,K (MXFP4), V (MXFP8 + fp16 copy) -> select -> fused mixed attention",
+                        f" + sink {cfg['sink_tiles']} + window {cfg['local_tiles']}"
+                        + (f", {cfg['n_lines']} vertical-line token(s) incl. {cfg['sink_tokens']} sink/CLS"
+                           if cfg.get("n_lines", 0) else ""),
+            "step": "quantize Q,K (MXFP4), V (MXFP8 + fp16 copy) -> select tiles"
+                    + (" and lines" if cfg.get("n_lines", 0) else "") + " -> fused mixed attention",
             "fp16_pair_fraction": round(pre["fp16_pairs"] / pre["total_pairs"], 5),
             "attn_ms": round(pre["attn_ms"], 4),
             "attn_tflops": round(pre["tflops_attn"], 2),

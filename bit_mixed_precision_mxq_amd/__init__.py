@@ -8,6 +8,7 @@ is missing or no GPU is present, these functions raise.
 Entry points (same names as the C ABI):
   mxq_quantize(x, fmt, axis, n_valid)         -> codes, scales[, zeros]
   attn_select_blocks(q, k, shape, params)     -> mask, n_fp16, scores
+  attn_select_lines(q, k, shape, n_lines, ..) -> lines, scores
   attn_mixed_fwd(ops, mask, shape, ...)       -> out, lse
   attn_quantkv_decode(q, cache, ...)          -> out
 """
@@ -30,7 +31,8 @@ MXQ_MIXED, MXQ_ALL_LOWBIT, MXQ_ALL_FP16 = 0, 1, 2
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 
 EXPORTED = [
-    "mxq_quantize", "attn_select_blocks_workspace", "attn_select_blocks", "attn_mixed_fwd",
+    "mxq_quantize", "attn_select_blocks_workspace", "attn_select_blocks", "attn_select_lines_workspace",
+    "attn_select_lines", "attn_mixed_fwd",
     "attn_quantkv_decode_workspace", "attn_quantkv_decode", "mxq_status_string",
     "mxq_last_error", "mxq_version",
 ]
@@ -48,6 +50,10 @@ class AttnShape(ctypes.Structure):
 
 class SelectParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("topk", "ratio_num", "ratio_den", "sink_tiles", "local_tiles")]
+
+
+class LineParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_lines", "sink_tokens", "group_shared")]
 
 
 class KVCache(ctypes.Structure):
@@ -81,7 +87,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_select_blocks.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(SelectParams),
                                        vp, sz, vp, vp, vp, vp]
     lib.attn_select_blocks.restype = i32
-    lib.attn_mixed_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AttnShape),
+    lib.attn_select_lines_workspace.argtypes = [ctypes.POINTER(AttnShape)]
+    lib.attn_select_lines_workspace.restype = sz
+    lib.attn_select_lines.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(LineParams),
+                                      vp, sz, vp, vp, vp]
+    lib.attn_select_lines.restype = i32
+    lib.attn_mixed_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(AttnShape),
                                    ctypes.c_float, i32, vp, i32, vp, vp]
     lib.attn_mixed_fwd.restype = i32
     lib.attn_quantkv_decode_workspace.argtypes = [i32, i32, i32, i32, i32]
@@ -190,6 +201,27 @@ def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0
     return mask, nfp, scores
 
 
+def lines_workspace(shape: Shape, device) -> torch.Tensor:
+    n = load_library().attn_select_lines_workspace(ctypes.byref(shape.c()))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def attn_select_lines(q, k, shape: Shape, n_lines, sink_tokens=1, group_shared=False, want_scores=False,
+                      workspace=None):
+    """Vertical-line keys per query head.  Returns (lines int32 [B,Hq,n_lines]
+    ascending and -1 padded, scores f32 [B,Hq,N] or None)."""
+    _need_gpu(q, k)
+    dev = q.device
+    lines = torch.empty((shape.B, shape.Hq, n_lines), dtype=torch.int32, device=dev)
+    scores = torch.empty((shape.B, shape.Hq, shape.N), dtype=torch.float32, device=dev) if want_scores else None
+    ws = workspace if workspace is not None else lines_workspace(shape, dev)
+    lp = LineParams(int(n_lines), int(sink_tokens), int(bool(group_shared)))
+    cs = shape.c()
+    _check(load_library().attn_select_lines(_ptr(q), _ptr(k), ctypes.byref(cs), ctypes.byref(lp), _ptr(ws),
+                                            ws.numel(), _ptr(lines), _ptr(scores), _stream()))
+    return lines, scores
+
+
 # ------------------------------------------------------------------ attention
 @dataclass
 class PrefillOperands:
@@ -204,21 +236,26 @@ class PrefillOperands:
     v_f16t: torch.Tensor | None = None
 
 
-def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED) -> PrefillOperands:
-    """Quantise Q/K (MXFP4), V (MXFP8 along keys) and make the fp16 V^T copy,
-    all on the GPU through mxq_quantize."""
+def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False) -> PrefillOperands:
+    """Quantise Q/K (MXFP4), V (MXFP8 along keys) and make the fp16 V^T copy
+    (needed by FP16 tiles and by vertical lines), all on the GPU through
+    mxq_quantize."""
     ops = PrefillOperands(q_bf16=q, k_bf16=k)
     if mode != MXQ_ALL_FP16:
         ops.q_codes, ops.q_scales, _ = mxq_quantize(q, MXQ_MXFP4_E2M1, MXQ_AXIS_D, n_valid)
         ops.k_codes, ops.k_scales, _ = mxq_quantize(k, MXQ_MXFP4_E2M1, MXQ_AXIS_D, n_valid)
         ops.v_codes, ops.v_scales, _ = mxq_quantize(v, MXQ_MXFP8_E4M3, MXQ_AXIS_N, n_valid)
-    if mode != MXQ_ALL_LOWBIT:
+    if mode != MXQ_ALL_LOWBIT or lines:
         ops.v_f16t, _, _ = mxq_quantize(v, MXQ_FP16, MXQ_AXIS_N, n_valid)
     return ops
 
 
 def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, mode=MXQ_MIXED,
-                   out_dtype=MXQ_OUT_F32, want_lse=True, out=None, lse=None):
+                   out_dtype=MXQ_OUT_F32, want_lse=True, out=None, lse=None, lines=None):
+    """lines: int32 [B,Hq,n_lines] vertical-line keys (attn_select_lines) or None."""
+    if lines is not None:
+        _need_gpu(lines)
+        assert lines.dtype == torch.int32 and lines.dim() == 3
     dev = (ops.q_bf16 if ops.q_bf16 is not None else ops.q_codes).device
     if out is None:
         out = torch.empty((shape.B, shape.Hq, shape.N, shape.D),
@@ -229,7 +266,7 @@ def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, 
     _check(load_library().attn_mixed_fwd(
         _ptr(ops.q_codes), _ptr(ops.q_scales), _ptr(ops.k_codes), _ptr(ops.k_scales), _ptr(ops.v_codes),
         _ptr(ops.v_scales), _ptr(ops.q_bf16), _ptr(ops.k_bf16), _ptr(ops.v_f16t), _ptr(mask),
-        ctypes.byref(cs), float(softmax_scale), int(mode), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
+        _ptr(lines), 0 if lines is None else int(lines.shape[-1]), ctypes.byref(cs), float(softmax_scale), int(mode), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
     return out, lse
 
 

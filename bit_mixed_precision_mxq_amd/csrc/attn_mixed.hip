@@ -39,6 +39,8 @@
 // (rings of four and three buffers, one barrier per chunk); a promoted tile's
 // bf16 K and fp16 V^T are copied into a stage one chunk ahead when the stage
 // is free; the bf16 Q rows of the workgroup sit in LDS for the FP16 tiles.
+#include <type_traits>
+
 #include "mxq_internal.h"
 
 // Products and sums round on their own unless written as __builtin_fmaf: the
@@ -61,10 +63,12 @@ struct AttnArgs {
   const uint16_t* k_bf16;
   const uint16_t* v_f16t;
   const uint32_t* mask;
+  const int32_t* lines;  // [B*Hq][n_lines] vertical-line keys
   void* out;
   float* lse;
   int Hq, Hkv, N, n_valid, n_qt, words, causal, mode, out_bf16;
   int sel_bq;  // query rows per selection tile (mask row = query row / sel_bq)
+  int n_lines;
   float c;  // fl32(softmax_scale * log2(e))
 };
 
@@ -74,6 +78,7 @@ constexpr int kPScale = 119;           // E8M0 code of 2^-8
 constexpr float kMaxLag = 64.0f;       // largest gap kept between O's reference and the running one
 constexpr float kMaxLag16 = 15.0f;     // the same for FP16 tiles, whose P must stay below 2^16
 constexpr int kMaxChunks = 1024;       // 128-key chunks: 2048 key tiles of 64
+constexpr int kMaxLines = 16;          // vertical-line keys per head: one 16-key MFMA block
 
 // Key (within the 128-key chunk) that A-operand row r of S-block beta holds.
 __device__ __forceinline__ int chunk_key(int beta, int r) {
@@ -119,6 +124,8 @@ __device__ __forceinline__ float rowmax4(float v) {
 //  FP16 tile (64 keys): bf16 K rows of 2*D bytes, unit index XOR-swizzled by 4
 //    key bits; fp16 V^T rows of 128 bytes swizzled like the FP8 V rows.
 //  bf16 Q of the workgroup's 128 rows (read by the FP16 tiles' QK), loaded once.
+//  Vertical lines: bf16 K rows of the 16 line entries (swizzled like Q) and
+//    their fp16 V as [d][entry], loaded once.
 template <int D>
 struct Lds {
   static constexpr int KROW = D / 2;
@@ -133,7 +140,9 @@ struct Lds {
   static constexpr int HK_OFF = V_OFF + RV * V_BYTES;     // bf16 K tile
   static constexpr int HV_OFF = HK_OFF + 64 * 2 * D;      // fp16 V^T tile
   static constexpr int Q_OFF = HV_OFF + D * 128;          // bf16 Q tile of the workgroup
-  static constexpr int BYTES = Q_OFF + 128 * 2 * D;
+  static constexpr int LK_OFF = Q_OFF + 128 * 2 * D;      // bf16 K rows of the line entries
+  static constexpr int LV_OFF = LK_OFF + kMaxLines * 2 * D;  // fp16 V of the lines, [d][entry]
+  static constexpr int BYTES = LV_OFF + D * kMaxLines * 2;
   // K codes of (key, 16-byte unit g) inside a K buffer
   __device__ static __forceinline__ int k_off(int key, int g) {
     if constexpr (D == 128) {
@@ -156,6 +165,9 @@ struct Lds {
   __device__ static __forceinline__ int q_off(int r, int u) {
     return Q_OFF + r * 2 * D + 16 * (u ^ (r & (D / 8 - 1)));
   }
+  __device__ static __forceinline__ int lk_off(int e, int u) {
+    return LK_OFF + e * 2 * D + 16 * (u ^ (e & (D / 8 - 1)));
+  }
 };
 
 
@@ -166,7 +178,9 @@ struct Lds {
 #define MXQ_PV_BLOCK(OPSEL) \
   __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, o, 0, 0, OPSEL, vs, 0, psc)
 
-template <int D>
+// LINES: vertical-line tokens are present (n_lines > 0); without them the
+// kernel carries none of their code.
+template <int D, bool LINES>
 __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   using LY = Lds<D>;
   constexpr int BQ = 128;        // query rows per workgroup
@@ -221,14 +235,32 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   const int wq_lo = __builtin_amdgcn_readfirstlane(qs + wave * 16);  // this wave's first row
   const bool wave_live = wq_lo < a.n_valid;
 
-  // FP4 Q fragment (B operand of S^T = K Q^T), held for the whole pass
-  v8i qf4 = {0, 0, 0, 0, 0, 0, 0, 0};
-  int qsc = 127;
-  if (a.mode != MXQ_ALL_FP16 && g < NSB) {
-    const v4i w = *reinterpret_cast<const v4i*>(a.q_codes + (bhq * a.N + q) * KROW + 16 * g);
-    qf4[0] = w[0]; qf4[1] = w[1]; qf4[2] = w[2]; qf4[3] = w[3];
-    qsc = a.q_scales[(bhq * a.N + q) * NSB + g];
-  }
+  // Buffer resources over slices of the operands: reads past a slice return
+  // zeros instead of faulting.
+  // (base, size) pass through readfirstlane so that the resource is built in
+  // scalar registers even where its offset arithmetic ran on the vector ALU
+  auto rsrc = [](const void* base, int64_t off_bytes, int64_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base) + (base ? off_bytes : 0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(base ? bytes : 0));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, n,
+                                             0x00020000);
+  };
+
+  // FP4 Q fragment (B operand of S^T = K Q^T), held for the whole pass.  Lane
+  // groups g >= D/32 carry no head_dim block: their offsets fall past the
+  // slice, so they read zero codes and a zero scale byte (2^-127, finite).
+  // Unconditional buffer loads land straight in the fragment's registers, so
+  // nothing waits for them before the prologue's other loads are out.
+  // (In MXQ_ALL_FP16 mode the codes may be absent: a null base gives an empty
+  // slice, so the loads return zeros there too.)
+  const auto r_qc = rsrc(a.q_codes, bhq * a.N * KROW, static_cast<int64_t>(a.N) * KROW);
+  const auto r_qs = rsrc(a.q_scales, bhq * a.N * NSB, static_cast<int64_t>(a.N) * NSB);
+  const v4i qw = __builtin_bit_cast(
+      v4i, __builtin_amdgcn_raw_buffer_load_b128(r_qc, g < NSB ? q * KROW + 16 * g : a.N * KROW, 0, 0));
+  const v8i qf4 = {qw[0], qw[1], qw[2], qw[3], 0, 0, 0, 0};
+  const int qsc = __builtin_amdgcn_raw_buffer_load_b8(r_qs, g < NSB ? q * NSB + g : a.N * NSB, 0, 0);
 
   v4f O[NDB];
 #pragma unroll
@@ -248,25 +280,28 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   const uint32_t* mrow_a = a.mask ? a.mask + (mbase + qs / a.sel_bq) * a.words : nullptr;
   const uint32_t* mrow_b = a.mask ? a.mask + (mbase + (qs + BQ - 1) / a.sel_bq) * a.words : nullptr;
   const bool w_in_b = __builtin_amdgcn_readfirstlane(static_cast<int>(wq_lo / a.sel_bq != qs / a.sel_bq)) != 0;
-  auto row_flags = [&](const uint32_t* mr, int ch) -> int {  // bit t: tile t of chunk ch is FP16
+  // bit t: tile t of chunk ch is FP16; wbits is the mask word holding tile 2ch
+  auto row_flags = [&](uint32_t wbits, int ch) -> int {
     const int j0 = 2 * ch;
     const bool valid1 = j0 + 1 <= last_tile;
     if (a.mode == MXQ_ALL_FP16) return 1 | (valid1 ? 2 : 0);
     if (a.mode == MXQ_ALL_LOWBIT) return 0;
-    const uint32_t wbits = mr[j0 >> 5];
     return static_cast<int>((wbits >> (j0 & 31)) & 1u) |
            (valid1 ? static_cast<int>(((wbits >> ((j0 + 1) & 31)) & 1u) << 1) : 0);
   };
-  __shared__ uint8_t s_fl[kMaxChunks];  // per chunk: bits 0-1 row ra, bits 2-3 row rb
-  for (int ch = tid; ch < n_chunks; ch += NT)
-    s_fl[ch] = static_cast<uint8_t>(row_flags(mrow_a, ch) | (row_flags(mrow_b, ch) << 2));
-  // packed: bits 0-1 this wave, 2-3 any wave, 4-5 every wave
-  auto chunk_flags = [&](int ch) -> int {
-    const int v = __builtin_amdgcn_readfirstlane(static_cast<int>(s_fl[ch]));
-    const int fa = v & 3, fb = v >> 2;
-    return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4);
+  auto mask_word = [&](const uint32_t* mr, int ch) -> uint32_t {
+    return a.mode == MXQ_MIXED ? mr[(2 * ch) >> 5] : 0u;
   };
-
+  // The prologue's loads go out before anything waits: this thread's first
+  // mask words (chunk tid) and line entry here, the first chunks' K/V copies
+  // and scales and the Q rows below; the flags, lines and scales are then
+  // unpacked while the copies land.
+  const uint32_t mw_a = tid < n_chunks ? mask_word(mrow_a, tid) : 0u;
+  const uint32_t mw_b = tid < n_chunks ? mask_word(mrow_b, tid) : 0u;
+  int line_raw = -1;
+  if constexpr (LINES) {
+    if (lane < 16 && lane < a.n_lines) line_raw = a.lines[bhq * a.n_lines + lane];
+  }
   auto rebase = [&](float m) {  // rescale O and L from m_o to m >= m_o (powers of two)
     if (__any(m != m_o)) {
       float f = 1.0f;
@@ -278,18 +313,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     m_o = m;
   };
 
-  // ---- staging.  Buffer resources over this (batch, kv head)'s slices:
-  // reads past a slice return zeros instead of faulting.
-  // (base, size) pass through readfirstlane so that the resource is built in
-  // scalar registers even where its offset arithmetic ran on the vector ALU
-  auto rsrc = [](const void* base, int64_t off_bytes, int64_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base) + (base ? off_bytes : 0);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
-    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(base ? bytes : 0));
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, n,
-                                             0x00020000);
-  };
+  // ---- staging.  Buffer resources (built above) over this (batch, kv
+  // head)'s slices: reads past a slice return zeros instead of faulting.
   const bool lowbit = a.mode != MXQ_ALL_FP16;  // low-bit operands exist
   const bool hibit = a.mode != MXQ_ALL_LOWBIT;  // FP16 operands exist
   const auto r_kc = rsrc(a.k_codes, bhk * a.N * KROW, static_cast<int64_t>(a.N) * KROW);
@@ -343,6 +368,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     }
   };
   uint32_t pks = 0, pvs = 0;  // scales in flight (one iteration)
+  auto ks_fetch = [&](int ch) -> uint32_t {
+    return tid < 128 * NSB ? __builtin_amdgcn_raw_buffer_load_b8(r_ks, ch * 128 * NSB + tid, 0, 0) : 0u;
+  };
+  auto vs_fetch = [&](int ch) -> uint32_t {
+    return tid < D ? __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32) + ch * 4, 0, 0) : 0u;
+  };
   auto ks_load = [&](int ch) {
     if (tid < 128 * NSB) pks = __builtin_amdgcn_raw_buffer_load_b8(r_ks, ch * 128 * NSB + tid, 0, 0);
   };
@@ -382,10 +413,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     }
   };
 
-  // all-ones MFMA operands for the row sums (E4M3 1.0 and fp16 1.0), kept in
-  // registers: an LDS read here would be made to wait for copies in flight
-  constexpr int kOne8 = 0x38383838, kOne16 = 0x3C003C00;
-  const v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
+  auto kbuf = [&](int ch) { return kring + (ch & (LY::RK - 1)) * LY::K_BYTES; };
+  auto vbuf = [&](int vslot) { return vring + vslot * LY::V_BYTES; };
   if constexpr (NSB < 4) {
     // lane groups g >= D/32 carry no head_dim data: their K scale bytes must be
     // a finite E8M0 (0xFF would be NaN), so set them to 127 (= 1.0) once
@@ -393,6 +422,23 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     for (int i = tid; i < LY::RK * PAD; i += NT)
       sm[LY::K_OFF + (i / PAD) * LY::K_BYTES + LY::KS_IN + NSB * 16 * 8 + i % PAD] = 127;
   }
+  // chunks 0, 1 (K) and 0 (V) in full, as iterations -3 and -2 would have
+  // staged them: copies and scale loads now, scale stores before the barrier
+  uint32_t pks0 = 0, pks1 = 0, pvs0 = 0;
+  if (lowbit) {
+    pks0 = ks_fetch(0);
+    pks1 = ks_fetch(1);
+    pvs0 = vs_fetch(0);
+    k_dma(0, kbuf(0));
+    k_dma(1, kbuf(1));
+    v_dma(0, vbuf(0));
+  }
+  issue_fence();
+
+  // all-ones MFMA operands for the row sums (E4M3 1.0 and fp16 1.0), kept in
+  // registers: an LDS read here would be made to wait for copies in flight
+  constexpr int kOne8 = 0x38383838, kOne16 = 0x3C003C00;
+  const v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
 
   // per-lane LDS byte offsets (constant over the pass)
   // K fragment of S block beta: a per-lane base plus a constant per block
@@ -523,7 +569,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     const int kc = ch * 128;
     const bool valid1 = 2 * ch + 1 <= last_tile;
     const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
-    return !((fl >> 2) & 3) && valid1 && !need_mask;
+    return !((fl >> 2) & 3) && !(LINES && (fl & 64)) && valid1 && !need_mask;
   };
   // P blocks of the chunk held in S (references hm0, hm1)
   auto p_scale = [&]() -> int {
@@ -594,17 +640,130 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     chunk_lag(hm0, hm1);
   };
 
-  if (a.mode != MXQ_ALL_LOWBIT) {  // bf16 Q rows of the workgroup -> LDS (rows past N are never read)
+  if (a.mode != MXQ_ALL_LOWBIT || LINES) {  // bf16 Q rows of the workgroup -> LDS (rows past N are never read)
     constexpr int QU = 128 * D / 8;  // 16-byte units
+    static_assert(QU % NT == 0, "Q units must divide evenly");
 #pragma unroll
-    for (int i = 0; i < (QU + NT - 1) / NT; ++i) {
+    for (int i = 0; i < QU / NT; ++i) {
       const int u = tid + i * NT;
-      if (u < QU) {
-        const int r = u / (D / 8), cu = u % (D / 8);
-        *reinterpret_cast<v4i*>(sm + LY::q_off(r, cu)) =
-            *reinterpret_cast<const v4i*>(a.q_bf16 + (bhq * a.N + qs + r) * D + 8 * cu);
+      *reinterpret_cast<v4i*>(sm + LY::q_off(u / (D / 8), u % (D / 8))) =
+          *reinterpret_cast<const v4i*>(a.q_bf16 + (bhq * a.N + qs + u / (D / 8)) * D + 8 * (u % (D / 8)));
+    }
+  }
+  // Vertical-line keys (HyQuant): entry e of the head's list takes part when
+  // 0 <= key < n_valid and it exceeds every earlier entry.  Lane e < 16 of
+  // every wave holds entry e's key in lkey (else -1) and, for a used entry,
+  // lslot = the rank of its 128-key chunk among the chunks holding line keys.
+  // (Cross-lane steps use DPP row shifts and readlane, vector-ALU
+  // operations: an LDS permute here would have to wait for the copies in
+  // flight, since they also write LDS.)
+  int lkey = -1, lslot = 0, n_line = 0;
+  // exclusive prefix maximum within each row of 16 lanes (INT_MIN before the first)
+  auto prefix_max_excl = [](int v) -> int {
+    constexpr int kMin = -2147483647 - 1;
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    return __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false);
+  };
+  if constexpr (LINES) {
+    const int e = lane & 15;
+    const int raw = line_raw;
+    if (lane < 16 && raw >= 0 && raw < a.n_valid && raw > prefix_max_excl(raw)) lkey = raw;
+    // chunk ranks: an entry opens a new chunk when its chunk exceeds every
+    // earlier used entry's (used keys ascend)
+    const int cb = prefix_max_excl(lkey >= 0 ? (lkey >> 7) : -1);
+    const uint64_t opens = __ballot(lane < 16 && lkey >= 0 && (lkey >> 7) > cb);
+    lslot = __popcll(opens & ((2ull << e) - 1)) - 1;
+    n_line = __popcll(__ballot(lkey >= 0));
+  }
+  // lkey of lane e (0..15) for a per-lane e: readlanes and selects
+  auto lane_key = [&](int e) -> int {
+    int k = -1;
+#pragma unroll
+    for (int x = 0; x < kMaxLines; ++x) k = e == x ? __builtin_amdgcn_readlane(lkey, x) : k;
+    return k;
+  };
+  // per chunk: bits 0-1 row ra, 2-3 row rb, 4 the chunk holds a line key,
+  // 8-11 its slot in s_lm
+  using FlagT = typename std::conditional<LINES, uint16_t, uint8_t>::type;
+  __shared__ FlagT s_fl[kMaxChunks];
+  // per slot and lane group g: the group's line keys in the chunk, bit
+  // 16t + (key & 15) for key = chunk start + 64t + 16g + (key & 15)
+  __shared__ uint32_t s_lm[kMaxLines * 4];
+  for (int ch = tid; ch < n_chunks; ch += NT) {
+    int add = 0;
+    if (LINES && n_line > 0) {
+#pragma unroll
+      for (int e = 0; e < kMaxLines; ++e) {
+        const int key = __builtin_amdgcn_readlane(lkey, e);
+        if (key >= 0 && (key >> 7) == ch) add = 16 | (__builtin_amdgcn_readlane(lslot, e) << 8);
       }
     }
+    const uint32_t wa = ch == tid ? mw_a : mask_word(mrow_a, ch);
+    const uint32_t wb = ch == tid ? mw_b : mask_word(mrow_b, ch);
+    s_fl[ch] = static_cast<FlagT>(row_flags(wa, ch) | (row_flags(wb, ch) << 2) | add);
+  }
+  // the line tile's keys: entries 4g..4g+3 of this lane's rows
+  int lkey4[4] = {-1, -1, -1, -1};
+  if constexpr (LINES) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lkey4[i] = lane_key(4 * g + i);
+  }
+  if (LINES && n_line > 0) {
+    if (wave == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < kMaxLines; ++e) {
+        const int key = __builtin_amdgcn_readlane(lkey, e);
+        const int sl = __builtin_amdgcn_readlane(lslot, e);
+        if (key >= 0 && sl == (lane >> 2) && ((key >> 4) & 3) == (lane & 3))
+          m |= 1u << ((((key & 127) >> 6) << 4) | (key & 15));
+      }
+      s_lm[lane] = m;
+    }
+    // the entries' bf16 K rows and fp16 V (zeros for unused entries), one
+    // unit of each per thread: buffer loads with out-of-range offsets for
+    // unused entries (they read zero), all issued before the stores
+    constexpr int LU = kMaxLines * D / 8;       // 16-byte units of K
+    constexpr int LV = D * (kMaxLines / 4);     // 4-entry groups of V
+    constexpr int kOut = 0x7FFFFFF0;            // past every slice
+    static_assert(LU <= NT && LV <= NT, "one line unit per thread");
+    const int ke = tid / (D / 8), kcu = tid % (D / 8);
+    const int kkey = lane_key(ke & 15);
+    const v4i kw = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                               r_hk, (tid < LU && kkey >= 0) ? kkey * 2 * D + 16 * kcu : kOut, 0, 0));
+    const int vd = tid / (kMaxLines / 4), ve0 = 4 * (tid % (kMaxLines / 4));
+    uint32_t hv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int key = lane_key(ve0 + x);
+      hv[x] = __builtin_amdgcn_raw_buffer_load_b16(r_hv, (tid < LV && key >= 0) ? (vd * a.N + key) * 2 : kOut, 0, 0);
+    }
+    if (tid < LU) *reinterpret_cast<v4i*>(sm + LY::lk_off(ke, kcu)) = kw;
+    if (tid < LV)
+      *reinterpret_cast<uint2*>(sm + LY::LV_OFF + (vd * kMaxLines + ve0) * 2) =
+          make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+  }
+  // packed: bits 0-1 this wave, 2-3 any wave, 4-5 every wave, 6 a line key
+  // in the chunk, 8-11 the chunk's line slot
+  auto chunk_flags = [&](int ch) -> int {
+    const int v = __builtin_amdgcn_readfirstlane(static_cast<int>(s_fl[ch]));
+    const int fa = v & 3, fb = (v >> 2) & 3;
+    if constexpr (LINES)
+      return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4) | ((v & 16) << 2) | (v & 0xF00);
+    else
+      return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4);
+  };
+
+  if (lowbit) {
+    pks = pks0;
+    ks_store(kbuf(0));
+    pks = pks1;
+    ks_store(kbuf(1));
+    pvs = pvs0;
+    vs_store(vbuf(0));
   }
   // the Q fragment is used in every chunk: wait for it here, once
   asm volatile("" ::"v"(qsc), "v"(qf4[0]), "v"(qf4[1]), "v"(qf4[2]), "v"(qf4[3]));
@@ -623,7 +782,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // barrier then publishes them to all waves.  A K buffer is rewritten three
   // iterations after its chunk was last read, a V buffer two, both after a
   // barrier that every reader has passed.
-  auto kbuf = [&](int ch) { return kring + (ch & (LY::RK - 1)) * LY::K_BYTES; };
   // Workgroup barrier without the memory fence __syncthreads() carries (that
   // fence waits for every load in flight, copies for later chunks included):
   // this wave's LDS writes are complete, then s_barrier.  Copies are waited
@@ -634,18 +792,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto vbuf = [&](int vslot) { return vring + vslot * LY::V_BYTES; };
-  if (lowbit) {  // chunks 0, 1 (K) and 0 (V) in full, as iterations -3 and -2 would have
-    ks_load(0);
-    ks_store(kbuf(0));
-    ks_load(1);
-    ks_store(kbuf(1));
-    vs_load(0);
-    vs_store(vbuf(0));
-    k_dma(0, kbuf(0));
-    k_dma(1, kbuf(1));
-    v_dma(0, vbuf(0));
-  }
   // FP16 tile of chunk 0, then iteration -1's regular loads
   bool hi_ready = false;  // the FP16 stage holds chunk ch's first promoted tile
   issue_fence();
@@ -659,6 +805,42 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     vs_load(1);
     k_dma(2, kbuf(2));
     v_dma(1, vbuf(1));
+  }
+  if (LINES && n_line > 0) {
+    // ---- the vertical-line tile, first in the reference order: S^T[16
+    // entries x 16 queries] = K_lines . Q^T (bf16, exact in fp16), lane (col,
+    // g) holding entries 4g..4g+3 of query col, which is also the P^T operand
+    // layout of the 16x16x16 fp16 MFMA that adds V_lines^T P^T to O^T
+    v4f SL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NSB; ++st) {
+      const v8bf ka = *reinterpret_cast<const v8bf*>(sm + LY::lk_off(col, 4 * st + g));
+      const v8bf qb = *reinterpret_cast<const v8bf*>(sm + LY::q_off(wave * 16 + col, 4 * st + g));
+      SL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, SL, 0, 0, 0);
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = lkey4[i];
+      const bool ok = key >= 0 && q < a.n_valid && (!a.causal || key <= q);
+      if (!ok) SL[i] = NEG_INF;
+      mx = fmaxf(mx, SL[i]);
+    }
+    mx = rowmax4(mx);
+    m_run = ceilf(mx * c);  // -inf when the row sees no line
+    m_o = m_run;
+    const float m_ref = m_run == NEG_INF ? 0.0f : m_run;
+    v4h ph;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ph[i] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(SL[i], c, -m_ref)));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const v4h va = *reinterpret_cast<const v4h*>(sm + LY::LV_OFF + ((16 * db + col) * kMaxLines + 4 * g) * 2);
+      O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, O[db], 0, 0, 0);
+    }
+    const v4h ones4 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f),
+                       static_cast<_Float16>(1.0f)};
+    L = __builtin_amdgcn_mfma_f32_16x16x16f16(ones4, ph, L, 0, 0, 0);
   }
   int vslot = 0;  // V buffer of chunk ch
 
@@ -715,7 +897,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     } else {
       s_ready = false;
       const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
-      // ================= general path: masks, FP16 tiles, a lone last tile
+      const bool has_line = LINES && (f_cur & 64);  // line keys run in the line tile, not here
+      // ================= general path: masks, FP16 tiles, line keys, a lone last tile
       const bool low_w = !(f_cur & 1) || (valid1 && !(f_cur & 2));  // this wave runs FP8 PV
       v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};
       float m_tile0 = NEG_INF;
@@ -773,6 +956,14 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
               const bool ok = key < a.n_valid && q < a.n_valid && (!a.causal || key <= q);
               if (!ok) S[bb][i] = NEG_INF;
             }
+        }
+        if (has_line) {  // bit 4bb + i: key kc + 64t + 16g + 4bb + i is a line key
+          const uint32_t lm = s_lm[4 * ((f_cur >> 8) & 15) + g] >> (16 * t);
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if ((lm >> (4 * bb + i)) & 1u) S[bb][i] = NEG_INF;
         }
         float mx = NEG_INF;
 #pragma unroll
@@ -871,7 +1062,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 
 template <int D>
 mxq_status launch(const AttnArgs& a, int n_qt, int Hq, int B, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_mixed<D>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
+  if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_mixed<D, true>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_mixed<D, false>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
   return check_launch("k_attn_mixed");
 }
 
@@ -885,6 +1077,7 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
                                      const uint8_t* v_codes, const uint8_t* v_scales,
                                      const uint16_t* q_bf16, const uint16_t* k_bf16,
                                      const uint16_t* v_f16t, const uint32_t* mask,
+                                     const int32_t* lines, int32_t n_lines,
                                      const mxq_attn_shape* s, float softmax_scale, mxq_mode mode,
                                      void* out, mxq_out_dtype out_dtype, float* lse,
                                      mxq_stream_t stream) {
@@ -902,12 +1095,16 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
   MXQ_REQUIRE(!hi || (q_bf16 && k_bf16 && v_f16t), MXQ_EINVAL,
               "attn_mixed_fwd: bf16 Q/K and fp16 V^T are required in this mode");
   MXQ_REQUIRE(mode != MXQ_MIXED || mask != nullptr, MXQ_EINVAL, "attn_mixed_fwd: mask required in MIXED mode");
+  MXQ_REQUIRE(n_lines >= 0 && n_lines <= kMaxLines, MXQ_EINVAL, "attn_mixed_fwd: n_lines must be in [0, 16]");
+  MXQ_REQUIRE(n_lines == 0 || (lines && q_bf16 && k_bf16 && v_f16t), MXQ_EINVAL,
+              "attn_mixed_fwd: vertical lines need lines, bf16 Q/K and fp16 V^T");
   MXQ_REQUIRE(!(softmax_scale != softmax_scale), MXQ_EINVAL, "attn_mixed_fwd: softmax_scale is NaN");
   double sc = softmax_scale > 0.0f ? static_cast<double>(softmax_scale) : 1.0 / __builtin_sqrt(static_cast<double>(s->D));
   AttnArgs a;
   a.q_codes = q_codes; a.q_scales = q_scales; a.k_codes = k_codes; a.k_scales = k_scales;
   a.v_codes = v_codes; a.v_scales = v_scales; a.q_bf16 = q_bf16; a.k_bf16 = k_bf16;
   a.v_f16t = v_f16t; a.mask = mask; a.out = out; a.lse = lse;
+  a.lines = lines; a.n_lines = n_lines;
   a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.n_qt = s->N / s->Bq;
   a.words = (s->N / s->Bk + 31) / 32; a.causal = s->causal; a.mode = mode;
   a.out_bf16 = out_dtype == MXQ_OUT_BF16;
@@ -915,7 +1112,7 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
   a.c = static_cast<float>(sc * 1.4426950408889634);
   hipStream_t strm = as_stream(stream);
   // 128-row workgroups of 8 waves whatever the selection tile height (the
-  // mask row is looked up per row block); two workgroups share a CU.
+  // mask row is looked up per row block); one workgroup per CU.
   const int n_qt = s->N / 128;
   a.n_qt = n_qt;
   if (s->D == 128) return launch<128>(a, n_qt, s->Hq, s->B, strm);

@@ -134,6 +134,146 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
   if (tid == 0 && a.n_fp16) a.n_fp16[bhq * a.n_qt + i] = s_count;
 }
 
+// ---- vertical-line tokens (HyQuant, summary and abstract: single key
+// positions that queries all along the sequence attend to stay in full
+// precision).  Probe of a head: the mean of its valid query tiles' means (of
+// the G heads of its kv group when lines are shared), summed tile by tile in
+// ascending order and divided once; score of key j: probe . k_j, fp32, d
+// ascending, rounded product then rounded sum.
+constexpr int kMaxLines = 16;
+
+struct LineArgs {
+  const float* qmean;   // [B*Hq][n_qt][D]
+  const uint16_t* k;    // bf16 [B*Hkv][N][D]
+  float* ws_scores;     // [B*Hsel][N]
+  float* scores;        // [B*Hq][N] or null
+  int32_t* lines;       // [B*Hq][n_lines]
+  int Hq, Hkv, N, n_valid, D, n_qt, n_vt, shared, n_lines, sink;
+};
+
+// One thread per key; every workgroup rebuilds the probe of its head (a few
+// hundred adds per head_dim element).
+__global__ void __launch_bounds__(256) k_line_scores(LineArgs a) {
+  __shared__ float s_probe[256];
+  const int hs = blockIdx.y, b = blockIdx.z;  // hs: query head, or kv head when shared
+  const int G = a.Hq / a.Hkv;
+  const int nh = a.shared ? G : 1;
+  const int h0 = a.shared ? hs * G : hs;
+  const int hk = a.shared ? hs : hs / G;
+  const int Hsel = a.shared ? a.Hkv : a.Hq;
+  for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
+    float acc = 0.0f;
+    for (int h = 0; h < nh; ++h) {
+      const float* qm = a.qmean + (static_cast<int64_t>(b) * a.Hq + h0 + h) * a.n_qt * a.D + d;
+      for (int i = 0; i < a.n_vt; ++i) acc = acc + qm[static_cast<int64_t>(i) * a.D];
+    }
+    s_probe[d] = acc / static_cast<float>(nh * a.n_vt);
+  }
+  __syncthreads();
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= a.N) return;
+  float v = -__builtin_inff();
+  if (j < a.n_valid) {
+    const uint4* row = reinterpret_cast<const uint4*>(a.k + ((static_cast<int64_t>(b) * a.Hkv + hk) * a.N + j) * a.D);
+    float acc = 0.0f;
+    for (int u = 0; u < a.D / 8; ++u) {
+      const uint4 w = row[u];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (ww[e >> 1] & 0xFFFF0000u) : (ww[e >> 1] << 16);
+        acc = acc + __uint_as_float(bits) * s_probe[8 * u + e];  // two roundings: contraction is off
+      }
+    }
+    v = acc;
+  }
+  a.ws_scores[(static_cast<int64_t>(b) * Hsel + hs) * a.N + j] = v;
+  if (a.scores)
+    for (int h = 0; h < nh; ++h) a.scores[(static_cast<int64_t>(b) * a.Hq + h0 + h) * a.N + j] = v;
+}
+
+// (v, j) ranks before (w, i): higher score, or the same score and lower index
+__device__ __forceinline__ bool line_before(float v, int j, float w, int i) {
+  return v > w || (v == w && j < i);
+}
+
+// One workgroup per (b, head or kv group): every thread keeps the best 16
+// candidates of its keys (j = tid + 256 m) in registers, sorted; the workgroup
+// then takes the overall best n_lines - sinks by repeated argmax over the
+// threads' list heads (ties to the lower index, as the key order defines).
+__global__ void __launch_bounds__(256) k_line_topk(LineArgs a) {
+  constexpr int T = 256;
+  __shared__ float s_v[T / 64];
+  __shared__ int s_j[T / 64];
+  __shared__ int s_take[kMaxLines];
+  const int hs = blockIdx.x, b = blockIdx.y;
+  const int G = a.Hq / a.Hkv;
+  const int Hsel = a.shared ? a.Hkv : a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sink = min(min(a.sink, a.n_valid), a.n_lines);
+  const int k = min(a.n_lines - sink, a.n_valid - sink);
+  const float* sc = a.ws_scores + (static_cast<int64_t>(b) * Hsel + hs) * a.N;
+  float lv[kMaxLines];
+  int lj[kMaxLines];
+#pragma unroll
+  for (int e = 0; e < kMaxLines; ++e) { lv[e] = -__builtin_inff(); lj[e] = 0x7FFFFFFF; }
+  for (int j = sink + tid; j < a.n_valid; j += T) {
+    float v = sc[j];
+    int jj = j;
+    // insertion into the sorted list: bubble the new entry up from the tail
+#pragma unroll
+    for (int e = 0; e < kMaxLines; ++e) {
+      if (line_before(v, jj, lv[e], lj[e])) {
+        const float tv = lv[e];
+        const int tj = lj[e];
+        lv[e] = v; lj[e] = jj;
+        v = tv; jj = tj;
+      }
+    }
+  }
+  int head = 0;  // this thread's first unused list entry
+  for (int r = 0; r < k; ++r) {
+    float v = -__builtin_inff();
+    int j = 0x7FFFFFFF;
+#pragma unroll
+    for (int e = 0; e < kMaxLines; ++e)
+      if (e == head) { v = lv[e]; j = lj[e]; }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(v, off);
+      const int oj = __shfl_xor(j, off);
+      if (line_before(ov, oj, v, j)) { v = ov; j = oj; }
+    }
+    if (lane == 0) { s_v[wave] = v; s_j[wave] = j; }
+    __syncthreads();
+    float bv = s_v[0];
+    int bj = s_j[0];
+    for (int w = 1; w < T / 64; ++w)
+      if (line_before(s_v[w], s_j[w], bv, bj)) { bv = s_v[w]; bj = s_j[w]; }
+    __syncthreads();
+    // keys are distinct, so exactly one thread's head holds the winner
+    if (bj < a.n_valid && (bj - sink) % T == tid) ++head;
+    if (tid == 0) s_take[r] = bj;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int out[kMaxLines];
+    int n = 0;
+    for (int e = 0; e < sink; ++e) out[n++] = e;
+    for (int r = 0; r < k; ++r) {  // insertion sort of the chosen keys (all >= sink)
+      int key = s_take[r], p = n;
+      while (p > sink && out[p - 1] > key) { out[p] = out[p - 1]; --p; }
+      out[p] = key;
+      ++n;
+    }
+    const int nh = a.shared ? G : 1;
+    const int h0 = a.shared ? hs * G : hs;
+    for (int h = 0; h < nh; ++h) {
+      int32_t* dst = a.lines + (static_cast<int64_t>(b) * a.Hq + h0 + h) * a.n_lines;
+      for (int e = 0; e < a.n_lines; ++e) dst[e] = e < n ? out[e] : -1;
+    }
+  }
+}
+
 mxq_status validate_shape(const mxq_attn_shape* s) {
   MXQ_REQUIRE(s != nullptr, MXQ_EINVAL, "shape is NULL");
   MXQ_REQUIRE(s->B >= 1 && s->Hq >= 1 && s->Hkv >= 1 && s->N >= 1, MXQ_EINVAL,
@@ -198,4 +338,47 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
   a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
   hipLaunchKernelGGL(k_select, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
   return check_launch("k_select");
+}
+
+extern "C" size_t attn_select_lines_workspace(const mxq_attn_shape* s) {
+  if (s == nullptr || s->Bq <= 0) return 0;
+  const size_t n_qt = static_cast<size_t>(s->N / s->Bq);
+  return (static_cast<size_t>(s->B) * s->Hq * n_qt * static_cast<size_t>(s->D) +
+          static_cast<size_t>(s->B) * s->Hq * static_cast<size_t>(s->N)) * sizeof(float);
+}
+
+extern "C" mxq_status attn_select_lines(const uint16_t* q, const uint16_t* k, const mxq_attn_shape* s,
+                                        const mxq_line_params* p, void* workspace, size_t ws_bytes,
+                                        int32_t* lines, float* scores, mxq_stream_t stream) {
+  mxq_status st = validate_shape(s);
+  if (st != MXQ_OK) return st;
+  MXQ_REQUIRE(p != nullptr, MXQ_EINVAL, "attn_select_lines: params is NULL");
+  MXQ_REQUIRE(p->n_lines >= 0 && p->n_lines <= kMaxLines, MXQ_EINVAL,
+              "attn_select_lines: n_lines must be in [0, 16]");
+  MXQ_REQUIRE(p->sink_tokens >= 0, MXQ_EINVAL, "attn_select_lines: sink_tokens must be >= 0");
+  MXQ_REQUIRE(p->group_shared == 0 || p->group_shared == 1, MXQ_EINVAL,
+              "attn_select_lines: group_shared must be 0 or 1");
+  if (p->n_lines == 0) return MXQ_OK;
+  MXQ_REQUIRE(q != nullptr && k != nullptr && lines != nullptr, MXQ_EINVAL,
+              "attn_select_lines: q, k and lines are required");
+  MXQ_REQUIRE(workspace != nullptr && ws_bytes >= attn_select_lines_workspace(s), MXQ_EINVAL,
+              "attn_select_lines: workspace too small");
+  hipStream_t strm = as_stream(stream);
+  const int n_qt = s->N / s->Bq;
+  float* qmean = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(k_tile_means, dim3(n_qt, s->B * s->Hq), dim3(s->D), 0, strm, q, qmean, s->N,
+                     s->D, s->Bq, s->n_valid, n_qt, 0);
+  if ((st = check_launch("k_tile_means(q)")) != MXQ_OK) return st;
+  LineArgs a;
+  a.qmean = qmean; a.k = k;
+  a.ws_scores = qmean + static_cast<size_t>(s->B) * s->Hq * n_qt * s->D;
+  a.scores = scores; a.lines = lines;
+  a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.D = s->D; a.n_qt = n_qt;
+  a.n_vt = (s->n_valid + s->Bq - 1) / s->Bq;
+  a.shared = p->group_shared; a.n_lines = p->n_lines; a.sink = p->sink_tokens;
+  const int Hsel = a.shared ? s->Hkv : s->Hq;
+  hipLaunchKernelGGL(k_line_scores, dim3((s->N + 255) / 256, Hsel, s->B), dim3(256), 0, strm, a);
+  if ((st = check_launch("k_line_scores")) != MXQ_OK) return st;
+  hipLaunchKernelGGL(k_line_topk, dim3(Hsel, s->B), dim3(256), 0, strm, a);
+  return check_launch("k_line_topk");
 }

@@ -130,6 +130,36 @@ mxq_status attn_select_blocks(const uint16_t* q_bf16, const uint16_t* k_bf16,
                               float* scores, mxq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * attn_select_lines -- HyQuant (summary and abstract): a few "vertical-line"
+ * tokens, single key positions that queries all along the sequence attend
+ * to, stay in full precision.  Signal (reading R28): the probe of a query head
+ * is the mean of its valid query tiles' means (Bq rows each, as in
+ * attn_select_blocks), summed tile by tile in ascending order and divided
+ * once; with group_shared the sum runs over the G query heads of the kv group
+ * (head, then tile, ascending) and one line set serves the whole group
+ * (reading R31).  Score of key j: probe . k_j, fp32, d ascending, rounded
+ * product then rounded sum.  Lines of a head: keys 0 .. sink_tokens-1 (the
+ * attention sink or CLS token; fewer if n_valid or n_lines is smaller), then
+ * the best-scoring remaining valid keys up to n_lines in all, ties to the
+ * lower index, listed ascending and padded with -1.  Bit-identical to a plain
+ * CPU evaluation of the same formula.
+ * Outputs: lines i32 [B][Hq][n_lines] (rows of one kv group identical when
+ * shared); scores f32 [B][Hq][N] or NULL (key scores, -inf for j >= n_valid).
+ * n_lines in [0, 16] (0: nothing is written).  workspace: at least
+ * attn_select_lines_workspace(shape) bytes, caller-owned, contents undefined
+ * after the call.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_lines, sink_tokens, group_shared;
+} mxq_line_params;
+
+size_t attn_select_lines_workspace(const mxq_attn_shape* shape);
+mxq_status attn_select_lines(const uint16_t* q_bf16, const uint16_t* k_bf16,
+                             const mxq_attn_shape* shape, const mxq_line_params* params,
+                             void* workspace, size_t ws_bytes, int32_t* lines, float* scores,
+                             mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * attn_mixed_fwd -- stage 2 of ThriftAttention (abstract): one fused pass over
  * the key tiles of each query tile, ascending; selected tiles in FP16, the
  * rest low-bit, merged through one online softmax.  Readings R7, R12-R18:
@@ -148,6 +178,14 @@ mxq_status attn_select_blocks(const uint16_t* q_bf16, const uint16_t* k_bf16,
  * NULL in MXQ_ALL_LOWBIT mode; the low-bit operands may be NULL in
  * MXQ_ALL_FP16 mode.  mask (from attn_select_blocks) is needed in MXQ_MIXED
  * mode only.  softmax_scale <= 0 means 1/sqrt(D).
+ * Vertical lines (HyQuant; readings R29, R30): lines i32 [B][Hq][n_lines]
+ * (from attn_select_lines), n_lines in [0, 16], in every mode.  An entry takes
+ * part when 0 <= key < n_valid and it exceeds every earlier entry of its row
+ * (so -1 padding, repeats and out-of-order or out-of-range values are
+ * ignored).  Those keys form one FP16 tile (bf16 Q and K, fp16 V, fp16 P)
+ * processed first in the reference order, and they are left out of their
+ * key tiles; causal masking applies to them as to any key.  They need q_bf16,
+ * k_bf16 and v_f16t in every mode.  lines may be NULL when n_lines is 0.
  * out: [B][Hq][N][D] fp32 or bf16; lse: f32 [B][Hq][N] or NULL (natural log).
  * Rows >= n_valid: out 0, lse -inf.
  * ------------------------------------------------------------------------- */
@@ -155,7 +193,8 @@ mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                           const uint8_t* k_codes, const uint8_t* k_scales,
                           const uint8_t* v_codes, const uint8_t* v_scales,
                           const uint16_t* q_bf16, const uint16_t* k_bf16, const uint16_t* v_f16t,
-                          const uint32_t* mask, const mxq_attn_shape* shape, float softmax_scale,
+                          const uint32_t* mask, const int32_t* lines, int32_t n_lines,
+                          const mxq_attn_shape* shape, float softmax_scale,
                           mxq_mode mode, void* out, mxq_out_dtype out_dtype, float* lse,
                           mxq_stream_t stream);
 

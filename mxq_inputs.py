@@ -30,19 +30,20 @@ import numpy as np
 PREFILL_CONFIGS = {
     # B=1, H=2, N=256, d=64, non-causal, 64x64 tiles, top-1 FP16 key tile per query tile
     "tiny": dict(B=1, Hq=2, Hkv=2, N=256, n_valid=256, D=64, causal=False, Bq=64, Bk=64,
-                 topk=1, ratio_num=0, ratio_den=1, sink_tiles=0, local_tiles=0,
+                 topk=1, ratio_num=0, ratio_den=1, sink_tiles=0, local_tiles=0, n_lines=0, sink_tokens=0,
                  outliers=False, sink=None, seed=1),
     # Llama-8B-shaped causal prefill, GQA 4:1, 128x64 tiles, 5% + sink column + 1-tile window
     "llama8b": dict(B=1, Hq=32, Hkv=8, N=8192, n_valid=8192, D=128, causal=True, Bq=128, Bk=64,
-                    topk=-1, ratio_num=5, ratio_den=100, sink_tiles=1, local_tiles=1,
+                    topk=-1, ratio_num=5, ratio_den=100, sink_tiles=1, local_tiles=1, n_lines=0, sink_tokens=0,
                     outliers=True, sink=8.0, seed=2),
     # long-context causal prefill, 5% + sink + 4-tile window
     "long32k": dict(B=1, Hq=32, Hkv=8, N=32768, n_valid=32768, D=128, causal=True, Bq=128, Bk=64,
-                    topk=-1, ratio_num=5, ratio_den=100, sink_tiles=1, local_tiles=4,
+                    topk=-1, ratio_num=5, ratio_den=100, sink_tiles=1, local_tiles=4, n_lines=0, sink_tokens=0,
                     outliers=True, sink=8.0, seed=3),
-    # ViT-B/16-shaped: batch 512, 12 heads, 197 tokens padded to 256, CLS key tile kept FP16
+    # ViT-B/16-shaped: batch 512, 12 heads, 197 tokens padded to 256; the CLS
+    # token's key column is kept FP16 as a one-token vertical line, no FP16 tile
     "vit": dict(B=512, Hq=12, Hkv=12, N=256, n_valid=197, D=64, causal=False, Bq=64, Bk=64,
-                topk=0, ratio_num=0, ratio_den=1, sink_tiles=1, local_tiles=0,
+                topk=0, ratio_num=0, ratio_den=1, sink_tiles=0, local_tiles=0, n_lines=1, sink_tokens=1,
                 outliers=False, sink=None, seed=5),
 }
 

@@ -19,18 +19,22 @@ def _shape(mxq, cfg):
                      cfg["causal"])
 
 
-def _gpu_prefill(mxq, cfg, mode=0, mask=None, out_dtype=0):
+def _gpu_prefill(mxq, cfg, mode=0, mask=None, out_dtype=0, with_lines=False):
     q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
     shape = _shape(mxq, cfg)
-    ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], mode)
+    lines = None
+    if with_lines:
+        lines, _ = mxq.attn_select_lines(q, k, shape, cfg["n_lines"], cfg["sink_tokens"])
+    ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], mode, lines=with_lines)
     if mode == mxq.MXQ_MIXED and mask is None:
         mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
                                             sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"])
     elif mask is not None:
         import torch
         mask = torch.from_numpy(np.ascontiguousarray(mask).view(np.int32)).to("cuda:0")
-    out, lse = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode, out_dtype=out_dtype)
-    return out.float().cpu().numpy(), lse.cpu().numpy(), (u32(mask) if mask is not None else None)
+    out, lse = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode, out_dtype=out_dtype, lines=lines)
+    res = (out.float().cpu().numpy(), lse.cpu().numpy(), (u32(mask) if mask is not None else None))
+    return res + (lines.cpu().numpy(),) if with_lines else res
 
 
 def _check(out, lse, ro, rl, rows=None):
@@ -115,12 +119,16 @@ def test_llama8b_full_size_sampled():
 
 
 def test_vit_batch_sampled():
+    """ViT-shaped batch: the CLS token is a one-token vertical line, every
+    tile low-bit."""
     mxq = gpu_or_skip()
     cfg = mxq_inputs.make_prefill("vit", B=8)
-    out, lse, mask = _gpu_prefill(mxq, cfg, 0)
+    out, lse, mask, lines = _gpu_prefill(mxq, cfg, 0, with_lines=True)
+    assert not mask.any() and np.all(lines[..., 0] == 0)
     for b, h in ((0, 0), (3, 7), (7, 11)):
         ro, rl = A.attn_mixed_ref(cfg["q"][b:b + 1, h:h + 1], cfg["k"][b:b + 1, h:h + 1], cfg["v"][b:b + 1, h:h + 1],
-                                  cfg["n_valid"], 64, 64, False, mask=mask[b:b + 1, h:h + 1])
+                                  cfg["n_valid"], 64, 64, False, mask=mask[b:b + 1, h:h + 1],
+                                  lines=lines[b:b + 1, h:h + 1])
         _check(out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
 
 
