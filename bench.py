@@ -352,10 +352,11 @@ def cpu_baseline(args, pre):
     tiles, pairs, heads = 0, 0, 0
     try:
         t0 = time.perf_counter()
-        for h in range(cfg["Hq"]):
+        for b, h in ((b, h) for b in range(cfg["B"]) for h in range(cfg["Hq"])):
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
-            sub = dict(q=cfg["q"][:1, h:h + 1], k=cfg["k"][:1, h // G:h // G + 1], v=cfg["v"][:1, h // G:h // G + 1])
+            kv = slice(h // G, h // G + 1)
+            sub = dict(q=cfg["q"][b:b + 1, h:h + 1], k=cfg["k"][b:b + 1, kv], v=cfg["v"][b:b + 1, kv])
             oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
                                  cfg["topk"], cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"],
                                  cfg["local_tiles"])
@@ -363,9 +364,9 @@ def cpu_baseline(args, pre):
             if cfg.get("n_lines", 0):
                 oracle.select_lines(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["n_lines"],
                                     cfg["sink_tokens"])
-                lines = pre["lines"][:1, h:h + 1]
+                lines = pre["lines"][b:b + 1, h:h + 1]
             ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
-            mask = pre["mask"][:1, h:h + 1]
+            mask = pre["mask"][b:b + 1, h:h + 1]
             heads += 1
             for i in range(n_qt - 1, -1, -1):
                 if time.perf_counter() - t0 >= args.cpu_seconds:
@@ -381,9 +382,9 @@ def cpu_baseline(args, pre):
             ctx.__exit__(None, None, None)
     flops = 4.0 * cfg["D"] * pairs
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"selection plus mixed attention of {tiles} query tiles over {heads} of {cfg['Hq']} query "
-                       f"heads ({pairs} valid pairs of {pre['total_pairs']}), {dt:.1f} s on 1 host thread, "
-                       f"same inputs")
+                sample=f"selection plus mixed attention of {tiles} query tiles over {heads} of "
+                       f"{cfg['B'] * cfg['Hq']} (batch, query head) pairs ({pairs} valid pairs of "
+                       f"{pre['total_pairs']}), {dt:.1f} s on 1 host thread, same inputs")
 
 
 def copy_calibration(dev, mib=256, reps=3):

@@ -30,6 +30,11 @@
 //   reference)), so O is rescaled only when that gap grows large; one more
 //   MFMA with an all-ones A operand accumulates l = sum(P).  FP16 tiles add
 //   their contribution with v_mfma_f32_16x16x32_f16.
+// Vertical-line tokens (HyQuant): up to 16 single keys per head, listed by the
+// caller, run as one FP16 tile ahead of the chunks: S^T[16 entries x 16
+// queries] with the bf16 MFMA, P = fp16(2^x), PV with the 16x16x16 fp16 MFMA;
+// those keys are masked out of their own tiles, so the chunks holding them
+// take the general path.  A kernel variant without lines carries none of it.
 // Runs of unmasked all-low-bit chunks are software-pipelined inside each wave:
 // the QK MFMAs of chunk c+1 are issued between the exponentials of chunk c,
 // and the row maxima of chunk c+1 between its PV MFMAs.  Masked chunks (the
