@@ -85,3 +85,40 @@ def attn_decode_ref(q_bits, cache, seq_len, n_sink, n_recent, softmax_scale=None
             p = np.exp(s - s.max(axis=1, keepdims=True))
             out[b, h * G:(h + 1) * G] = (p @ vv) / p.sum(axis=1, keepdims=True)
     return out
+
+
+def append_kv_ref(cache, seq_len, k_new_bits, v_new_bits, n_sink, n_recent):
+    """One decode step's cache update (reading R32), on copies of the inputs.
+
+    HyQuant (summary, abstract) applies its hybrid principle to KV-cache
+    compression in decode: the recent window stays in full precision and the
+    rest is low-bit.  As the sequence grows, token t = seq_len[b] (k_new,
+    v_new bf16 [B,Hkv,D]) enters the fp16 window as its last row and the
+    window's first row, token t - n_recent, leaves it: unless it is a sink
+    token (t - n_recent < n_sink) it is quantised to INT4 (R19) from its fp16
+    copy at position t - n_recent.  With n_recent = 0 the new token itself is
+    quantised, from its fp16 rounding.  A token t < n_sink is also written to
+    the sink copy.  seq_len[b] grows by one.  Returns (cache, seq_len)."""
+    c = {name: arr.copy() for name, arr in cache.items()}
+    lens = np.asarray(seq_len, dtype=np.int32).copy()
+    kn = bf16_bits_to_f32(k_new_bits).astype(np.float16)
+    vn = bf16_bits_to_f32(v_new_bits).astype(np.float16)
+    B = kn.shape[0]
+    for b in range(B):
+        t = int(lens[b])
+        t_old = t - n_recent
+        for which, new in (("k", kn), ("v", vn)):
+            rec = c[which + "_recent"]
+            leaving = rec[b, :, 0] if n_recent > 0 else new[b]
+            if t_old >= n_sink and t_old >= 0:
+                codes, sc, z = quantize_int4_g32(leaving.astype(np.float32))
+                c[which + "_codes"][b, :, t_old] = codes
+                c[which + "_scale"][b, :, t_old] = sc
+                c[which + "_zero"][b, :, t_old] = z
+            if n_recent > 0:
+                rec[b, :, :-1] = rec[b, :, 1:].copy()
+                rec[b, :, -1] = new[b]
+            if t < n_sink:
+                c[which + "_sink"][b, :, t] = new[b]
+        lens[b] = t + 1
+    return c, lens

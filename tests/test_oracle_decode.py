@@ -3,6 +3,7 @@
 import math
 
 import numpy as np
+import pytest
 
 import mxq_inputs
 from oracle import decode as Dm
@@ -97,3 +98,65 @@ def test_recent_rows_hold_the_last_tokens():
         for r in range(32):
             t = n - 32 + r
             assert np.array_equal(cache["k_recent"][b, :, r], kb[b, :, t].astype(np.float16))
+
+
+# ------------------------------------------------------------ cache append
+def _fp16_exact(bits):
+    """Zero every bf16 value below fp16's normal range, so that every value is
+    exact in fp16 (bf16's 8-bit significand fits fp16's 11 bits)."""
+    x = F.bf16_bits_to_f32(bits)
+    x = np.where(np.abs(x) < 2.0 ** -14, np.float32(0), x)
+    return F.f32_to_bf16_bits(x)
+
+
+def _grow(d, lens0, steps, n_sink, n_recent):
+    """Build the cache at lens0 from K/V with every later position zeroed (the
+    future is unknown), then append `steps` tokens per sequence from K/V."""
+    k, v = d["k"].copy(), d["v"].copy()
+    lens0 = np.asarray(lens0, dtype=np.int32)
+    for b in range(k.shape[0]):
+        k[b, :, lens0[b]:] = 0
+        v[b, :, lens0[b]:] = 0
+    cache = Dm.build_kv_cache_ref(k, v, lens0, n_sink, n_recent)
+    lens = lens0
+    for _ in range(steps):
+        kn = np.stack([d["k"][b, :, lens[b]] for b in range(len(lens))])
+        vn = np.stack([d["v"][b, :, lens[b]] for b in range(len(lens))])
+        cache, lens = Dm.append_kv_ref(cache, lens, kn, vn, n_sink, n_recent)
+    return cache, lens
+
+
+@pytest.mark.parametrize("n_sink,n_recent,lens0", [(16, 32, [100, 40, 5]), (0, 32, [64, 33, 1]),
+                                                    (16, 0, [100, 17, 3])])
+def test_append_equals_rebuild_on_fp16_exact_inputs(n_sink, n_recent, lens0):
+    """Appending tokens one at a time gives the cache a build at the final
+    length gives, wherever decode reads it, and the same decode output."""
+    d = _small(B=3, L=256, Hq=8, Hkv=2, D=64, seed=7)
+    d["k"], d["v"] = _fp16_exact(d["k"]), _fp16_exact(d["v"])
+    steps = 60
+    cache, lens = _grow(d, lens0, steps, n_sink, n_recent)
+    assert np.array_equal(lens, np.asarray(lens0) + steps)
+    ref = Dm.build_kv_cache_ref(d["k"], d["v"], lens, n_sink, n_recent)
+    for which in ("k", "v"):
+        assert np.array_equal(cache[which + "_sink"], ref[which + "_sink"])
+        assert np.array_equal(cache[which + "_recent"], ref[which + "_recent"])
+        for b in range(3):
+            lo, hi = n_sink, int(lens[b]) - n_recent  # the INT4 region decode reads
+            for name in ("_codes", "_scale", "_zero"):
+                assert np.array_equal(cache[which + name][b, :, lo:hi], ref[which + name][b, :, lo:hi])
+    out = Dm.attn_decode_ref(d["q"], cache, lens, n_sink, n_recent)
+    want = Dm.attn_decode_ref(d["q"], ref, lens, n_sink, n_recent)
+    assert np.array_equal(out, want)
+
+
+def test_append_window_holds_the_last_tokens():
+    d = _small(B=2, L=128, Hq=4, Hkv=1, D=64, seed=8)
+    cache, lens = _grow(d, [50, 7], 9, 4, 8)
+    kf = F.bf16_bits_to_f32(d["k"]).astype(np.float16)
+    for b in range(2):
+        n = int(lens[b])
+        for r in range(8):
+            t = n - 8 + r
+            if t >= 0:
+                assert np.array_equal(cache["k_recent"][b, 0, r], kf[b, 0, t])
+    assert np.array_equal(cache["k_sink"][1, 0, :4], kf[1, 0, :4])
