@@ -326,7 +326,32 @@ def bench_decode(args, dev):
     byts = int((n_q * per_tok_q + n_fp * per_tok_f).sum()) * Hkv + B * Hq * D * 2 + B * Hq * D * 4
     gbs = byts / (ms * 1e-3) / 1e9
     log(f"decode: {ms:.4f} ms/step, {byts / 1e9:.4f} GB, {gbs:.0f} GB/s ({gbs / PEAK_HBM:.3f} of HBM peak)")
-    return dict(ms=ms, bytes=byts, gbs=gbs)
+    # the step's cache update: one new token per sequence enters the fp16
+    # window, the token leaving it is quantised.  Timed on the same arrays with
+    # the lengths pulled back so that every append has room (contents differ
+    # from the timed decode's from here on; nothing reads them afterwards).
+    n_app = max(args.warmup, 50) + args.steps
+    seq = torch.from_numpy(lens - n_app).to(dev)
+    app_cache = mxq.QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, seq, n_sink, n_recent)
+    g = torch.Generator(device=dev).manual_seed(4)
+    kn = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    for _ in range(max(args.warmup, 50)):
+        mxq.attn_quantkv_append(app_cache, kn, vn)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        mxq.attn_quantkv_append(app_cache, kn, vn)
+    e1.record()
+    torch.cuda.synchronize()
+    app_ms = e0.elapsed_time(e1) / args.steps
+    assert int(seq[0]) == int(lens[0])
+    # bytes per append: the window read and written (K and V), the leaving
+    # token's fp16 row read and its codes, scales and zeros written, the new rows
+    app_bytes = B * Hkv * 2 * (2 * n_recent * D * 2 + D * 2 + D // 2 + 2 * 2 * (D // 32) + D * 2)
+    log(f"append: {app_ms * 1e3:.1f} us/step, {app_bytes / 1e6:.1f} MB, "
+        f"{app_bytes / (app_ms * 1e-3) / 1e9:.0f} GB/s")
+    return dict(ms=ms, bytes=byts, gbs=gbs, append_ms=app_ms, append_bytes=app_bytes)
 
 
 def cpu_baseline(args, pre):
@@ -479,7 +504,11 @@ def main():
                              "first 64 / last 128 tokens",
                  "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": PEAK_HBM, "unit": "GB/s",
                               "frac": round(dec["gbs"] / PEAK_HBM, 4),
-                              "traffic": recorded_traffic("attn_quantkv_decode")}}
+                              "traffic": recorded_traffic("attn_quantkv_decode")},
+                 "append": {"ms_per_step": round(dec["append_ms"], 5), "bytes": dec["append_bytes"],
+                            "gbs": round(dec["append_bytes"] / (dec["append_ms"] * 1e-3) / 1e9, 1),
+                            "what": "attn_quantkv_append: one token per sequence into the fp16 window, the "
+                                    "leaving token quantised to INT4"}}
         line["decode"] = dline
         if pre is None:
             line.update(value=dline["value"], unit="GB/s", ms_per_step=dline["ms_per_step"], dtype="int4 KV, fp32",

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   attn_select_lines(q, k, shape, n_lines, ..) -> lines, scores
   attn_mixed_fwd(ops, mask, shape, ...)       -> out, lse
   attn_quantkv_decode(q, cache, ...)          -> out
+  attn_quantkv_append(cache, k_new, v_new)    -> None (updates the cache in place)
 """
 
 from __future__ import annotations
@@ -33,7 +34,7 @@ MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 EXPORTED = [
     "mxq_quantize", "attn_select_blocks_workspace", "attn_select_blocks", "attn_select_lines_workspace",
     "attn_select_lines", "attn_mixed_fwd",
-    "attn_quantkv_decode_workspace", "attn_quantkv_decode", "mxq_status_string",
+    "attn_quantkv_decode_workspace", "attn_quantkv_decode", "attn_quantkv_append", "mxq_status_string",
     "mxq_last_error", "mxq_version",
 ]
 
@@ -100,6 +101,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_quantkv_decode.argtypes = [vp, ctypes.POINTER(KVCache), i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, vp, sz, vp, vp]
     lib.attn_quantkv_decode.restype = i32
+    # mxq_kv_cache_rw has mxq_kv_cache's layout (pointers, then three int32)
+    lib.attn_quantkv_append.argtypes = [vp, vp, ctypes.POINTER(KVCache), i32, i32, i32, vp]
+    lib.attn_quantkv_append.restype = i32
     lib.mxq_status_string.argtypes = [i32]
     lib.mxq_status_string.restype = ctypes.c_char_p
     lib.mxq_last_error.argtypes = []
@@ -329,3 +333,14 @@ def attn_quantkv_decode(q, cache: QuantKVCache, Hkv, max_seq_len, softmax_scale=
                                               float(softmax_scale), int(num_splits), _ptr(ws), ws.numel(),
                                               _ptr(out), _stream()))
     return out
+
+
+def attn_quantkv_append(cache: QuantKVCache, k_new, v_new):
+    """Append one token per sequence (k_new, v_new: bf16 [B,Hkv,D] on the GPU):
+    it enters the fp16 recent window, the token leaving the window is quantised
+    to INT4, and seq_len grows by one -- all on the GPU, in place."""
+    _need_gpu(k_new, v_new)
+    assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16 and k_new.shape == v_new.shape
+    B, Hkv, D = k_new.shape
+    kv = cache.c()
+    _check(load_library().attn_quantkv_append(_ptr(k_new), _ptr(v_new), ctypes.byref(kv), B, Hkv, D, _stream()))

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmxq.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["api.cpp", "quantize.hip", "select.hip", "attn_mixed.hip", "decode.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "select.hip", "attn_mixed.hip", "decode.hip", "kvcache.hip"]
 ARCH = os.environ.get("MXQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -73,6 +73,35 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return code | sign;
 }
 
+// Asymmetric 4-bit group of 32 values (reading R19): s = fp16(fl32(max-min)/15),
+// z = fp16(min), code = clamp(rint(fl32(x - z) / s), 0, 15), all codes 0 when
+// s == 0; codes packed two per byte, element 2k in the low nibble.  Every
+// operation rounds on its own (no fused multiply-add can form here).
+__device__ __forceinline__ void int4_group(const float (&v)[32], uint32_t (&packed)[4], uint16_t& sbits,
+                                           uint16_t& zbits) {
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+  const float s32 = (mx - mn) / 15.0f;
+  const _Float16 sh = static_cast<_Float16>(s32);
+  const _Float16 zh = static_cast<_Float16>(mn);
+  const float s = static_cast<float>(sh), z = static_cast<float>(zh);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) packed[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t c = 0;
+    if (s != 0.0f) {
+      float q = __builtin_rintf((v[i] - z) / s);
+      q = fminf(fmaxf(q, 0.0f), 15.0f);
+      c = static_cast<uint32_t>(q);
+    }
+    packed[i / 8] |= c << (4 * (i % 8));
+  }
+  sbits = __builtin_bit_cast(uint16_t, sh);
+  zbits = __builtin_bit_cast(uint16_t, zh);
+}
+
 // Exact floor division helpers
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -251,27 +251,12 @@ __global__ void __launch_bounds__(256) k_quant_int4_d(const uint16_t* __restrict
       v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
     }
   }
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 1; i < 32; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-  float s32 = (mx - mn) / 15.0f;
-  _Float16 sh = static_cast<_Float16>(s32);
-  _Float16 zh = static_cast<_Float16>(mn);
-  float s = static_cast<float>(sh), z = static_cast<float>(zh);
-  uint32_t packed[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    uint32_t c = 0;
-    if (s != 0.0f) {
-      float q = __builtin_rintf((v[i] - z) / s);
-      q = fminf(fmaxf(q, 0.0f), 15.0f);
-      c = static_cast<uint32_t>(q);
-    }
-    packed[i / 8] |= c << (4 * (i % 8));
-  }
+  uint32_t packed[4];
+  uint16_t sb, zb;
+  int4_group(v, packed, sb, zb);
   reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  scales[g] = __builtin_bit_cast(uint16_t, sh);
-  zeros[g] = __builtin_bit_cast(uint16_t, zh);
+  scales[g] = sb;
+  zeros[g] = zb;
 }
 
 inline unsigned grid_for(int64_t n, int threads) {

@@ -246,6 +246,41 @@ mxq_status attn_quantkv_decode(const uint16_t* q_bf16, const mxq_kv_cache* cache
                                float softmax_scale, int32_t num_splits, void* workspace,
                                size_t ws_bytes, float* out, mxq_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * attn_quantkv_append -- one decode step's cache update (HyQuant summary and
+ * abstract: the hybrid principle applied to KV-cache compression; reading
+ * R32).  For every sequence b, token t = seq_len[b] (k_new, v_new: bf16
+ * [B][Hkv][D], device) enters the fp16 recent window as its last row (the
+ * rows move up by one, row r then holds token t+1-n_recent+r), and the row
+ * that leaves, token t - n_recent, is quantised to INT4 from its fp16 copy
+ * at position t - n_recent unless it is a sink token (t - n_recent < n_sink).
+ * With n_recent = 0 the new token itself is quantised (from its fp16
+ * rounding) at position t.  A token t < n_sink is also written to the sink
+ * copy.  seq_len[b] then becomes t + 1.  The cache layout is the one
+ * attn_quantkv_decode reads (mxq_kv_cache); the pointers here are writable.
+ * A sequence with seq_len[b] outside [0, L_cap) is left unchanged (device
+ * data cannot be checked on the host).  D a multiple of 32, at most 256.
+ * Calls on one cache must not overlap (they read and write seq_len).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint16_t* k_scale;
+  uint16_t* k_zero;
+  uint16_t* v_scale;
+  uint16_t* v_zero;
+  uint16_t* k_sink;
+  uint16_t* v_sink;
+  uint16_t* k_recent;
+  uint16_t* v_recent;
+  int32_t* seq_len;
+  int32_t L_cap, n_sink, n_recent;
+} mxq_kv_cache_rw;
+
+mxq_status attn_quantkv_append(const uint16_t* k_new_bf16, const uint16_t* v_new_bf16,
+                               const mxq_kv_cache_rw* cache, int32_t B, int32_t Hkv, int32_t D,
+                               mxq_stream_t stream);
+
 /* Status text, and the message of the last failing call on this thread. */
 const char* mxq_status_string(mxq_status s);
 const char* mxq_last_error(void);

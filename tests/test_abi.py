@@ -110,3 +110,15 @@ def test_host_validation_rejects_before_launch(lib):
     assert st == mxq.MXQ_EINVAL
     st = so.attn_quantkv_decode(fake, ctypes.byref(kv), 1, 8, 2, 64, 64, 0.0, 0, fake, 1 << 20, fake, None)
     assert st == mxq.MXQ_EUNSUPPORTED
+    # cache append: validation before any launch
+    st = so.attn_quantkv_append(fake, fake, None, 1, 2, 128, None)
+    assert st == mxq.MXQ_EINVAL
+    rw = mxq.KVCache(fake, fake, fake, fake, fake, fake, None, None, fake, fake, fake, 64, 4, 8)
+    st = so.attn_quantkv_append(fake, fake, ctypes.byref(rw), 1, 2, 128, None)
+    assert st == mxq.MXQ_EINVAL and b"sink" in so.mxq_last_error()
+    rw = mxq.KVCache(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, 4, 8)
+    st = so.attn_quantkv_append(fake, fake, ctypes.byref(rw), 1, 2, 48, None)
+    assert st == mxq.MXQ_EUNSUPPORTED
+    rw = mxq.KVCache(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, 64, 4, 8)
+    st = so.attn_quantkv_append(fake, fake, ctypes.byref(rw), 1, 2, 128, None)
+    assert st == mxq.MXQ_EINVAL and b"seq_len" in so.mxq_last_error()

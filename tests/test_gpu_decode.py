@@ -105,3 +105,83 @@ def test_error_paths():
     with pytest.raises(mxq.MxqError) as ei:        # max_seq_len above the cache capacity
         mxq.attn_quantkv_decode(q[:, :8].contiguous(), cache, 4, 4096)
     assert ei.value.status == mxq.MXQ_EINVAL
+
+
+def _host_cache(cache):
+    from gpu_helpers import u8, u16
+
+    out = {}
+    for n in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_sink", "v_sink", "k_recent",
+              "v_recent"):
+        t = getattr(cache, n)
+        out[n] = None if t is None else (u8(t) if n.endswith("codes") else u16(t))
+    return out
+
+
+@pytest.mark.parametrize("n_sink,n_recent", [(64, 128), (16, 0)])
+def test_append_bit_exact_then_decode(n_sink, n_recent):
+    """attn_quantkv_append against the oracle's append, step by step from the
+    same cache: every array bit-exact after 24 steps (window moves, tokens
+    leaving it re-quantised, sink writes for a short sequence), then decode
+    over the grown cache against the oracle."""
+    mxq = gpu_or_skip()
+    import torch
+    from oracle.formats import pack_nibbles
+
+    lens0 = np.array([300, 150, 40], dtype=np.int32)
+    d = mxq_inputs.make_decode(dict(B=3, L=512, Hq=8, Hkv=2, D=128, n_sink=n_sink, n_recent=n_recent, seed=11,
+                                    seq_len=list(lens0)), threads=3)
+    k0, v0 = d["k"].copy(), d["v"].copy()
+    for b in range(3):  # the future is unknown when the cache is built
+        k0[b, :, lens0[b]:] = 0
+        v0[b, :, lens0[b]:] = 0
+    krec = vrec = None
+    if n_recent:
+        krec = np.zeros((3, 2, n_recent, 128), dtype=np.uint16)
+        vrec = np.zeros_like(krec)
+        for b in range(3):
+            for r in range(n_recent):
+                t = lens0[b] - n_recent + r
+                if t >= 0:
+                    krec[b, :, r], vrec[b, :, r] = k0[b, :, t], v0[b, :, t]
+        krec, vrec = bf16_dev(krec), bf16_dev(vrec)
+    seq = torch.from_numpy(lens0.copy()).to("cuda:0")
+    cache = mxq.build_quant_kv_cache(bf16_dev(k0), bf16_dev(v0), seq, n_sink, n_recent, krec, vrec)
+    ref = Dm.build_kv_cache_ref(k0, v0, lens0, n_sink, n_recent)
+    lens = lens0
+    for _ in range(24):
+        kn = np.stack([d["k"][b, :, lens[b]] for b in range(3)])
+        vn = np.stack([d["v"][b, :, lens[b]] for b in range(3)])
+        mxq.attn_quantkv_append(cache, bf16_dev(kn), bf16_dev(vn))
+        ref, lens = Dm.append_kv_ref(ref, lens, kn, vn, n_sink, n_recent)
+    got = _host_cache(cache)
+    assert np.array_equal(seq.cpu().numpy(), lens)
+    for which in ("k", "v"):
+        assert np.array_equal(got[which + "_codes"], pack_nibbles(ref[which + "_codes"])), which
+        for name in ("_scale", "_zero", "_sink", "_recent"):
+            if got[which + name] is None:  # no copy kept (n_recent = 0)
+                assert ref[which + name].size == 0
+                continue
+            assert np.array_equal(got[which + name], ref[which + name].view(np.uint16)), which + name
+    out = mxq.attn_quantkv_decode(bf16_dev(d["q"]), cache, 2, int(lens.max())).cpu().numpy()
+    want = Dm.attn_decode_ref(d["q"], ref, lens, n_sink, n_recent)
+    assert np.abs(out - want).max() <= TIGHT
+
+
+def test_append_leaves_out_of_range_sequences_alone():
+    mxq = gpu_or_skip()
+    import torch
+
+    d = mxq_inputs.make_decode(dict(B=2, L=128, Hq=4, Hkv=1, D=128, n_sink=4, n_recent=8, seed=12,
+                                    seq_len=[128, 60]), threads=2)
+    krec = bf16_dev(np.stack([d["k"][b, :, d["seq_len"][b] - 8:d["seq_len"][b]] for b in range(2)]))
+    vrec = bf16_dev(np.stack([d["v"][b, :, d["seq_len"][b] - 8:d["seq_len"][b]] for b in range(2)]))
+    seq = torch.from_numpy(d["seq_len"].copy()).to("cuda:0")
+    cache = mxq.build_quant_kv_cache(bf16_dev(d["k"]), bf16_dev(d["v"]), seq, 4, 8, krec, vrec)
+    before = _host_cache(cache)
+    kn = bf16_dev(d["k"][:, :, 0].copy())
+    mxq.attn_quantkv_append(cache, kn, kn)
+    after = _host_cache(cache)
+    assert seq.cpu().numpy().tolist() == [128, 61]   # sequence 0 is full (L_cap = 128)
+    assert np.array_equal(after["k_recent"][0], before["k_recent"][0])
+    assert not np.array_equal(after["k_recent"][1], before["k_recent"][1])
