@@ -27,7 +27,7 @@ What it follows (the pages and the readings of them):
 Element formats follow the public OCP Microscaling (MX) v1.0 rules (E2M1 and
 E4M3 elements with an E8M0 shared exponent per 32 elements), which is what
 "MX-style" means.  Every point the pages leave open is settled by a numbered
-reading (R1-R32); the functions below state the reading they implement.
+reading (R1-R33); the functions below state the reading they implement.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against closed forms, brute force, exhaustive
@@ -66,4 +66,4 @@ from .attention import (  # noqa: F401
     attn_exact_ref,
     softmax_scale_log2,
 )
-from .decode import build_kv_cache_ref, attn_decode_ref, append_kv_ref  # noqa: F401
+from .decode import build_kv_cache_ref, attn_decode_ref, append_kv_ref, used_decode_lines  # noqa: F401

@@ -23,14 +23,16 @@ import numpy as np
 from .formats import bf16_bits_to_f32, quantize_int4_g32, dequantize_int4_g32
 
 
-def build_kv_cache_ref(k_bits, v_bits, seq_len, n_sink, n_recent):
+def build_kv_cache_ref(k_bits, v_bits, seq_len, n_sink, n_recent, lines=None):
     """Quantise a bf16 cache [B,Hkv,L,D].
 
     Returns dict with k_codes/v_codes uint8 [B,Hkv,L,D] (unpacked), k_scale,
     k_zero, v_scale, v_zero float16 [B,Hkv,L,D/32], k_sink/v_sink float16
     [B,Hkv,n_sink,D] (tokens 0..n_sink-1) and k_recent/v_recent float16
     [B,Hkv,n_recent,D] (row r holds token len_b - n_recent + r; rows whose
-    token would be negative are zero)."""
+    token would be negative are zero).  With ``lines`` (int32 [B,Hkv,n]), also
+    lines and k_lines/v_lines float16 [B,Hkv,n,D]: the fp16 rows of the listed
+    tokens (zero rows for entries outside [0, L))."""
     k = bf16_bits_to_f32(k_bits)
     v = bf16_bits_to_f32(v_bits)
     B, Hkv, L, D = k.shape
@@ -47,13 +49,39 @@ def build_kv_cache_ref(k_bits, v_bits, seq_len, n_sink, n_recent):
             if 0 <= t < L:
                 k_rec[b, :, r] = k[b, :, t].astype(np.float16)
                 v_rec[b, :, r] = v[b, :, t].astype(np.float16)
-    return dict(k_codes=kc, k_scale=ksc, k_zero=kz, v_codes=vc, v_scale=vsc, v_zero=vz,
-                k_sink=k_sink, v_sink=v_sink, k_recent=k_rec, v_recent=v_rec)
+    out = dict(k_codes=kc, k_scale=ksc, k_zero=kz, v_codes=vc, v_scale=vsc, v_zero=vz,
+               k_sink=k_sink, v_sink=v_sink, k_recent=k_rec, v_recent=v_rec)
+    if lines is not None:
+        lines = np.asarray(lines, dtype=np.int32)
+        kl = np.zeros(lines.shape + (D,), dtype=np.float16)
+        vl = np.zeros(lines.shape + (D,), dtype=np.float16)
+        for b in range(B):
+            for h in range(Hkv):
+                for e, t in enumerate(lines[b, h]):
+                    if 0 <= t < L:
+                        kl[b, h, e] = k[b, h, t].astype(np.float16)
+                        vl[b, h, e] = v[b, h, t].astype(np.float16)
+        out.update(lines=lines.copy(), k_lines=kl, v_lines=vl)
+    return out
+
+
+def used_decode_lines(row, n, n_sink, n_recent):
+    """(entry, token) pairs of one line list that decode reads from the fp16
+    line rows (reading R33): an entry counts when its token lies in the INT4
+    region [n_sink, n - n_recent) and exceeds every earlier entry of the row;
+    tokens in the sink or the window are fp16 already."""
+    out, top = [], -1
+    for e, t in enumerate(int(x) for x in row):
+        if n_sink <= t < n - n_recent and t > top:
+            out.append((e, t))
+        top = max(top, t)
+    return out
 
 
 def cache_rows(cache, b, h, n, n_sink, n_recent, which):
     """Dequantised key (which='k') or value rows 0..n-1 of sequence b, kv head h,
-    float64 [n, D]: fp16 for t < n_sink or t >= n - n_recent, INT4 otherwise."""
+    float64 [n, D]: fp16 for t < n_sink or t >= n - n_recent, and for the
+    cache's vertical-line tokens if it has them; INT4 otherwise."""
     codes = cache[which + "_codes"][b, h, :n]
     rows = dequantize_int4_g32(codes, cache[which + "_scale"][b, h, :n],
                                cache[which + "_zero"][b, h, :n]).astype(np.float64)
@@ -63,6 +91,9 @@ def cache_rows(cache, b, h, n, n_sink, n_recent, which):
     rec = (t >= n - n_recent) & ~sink
     r_idx = t[rec] - (n - n_recent)
     rows[rec] = cache[which + "_recent"][b, h, r_idx].astype(np.float64)
+    if "lines" in cache:  # vertical-line tokens kept in fp16 (R33)
+        for e, tok in used_decode_lines(cache["lines"][b, h], n, n_sink, n_recent):
+            rows[tok] = cache[which + "_lines"][b, h, e].astype(np.float64)
     return rows
 
 

@@ -160,3 +160,54 @@ def test_append_window_holds_the_last_tokens():
             if t >= 0:
                 assert np.array_equal(cache["k_recent"][b, 0, r], kf[b, 0, t])
     assert np.array_equal(cache["k_sink"][1, 0, :4], kf[1, 0, :4])
+
+
+# ------------------------------------------------------- vertical lines in decode
+def test_lines_over_the_whole_int4_region_give_fp16_attention():
+    """With every token of the INT4 region listed as a line, decode reads
+    every token in fp16: exact softmax attention over fp16 K and V."""
+    d = _small(B=2, L=128, Hq=8, Hkv=2, D=64, seed=21, lens=[60, 44])
+    lines = np.full((2, 2, 16), -1, dtype=np.int32)
+    lines[0, :, :12] = np.arange(16, 28)          # INT4 region [16, 60 - 32) = 12 tokens
+    lines[1, :] = [-1, 3, 16, 20, 5] + [-1] * 11  # [16, 12): empty; entries ignored
+    cache = Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 16, 32, lines=lines)
+    out = Dm.attn_decode_ref(d["q"], cache, d["seq_len"], 16, 32)
+    qf = F.bf16_bits_to_f32(d["q"]).astype(np.float64)
+    kf = F.bf16_bits_to_f32(d["k"]).astype(np.float16).astype(np.float64)
+    vf = F.bf16_bits_to_f32(d["v"]).astype(np.float16).astype(np.float64)
+    for b in range(2):
+        n = int(d["seq_len"][b])
+        for h in range(8):
+            want = _softmax_attn(qf[b, h], kf[b, h // 4, :n], vf[b, h // 4, :n], 1 / 8.0)
+            assert np.allclose(out[b, h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_lines_outside_the_int4_region_change_nothing():
+    d = _small(B=2, L=256, Hq=8, Hkv=2, D=64, seed=22, lens=[256, 100])
+    plain = Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 16, 32)
+    lines = np.array([[[0, 15, 224, 255, 300, -1]] * 2, [[5, 68, 99, 99, 7, -3]] * 2], dtype=np.int32)
+    withl = Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 16, 32, lines=lines)
+    assert np.array_equal(Dm.attn_decode_ref(d["q"], plain, d["seq_len"], 16, 32),
+                          Dm.attn_decode_ref(d["q"], withl, d["seq_len"], 16, 32))
+    assert [t for _, t in Dm.used_decode_lines(lines[1, 0], 100, 16, 32)] == []
+    assert Dm.used_decode_lines(np.array([40, 40, 20, 50, -1]), 100, 16, 32) == [(0, 40), (3, 50)]
+
+
+def test_a_heavy_token_kept_as_a_line_cuts_the_error():
+    """A token whose key lines up with every query carries most of the
+    attention; quantised to 4 bits it drags the output, kept in fp16 as a
+    line it does not (HyQuant's point, in decode)."""
+    d = _small(B=1, L=512, Hq=4, Hkv=1, D=64, seed=23, lens=[512])
+    q = F.bf16_bits_to_f32(d["q"])
+    k = F.bf16_bits_to_f32(d["k"]).copy()
+    k[0, 0, 200] = 3.0 * q[0].mean(axis=0) / np.linalg.norm(q[0].mean(axis=0)) * 8.0
+    k[0, 0, 200, :8] += 37.0  # an outlier the 4-bit group cannot hold finely
+    kb = F.f32_to_bf16_bits(k)
+    lines = np.array([[[200] + [-1] * 15]], dtype=np.int32)
+    exact = np.stack([_softmax_attn(q[0, h].astype(np.float64), F.bf16_bits_to_f32(kb)[0, 0].astype(np.float64),
+                                    F.bf16_bits_to_f32(d["v"])[0, 0].astype(np.float64), 1 / 8.0) for h in range(4)])
+    e_plain = np.abs(Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(kb, d["v"], d["seq_len"], 16, 32),
+                                        d["seq_len"], 16, 32)[0] - exact).max()
+    e_line = np.abs(Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(kb, d["v"], d["seq_len"], 16, 32, lines=lines),
+                                       d["seq_len"], 16, 32)[0] - exact).max()
+    assert e_line < 0.5 * e_plain, (e_line, e_plain)
