@@ -292,9 +292,24 @@ def bench_decode(args, dev):
     v_sink = torch.empty_like(k_sink)
     k_rec = torch.empty((B, Hkv, n_recent, D), dtype=torch.float16, device=dev)
     v_rec = torch.empty_like(k_rec)
+    # vertical-line tokens (optional): evenly spread over the INT4 region
+    n_lines = args.decode_lines
+    lines_np = None
+    if n_lines:
+        lines_np = np.zeros((B, Hkv, n_lines), dtype=np.int32)
+        for b in range(B):
+            lo, hi = n_sink, int(lens[b]) - n_recent
+            lines_np[b, :] = np.linspace(lo, hi - 1, n_lines).round().astype(np.int32)
+        k_ln = torch.empty((B, Hkv, n_lines, D), dtype=torch.bfloat16, device=dev)
+        v_ln = torch.empty_like(k_ln)
     for b in range(B):
         kb = _bf16(d["k"][b:b + 1], dev)
         vb = _bf16(d["v"][b:b + 1], dev)
+        if n_lines:
+            idx = torch.from_numpy(lines_np[b]).long().to(dev)  # [Hkv, n_lines]
+            for h in range(Hkv):
+                k_ln[b, h] = kb[0, h, idx[h]]
+                v_ln[b, h] = vb[0, h, idx[h]]
         c = mxq.build_quant_kv_cache(kb, vb, torch.tensor([int(lens[b])], dtype=torch.int32, device=dev), n_sink,
                                      n_recent, kb[:, :, lens[b] - n_recent:lens[b]], vb[:, :, lens[b] - n_recent:lens[b]])
         kc[b], vc[b], ks[b], kz[b], vs[b], vz[b] = c.k_codes[0], c.v_codes[0], c.k_scale[0], c.k_zero[0], c.v_scale[0], c.v_zero[0]
@@ -302,6 +317,12 @@ def bench_decode(args, dev):
     del d["k"], d["v"]
     cache = mxq.QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec,
                              torch.from_numpy(lens).to(dev), n_sink, n_recent)
+    line_cache = None
+    if n_lines:
+        k_lf, _, _ = mxq.mxq_quantize(k_ln, mxq.MXQ_FP16, mxq.MXQ_AXIS_D)
+        v_lf, _, _ = mxq.mxq_quantize(v_ln, mxq.MXQ_FP16, mxq.MXQ_AXIS_D)
+        line_cache = mxq.QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, cache.seq_len, n_sink,
+                                      n_recent, torch.from_numpy(lines_np).to(dev), k_lf, v_lf)
     q = _bf16(d["q"], dev)
     ws = mxq.decode_workspace(B, Hq, D, 0, int(lens.max()), dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
@@ -326,6 +347,18 @@ def bench_decode(args, dev):
     byts = int((n_q * per_tok_q + n_fp * per_tok_f).sum()) * Hkv + B * Hq * D * 2 + B * Hq * D * 4
     gbs = byts / (ms * 1e-3) / 1e9
     log(f"decode: {ms:.4f} ms/step, {byts / 1e9:.4f} GB, {gbs:.0f} GB/s ({gbs / PEAK_HBM:.3f} of HBM peak)")
+    lines_ms = None
+    if line_cache is not None:
+        for _ in range(20):
+            mxq.attn_quantkv_decode(q, line_cache, Hkv, int(lens.max()), workspace=ws, out=out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            mxq.attn_quantkv_decode(q, line_cache, Hkv, int(lens.max()), workspace=ws, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        lines_ms = e0.elapsed_time(e1) / args.steps
+        log(f"decode with {n_lines} vertical-line tokens per kv head: {lines_ms:.4f} ms/step")
     # the step's cache update: one new token per sequence enters the fp16
     # window, the token leaving it is quantised.  Timed on the same arrays with
     # the lengths pulled back so that every append has room (contents differ
@@ -351,7 +384,8 @@ def bench_decode(args, dev):
     app_bytes = B * Hkv * 2 * (2 * n_recent * D * 2 + D * 2 + D // 2 + 2 * 2 * (D // 32) + D * 2)
     log(f"append: {app_ms * 1e3:.1f} us/step, {app_bytes / 1e6:.1f} MB, "
         f"{app_bytes / (app_ms * 1e-3) / 1e9:.0f} GB/s")
-    return dict(ms=ms, bytes=byts, gbs=gbs, append_ms=app_ms, append_bytes=app_bytes)
+    return dict(ms=ms, bytes=byts, gbs=gbs, append_ms=app_ms, append_bytes=app_bytes, lines_ms=lines_ms,
+                n_lines=n_lines)
 
 
 def cpu_baseline(args, pre):
@@ -442,6 +476,8 @@ def main():
                          "quality: the synthetic error/speed curve over the FP16 fraction")
     ap.add_argument("--quality-n", default="8192,16384,32768", help="sequence lengths of the quality sweep")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--decode-lines", type=int, default=0,
+                    help="also time decode with this many vertical-line tokens (fp16) per kv head, at most 16")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; each (batch, kv head) is independent, so more GPUs "
@@ -509,6 +545,8 @@ def main():
                             "gbs": round(dec["append_bytes"] / (dec["append_ms"] * 1e-3) / 1e9, 1),
                             "what": "attn_quantkv_append: one token per sequence into the fp16 window, the "
                                     "leaving token quantised to INT4"}}
+        if dec["lines_ms"] is not None:
+            dline["with_lines"] = {"n_lines": dec["n_lines"], "ms_per_step": round(dec["lines_ms"], 5)}
         line["decode"] = dline
         if pre is None:
             line.update(value=dline["value"], unit="GB/s", ms_per_step=dline["ms_per_step"], dtype="int4 KV, fp32",

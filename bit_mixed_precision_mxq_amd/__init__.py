@@ -57,16 +57,26 @@ class LineParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_lines", "sink_tokens", "group_shared")]
 
 
-class KVCache(ctypes.Structure):
-    _fields_ = [
-        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
-        ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
-        ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
-        ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
-        ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p),
-        ("seq_len", ctypes.c_void_p),
-        ("L_cap", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+_KV_FIELDS = [
+    ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+    ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+    ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+    ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
+    ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p),
+    ("seq_len", ctypes.c_void_p),
+    ("L_cap", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+]
+
+
+class KVCache(ctypes.Structure):  # mxq_kv_cache
+    _fields_ = _KV_FIELDS + [
+        ("lines", ctypes.c_void_p), ("k_lines", ctypes.c_void_p), ("v_lines", ctypes.c_void_p),
+        ("n_lines", ctypes.c_int32),
     ]
+
+
+class KVCacheRW(ctypes.Structure):  # mxq_kv_cache_rw
+    _fields_ = _KV_FIELDS
 
 
 _lib = None
@@ -101,8 +111,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_quantkv_decode.argtypes = [vp, ctypes.POINTER(KVCache), i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, vp, sz, vp, vp]
     lib.attn_quantkv_decode.restype = i32
-    # mxq_kv_cache_rw has mxq_kv_cache's layout (pointers, then three int32)
-    lib.attn_quantkv_append.argtypes = [vp, vp, ctypes.POINTER(KVCache), i32, i32, i32, vp]
+    lib.attn_quantkv_append.argtypes = [vp, vp, ctypes.POINTER(KVCacheRW), i32, i32, i32, vp]
     lib.attn_quantkv_append.restype = i32
     lib.mxq_status_string.argtypes = [i32]
     lib.mxq_status_string.restype = ctypes.c_char_p
@@ -290,19 +299,32 @@ class QuantKVCache:
     seq_len: torch.Tensor
     n_sink: int
     n_recent: int
+    lines: torch.Tensor | None = None     # int32 [B,Hkv,n_lines] vertical-line tokens
+    k_lines: torch.Tensor | None = None   # fp16 [B,Hkv,n_lines,D]
+    v_lines: torch.Tensor | None = None
+
+    def _common(self):
+        return (_ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.k_zero),
+                _ptr(self.v_scale), _ptr(self.v_zero), _ptr(self.k_sink), _ptr(self.v_sink),
+                _ptr(self.k_recent), _ptr(self.v_recent), _ptr(self.seq_len),
+                int(self.k_codes.shape[2]), int(self.n_sink), int(self.n_recent))
 
     def c(self) -> KVCache:
-        return KVCache(_ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.k_zero),
-                       _ptr(self.v_scale), _ptr(self.v_zero), _ptr(self.k_sink), _ptr(self.v_sink),
-                       _ptr(self.k_recent), _ptr(self.v_recent), _ptr(self.seq_len),
-                       int(self.k_codes.shape[2]), int(self.n_sink), int(self.n_recent))
+        n_lines = 0 if self.lines is None else int(self.lines.shape[-1])
+        return KVCache(*self._common(), _ptr(self.lines), _ptr(self.k_lines), _ptr(self.v_lines), n_lines)
+
+    def rw(self) -> KVCacheRW:
+        return KVCacheRW(*self._common())
 
 
-def build_quant_kv_cache(k, v, seq_len, n_sink, n_recent, k_recent=None, v_recent=None) -> QuantKVCache:
+def build_quant_kv_cache(k, v, seq_len, n_sink, n_recent, k_recent=None, v_recent=None, lines=None,
+                         k_line_rows=None, v_line_rows=None) -> QuantKVCache:
     """k, v: bf16 [B,Hkv,L,D] on the GPU; seq_len int32 [B] on the GPU.  The
     INT4 arrays cover all L positions; the sink copy is tokens 0..n_sink-1 and
     the recent copy (bf16 [B,Hkv,n_recent,D], given by the caller, who knows
-    each sequence's last tokens) is converted to fp16."""
+    each sequence's last tokens) is converted to fp16.  Optional vertical-line
+    tokens: lines int32 [B,Hkv,n] on the GPU and their bf16 rows
+    [B,Hkv,n,D] (gathered by the caller), kept in fp16."""
     kc, ks, kz = mxq_quantize(k, MXQ_INT4_ASYM_G32, MXQ_AXIS_D)
     vc, vs, vz = mxq_quantize(v, MXQ_INT4_ASYM_G32, MXQ_AXIS_D)
     k_sink = v_sink = k_rec = v_rec = None
@@ -312,7 +334,13 @@ def build_quant_kv_cache(k, v, seq_len, n_sink, n_recent, k_recent=None, v_recen
     if n_recent > 0:
         k_rec, _, _ = mxq_quantize(k_recent.contiguous(), MXQ_FP16, MXQ_AXIS_D)
         v_rec, _, _ = mxq_quantize(v_recent.contiguous(), MXQ_FP16, MXQ_AXIS_D)
-    return QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, seq_len, n_sink, n_recent)
+    k_ln = v_ln = None
+    if lines is not None:
+        _need_gpu(lines)
+        k_ln, _, _ = mxq_quantize(k_line_rows.contiguous(), MXQ_FP16, MXQ_AXIS_D)
+        v_ln, _, _ = mxq_quantize(v_line_rows.contiguous(), MXQ_FP16, MXQ_AXIS_D)
+    return QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, seq_len, n_sink, n_recent,
+                        lines, k_ln, v_ln)
 
 
 def decode_workspace(B, Hq, D, num_splits, max_seq_len, device) -> torch.Tensor:
@@ -342,5 +370,5 @@ def attn_quantkv_append(cache: QuantKVCache, k_new, v_new):
     _need_gpu(k_new, v_new)
     assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16 and k_new.shape == v_new.shape
     B, Hkv, D = k_new.shape
-    kv = cache.c()
+    kv = cache.rw()
     _check(load_library().attn_quantkv_append(_ptr(k_new), _ptr(v_new), ctypes.byref(kv), B, Hkv, D, _stream()))

@@ -34,6 +34,9 @@
 //          Row (h, g) is meaningful for the head_dim columns of group g; the
 //          zero-point term sum_t p_t z_t,g is accumulated on the side.
 //  Loads for the next block are issued before the current one is computed.
+// Vertical-line tokens (the LINES variant): up to 16 listed tokens of the INT4
+// region are read from fp16 rows instead; the INT4 splits mask them out of
+// their blocks and split S adds them to its fp16 tokens.
 // k_decode_merge: (sequence, query head): merge the S+1 partials in ascending
 // split order, 16 at a time.
 #include "mxq_internal.h"
@@ -45,6 +48,7 @@ constexpr int kD = 128;      // head_dim supported by the decode kernel
 constexpr int kWaves = 4;    // waves per workgroup
 constexpr int kBlk = 32;     // INT4 tokens per wave block
 constexpr int kCodeScale = 136;  // E8M0 of 2^9: a code byte c is the E4M3 value c * 2^-9
+constexpr int kMaxLines = 16;    // vertical-line tokens per (sequence, kv head)
 
 struct DecodeArgs {
   const uint16_t* q;  // bf16 [B][Hq][D]
@@ -160,14 +164,15 @@ __device__ __forceinline__ v8i widen_codes(u4v c4) {
 // fp16 sink/recent tokens of one (sequence, kv head): plain fp32 online
 // softmax, lane l owns head_dim elements 2l and 2l+1.  Writes the wave's
 // partial (m, l, o) to LDS.
-template <int G>
+template <int G, bool LINES>
 __device__ void fp16_tokens(const DecodeArgs& a, int hk, int b, int len, int wave, int lane,
-                            float (*s_o)[4][kD], float (*s_ml)[4][2]) {
+                            float (*s_o)[4][kD], float (*s_ml)[4][2], int lkey) {
   const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
   const int n_sink = a.kv.n_sink, n_recent = a.kv.n_recent;
   const int a0 = min(n_sink, len);
   const int r0 = max(len - n_recent, a0);
-  const int nF = a0 + (len - r0);
+  const int nSR = a0 + (len - r0);               // sink and window tokens
+  const int nF = nSR + (LINES ? kMaxLines : 0);  // then the line entries (masked when unused)
   const int rec_base = len - n_recent;  // recent row r holds token rec_base + r
   float qf[G][2], m[G], l[G], o[G][2];
 #pragma unroll
@@ -180,22 +185,32 @@ __device__ void fp16_tokens(const DecodeArgs& a, int hk, int b, int len, int wav
   }
   for (int base = 8 * wave; base < nF; base += 8 * kWaves) {
     uint32_t kk[8], vv[8];
+    bool ok[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int idx = base + u;
       kk[u] = 0u; vv[u] = 0u;
-      if (idx < nF) {
+      ok[u] = idx < nF;
+      if (idx < nSR) {
         const int t = idx < a0 ? idx : r0 + (idx - a0);
         const int64_t off = t < n_sink ? (bh * n_sink + t) * kD : (bh * n_recent + (t - rec_base)) * kD;
         const uint16_t* ks = t < n_sink ? a.kv.k_sink : a.kv.k_recent;
         const uint16_t* vs = t < n_sink ? a.kv.v_sink : a.kv.v_recent;
         kk[u] = *reinterpret_cast<const uint32_t*>(ks + off + 2 * lane);
         vv[u] = *reinterpret_cast<const uint32_t*>(vs + off + 2 * lane);
+      } else if (LINES && idx < nF) {
+        const int e = idx - nSR;  // line entry (wave-uniform)
+        ok[u] = __builtin_amdgcn_readlane(lkey, e) >= 0;
+        if (ok[u]) {
+          const int64_t off = (bh * a.kv.n_lines + e) * kD + 2 * lane;
+          kk[u] = *reinterpret_cast<const uint32_t*>(a.kv.k_lines + off);
+          vv[u] = *reinterpret_cast<const uint32_t*>(a.kv.v_lines + off);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const bool valid = base + u < nF;
+      const bool valid = ok[u];
       const float k0 = h_lo(kk[u]), k1 = h_hi(kk[u]), v0 = h_lo(vv[u]), v1 = h_hi(vv[u]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -246,11 +261,13 @@ struct Ctx {
 // The LDS pointers are restrict parameters: after inlining, their accesses
 // carry alias scopes, which lets the compiler's wait insertion see that reads
 // of this block's slot do not depend on loads still landing in other slots.
+// lmask bit j: token t0 + j is a vertical line, read elsewhere (masked here)
 template <int G>
 __device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const KBlk& x,
                                             const lds_char* __restrict__ slot, u2v* __restrict__ szw,
                                             uint2* __restrict__ wr, uint2* __restrict__ wr2,
-                                            lds_s4* __restrict__ rd0, lds_s4* __restrict__ rd1, int t0) {
+                                            lds_s4* __restrict__ rd0, lds_s4* __restrict__ rd1, int t0,
+                                            uint32_t lmask) {
   // this block's V codes have landed once only the later blocks' loads may
   // still be in flight (vector-memory loads complete in order); the compiler
   // does not track loads that write LDS directly
@@ -288,7 +305,8 @@ __device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const KBlk&
       sc = __builtin_fmaf(half_at(sz[st][0], g), acc[g], sc);
       sc = __builtin_fmaf(half_at(sz[st][1], g), cx.qs[g], sc);
     }
-    xs[st] = (t0 + 16 * st + tl < cx.end) ? sc * cx.c : -__builtin_inff();
+    const bool live = t0 + 16 * st + tl < cx.end && !((lmask >> (16 * st + tl)) & 1u);
+    xs[st] = live ? sc * cx.c : -__builtin_inff();
   }
   const float mx = row_max16(fmaxf(xs[0], xs[1]));
   const float m_new = fmaxf(S.m_run, mx);
@@ -357,7 +375,7 @@ __device__ __forceinline__ void process_blk(St& S, const Ctx<G>& cx, const KBlk&
   }
 }
 
-template <int G>
+template <int G, bool LINES>
 __global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
   __shared__ float s_o[kWaves][4][kD];
   __shared__ float s_ml[kWaves][4][2];
@@ -379,8 +397,41 @@ __global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
   const int lane = tid & 63;
   const int len = min(a.kv.seq_len[b], a.kv.L_cap);  // never read past the cache
 
+  // Vertical lines (R33): lane e < 16 of every wave holds entry e's token when
+  // it lies in the INT4 region [n_sink, len - n_recent) and exceeds every
+  // earlier entry (an exclusive prefix maximum by DPP row shifts), else -1
+  int lkey = -1;
+  if constexpr (LINES) {
+    const int e = lane & 15;
+    const int raw = (lane < 16 && e < a.kv.n_lines)
+                        ? a.kv.lines[(static_cast<int64_t>(b) * a.Hkv + hk) * a.kv.n_lines + e] : -1;
+    constexpr int kMin = -2147483647 - 1;
+    int pm = raw;
+    pm = max(pm, __builtin_amdgcn_update_dpp(kMin, pm, 0x111, 0xF, 0xF, false));  // row_shr:1
+    pm = max(pm, __builtin_amdgcn_update_dpp(kMin, pm, 0x112, 0xF, 0xF, false));  // row_shr:2
+    pm = max(pm, __builtin_amdgcn_update_dpp(kMin, pm, 0x114, 0xF, 0xF, false));  // row_shr:4
+    pm = max(pm, __builtin_amdgcn_update_dpp(kMin, pm, 0x118, 0xF, 0xF, false));  // row_shr:8
+    const int before = __builtin_amdgcn_update_dpp(kMin, pm, 0x111, 0xF, 0xF, false);
+    if (lane < 16 && raw >= a.kv.n_sink && raw < len - a.kv.n_recent && raw > before) lkey = raw;
+  }
+  // line tokens inside the 32-token block starting at t
+  auto line_mask = [&](int t) -> uint32_t {
+    if constexpr (!LINES) {
+      return 0u;
+    } else {
+      uint64_t bal = __ballot(lkey >= t && lkey < t + kBlk);
+      uint32_t m = 0;
+      while (bal) {
+        const int e = __builtin_ctzll(bal);
+        m |= 1u << (__builtin_amdgcn_readlane(lkey, e) - t);
+        bal &= bal - 1;
+      }
+      return m;
+    }
+  };
+
   if (s == a.S) {
-    fp16_tokens<G>(a, hk, b, len, wave, lane, s_o, s_ml);
+    fp16_tokens<G, LINES>(a, hk, b, len, wave, lane, s_o, s_ml, lkey);
   } else {
     const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
     const int int_lo = min(a.kv.n_sink, len);
@@ -500,16 +551,16 @@ __global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
       issue_blk(k2, rs, MXQ_AT(2), offk, lane, sl2);
       issue_blk(k3, rs, MXQ_AT(3), offk, lane, sl3);
       for (int grp = 0; grp < n_groups; ++grp) {
-        process_blk<G>(st_, cx, k0, sl0, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        process_blk<G>(st_, cx, k0, sl0, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0, line_mask(t0));
         issue_blk(k0, rs, MXQ_AT(4), offk, lane, sl0);
         t0 += kStep;
-        process_blk<G>(st_, cx, k1, sl1, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        process_blk<G>(st_, cx, k1, sl1, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0, line_mask(t0));
         issue_blk(k1, rs, MXQ_AT(4), offk, lane, sl1);
         t0 += kStep;
-        process_blk<G>(st_, cx, k2, sl2, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        process_blk<G>(st_, cx, k2, sl2, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0, line_mask(t0));
         issue_blk(k2, rs, MXQ_AT(4), offk, lane, sl2);
         t0 += kStep;
-        process_blk<G>(st_, cx, k3, sl3, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0);
+        process_blk<G>(st_, cx, k3, sl3, szw, cx.wr, cx.wr2, cx.rd0, cx.rd1, t0, line_mask(t0));
         issue_blk(k3, rs, MXQ_AT(4), offk, lane, sl3);
         t0 += kStep;
       }
@@ -638,6 +689,10 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
   MXQ_REQUIRE(kv->n_sink == 0 || (kv->k_sink && kv->v_sink), MXQ_EINVAL, "attn_quantkv_decode: sink arrays missing");
   MXQ_REQUIRE(kv->n_recent == 0 || (kv->k_recent && kv->v_recent), MXQ_EINVAL,
               "attn_quantkv_decode: recent arrays missing");
+  MXQ_REQUIRE(kv->n_lines >= 0 && kv->n_lines <= kMaxLines, MXQ_EINVAL,
+              "attn_quantkv_decode: n_lines must be in [0, 16]");
+  MXQ_REQUIRE(kv->n_lines == 0 || (kv->lines && kv->k_lines && kv->v_lines), MXQ_EINVAL,
+              "attn_quantkv_decode: lines, k_lines and v_lines are required when n_lines > 0");
   MXQ_REQUIRE(max_seq_len >= 1 && max_seq_len <= kv->L_cap, MXQ_EINVAL,
               "attn_quantkv_decode: need 1 <= max_seq_len <= L_cap");
   // each (sequence, kv head) region of the code arrays is addressed with
@@ -659,10 +714,14 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
   a.c = static_cast<float>(sc * 1.4426950408889634);
   hipStream_t st = as_stream(stream);
   dim3 grid(S + 1, Hkv, B);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(k_decode_split<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_split<2>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_decode_split<4>, grid, dim3(256), 0, st, a); break;
+  const bool lines = kv->n_lines > 0;
+  switch (G * 2 + (lines ? 1 : 0)) {
+    case 2: hipLaunchKernelGGL((k_decode_split<1, false>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_split<1, true>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_split<2, false>), grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_split<4, false>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(256), 0, st, a); break;
   }
   mxq_status stt = check_launch("k_decode_split");
   if (stt != MXQ_OK) return stt;

@@ -205,6 +205,11 @@ mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
  *   - k_sink/v_sink   fp16 [B][Hkv][n_sink][D]      when t < n_sink,
  *   - k_recent/v_recent fp16 [B][Hkv][n_recent][D]  when t >= seq_len[b]-n_recent
  *     (row r holds token seq_len[b]-n_recent+r),
+ *   - k_lines/v_lines fp16 [B][Hkv][n_lines][D] row e when t is entry e of
+ *     lines i32 [B][Hkv][n_lines] and that entry counts (reading R33: the
+ *     token lies in [n_sink, seq_len[b] - n_recent) and exceeds every earlier
+ *     entry of the row) -- vertical-line tokens kept in fp16, HyQuant's
+ *     hybrid principle in decode; n_lines in [0, 16], arrays NULL when 0,
  *   - otherwise the INT4 arrays: codes u8 [B][Hkv][L_cap][D/2], scale and zero
  *     fp16 [B][Hkv][L_cap][D/32] (mxq_quantize INT4_ASYM_G32 layout), with
  *     x = fl32(code*s + z).
@@ -222,6 +227,10 @@ typedef struct {
   const uint16_t* v_recent;
   const int32_t* seq_len;
   int32_t L_cap, n_sink, n_recent;
+  const int32_t* lines;
+  const uint16_t* k_lines;
+  const uint16_t* v_lines;
+  int32_t n_lines;
 } mxq_kv_cache;
 
 /* ---------------------------------------------------------------------------
@@ -257,7 +266,8 @@ mxq_status attn_quantkv_decode(const uint16_t* q_bf16, const mxq_kv_cache* cache
  * With n_recent = 0 the new token itself is quantised (from its fp16
  * rounding) at position t.  A token t < n_sink is also written to the sink
  * copy.  seq_len[b] then becomes t + 1.  The cache layout is the one
- * attn_quantkv_decode reads (mxq_kv_cache); the pointers here are writable.
+ * attn_quantkv_decode reads (mxq_kv_cache, whose vertical-line rows need no
+ * update: they hold fixed tokens); the pointers here are writable.
  * A sequence with seq_len[b] outside [0, L_cap) is left unchanged (device
  * data cannot be checked on the host).  D a multiple of 32, at most 256.
  * Calls on one cache must not overlap (they read and write seq_len).

@@ -113,12 +113,19 @@ def test_host_validation_rejects_before_launch(lib):
     # cache append: validation before any launch
     st = so.attn_quantkv_append(fake, fake, None, 1, 2, 128, None)
     assert st == mxq.MXQ_EINVAL
-    rw = mxq.KVCache(fake, fake, fake, fake, fake, fake, None, None, fake, fake, fake, 64, 4, 8)
+    rw = mxq.KVCacheRW(fake, fake, fake, fake, fake, fake, None, None, fake, fake, fake, 64, 4, 8)
     st = so.attn_quantkv_append(fake, fake, ctypes.byref(rw), 1, 2, 128, None)
     assert st == mxq.MXQ_EINVAL and b"sink" in so.mxq_last_error()
-    rw = mxq.KVCache(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, 4, 8)
+    rw = mxq.KVCacheRW(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, 4, 8)
     st = so.attn_quantkv_append(fake, fake, ctypes.byref(rw), 1, 2, 48, None)
     assert st == mxq.MXQ_EUNSUPPORTED
-    rw = mxq.KVCache(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, 64, 4, 8)
+    rw = mxq.KVCacheRW(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, 64, 4, 8)
     st = so.attn_quantkv_append(fake, fake, ctypes.byref(rw), 1, 2, 128, None)
     assert st == mxq.MXQ_EINVAL and b"seq_len" in so.mxq_last_error()
+    # decode with vertical lines: at most 16, arrays required
+    kvl = mxq.KVCache(fake, fake, fake, fake, fake, fake, None, None, None, None, fake, 64, 0, 0, fake, fake, fake, 17)
+    st = so.attn_quantkv_decode(fake, ctypes.byref(kvl), 1, 8, 2, 128, 64, 0.0, 0, fake, 1 << 20, fake, None)
+    assert st == mxq.MXQ_EINVAL and b"n_lines" in so.mxq_last_error()
+    kvl = mxq.KVCache(fake, fake, fake, fake, fake, fake, None, None, None, None, fake, 64, 0, 0, fake, None, fake, 4)
+    st = so.attn_quantkv_decode(fake, ctypes.byref(kvl), 1, 8, 2, 128, 64, 0.0, 0, fake, 1 << 20, fake, None)
+    assert st == mxq.MXQ_EINVAL and b"lines" in so.mxq_last_error()

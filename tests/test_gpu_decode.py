@@ -185,3 +185,84 @@ def test_append_leaves_out_of_range_sequences_alone():
     assert seq.cpu().numpy().tolist() == [128, 61]   # sequence 0 is full (L_cap = 128)
     assert np.array_equal(after["k_recent"][0], before["k_recent"][0])
     assert not np.array_equal(after["k_recent"][1], before["k_recent"][1])
+
+
+def _gather_lines(x, lines):
+    """bf16 bits [B,Hkv,L,D] -> the rows of the listed tokens [B,Hkv,n,D] (zero rows for entries outside [0, L))."""
+    B, H, L, D = x.shape
+    out = np.zeros(lines.shape + (D,), dtype=x.dtype)
+    for b in range(B):
+        for h in range(H):
+            for e, t in enumerate(lines[b, h]):
+                if 0 <= t < L:
+                    out[b, h, e] = x[b, h, t]
+    return out
+
+
+def _run_lines(mxq, d, n_sink, n_recent, lines, num_splits=0):
+    import torch
+
+    k, v, q = bf16_dev(d["k"]), bf16_dev(d["v"]), bf16_dev(d["q"])
+    lens = d["seq_len"]
+    krec = torch.stack([k[b, :, lens[b] - n_recent:lens[b]] for b in range(len(lens))])
+    vrec = torch.stack([v[b, :, lens[b] - n_recent:lens[b]] for b in range(len(lens))])
+    lt = torch.from_numpy(lines).to("cuda:0")
+    cache = mxq.build_quant_kv_cache(k, v, torch.from_numpy(lens).to("cuda:0"), n_sink, n_recent, krec, vrec,
+                                     lines=lt, k_line_rows=bf16_dev(_gather_lines(d["k"], lines)),
+                                     v_line_rows=bf16_dev(_gather_lines(d["v"], lines)))
+    return mxq.attn_quantkv_decode(q, cache, d["Hkv"], int(lens.max()), num_splits=num_splits).cpu().numpy()
+
+
+@pytest.mark.parametrize("num_splits", [0, 3, 16])
+@pytest.mark.parametrize("G", [1, 4])
+def test_decode_with_lines(num_splits, G):
+    """Line tokens spread over the INT4 region (block edges, several splits),
+    in the sink and the window (ignored) and in messy lists."""
+    mxq = gpu_or_skip()
+    Hkv = 2
+    lens = [1000, 400, 64 + 128 + 40]
+    d = mxq_inputs.make_decode(dict(B=3, L=1024, Hq=Hkv * G, Hkv=Hkv, D=128, n_sink=64, n_recent=128, seed=31,
+                                    seq_len=lens), threads=3)
+    rng = np.random.default_rng(31)
+    lines = np.full((3, Hkv, 16), -1, dtype=np.int32)
+    for b in range(3):
+        for h in range(Hkv):
+            picks = np.sort(rng.choice(np.arange(64, lens[b] - 128), size=min(10, lens[b] - 192), replace=False))
+            row = list(picks) + [5, lens[b] - 3, 63, 64, 95, 96][: 16 - len(picks)]
+            lines[b, h, :len(row)] = row
+    lines[0, 0, :6] = [64, 95, 96, 127, 128, 200]  # block edges
+    lines[1, 1, :5] = [300, 300, 200, 310, -1]     # a repeat and an out-of-order entry
+    out = _run_lines(mxq, d, 64, 128, lines, num_splits)
+    cache = Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], 64, 128, lines=lines)
+    ref = Dm.attn_decode_ref(d["q"], cache, d["seq_len"], 64, 128)
+    err = np.abs(out - ref).max()
+    assert err <= TIGHT, err
+
+
+def test_decode_heavy_token_as_a_line():
+    """A planted heavy token: its 4-bit codes drag decode far from exact
+    attention; kept as a line, the GPU result is close to exact."""
+    mxq = gpu_or_skip()
+    from oracle import formats as F
+
+    d = mxq_inputs.make_decode(dict(B=1, L=2048, Hq=4, Hkv=1, D=128, n_sink=64, n_recent=128, seed=32,
+                                    seq_len=[2048]), threads=1)
+    q = F.bf16_bits_to_f32(d["q"])
+    k = F.bf16_bits_to_f32(d["k"]).copy()
+    u = q[0].mean(axis=0)
+    k[0, 0, 1000] = 3.0 * u / np.linalg.norm(u) * 11.3
+    k[0, 0, 1000, :8] += 37.0
+    d["k"] = F.f32_to_bf16_bits(k)
+    lines = np.array([[[1000] + [-1] * 15]], dtype=np.int32)
+    out = _run_lines(mxq, d, 64, 128, lines)
+    kf = F.bf16_bits_to_f32(d["k"]).astype(np.float64)[0, 0]
+    vf = F.bf16_bits_to_f32(d["v"]).astype(np.float64)[0, 0]
+    exact = []
+    for h in range(4):
+        s = kf @ q[0, h].astype(np.float64) / np.sqrt(128.0)
+        p = np.exp(s - s.max())
+        exact.append(p @ vf / p.sum())
+    exact = np.stack(exact)
+    plain, _ = _run(mxq, d, 64, 128)
+    e_line, e_plain = np.abs(out[0] - exact).max(), np.abs(plain[0] - exact).max()
+    assert e_line < 0.2 * e_plain, (e_line, e_plain)
