@@ -27,7 +27,7 @@ What it follows (the pages and the readings of them):
 Element formats follow the public OCP Microscaling (MX) v1.0 rules (E2M1 and
 E4M3 elements with an E8M0 shared exponent per 32 elements), which is what
 "MX-style" means.  Every point the pages leave open is settled by a numbered
-reading (R1-R33); the functions below state the reading they implement.
+reading (R1-R34); the functions below state the reading they implement.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against closed forms, brute force, exhaustive
@@ -45,6 +45,7 @@ from .formats import (  # noqa: F401
     e4m3_round_code,
     e4m3_value,
     quantize_mxfp4,
+    hadamard_rotate,
     dequantize_mxfp4,
     pack_nibbles,
     unpack_nibbles,

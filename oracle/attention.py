@@ -37,6 +37,7 @@ import numpy as np
 
 from .formats import (
     bf16_bits_to_f32,
+    hadamard_rotate,
     quantize_mxfp4,
     dequantize_mxfp4,
     quantize_mxfp8_keys,
@@ -69,13 +70,16 @@ def _zero_padding_rows(x: np.ndarray, n_valid: int) -> np.ndarray:
     return x
 
 
-def prepare_operands(q_bits, k_bits, v_bits, n_valid):
-    """Every operand form the attention needs, as float64 arrays (exact)."""
+def prepare_operands(q_bits, k_bits, v_bits, n_valid, rotate=False):
+    """Every operand form the attention needs, as float64 arrays (exact).
+    With ``rotate`` the MXFP4 operands are those of Q and K rotated by the
+    Walsh-Hadamard matrix (R34); FP16 tiles keep the unrotated bf16 values
+    (the rotation is orthonormal, so both estimate the same QK^T)."""
     qf = _zero_padding_rows(bf16_bits_to_f32(q_bits), n_valid)
     kf = _zero_padding_rows(bf16_bits_to_f32(k_bits), n_valid)
     vf = _zero_padding_rows(bf16_bits_to_f32(v_bits), n_valid)
-    qc, qs = quantize_mxfp4(qf)
-    kc, ks = quantize_mxfp4(kf)
+    qc, qs = quantize_mxfp4(hadamard_rotate(qf) if rotate else qf)
+    kc, ks = quantize_mxfp4(hadamard_rotate(kf) if rotate else kf)
     vc, vs = quantize_mxfp8_keys(vf)
     return dict(
         q=qf.astype(np.float64), k=kf.astype(np.float64),
@@ -102,7 +106,7 @@ def _exact_lowbit_scores(q_hat, k_hat, q_exp, k_exp):
 
 def attn_mixed_ref(q_bits, k_bits, v_bits, n_valid, Bq, Bk, causal, mask=None,
                    mode=MODE_MIXED, softmax_scale=None, heads=None, qtiles=None,
-                   ops=None, lines=None):
+                   ops=None, lines=None, rotate=False):
     """Reference mixed-precision attention.
 
     q_bits [B,Hq,N,D], k_bits/v_bits [B,Hkv,N,D] (bf16 bit patterns); mask u32
@@ -117,7 +121,7 @@ def attn_mixed_ref(q_bits, k_bits, v_bits, n_valid, Bq, Bk, causal, mask=None,
     n_qt, n_kt = N // Bq, N // Bk
     c = softmax_scale_log2(D, softmax_scale)
     if ops is None:
-        ops = prepare_operands(q_bits, k_bits, v_bits, n_valid)
+        ops = prepare_operands(q_bits, k_bits, v_bits, n_valid, rotate=rotate)
     out = np.full((B, Hq, N, D), np.nan, dtype=np.float32)
     lse = np.full((B, Hq, N), np.nan, dtype=np.float32)
     sets = tile_sets(n_valid, N, Bq, Bk, causal, 0, 0)

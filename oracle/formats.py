@@ -135,6 +135,31 @@ def quantize_mxfp4(x: np.ndarray):
     return codes, (e + 127).astype(np.uint8)
 
 
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """Data-free rotation of each row of float32 ``x[..., D]`` (D a power of
+    two) by the orthonormal Walsh-Hadamard matrix H/sqrt(D), Sylvester order
+    (reading R34): the fast transform in place, stages h = 1, 2, 4, ..., D/2,
+    each pair (j, j+h) in ascending j becoming (a+b, a-b), every sum rounded to
+    fp32; then one fp32 multiply by fl32(1/sqrt(D)).
+
+    The pages name rotation as the main alternative to promotion: it spreads
+    outlier channels over every element of a block before MXFP4.  Applied to
+    both Q and K it leaves QK^T unchanged in exact arithmetic."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    D = y.shape[-1]
+    assert D & (D - 1) == 0
+    h = 1
+    while h < D:
+        yb = y.reshape(y.shape[:-1] + (D // (2 * h), 2, h))
+        a = yb[..., 0, :].copy()
+        b = yb[..., 1, :].copy()
+        yb[..., 0, :] = (a + b).astype(np.float32)
+        yb[..., 1, :] = (a - b).astype(np.float32)
+        y = yb.reshape(y.shape)
+        h *= 2
+    return (y * np.float32(1.0 / np.sqrt(D))).astype(np.float32)
+
+
 def dequantize_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """E2M1(code) * 2**(scale-127), float64 (exact)."""
     codes = np.asarray(codes)
