@@ -190,9 +190,11 @@ def quality_sweep(args, dev):
     to all FP16: the error of attn_mixed_fwd (fp32 output) against exact
     softmax attention computed in float64 by torch on sampled query rows, the
     kernel time, and the share of the all-low-bit-to-all-FP16 error gap each
-    fraction recovers, (e_lowbit - e) / (e_lowbit - e_fp16).  The pages report
-    this quantity on real models and benchmarks; here it is measured on
-    seeded synthetic inputs only."""
+    fraction recovers, (e_lowbit - e) / (e_lowbit - e_fp16).  Two more rows
+    put the pages' alternative beside promotion: Q and K rotated by the
+    Walsh-Hadamard matrix before MXFP4, all low-bit and with 5% promoted.  The
+    pages report this quantity on real models and benchmarks; here it is
+    measured on seeded synthetic inputs only."""
     import numpy as np
     import torch
 
@@ -201,7 +203,8 @@ def quality_sweep(args, dev):
 
     sizes = [int(x) for x in args.quality_n.split(",")]
     recipes = {"outliers+sink": {}, "sink": dict(outliers=False), "plain": dict(outliers=False, sink=None)}
-    fracs = [("lowbit", None), ("forced", 0), ("1%", 1), ("2%", 2), ("5%", 5), ("10%", 10), ("20%", 20), ("fp16", None)]
+    fracs = [("lowbit", None), ("forced", 0), ("1%", 1), ("2%", 2), ("5%", 5), ("10%", 10), ("20%", 20), ("fp16", None),
+             ("lowbit+rot", None), ("5%+rot", 5)]
     rows_per_head = 16
     results = []
     for recipe, N in [(r, n) for r in recipes for n in sizes]:
@@ -224,12 +227,16 @@ def quality_sweep(args, dev):
             exact.append(torch.softmax(sc, dim=-1) @ vd)
         exact = torch.stack(exact)  # [Hq, rows, D]
         ops_mixed = mxq.prepare_prefill(q, k, v, N, mode=mxq.MXQ_MIXED)
+        ops_rot = mxq.prepare_prefill(q, k, v, N, mode=mxq.MXQ_MIXED, rotate=True)
         ws = mxq.select_workspace(shape, dev)
         errs = {}
         for label, pct in fracs:
-            mode = mxq.MXQ_ALL_LOWBIT if label == "lowbit" else mxq.MXQ_ALL_FP16 if label == "fp16" else mxq.MXQ_MIXED
+            base_label = label.replace("+rot", "")
+            ops_use = ops_rot if label.endswith("+rot") else ops_mixed
+            mode = (mxq.MXQ_ALL_LOWBIT if base_label == "lowbit" else mxq.MXQ_ALL_FP16 if base_label == "fp16"
+                    else mxq.MXQ_MIXED)
             mask = None
-            fp16_frac = 0.0 if label == "lowbit" else 1.0
+            fp16_frac = 0.0 if base_label == "lowbit" else 1.0
             if mode == mxq.MXQ_MIXED:
                 mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(pct, 100),
                                                     sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
@@ -237,7 +244,7 @@ def quality_sweep(args, dev):
                 total, fp16 = pair_counts(cfg, mask.cpu().numpy().view(np.uint32))
                 fp16_frac = fp16 / total
             out = torch.empty((B, Hq, N, D), dtype=torch.float32, device=dev)
-            call = lambda: mxq.attn_mixed_fwd(ops_mixed, mask, shape, mode=mode, out_dtype=mxq.MXQ_OUT_F32,
+            call = lambda: mxq.attn_mixed_fwd(ops_use, mask, shape, mode=mode, out_dtype=mxq.MXQ_OUT_F32,
                                               out=out, want_lse=False)
             for _ in range(5):
                 call()
@@ -262,7 +269,7 @@ def quality_sweep(args, dev):
         for r in results:
             if r["N"] == N and r["recipe"] == recipe:
                 r["gap_recovered"] = round((errs["lowbit"] - r["rel_l2"]) / gap, 4) if gap > 0 else None
-        del q, k, v, ops_mixed, out
+        del q, k, v, ops_mixed, ops_rot, out
         torch.cuda.empty_cache()
     print(json.dumps({"quality_sweep": results, "rows_sampled_per_head": rows_per_head,
                       "reference": "float64 softmax attention (torch) on the sampled rows",

@@ -26,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmxq.so")
 
 MXQ_OK, MXQ_EINVAL, MXQ_EUNSUPPORTED, MXQ_EHIP = 0, 1, 2, 3
-MXQ_MXFP4_E2M1, MXQ_MXFP8_E4M3, MXQ_INT4_ASYM_G32, MXQ_FP16 = 1, 2, 3, 4
+MXQ_MXFP4_E2M1, MXQ_MXFP8_E4M3, MXQ_INT4_ASYM_G32, MXQ_FP16, MXQ_MXFP4_E2M1_HADAMARD = 1, 2, 3, 4, 5
 MXQ_AXIS_D, MXQ_AXIS_N = 0, 1
 MXQ_MIXED, MXQ_ALL_LOWBIT, MXQ_ALL_FP16 = 0, 1, 2
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
@@ -153,7 +153,7 @@ def mxq_quantize(x: torch.Tensor, fmt: int, axis: int, n_valid: int | None = Non
     nv = N if n_valid is None else int(n_valid)
     dev = x.device
     zeros = None
-    if fmt == MXQ_MXFP4_E2M1:
+    if fmt in (MXQ_MXFP4_E2M1, MXQ_MXFP4_E2M1_HADAMARD):
         codes = torch.empty((B, H, N, D // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((B, H, N, D // 32), dtype=torch.uint8, device=dev)
     elif fmt == MXQ_MXFP8_E4M3:
@@ -249,14 +249,15 @@ class PrefillOperands:
     v_f16t: torch.Tensor | None = None
 
 
-def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False) -> PrefillOperands:
-    """Quantise Q/K (MXFP4), V (MXFP8 along keys) and make the fp16 V^T copy
-    (needed by FP16 tiles and by vertical lines), all on the GPU through
-    mxq_quantize."""
+def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False, rotate=False) -> PrefillOperands:
+    """Quantise Q/K (MXFP4, optionally of the Walsh-Hadamard-rotated rows),
+    V (MXFP8 along keys) and make the fp16 V^T copy (needed by FP16 tiles and
+    by vertical lines), all on the GPU through mxq_quantize."""
     ops = PrefillOperands(q_bf16=q, k_bf16=k)
     if mode != MXQ_ALL_FP16:
-        ops.q_codes, ops.q_scales, _ = mxq_quantize(q, MXQ_MXFP4_E2M1, MXQ_AXIS_D, n_valid)
-        ops.k_codes, ops.k_scales, _ = mxq_quantize(k, MXQ_MXFP4_E2M1, MXQ_AXIS_D, n_valid)
+        f4 = MXQ_MXFP4_E2M1_HADAMARD if rotate else MXQ_MXFP4_E2M1
+        ops.q_codes, ops.q_scales, _ = mxq_quantize(q, f4, MXQ_AXIS_D, n_valid)
+        ops.k_codes, ops.k_scales, _ = mxq_quantize(k, f4, MXQ_AXIS_D, n_valid)
         ops.v_codes, ops.v_scales, _ = mxq_quantize(v, MXQ_MXFP8_E4M3, MXQ_AXIS_N, n_valid)
     if mode != MXQ_ALL_LOWBIT or lines:
         ops.v_f16t, _, _ = mxq_quantize(v, MXQ_FP16, MXQ_AXIS_N, n_valid)

@@ -58,6 +58,87 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4_d(const uint16_t* __restric
   scales[blk] = static_cast<uint8_t>(e + 127);
 }
 
+// ---- MXFP4 of Walsh-Hadamard-rotated rows (reading R34) ---------------------
+// x [rows][D] bf16 -> MXFP4 codes and scales of each row times H/sqrt(D).
+// D/8 consecutive lanes hold a row, 8 contiguous elements each (one 16-byte
+// load per lane).  Butterfly stages h = 1, 2, 4 run inside a lane; stages
+// h = 8 ... D/2 pair lane u with lane u ^ (h/8): the lane holding the lower
+// index keeps a + b, the other a - b, every sum rounded to fp32 (the same
+// values the in-place transform produces, whatever the order of the pairs).
+// Then one multiply by fl32(1/sqrt(D)), and each 32-element block (4 lanes)
+// is quantised as in k_quant_mxfp4_d.
+template <int D>
+__global__ void __launch_bounds__(256) k_quant_mxfp4_had(const uint16_t* __restrict__ x,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales, int64_t rows,
+                                                         int64_t N, int64_t n_valid) {
+  constexpr int LPR = D / 8;  // lanes per row
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "power-of-two head_dim");
+  // fl32(1/sqrt(D)), the double quotient rounded once to fp32
+  constexpr float kInv = D == 32 ? 0x1.6a09e6p-3f : D == 64 ? 0.125f : D == 128 ? 0x1.6a09e6p-4f : 0.0625f;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int u = static_cast<int>(gid % LPR);
+  const bool in = row < rows;
+  const bool live = in && (row % N) < n_valid;
+  const uint4 w4 = live ? *reinterpret_cast<const uint4*>(x + row * D + 8 * u) : make_uint4(0, 0, 0, 0);
+  const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (!(i & h)) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __shfl_xor(v[i], m);
+      v[i] = (u & m) ? (p - v[i]) : (v[i] + p);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = v[i] * kInv;
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = shared_exponent(amax, 2);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float s = __builtin_ldexpf(v[i], -e);
+    const uint32_t c = e2m1_mag_code(fabsf(s)) | ((__float_as_uint(v[i]) >> 28) & 8u);
+    packed |= c << (4 * i);
+  }
+  if (in) {
+    reinterpret_cast<uint32_t*>(codes)[row * (D / 8) + u] = packed;
+    if ((u & 3) == 0) scales[row * (D / 32) + u / 4] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+template <int D>
+mxq_status launch_had(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t rows, int64_t N,
+                      int64_t n_valid, hipStream_t st) {
+  const int64_t lanes = rows * (D / 8);
+  hipLaunchKernelGGL((k_quant_mxfp4_had<D>), dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0, st,
+                     x, codes, scales, rows, N, n_valid);
+  return check_launch("k_quant_mxfp4_had");
+}
+
 // ---- MXFP8 along N (V): x [BH][N][D] -> codes [BH][D][N], scales [BH][D][N/32]
 // One thread per (bh, 32-row block, d).  Lanes run over d, so each of the 32
 // column loads is a contiguous 128-byte read across the wave.
@@ -290,6 +371,21 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), nb, D / 32, N,
                        n_valid);
     return check_launch("k_quant_mxfp4_d");
+  }
+  if (fmt == MXQ_MXFP4_E2M1_HADAMARD) {
+    MXQ_REQUIRE(axis == MXQ_AXIS_D, MXQ_EUNSUPPORTED, "mxq_quantize MXFP4_HADAMARD: AXIS_D only");
+    MXQ_REQUIRE(scales != nullptr && zeros == nullptr, MXQ_EINVAL,
+                "mxq_quantize MXFP4_HADAMARD: scales required, zeros must be NULL");
+    MXQ_REQUIRE(rows * (D / 8) <= (int64_t{1} << 40), MXQ_EUNSUPPORTED, "mxq_quantize: tensor too large");
+    uint8_t* c8 = static_cast<uint8_t*>(codes);
+    uint8_t* s8 = static_cast<uint8_t*>(scales);
+    switch (D) {
+      case 32: return launch_had<32>(x, c8, s8, rows, N, n_valid, st);
+      case 64: return launch_had<64>(x, c8, s8, rows, N, n_valid, st);
+      case 128: return launch_had<128>(x, c8, s8, rows, N, n_valid, st);
+      case 256: return launch_had<256>(x, c8, s8, rows, N, n_valid, st);
+      default: return fail(MXQ_EUNSUPPORTED, "mxq_quantize MXFP4_HADAMARD: D must be 32, 64, 128 or 256");
+    }
   }
   if (fmt == MXQ_MXFP8_E4M3 && axis == MXQ_AXIS_N) {
     MXQ_REQUIRE(scales != nullptr && zeros == nullptr, MXQ_EINVAL,

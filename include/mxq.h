@@ -55,7 +55,8 @@ typedef enum {
   MXQ_MXFP4_E2M1 = 1,   /* E2M1 codes + one E8M0 scale per 32 elements      */
   MXQ_MXFP8_E4M3 = 2,   /* E4M3 codes + one E8M0 scale per 32 elements      */
   MXQ_INT4_ASYM_G32 = 3,/* 4-bit codes + fp16 scale and zero per 32 elements */
-  MXQ_FP16 = 4          /* plain fp16 copy                                  */
+  MXQ_FP16 = 4,         /* plain fp16 copy                                  */
+  MXQ_MXFP4_E2M1_HADAMARD = 5 /* MXFP4 of each row rotated by H/sqrt(D)     */
 } mxq_format;
 
 typedef enum {
@@ -98,6 +99,13 @@ typedef struct {
  *  MXFP8_E4M3, AXIS_N: codes u8 [B][H][D][N], scales u8 [B][H][D][N/32]
  *     (blocks of 32 consecutive rows n per column d).  e = floor(log2 amax)-8,
  *     code = OCP E4M3 round-half-even of x*2^-e, saturating at 448.
+ *  MXFP4_E2M1_HADAMARD, AXIS_D: as MXFP4 above, of each row times the
+ *     orthonormal Walsh-Hadamard matrix H/sqrt(D), Sylvester order (reading
+ *     R34: the fast transform with stages h = 1, 2, ..., D/2, each pair
+ *     (j, j+h) becoming (a+b, a-b) rounded to fp32, then one fp32 multiply by
+ *     fl32(1/sqrt(D))).  The rotation the pages name as the alternative to
+ *     promotion: applied to Q and K it keeps QK^T and spreads outlier
+ *     channels over each block.  D in {32, 64, 128, 256}.
  *  FP16, AXIS_D: codes u16 [B][H][N][D];  FP16, AXIS_N: codes u16 [B][H][D][N].
  *  INT4_ASYM_G32, AXIS_D: codes u8 [B][H][N][D/2]; scales (fp16) and zeros
  *     (fp16) [B][H][N][D/32]:  s = fp16(fl32(max-min)/15), z = fp16(min),

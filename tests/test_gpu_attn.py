@@ -158,3 +158,23 @@ def test_error_paths():
     with pytest.raises(mxq.MxqError) as ei:
         mxq.attn_mixed_fwd(ops, torch.zeros(1, dtype=torch.int32, device="cuda:0"), bad)
     assert ei.value.status == mxq.MXQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_rotated_lowbit_operands(mode):
+    """Q/K rotated by the Walsh-Hadamard matrix before MXFP4 (the pages'
+    alternative to promotion), on the outlier recipe, against the oracle."""
+    mxq = gpu_or_skip()
+    import torch
+
+    cfg = mxq_inputs.make_prefill("llama8b", N=1024, n_valid=1000, Hq=4, Hkv=1, B=1)
+    q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    shape = _shape(mxq, cfg)
+    ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], mode, rotate=True)
+    mask = None
+    if mode == 0:
+        mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(5, 100), sink_tiles=1, local_tiles=1)
+    out, lse = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode)
+    ro, rl = A.attn_mixed_ref(cfg["q"], cfg["k"], cfg["v"], cfg["n_valid"], 128, 64, True,
+                              mask=u32(mask) if mask is not None else None, mode=mode, rotate=True)
+    _check(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)

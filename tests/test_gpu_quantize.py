@@ -121,3 +121,17 @@ def test_error_paths_return_status():
     with pytest.raises(mxq.MxqError) as ei:
         mxq.mxq_quantize(y, mxq.MXQ_MXFP4_E2M1, mxq.MXQ_AXIS_N)
     assert ei.value.status == mxq.MXQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 256, 128, 256), (2, 3, 384, 64, 301), (1, 1, 128, 32, 77),
+                                   (1, 2, 128, 256, 128)])
+def test_mxfp4_hadamard_bit_exact(shape):
+    """MXFP4 of Walsh-Hadamard-rotated rows (with special values mixed in)."""
+    mxq = gpu_or_skip()
+    B, H, N, D, nv = shape
+    bits = random_bf16((B, H, N, D), seed=5 * N + D, scale=3.0)
+    bits[..., 3] = F.f32_to_bf16_bits(np.float32(40.0))  # an outlier channel
+    codes, scales, _ = mxq.mxq_quantize(bf16_dev(bits), mxq.MXQ_MXFP4_E2M1_HADAMARD, mxq.MXQ_AXIS_D, nv)
+    rc, rs = F.quantize_mxfp4(F.hadamard_rotate(_zero_pad(F.bf16_bits_to_f32(bits), nv)))
+    assert np.array_equal(u8(codes), F.pack_nibbles(rc))
+    assert np.array_equal(u8(scales), rs)
