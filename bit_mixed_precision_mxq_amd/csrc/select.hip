@@ -26,7 +26,7 @@ namespace {
 constexpr int kMaxKeyTiles = 2048;
 
 // mean of rows [tile*T, tile*T + T) of x (capped at n_valid), column d.  The
-// row loads are issued 16 at a time; the sum is taken in ascending row order.
+// row loads are issued 64 at a time; the sum is taken in ascending row order.
 // transposed == 0 writes mean[(bh*n_tiles + tile)*D + d], else
 // mean[(bh*D + d)*n_tiles + tile] (so that a thread per key tile reads a
 // column of means with consecutive threads at consecutive addresses).
@@ -41,12 +41,13 @@ __global__ void __launch_bounds__(128) k_tile_means(const uint16_t* __restrict__
   const int rows = max(0, min(T, n_valid - tile * T));
   float acc = 0.0f;
   int r = 0;
-  for (; r + 16 <= rows; r += 16) {
-    uint16_t v[16];
+  for (; r + 64 <= rows; r += 64) {
+    uint16_t v[64];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = base[static_cast<int64_t>(r + u) * D];
+    for (int u = 0; u < 64; ++u) v[u] = base[static_cast<int64_t>(r + u) * D];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc = acc + bf16_to_f32(v[u]);
+    for (int u = 0; u < 64; ++u) acc = acc + bf16_to_f32(v[u]);
+    __builtin_amdgcn_sched_barrier(0);  // 64 loads in flight at a time
   }
   for (; r < rows; ++r) acc = acc + bf16_to_f32(base[static_cast<int64_t>(r) * D]);
   const float m = rows > 0 ? acc / static_cast<float>(rows) : 0.0f;  // correctly rounded division
@@ -64,8 +65,12 @@ struct SelectArgs {
   int topk, ratio_num, ratio_den, sink_tiles, local_tiles;
 };
 
+// D: head_dim (64 or 128), a compile-time constant so that each score's column
+// loads go out 64 at a time before their products (one memory round trip per
+// 64 instead of per 16); the sum still runs over d in order.
+template <int D>
 __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
-  __shared__ float s_score[kMaxKeyTiles];
+  __shared__ __attribute__((aligned(16))) float s_score[kMaxKeyTiles];
   __shared__ float s_q[256];
   __shared__ uint32_t s_mask[kMaxKeyTiles / 32];
   __shared__ int s_count;
@@ -81,12 +86,28 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
   if (tid == 0) s_count = 0;
   __syncthreads();
 
+  // kmean[bhk] as a buffer (base and size through readfirstlane, so the
+  // resource sits in scalar registers)
+  const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
+  const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
+  const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
+  const auto r_km = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
+      __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
   // scores of every key tile (also invalid ones, for inspection)
   for (int j = tid; j < a.n_kt; j += blockDim.x) {
-    const float* km = a.kmean + bhk * a.D * a.n_kt + j;
     float acc = 0.0f;
-#pragma unroll 16
-    for (int d = 0; d < a.D; ++d) acc = acc + s_q[d] * km[static_cast<int64_t>(d) * a.n_kt];  // two roundings: contraction is off here
+    constexpr int C = 64;  // loads in flight per round trip
+#pragma unroll
+    for (int d0 = 0; d0 < D; d0 += C) {
+      float kv[C];
+#pragma unroll
+      for (int d = 0; d < C; ++d)  // column j of row d0 + d: lane offset plus a scalar row offset
+        kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
+#pragma unroll
+      for (int d = 0; d < C; ++d) acc = acc + s_q[d0 + d] * kv[d];  // two roundings: contraction is off here
+      __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
+    }
     s_score[j] = acc;
     if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
   }
@@ -111,15 +132,29 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
     if (a.topk >= 0) k = a.topk;
     else k = (static_cast<int64_t>(a.ratio_num) * nvt + a.ratio_den - 1) / a.ratio_den;
     if (k > n_cand) k = n_cand;
+    // forced and invalid tiles (up to a multiple of 4) become -inf: they then
+    // never outrank a candidate, whose score is finite, and the count below
+    // needs no per-tile test
+    const int nvt4 = (nvt + 3) & ~3;
+    for (int j = tid; j < nvt4; j += blockDim.x)
+      if (j >= nvt || forced(j)) s_score[j] = -__builtin_inff();
+    __syncthreads();
+    const float4* s4 = reinterpret_cast<const float4*>(s_score);
     for (int j = tid; j < nvt; j += blockDim.x) {
       bool take = forced(j);
       if (!take && k > 0) {
+        // rank of candidate j: candidates with a higher score, or the same
+        // score and a lower index (the same tile never counts itself)
         const float sj = s_score[j];
         int rank = 0;
-        for (int jj = 0; jj < nvt; ++jj) {
-          if (jj == j || forced(jj)) continue;
-          const float so = s_score[jj];
-          rank += (so > sj || (so == sj && jj < j)) ? 1 : 0;
+        for (int q4 = 0; q4 < nvt4 / 4; ++q4) {
+          const float4 o = s4[q4];
+          const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int jj = 4 * q4 + c;
+            rank += (ov[c] > sj || (ov[c] == sj && jj < j)) ? 1 : 0;
+          }
         }
         take = rank < k;
       }
@@ -336,7 +371,8 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
   a.Bk = s->Bk; a.causal = s->causal; a.n_qt = n_qt; a.n_kt = n_kt; a.words = (n_kt + 31) / 32;
   a.topk = p->topk; a.ratio_num = p->ratio_num; a.ratio_den = p->ratio_den;
   a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
-  hipLaunchKernelGGL(k_select, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
+  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
+  else hipLaunchKernelGGL(k_select<64>, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
   return check_launch("k_select");
 }
 
