@@ -3,7 +3,8 @@
 One step = the whole prefill path on one batch: MXFP4 quantisation of Q and K,
 MXFP8 quantisation of V (blocks along keys) and its fp16 copy, block selection
 (5% of tiles plus the sink column and local window), and the fused
-mixed-precision attention pass.  Inputs are bf16 tensors already resident in
+mixed-precision attention pass.  Selection runs on a second stream beside the
+quantisers (PrefillPipeline).  Inputs are bf16 tensors already resident in
 HBM when the timed region starts.
 
 The JSON line reports effective attention TFLOP/s (4*D per valid query-key
@@ -130,28 +131,18 @@ def bench_prefill(args, dev):
     q, k, v = _bf16(cfg["q"], dev), _bf16(cfg["k"], dev), _bf16(cfg["v"], dev)
     shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
                       cfg["causal"])
-    ws = mxq.select_workspace(shape, dev)
     n_lines = cfg.get("n_lines", 0)
-    lws = mxq.lines_workspace(shape, dev) if n_lines else None
-    out = torch.empty((cfg["B"], cfg["Hq"], cfg["N"], cfg["D"]), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((cfg["B"], cfg["Hq"], cfg["N"]), dtype=torch.float32, device=dev)
+    # the step's DAG: selection on a second stream beside the quantisers,
+    # attention after both (PrefillPipeline)
+    pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                               sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"], n_lines=n_lines,
+                               sink_tokens=cfg.get("sink_tokens", 0), out_dtype=mxq.MXQ_OUT_BF16, device=dev)
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
     def step(i=None):
-        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], lines=bool(n_lines))
-        mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
-                                            sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
-                                            workspace=ws)
-        lines = None
-        if n_lines:
-            lines, _ = mxq.attn_select_lines(q, k, shape, n_lines, cfg["sink_tokens"], workspace=lws)
-        if i is not None:
-            ev_a0[i].record()
-        mxq.attn_mixed_fwd(ops, mask, shape, out_dtype=mxq.MXQ_OUT_BF16, out=out, lse=lse, lines=lines)
-        if i is not None:
-            ev_a1[i].record()
-        return mask, lines
+        pipe(q, k, v, events=None if i is None else (ev_a0[i], ev_a1[i]))
+        return pipe.mask, pipe.lines
 
     for _ in range(args.warmup):
         mask, lines = step()

@@ -197,14 +197,18 @@ def select_workspace(shape: Shape, device) -> torch.Tensor:
 
 
 def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0,
-                       want_scores=False, workspace=None):
-    """Returns (mask u32-as-int32 [B,Hq,n_qt,words], n_fp16 [B,Hq,n_qt], scores or None)."""
+                       want_scores=False, workspace=None, mask=None, n_fp16=None):
+    """Returns (mask u32-as-int32 [B,Hq,n_qt,words], n_fp16 [B,Hq,n_qt], scores or None);
+    mask and n_fp16 may be passed in to be reused."""
     _need_gpu(q, k)
     n_qt, n_kt = shape.N // shape.Bq, shape.N // shape.Bk
     words = (n_kt + 31) // 32
     dev = q.device
-    mask = torch.empty((shape.B, shape.Hq, n_qt, words), dtype=torch.int32, device=dev)
-    nfp = torch.empty((shape.B, shape.Hq, n_qt), dtype=torch.int32, device=dev)
+    if mask is None:
+        mask = torch.empty((shape.B, shape.Hq, n_qt, words), dtype=torch.int32, device=dev)
+    nfp = n_fp16 if n_fp16 is not None else torch.empty((shape.B, shape.Hq, n_qt), dtype=torch.int32, device=dev)
+    _need_gpu(mask, nfp)
+    assert mask.numel() == shape.B * shape.Hq * n_qt * words and nfp.numel() == shape.B * shape.Hq * n_qt
     scores = torch.empty((shape.B, shape.Hq, n_qt, n_kt), dtype=torch.float32, device=dev) if want_scores else None
     ws = workspace if workspace is not None else select_workspace(shape, dev)
     sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles))
@@ -220,12 +224,16 @@ def lines_workspace(shape: Shape, device) -> torch.Tensor:
 
 
 def attn_select_lines(q, k, shape: Shape, n_lines, sink_tokens=1, group_shared=False, want_scores=False,
-                      workspace=None):
+                      workspace=None, lines=None):
     """Vertical-line keys per query head.  Returns (lines int32 [B,Hq,n_lines]
-    ascending and -1 padded, scores f32 [B,Hq,N] or None)."""
+    ascending and -1 padded, scores f32 [B,Hq,N] or None); lines may be passed
+    in to be reused."""
     _need_gpu(q, k)
     dev = q.device
-    lines = torch.empty((shape.B, shape.Hq, n_lines), dtype=torch.int32, device=dev)
+    if lines is None:
+        lines = torch.empty((shape.B, shape.Hq, n_lines), dtype=torch.int32, device=dev)
+    _need_gpu(lines)
+    assert lines.dtype == torch.int32 and lines.numel() == shape.B * shape.Hq * n_lines
     scores = torch.empty((shape.B, shape.Hq, shape.N), dtype=torch.float32, device=dev) if want_scores else None
     ws = workspace if workspace is not None else lines_workspace(shape, dev)
     lp = LineParams(int(n_lines), int(sink_tokens), int(bool(group_shared)))
@@ -282,6 +290,55 @@ def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, 
         _ptr(ops.v_scales), _ptr(ops.q_bf16), _ptr(ops.k_bf16), _ptr(ops.v_f16t), _ptr(mask),
         _ptr(lines), 0 if lines is None else int(lines.shape[-1]), ctypes.byref(cs), float(softmax_scale), int(mode), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
     return out, lse
+
+
+class PrefillPipeline:
+    """One prefill step as a small DAG on two HIP streams (default priority).
+    Tile selection (and line selection) reads only bf16 Q and K and is bound
+    by latency, the quantisers are bound by HBM bandwidth: selection runs on
+    a second stream while Q, K and V are quantised on the caller's stream, and
+    the attention waits for both.  Workspaces and outputs are allocated once."""
+
+    def __init__(self, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0, n_lines=0,
+                 sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0"):
+        self.shape, self.topk, self.ratio = shape, topk, ratio
+        self.sink_tiles, self.local_tiles = sink_tiles, local_tiles
+        self.n_lines, self.sink_tokens, self.rotate, self.out_dtype = n_lines, sink_tokens, rotate, out_dtype
+        dev = torch.device(device)
+        n_qt, n_kt = shape.N // shape.Bq, shape.N // shape.Bk
+        self.ws = select_workspace(shape, dev)
+        self.mask = torch.empty((shape.B, shape.Hq, n_qt, (n_kt + 31) // 32), dtype=torch.int32, device=dev)
+        self.nfp = torch.empty((shape.B, shape.Hq, n_qt), dtype=torch.int32, device=dev)
+        self.lws = lines_workspace(shape, dev) if n_lines else None
+        self.lines = torch.empty((shape.B, shape.Hq, n_lines), dtype=torch.int32, device=dev) if n_lines else None
+        odt = torch.float32 if out_dtype == MXQ_OUT_F32 else torch.bfloat16
+        self.out = torch.empty((shape.B, shape.Hq, shape.N, shape.D), dtype=odt, device=dev)
+        self.lse = torch.empty((shape.B, shape.Hq, shape.N), dtype=torch.float32, device=dev)
+        self.aux = torch.cuda.Stream(device=dev)
+        self.ev_in, self.ev_sel = torch.cuda.Event(), torch.cuda.Event()
+
+    def __call__(self, q, k, v, events=None):
+        """Returns (out, lse).  events=(e0, e1) are recorded around the
+        attention kernel on the caller's stream."""
+        main = torch.cuda.current_stream()
+        self.ev_in.record(main)
+        with torch.cuda.stream(self.aux):
+            self.aux.wait_event(self.ev_in)
+            attn_select_blocks(q, k, self.shape, topk=self.topk, ratio=self.ratio, sink_tiles=self.sink_tiles,
+                               local_tiles=self.local_tiles, workspace=self.ws, mask=self.mask, n_fp16=self.nfp)
+            if self.n_lines:
+                attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
+                                  lines=self.lines)
+            self.ev_sel.record(self.aux)
+        ops = prepare_prefill(q, k, v, self.shape.n_valid, lines=bool(self.n_lines), rotate=self.rotate)
+        main.wait_event(self.ev_sel)
+        if events is not None:
+            events[0].record(main)
+        attn_mixed_fwd(ops, self.mask, self.shape, out_dtype=self.out_dtype, out=self.out, lse=self.lse,
+                       lines=self.lines)
+        if events is not None:
+            events[1].record(main)
+        return self.out, self.lse
 
 
 # ------------------------------------------------------------------ decode

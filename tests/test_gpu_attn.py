@@ -178,3 +178,27 @@ def test_rotated_lowbit_operands(mode):
     ro, rl = A.attn_mixed_ref(cfg["q"], cfg["k"], cfg["v"], cfg["n_valid"], 128, 64, True,
                               mask=u32(mask) if mask is not None else None, mode=mode, rotate=True)
     _check(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+
+
+def test_prefill_pipeline_matches_the_sequential_calls():
+    """PrefillPipeline (selection on a second stream) gives bit-identical
+    results to the calls made one after another, over repeated steps."""
+    mxq = gpu_or_skip()
+    import torch
+
+    for name, over in (("llama8b", dict(N=2048, n_valid=2000, Hq=8, Hkv=2)), ("vit", dict(B=4))):
+        cfg = mxq_inputs.make_prefill(name, **over)
+        q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+        shape = _shape(mxq, cfg)
+        pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                                   sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
+                                   n_lines=cfg["n_lines"], sink_tokens=cfg["sink_tokens"], out_dtype=mxq.MXQ_OUT_F32)
+        mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                                            sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"])
+        lines = mxq.attn_select_lines(q, k, shape, cfg["n_lines"], cfg["sink_tokens"])[0] if cfg["n_lines"] else None
+        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], lines=lines is not None)
+        ref, ref_lse = mxq.attn_mixed_fwd(ops, mask, shape, lines=lines)
+        for _ in range(3):
+            out, lse = pipe(q, k, v)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref) and torch.equal(lse, ref_lse), name
