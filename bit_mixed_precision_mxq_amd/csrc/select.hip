@@ -6,7 +6,7 @@
 //  k_tile_means : fp32 mean of every query tile (per query head) and key tile
 //                 (per kv head); one thread per (tile, d), rows summed in
 //                 ascending order, then one correctly rounded division.
-//  k_select     : one workgroup per (b, query head, query tile): scores of all
+//  k_select     : one wave per (b, query head, query tile): scores of all
 //                 key tiles against the tile mean (sequential over d, rounded
 //                 product then rounded sum, never fused), forced tiles, and the
 //                 top-k by rank counting with ties to the lower index.
@@ -63,31 +63,37 @@ struct SelectArgs {
   float* scores;       // [B*Hq][n_qt][n_kt] or null
   int Hq, Hkv, N, n_valid, D, Bq, Bk, causal, n_qt, n_kt, words;
   int topk, ratio_num, ratio_den, sink_tiles, local_tiles;
+  int B;
 };
 
-// D: head_dim (64 or 128), a compile-time constant so that each score's column
-// loads go out 64 at a time before their products (one memory round trip per
-// 64 instead of per 16); the sum still runs over d in order.
+// One wave per (batch, query head, query tile), four per workgroup, with no
+// workgroup barrier: the wave keeps its tile mean and scores in its own slice
+// of LDS.  D (64 or 128) is a compile-time constant so that a score's column
+// loads go out 64 at a time before their products; the sum still runs over d
+// in order.  Candidates are ranked by counting, against a score row in which
+// forced and invalid tiles are -inf; each group of 64 tiles' verdicts becomes
+// two mask words by one ballot.
+constexpr int kSelWaves = 4;
+
 template <int D>
-__global__ void __launch_bounds__(256) k_select(SelectArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_score[kMaxKeyTiles];
-  __shared__ float s_q[256];
-  __shared__ uint32_t s_mask[kMaxKeyTiles / 32];
-  __shared__ int s_count;
-  const int i = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
-  const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + h / (a.Hq / a.Hkv);
-  const int tid = threadIdx.x;
+__global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_score[kSelWaves][kMaxKeyTiles];
+  __shared__ float s_q[kSelWaves][D];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kSelWaves + wave;
+  if (item >= static_cast<int64_t>(a.n_qt) * a.Hq * a.B) return;  // the whole wave
+  const int i = static_cast<int>(item % a.n_qt);
+  const int64_t bhq = item / a.n_qt;  // b * Hq + h
+  const int h = static_cast<int>(bhq % a.Hq);
+  const int64_t bhk = (bhq / a.Hq) * a.Hkv + h / (a.Hq / a.Hkv);
+  float* sc = s_score[wave];
+  float* sq = s_q[wave];
 
-  for (int d = tid; d < a.D; d += blockDim.x) s_q[d] = a.qmean[(bhq * a.n_qt + i) * a.D + d];
-  for (int w = tid; w < a.words; w += blockDim.x) s_mask[w] = 0u;
-  if (tid == 0) s_count = 0;
-  __syncthreads();
+  for (int d = lane; d < D; d += 64) sq[d] = a.qmean[(bhq * a.n_qt + i) * D + d];
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, read by every lane
 
-  // kmean[bhk] as a buffer (base and size through readfirstlane, so the
-  // resource sits in scalar registers)
+  // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
   const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
   const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
   const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
@@ -95,25 +101,27 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
       reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
       __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
   // scores of every key tile (also invalid ones, for inspection)
-  for (int j = tid; j < a.n_kt; j += blockDim.x) {
+  for (int j = lane; j < a.n_kt; j += 64) {
     float acc = 0.0f;
     constexpr int C = 64;  // loads in flight per round trip
 #pragma unroll
     for (int d0 = 0; d0 < D; d0 += C) {
       float kv[C];
 #pragma unroll
-      for (int d = 0; d < C; ++d)  // column j of row d0 + d: lane offset plus a scalar row offset
+      for (int d = 0; d < C; ++d)
         kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
 #pragma unroll
-      for (int d = 0; d < C; ++d) acc = acc + s_q[d0 + d] * kv[d];  // two roundings: contraction is off here
+      for (int d = 0; d < C; ++d) acc = acc + sq[d0 + d] * kv[d];  // two roundings: contraction is off here
       __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
     }
-    s_score[j] = acc;
+    sc[j] = acc;
     if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
   }
-  __syncthreads();
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
+  uint32_t* mrow = a.mask + (bhq * a.n_qt + i) * a.words;
   const int qs = i * a.Bq;
+  int count = 0;
   if (qs < a.n_valid) {
     const int qe = min(qs + a.Bq, a.n_valid) - 1;
     int last = (a.n_valid - 1) / a.Bk;
@@ -125,27 +133,32 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
       bool local = a.local_tiles >= 1 && (j + 1) * a.Bk - 1 >= lo && j * a.Bk <= qe;
       return sink || local;
     };
-    int n_forced = 0;
-    for (int j = 0; j < nvt; ++j) n_forced += forced(j) ? 1 : 0;
+    // forced tiles: the sink tiles [0, ns) and the window tiles [lw, hw]
+    const int ns = min(a.sink_tiles, nvt);
+    int n_forced = ns;
+    if (a.local_tiles >= 1) {
+      const int lw = max(0, (lo >= 0 ? lo : lo - a.Bk + 1) / a.Bk), hw = min(nvt - 1, qe / a.Bk);
+      if (hw >= lw) n_forced += (hw - lw + 1) - max(0, min(hw, ns - 1) - lw + 1);
+    }
     const int n_cand = nvt - n_forced;
     int64_t k;
     if (a.topk >= 0) k = a.topk;
     else k = (static_cast<int64_t>(a.ratio_num) * nvt + a.ratio_den - 1) / a.ratio_den;
     if (k > n_cand) k = n_cand;
     // forced and invalid tiles (up to a multiple of 4) become -inf: they then
-    // never outrank a candidate, whose score is finite, and the count below
-    // needs no per-tile test
+    // never outrank a candidate, whose score is finite
     const int nvt4 = (nvt + 3) & ~3;
-    for (int j = tid; j < nvt4; j += blockDim.x)
-      if (j >= nvt || forced(j)) s_score[j] = -__builtin_inff();
-    __syncthreads();
-    const float4* s4 = reinterpret_cast<const float4*>(s_score);
-    for (int j = tid; j < nvt; j += blockDim.x) {
-      bool take = forced(j);
-      if (!take && k > 0) {
+    for (int j = lane; j < nvt4; j += 64)
+      if (j >= nvt || forced(j)) sc[j] = -__builtin_inff();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const float4* s4 = reinterpret_cast<const float4*>(sc);
+    for (int j0 = 0; j0 < a.n_kt; j0 += 64) {
+      const int j = j0 + lane;
+      bool take = j < nvt && forced(j);
+      if (j < nvt && !take && k > 0) {
         // rank of candidate j: candidates with a higher score, or the same
         // score and a lower index (the same tile never counts itself)
-        const float sj = s_score[j];
+        const float sj = sc[j];
         int rank = 0;
         for (int q4 = 0; q4 < nvt4 / 4; ++q4) {
           const float4 o = s4[q4];
@@ -158,15 +171,14 @@ __global__ void __launch_bounds__(256) k_select(SelectArgs a) {
         }
         take = rank < k;
       }
-      if (take) {
-        atomicOr(&s_mask[j / 32], 1u << (j % 32));
-        atomicAdd(&s_count, 1);
-      }
+      const uint64_t bits = __ballot(take);
+      count += __popcll(bits);
+      if (lane < 2 && j0 / 32 + lane < a.words) mrow[j0 / 32 + lane] = static_cast<uint32_t>(bits >> (32 * lane));
     }
+  } else {
+    for (int w = lane; w < a.words; w += 64) mrow[w] = 0u;
   }
-  __syncthreads();
-  for (int w = tid; w < a.words; w += blockDim.x) a.mask[(bhq * a.n_qt + i) * a.words + w] = s_mask[w];
-  if (tid == 0 && a.n_fp16) a.n_fp16[bhq * a.n_qt + i] = s_count;
+  if (lane == 0 && a.n_fp16) a.n_fp16[bhq * a.n_qt + i] = count;
 }
 
 // ---- vertical-line tokens (HyQuant, summary and abstract: single key
@@ -371,8 +383,11 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
   a.Bk = s->Bk; a.causal = s->causal; a.n_qt = n_qt; a.n_kt = n_kt; a.words = (n_kt + 31) / 32;
   a.topk = p->topk; a.ratio_num = p->ratio_num; a.ratio_den = p->ratio_den;
   a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
-  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
-  else hipLaunchKernelGGL(k_select<64>, dim3(n_qt, s->Hq, s->B), dim3(256), 0, strm, a);
+  a.B = s->B;
+  const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
+  const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
+  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
+  else hipLaunchKernelGGL(k_select<64>, grid, dim3(64 * kSelWaves), 0, strm, a);
   return check_launch("k_select");
 }
 
