@@ -32,7 +32,7 @@ MXQ_MIXED, MXQ_ALL_LOWBIT, MXQ_ALL_FP16 = 0, 1, 2
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 
 EXPORTED = [
-    "mxq_quantize", "attn_select_blocks_workspace", "attn_select_blocks", "attn_select_lines_workspace",
+    "mxq_quantize", "mxq_prefill_operands", "attn_select_blocks_workspace", "attn_select_blocks", "attn_select_lines_workspace",
     "attn_select_lines", "attn_mixed_fwd",
     "attn_quantkv_decode_workspace", "attn_quantkv_decode", "attn_quantkv_append", "mxq_status_string",
     "mxq_last_error", "mxq_version",
@@ -93,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.mxq_quantize.argtypes = [vp, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.mxq_quantize.restype = i32
+    lib.mxq_prefill_operands.argtypes = [vp, vp, vp, ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mxq_prefill_operands.restype = i32
     lib.attn_select_blocks_workspace.argtypes = [ctypes.POINTER(AttnShape)]
     lib.attn_select_blocks_workspace.restype = sz
     lib.attn_select_blocks.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(SelectParams),
@@ -260,15 +262,27 @@ class PrefillOperands:
 def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False, rotate=False) -> PrefillOperands:
     """Quantise Q/K (MXFP4, optionally of the Walsh-Hadamard-rotated rows),
     V (MXFP8 along keys) and make the fp16 V^T copy (needed by FP16 tiles and
-    by vertical lines), all on the GPU through mxq_quantize."""
+    by vertical lines), all on the GPU in two launches (mxq_prefill_operands)."""
+    _need_gpu(q, k, v)
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16 and q.dim() == k.dim() == v.dim() == 4
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == v.shape == (B, Hkv, N, D)
+    dev = q.device
     ops = PrefillOperands(q_bf16=q, k_bf16=k)
     if mode != MXQ_ALL_FP16:
-        f4 = MXQ_MXFP4_E2M1_HADAMARD if rotate else MXQ_MXFP4_E2M1
-        ops.q_codes, ops.q_scales, _ = mxq_quantize(q, f4, MXQ_AXIS_D, n_valid)
-        ops.k_codes, ops.k_scales, _ = mxq_quantize(k, f4, MXQ_AXIS_D, n_valid)
-        ops.v_codes, ops.v_scales, _ = mxq_quantize(v, MXQ_MXFP8_E4M3, MXQ_AXIS_N, n_valid)
+        ops.q_codes = torch.empty((B, Hq, N, D // 2), dtype=torch.uint8, device=dev)
+        ops.q_scales = torch.empty((B, Hq, N, D // 32), dtype=torch.uint8, device=dev)
+        ops.k_codes = torch.empty((B, Hkv, N, D // 2), dtype=torch.uint8, device=dev)
+        ops.k_scales = torch.empty((B, Hkv, N, D // 32), dtype=torch.uint8, device=dev)
+        ops.v_codes = torch.empty((B, Hkv, D, N), dtype=torch.uint8, device=dev)
+        ops.v_scales = torch.empty((B, Hkv, D, N // 32), dtype=torch.uint8, device=dev)
     if mode != MXQ_ALL_LOWBIT or lines:
-        ops.v_f16t, _, _ = mxq_quantize(v, MXQ_FP16, MXQ_AXIS_N, n_valid)
+        ops.v_f16t = torch.empty((B, Hkv, D, N), dtype=torch.float16, device=dev)
+    cs = Shape(B, Hq, Hkv, N, int(n_valid), D, 64, 64, False).c()
+    _check(load_library().mxq_prefill_operands(
+        _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), int(bool(rotate)), _ptr(ops.q_codes), _ptr(ops.q_scales),
+        _ptr(ops.k_codes), _ptr(ops.k_scales), _ptr(ops.v_codes), _ptr(ops.v_scales), _ptr(ops.v_f16t), _stream()))
     return ops
 
 

@@ -19,13 +19,26 @@ namespace {
 // ---- MXFP4 along D: one thread per 32-element block ---------------------------
 // x [rows][D] bf16 -> codes [rows][D/2], scales [rows][D/32].  Consecutive
 // threads take consecutive blocks, so a wave reads 4 KB of contiguous input.
+// A second tensor (x2, codes2, scales2; n_blocks2 blocks of the same row
+// length, N and n_valid) may follow the first in the same launch: blocks
+// n_blocks .. n_blocks + n_blocks2 - 1 are its blocks 0 .. n_blocks2 - 1.
 __global__ void __launch_bounds__(256) k_quant_mxfp4_d(const uint16_t* __restrict__ x,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        int64_t n_blocks, int64_t blocks_per_row,
-                                                       int64_t N, int64_t n_valid) {
+                                                       int64_t N, int64_t n_valid,
+                                                       const uint16_t* __restrict__ x2 = nullptr,
+                                                       uint8_t* __restrict__ codes2 = nullptr,
+                                                       uint8_t* __restrict__ scales2 = nullptr,
+                                                       int64_t n_blocks2 = 0) {
   int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (blk >= n_blocks) return;
+  if (blk >= n_blocks + n_blocks2) return;
+  if (blk >= n_blocks) {
+    blk -= n_blocks;
+    x = x2;
+    codes = codes2;
+    scales = scales2;
+  }
   int64_t row = blk / blocks_per_row;
   bool live = (row % N) < n_valid;
   const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);
@@ -71,14 +84,24 @@ template <int D>
 __global__ void __launch_bounds__(256) k_quant_mxfp4_had(const uint16_t* __restrict__ x,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int64_t rows,
-                                                         int64_t N, int64_t n_valid) {
+                                                         int64_t N, int64_t n_valid,
+                                                         const uint16_t* __restrict__ x2,
+                                                         uint8_t* __restrict__ codes2,
+                                                         uint8_t* __restrict__ scales2, int64_t rows2) {
   constexpr int LPR = D / 8;  // lanes per row
   static_assert(D == 32 || D == 64 || D == 128 || D == 256, "power-of-two head_dim");
   // fl32(1/sqrt(D)), the double quotient rounded once to fp32
   constexpr float kInv = D == 32 ? 0x1.6a09e6p-3f : D == 64 ? 0.125f : D == 128 ? 0x1.6a09e6p-4f : 0.0625f;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t row = gid / LPR;
+  int64_t row = gid / LPR;
   const int u = static_cast<int>(gid % LPR);
+  if (row >= rows) {  // a second tensor may follow in the same launch (whole rows, so whole groups of lanes)
+    row -= rows;
+    rows = rows2;
+    x = x2;
+    codes = codes2;
+    scales = scales2;
+  }
   const bool in = row < rows;
   const bool live = in && (row % N) < n_valid;
   const uint4 w4 = live ? *reinterpret_cast<const uint4*>(x + row * D + 8 * u) : make_uint4(0, 0, 0, 0);
@@ -132,10 +155,11 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4_had(const uint16_t* __restr
 
 template <int D>
 mxq_status launch_had(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t rows, int64_t N,
-                      int64_t n_valid, hipStream_t st) {
-  const int64_t lanes = rows * (D / 8);
+                      int64_t n_valid, hipStream_t st, const uint16_t* x2 = nullptr, uint8_t* codes2 = nullptr,
+                      uint8_t* scales2 = nullptr, int64_t rows2 = 0) {
+  const int64_t lanes = (rows + rows2) * (D / 8);
   hipLaunchKernelGGL((k_quant_mxfp4_had<D>), dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0, st,
-                     x, codes, scales, rows, N, n_valid);
+                     x, codes, scales, rows, N, n_valid, x2, codes2, scales2, rows2);
   return check_launch("k_quant_mxfp4_had");
 }
 
@@ -226,10 +250,13 @@ __global__ void __launch_bounds__(256) k_to_f16_n(const uint16_t* __restrict__ x
 // 16-byte aligned), and the writers read contiguous keys of one row and store
 // 16 bytes at a time.  The arithmetic is that of the per-element kernels
 // above, so codes, scales and fp16 values are identical.
-template <int KB, bool FP8>
-__global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, void* __restrict__ out,
-                                              uint8_t* __restrict__ scales, int64_t N, int D,
-                                              int64_t n_valid, int64_t n_kb) {
+// OUT: kVtF16 writes the fp16 copy (to f16), kVtF8 the MXFP8 codes and
+// scales, kVtBoth both from the one LDS tile.
+constexpr int kVtF16 = 1, kVtF8 = 2, kVtBoth = 3;
+template <int KB, int OUT>
+__global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, uint16_t* __restrict__ f16,
+                                              uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                              int64_t N, int D, int64_t n_valid, int64_t n_kb) {
   constexpr int S = KB + 8;
   extern __shared__ __attribute__((aligned(16))) uint16_t tt[];  // [D][S]
   const int64_t bh = blockIdx.x / n_kb;
@@ -247,8 +274,8 @@ __global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, vo
     }
   }
   __syncthreads();
-  if constexpr (!FP8) {
-    uint16_t* y = static_cast<uint16_t*>(out);
+  if constexpr ((OUT & kVtF16) != 0) {
+    uint16_t* y = f16;
     for (int t = threadIdx.x; t < D * (KB / 8); t += 256) {
       const int d = t / (KB / 8), c = t % (KB / 8);
       const uint4 v = *reinterpret_cast<const uint4*>(tt + d * S + 8 * c);
@@ -263,8 +290,8 @@ __global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, vo
       }
       *reinterpret_cast<uint4*>(y + (bh * D + d) * N + n0 + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-  } else {
-    uint8_t* codes = static_cast<uint8_t*>(out);
+  }
+  if constexpr ((OUT & kVtF8) != 0) {
     for (int t = threadIdx.x; t < D * (KB / 32); t += 256) {
       const int d = t / (KB / 32), b = t % (KB / 32);
       const uint4* r = reinterpret_cast<const uint4*>(tt + d * S + 32 * b);
@@ -299,14 +326,14 @@ __global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, vo
   }
 }
 
-template <int KB, bool FP8>
-mxq_status launch_vt_n(const uint16_t* x, void* out, uint8_t* scales, int64_t BH, int64_t N, int64_t D,
-                       int64_t n_valid, hipStream_t st) {
+template <int KB, int OUT>
+mxq_status launch_vt_n(const uint16_t* x, uint16_t* f16, uint8_t* codes, uint8_t* scales, int64_t BH, int64_t N,
+                       int64_t D, int64_t n_valid, hipStream_t st) {
   const int64_t n_kb = N / KB;
   const size_t lds = static_cast<size_t>(D) * (KB + 8) * sizeof(uint16_t);
-  hipLaunchKernelGGL((k_vt_n<KB, FP8>), dim3(static_cast<unsigned>(BH * n_kb)), dim3(256), lds, st, x, out,
+  hipLaunchKernelGGL((k_vt_n<KB, OUT>), dim3(static_cast<unsigned>(BH * n_kb)), dim3(256), lds, st, x, f16, codes,
                      scales, N, static_cast<int>(D), n_valid, n_kb);
-  return check_launch(FP8 ? "k_vt_n<fp8>" : "k_vt_n<fp16>");
+  return check_launch("k_vt_n");
 }
 
 // ---- INT4 asymmetric, groups of 32 along D: one thread per group ----------------
@@ -392,7 +419,8 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
                 "mxq_quantize MXFP8: scales required, zeros must be NULL");
     MXQ_REQUIRE(N % 128 == 0, MXQ_EUNSUPPORTED, "mxq_quantize MXFP8 AXIS_N: N must be a multiple of 128");
     if (D <= 256 && BH * (N / 64) <= 0x7FFFFFFF)
-      return launch_vt_n<64, true>(x, codes, static_cast<uint8_t*>(scales), BH, N, D, n_valid, st);
+      return launch_vt_n<64, kVtF8>(x, nullptr, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), BH, N,
+                                    D, n_valid, st);
     int64_t total = BH * (N / 32) * D;
     hipLaunchKernelGGL(k_quant_mxfp8_n, dim3(grid_for(total, 256)), dim3(256), 0, st, x,
                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), BH, N, D, n_valid);
@@ -408,8 +436,9 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
       return check_launch("k_to_f16_d");
     }
     if (D <= 256 && BH * (N / 32) <= 0x7FFFFFFF) {
-      if (N % 64 == 0) return launch_vt_n<64, false>(x, codes, nullptr, BH, N, D, n_valid, st);
-      return launch_vt_n<32, false>(x, codes, nullptr, BH, N, D, n_valid, st);
+      uint16_t* f16 = static_cast<uint16_t*>(codes);
+      if (N % 64 == 0) return launch_vt_n<64, kVtF16>(x, f16, nullptr, nullptr, BH, N, D, n_valid, st);
+      return launch_vt_n<32, kVtF16>(x, f16, nullptr, nullptr, BH, N, D, n_valid, st);
     }
     MXQ_REQUIRE(BH <= 65535, MXQ_EUNSUPPORTED, "mxq_quantize FP16 AXIS_N: B*H must be <= 65535");
     hipLaunchKernelGGL(k_to_f16_n, dim3(static_cast<unsigned>(N / 32), static_cast<unsigned>(D / 32),
@@ -427,4 +456,44 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
     return check_launch("k_quant_int4_d");
   }
   return fail(MXQ_EUNSUPPORTED, "mxq_quantize: unsupported (format, axis) pair");
+}
+
+extern "C" mxq_status mxq_prefill_operands(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                           const mxq_attn_shape* s, int32_t rotate, uint8_t* q_codes,
+                                           uint8_t* q_scales, uint8_t* k_codes, uint8_t* k_scales,
+                                           uint8_t* v_codes, uint8_t* v_scales, uint16_t* v_f16t,
+                                           mxq_stream_t stream) {
+  MXQ_REQUIRE(s != nullptr, MXQ_EINVAL, "mxq_prefill_operands: shape is NULL");
+  MXQ_REQUIRE(s->B >= 1 && s->Hq >= 1 && s->Hkv >= 1 && s->N >= 1 && s->n_valid >= 1 && s->n_valid <= s->N,
+              MXQ_EINVAL, "mxq_prefill_operands: bad shape");
+  MXQ_REQUIRE(s->D == 64 || s->D == 128, MXQ_EUNSUPPORTED, "mxq_prefill_operands: D must be 64 or 128");
+  MXQ_REQUIRE(s->N % 128 == 0, MXQ_EUNSUPPORTED, "mxq_prefill_operands: N must be a multiple of 128");
+  MXQ_REQUIRE(rotate == 0 || rotate == 1, MXQ_EINVAL, "mxq_prefill_operands: rotate must be 0 or 1");
+  const bool qk = q_codes || q_scales || k_codes || k_scales;
+  const bool v8 = v_codes || v_scales;
+  MXQ_REQUIRE(!qk || (q && k && q_codes && q_scales && k_codes && k_scales), MXQ_EINVAL,
+              "mxq_prefill_operands: Q/K outputs need q, k and all four arrays");
+  MXQ_REQUIRE(!v8 || (v && v_codes && v_scales), MXQ_EINVAL, "mxq_prefill_operands: V MXFP8 needs v, codes and scales");
+  MXQ_REQUIRE(!v_f16t || v, MXQ_EINVAL, "mxq_prefill_operands: the fp16 V^T copy needs v");
+  hipStream_t st = as_stream(stream);
+  const int64_t D = s->D, N = s->N, nv = s->n_valid;
+  const int64_t rows_q = static_cast<int64_t>(s->B) * s->Hq * N, rows_k = static_cast<int64_t>(s->B) * s->Hkv * N;
+  mxq_status r = MXQ_OK;
+  if (qk) {  // Q and K in one launch
+    if (rotate) {
+      r = D == 128 ? launch_had<128>(q, q_codes, q_scales, rows_q, N, nv, st, k, k_codes, k_scales, rows_k)
+                   : launch_had<64>(q, q_codes, q_scales, rows_q, N, nv, st, k, k_codes, k_scales, rows_k);
+    } else {
+      const int64_t nb_q = rows_q * (D / 32), nb_k = rows_k * (D / 32);
+      hipLaunchKernelGGL(k_quant_mxfp4_d, dim3(grid_for(nb_q + nb_k, 256)), dim3(256), 0, st, q, q_codes, q_scales,
+                         nb_q, D / 32, N, nv, k, k_codes, k_scales, nb_k);
+      r = check_launch("k_quant_mxfp4_d");
+    }
+    if (r != MXQ_OK) return r;
+  }
+  const int64_t BH = static_cast<int64_t>(s->B) * s->Hkv;
+  if (v8 && v_f16t) return launch_vt_n<64, kVtBoth>(v, v_f16t, v_codes, v_scales, BH, N, D, nv, st);
+  if (v8) return launch_vt_n<64, kVtF8>(v, nullptr, v_codes, v_scales, BH, N, D, nv, st);
+  if (v_f16t) return launch_vt_n<64, kVtF16>(v, v_f16t, nullptr, nullptr, BH, N, D, nv, st);
+  return MXQ_OK;
 }

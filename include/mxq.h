@@ -118,6 +118,23 @@ mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t B, int64_t H, int64_t N,
                         uint16_t* zeros, mxq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * mxq_prefill_operands -- every quantised operand attn_mixed_fwd reads, in two
+ * launches, with the values the separate mxq_quantize calls give:
+ *   q_codes/q_scales, k_codes/k_scales: MXFP4 AXIS_D of Q [B][Hq][N][D] and K
+ *     [B][Hkv][N][D] (MXFP4_E2M1_HADAMARD when rotate = 1), one launch;
+ *   v_codes/v_scales: MXFP8 AXIS_N of V [B][Hkv][N][D], and v_f16t the fp16
+ *     AXIS_N copy, both written from one read of V.
+ * Groups may be left out by passing NULL for all of their arrays (Q/K when
+ * the attention runs all-FP16; V's MXFP8 likewise; v_f16t when no FP16 tile
+ * or line is used).  Shape as for attn_mixed_fwd (rows >= n_valid are zero);
+ * D in {64, 128}, N a multiple of 128.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_prefill_operands(const uint16_t* q_bf16, const uint16_t* k_bf16, const uint16_t* v_bf16,
+                                const mxq_attn_shape* shape, int32_t rotate, uint8_t* q_codes,
+                                uint8_t* q_scales, uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                                uint8_t* v_scales, uint16_t* v_f16t, mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * attn_select_blocks -- stage 1 of ThriftAttention (abstract): choose the
  * query-key tiles that run in FP16.  Importance estimate (reading R8): the
  * score of tile pair (i, j) is mean(Q rows of tile i) . mean(K rows of tile j)

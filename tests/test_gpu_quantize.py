@@ -135,3 +135,27 @@ def test_mxfp4_hadamard_bit_exact(shape):
     rc, rs = F.quantize_mxfp4(F.hadamard_rotate(_zero_pad(F.bf16_bits_to_f32(bits), nv)))
     assert np.array_equal(u8(codes), F.pack_nibbles(rc))
     assert np.array_equal(u8(scales), rs)
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("shape", [(1, 4, 1, 384, 128, 301), (2, 2, 2, 256, 64, 256)])
+def test_prefill_operands_equal_the_separate_calls(shape, rotate):
+    """mxq_prefill_operands (Q and K in one launch, V's MXFP8 and fp16 copies
+    from one read) writes what the per-tensor mxq_quantize calls write."""
+    mxq = gpu_or_skip()
+    B, Hq, Hkv, N, D, nv = shape
+    q = bf16_dev(random_bf16((B, Hq, N, D), seed=N + 1, scale=2.0))
+    k = bf16_dev(random_bf16((B, Hkv, N, D), seed=N + 2, scale=2.0))
+    v = bf16_dev(random_bf16((B, Hkv, N, D), seed=N + 3, scale=2.0))
+    ops = mxq.prepare_prefill(q, k, v, nv, rotate=rotate)
+    f4 = mxq.MXQ_MXFP4_E2M1_HADAMARD if rotate else mxq.MXQ_MXFP4_E2M1
+    for got, ref in ((ops.q_codes, mxq.mxq_quantize(q, f4, 0, nv)[0]), (ops.q_scales, mxq.mxq_quantize(q, f4, 0, nv)[1]),
+                     (ops.k_codes, mxq.mxq_quantize(k, f4, 0, nv)[0]), (ops.k_scales, mxq.mxq_quantize(k, f4, 0, nv)[1]),
+                     (ops.v_codes, mxq.mxq_quantize(v, mxq.MXQ_MXFP8_E4M3, 1, nv)[0]),
+                     (ops.v_scales, mxq.mxq_quantize(v, mxq.MXQ_MXFP8_E4M3, 1, nv)[1])):
+        assert np.array_equal(u8(got), u8(ref))
+    assert np.array_equal(u16(ops.v_f16t), u16(mxq.mxq_quantize(v, mxq.MXQ_FP16, 1, nv)[0]))
+    low = mxq.prepare_prefill(q, k, v, nv, mode=mxq.MXQ_ALL_LOWBIT)
+    assert low.v_f16t is None and np.array_equal(u8(low.v_codes), u8(ops.v_codes))
+    hi = mxq.prepare_prefill(q, k, v, nv, mode=mxq.MXQ_ALL_FP16)
+    assert hi.q_codes is None and np.array_equal(u16(hi.v_f16t), u16(ops.v_f16t))
