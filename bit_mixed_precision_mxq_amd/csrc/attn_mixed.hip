@@ -303,9 +303,21 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // unpacked while the copies land.
   const uint32_t mw_a = tid < n_chunks ? mask_word(mrow_a, tid) : 0u;
   const uint32_t mw_b = tid < n_chunks ? mask_word(mrow_b, tid) : 0u;
+  // the line list through the scalar unit (its own wait counter, so the
+  // dependent gathers below need not wait for the vector loads in flight):
+  // 16 loads with indices clamped to the row, then entry e to lane e
   int line_raw = -1;
   if constexpr (LINES) {
-    if (lane < 16 && lane < a.n_lines) line_raw = a.lines[bhq * a.n_lines + lane];
+    const uint64_t pa = reinterpret_cast<uint64_t>(a.lines + bhq * a.n_lines);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32));
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    cint* lrow = reinterpret_cast<cint*>((static_cast<uint64_t>(hi) << 32) | lo);
+    int raw_s[kMaxLines];
+#pragma unroll
+    for (int e = 0; e < kMaxLines; ++e) raw_s[e] = lrow[min(e, a.n_lines - 1)];
+#pragma unroll
+    for (int e = 0; e < kMaxLines; ++e) line_raw = (lane == e && e < a.n_lines) ? raw_s[e] : line_raw;
   }
   auto rebase = [&](float m) {  // rescale O and L from m_o to m >= m_o (powers of two)
     if (__any(m != m_o)) {
@@ -437,6 +449,64 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     k_dma(0, kbuf(0));
     k_dma(1, kbuf(1));
     v_dma(0, vbuf(0));
+  }
+  issue_fence();
+
+  // Vertical-line keys (HyQuant): entry e of the head's list takes part when
+  // 0 <= key < n_valid and it exceeds every earlier entry.  Lane e < 16 of
+  // every wave holds entry e's key in lkey (else -1) and, for a used entry,
+  // lslot = the rank of its 128-key chunk among the chunks holding line keys.
+  // (Cross-lane steps use DPP row shifts and readlane, vector-ALU
+  // operations: an LDS permute here would have to wait for the copies in
+  // flight, since they also write LDS.)
+  int lkey = -1, lslot = 0, n_line = 0;
+  // exclusive prefix maximum within each row of 16 lanes (INT_MIN before the first)
+  auto prefix_max_excl = [](int v) -> int {
+    constexpr int kMin = -2147483647 - 1;
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    return __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false);
+  };
+  if constexpr (LINES) {
+    const int e = lane & 15;
+    const int raw = line_raw;
+    if (lane < 16 && raw >= 0 && raw < a.n_valid && raw > prefix_max_excl(raw)) lkey = raw;
+    // chunk ranks: an entry opens a new chunk when its chunk exceeds every
+    // earlier used entry's (used keys ascend)
+    const int cb = prefix_max_excl(lkey >= 0 ? (lkey >> 7) : -1);
+    const uint64_t opens = __ballot(lane < 16 && lkey >= 0 && (lkey >> 7) > cb);
+    lslot = __popcll(opens & ((2ull << e) - 1)) - 1;
+    n_line = __popcll(__ballot(lkey >= 0));
+  }
+  // lkey of lane e (0..15) for a per-lane e: readlanes and selects
+  auto lane_key = [&](int e) -> int {
+    int k = -1;
+#pragma unroll
+    for (int x = 0; x < kMaxLines; ++x) k = e == x ? __builtin_amdgcn_readlane(lkey, x) : k;
+    return k;
+  };
+  // the entries' bf16 K rows and fp16 V (zeros for unused entries), one
+  // unit of each per thread, issued here with the other prologue loads:
+  // buffer loads with out-of-range offsets for unused entries (they read zero)
+  constexpr int LU = kMaxLines * D / 8;       // 16-byte units of K
+  constexpr int LV = D * (kMaxLines / 4);     // 4-entry groups of V
+  static_assert(LU <= NT && LV <= NT, "one line unit per thread");
+  const int ke = tid / (D / 8), kcu = tid % (D / 8);
+  const int vd = tid / (kMaxLines / 4), ve0 = 4 * (tid % (kMaxLines / 4));
+  v4i kw = {0, 0, 0, 0};
+  uint32_t hv[4] = {0u, 0u, 0u, 0u};
+  if constexpr (LINES) {  // unconditional inside the variant: no merge of values forces a wait
+    constexpr int kOut = 0x7FFFFFF0;  // past every slice
+    const int kkey = lane_key(ke & 15);
+    kw = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                     r_hk, (tid < LU && kkey >= 0) ? kkey * 2 * D + 16 * kcu : kOut, 0, 0));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int key = lane_key(ve0 + x);
+      hv[x] = __builtin_amdgcn_raw_buffer_load_b16(r_hv, (tid < LV && key >= 0) ? (vd * a.N + key) * 2 : kOut, 0, 0);
+    }
   }
   issue_fence();
 
@@ -655,41 +725,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
           *reinterpret_cast<const v4i*>(a.q_bf16 + (bhq * a.N + qs + u / (D / 8)) * D + 8 * (u % (D / 8)));
     }
   }
-  // Vertical-line keys (HyQuant): entry e of the head's list takes part when
-  // 0 <= key < n_valid and it exceeds every earlier entry.  Lane e < 16 of
-  // every wave holds entry e's key in lkey (else -1) and, for a used entry,
-  // lslot = the rank of its 128-key chunk among the chunks holding line keys.
-  // (Cross-lane steps use DPP row shifts and readlane, vector-ALU
-  // operations: an LDS permute here would have to wait for the copies in
-  // flight, since they also write LDS.)
-  int lkey = -1, lslot = 0, n_line = 0;
-  // exclusive prefix maximum within each row of 16 lanes (INT_MIN before the first)
-  auto prefix_max_excl = [](int v) -> int {
-    constexpr int kMin = -2147483647 - 1;
-    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false));  // row_shr:1
-    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x112, 0xF, 0xF, false));  // row_shr:2
-    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x114, 0xF, 0xF, false));  // row_shr:4
-    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x118, 0xF, 0xF, false));  // row_shr:8
-    return __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false);
-  };
-  if constexpr (LINES) {
-    const int e = lane & 15;
-    const int raw = line_raw;
-    if (lane < 16 && raw >= 0 && raw < a.n_valid && raw > prefix_max_excl(raw)) lkey = raw;
-    // chunk ranks: an entry opens a new chunk when its chunk exceeds every
-    // earlier used entry's (used keys ascend)
-    const int cb = prefix_max_excl(lkey >= 0 ? (lkey >> 7) : -1);
-    const uint64_t opens = __ballot(lane < 16 && lkey >= 0 && (lkey >> 7) > cb);
-    lslot = __popcll(opens & ((2ull << e) - 1)) - 1;
-    n_line = __popcll(__ballot(lkey >= 0));
-  }
-  // lkey of lane e (0..15) for a per-lane e: readlanes and selects
-  auto lane_key = [&](int e) -> int {
-    int k = -1;
-#pragma unroll
-    for (int x = 0; x < kMaxLines; ++x) k = e == x ? __builtin_amdgcn_readlane(lkey, x) : k;
-    return k;
-  };
   // per chunk: bits 0-1 row ra, 2-3 row rb, 4 the chunk holds a line key,
   // 8-11 its slot in s_lm
   using FlagT = typename std::conditional<LINES, uint16_t, uint8_t>::type;
@@ -728,24 +763,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       }
       s_lm[lane] = m;
     }
-    // the entries' bf16 K rows and fp16 V (zeros for unused entries), one
-    // unit of each per thread: buffer loads with out-of-range offsets for
-    // unused entries (they read zero), all issued before the stores
-    constexpr int LU = kMaxLines * D / 8;       // 16-byte units of K
-    constexpr int LV = D * (kMaxLines / 4);     // 4-entry groups of V
-    constexpr int kOut = 0x7FFFFFF0;            // past every slice
-    static_assert(LU <= NT && LV <= NT, "one line unit per thread");
-    const int ke = tid / (D / 8), kcu = tid % (D / 8);
-    const int kkey = lane_key(ke & 15);
-    const v4i kw = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                               r_hk, (tid < LU && kkey >= 0) ? kkey * 2 * D + 16 * kcu : kOut, 0, 0));
-    const int vd = tid / (kMaxLines / 4), ve0 = 4 * (tid % (kMaxLines / 4));
-    uint32_t hv[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int key = lane_key(ve0 + x);
-      hv[x] = __builtin_amdgcn_raw_buffer_load_b16(r_hv, (tid < LV && key >= 0) ? (vd * a.N + key) * 2 : kOut, 0, 0);
-    }
+    // the gathered line rows (loaded in the prologue) -> LDS
     if (tid < LU) *reinterpret_cast<v4i*>(sm + LY::lk_off(ke, kcu)) = kw;
     if (tid < LV)
       *reinterpret_cast<uint2*>(sm + LY::LV_OFF + (vd * kMaxLines + ve0) * 2) =
