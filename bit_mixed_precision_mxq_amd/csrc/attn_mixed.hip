@@ -613,18 +613,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
   };
-  // O^T += V^T P^T (FP8 x FP8) and L += sum(P) for a staged chunk
-  auto pv_lowbit = [&](const uint8_t* vb, const v8i& pb, int psc) {
-    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
-    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const v8i va = vfrag(vb, db);
-      const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
-      O[db] = pv_block(va, pb, O[db], vs, psc, db);
-    }
-    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
-  };
 
   // ---- main loop over 128-key chunks.
   // Ring protocol: chunk ch+1's low-bit data (loaded into registers during
@@ -637,7 +625,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // exponentials of chunk ch are computed, the FP4 QK MFMAs of chunk ch+1 are
   // issued into the score registers just consumed, and the row maxima of chunk
   // ch+1 are taken while the PV MFMAs of chunk ch run.
-  v4f S[8];
+  // (zeroed: the shared PV step below also reduces S when it holds no next chunk)
+  v4f S[8] = {};
   float hm0 = 0.0f, hm1 = 0.0f;   // tile references of the chunk whose scores S holds
   bool s_ready = false;           // S already holds the scores of chunk ch
   auto is_hot = [&](int ch, int fl) -> bool {
@@ -651,22 +640,19 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     // 2^-8 * 2^(m_t - m_o); below 2^-127 (after a forced rebase) the tile adds nothing visible
     return static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + ((g < 2 ? hm0 : hm1) - m_o), 0.0f), 254.0f));
   };
-  // last chunk of a run: exponentials and PV only
-  auto hot_chunk = [&](const uint8_t* vb) {
+  // last chunk of a run: its P blocks only
+  auto hot_exp = [&](v8i& pb) {
     const float off0 = kGridMagic + kExpOffset - hm0;  // hm0 is finite: key 0.. are valid
     const float off1 = kGridMagic + kExpOffset - hm1;
-    v8i pb;
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
-    pv_lowbit(vb, pb, p_scale());
   };
-  // chunk ch (scores in S, V in vb) followed by another hot chunk (K in kbn).  Issue order,
-  // fixed with scheduling barriers: the next chunk's K fragments; per S block
-  // its exponentials and then the FP4 QK MFMA of the next chunk into the same
-  // registers (the vector ALU and the matrix core work side by side); per
-  // head_dim block the V fragments two blocks ahead, one PV MFMA and a slice of
-  // the next chunk's row maxima.
-  auto hot_chunk_next = [&](const uint8_t* vb, const uint8_t* kbn) {
+  // P blocks of chunk ch (scores in S) while the FP4 QK MFMAs of the next hot
+  // chunk (K in kbn) are issued into the same registers.  Issue order, fixed
+  // with scheduling barriers: the next chunk's K fragments; per S block its
+  // exponentials and then the QK MFMA (the vector ALU and the matrix core work
+  // side by side).
+  auto hot_exp_next = [&](const uint8_t* kbn, v8i& pb) {
     const float off0 = kGridMagic + kExpOffset - hm0;
     const float off1 = kGridMagic + kExpOffset - hm1;
     const uint32_t* ksw = reinterpret_cast<const uint32_t*>(kbn + ksoff);
@@ -676,7 +662,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 #pragma unroll
     for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(kbn + koff(beta));
     __builtin_amdgcn_sched_barrier(0);
-    v8i pb;
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) {
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
@@ -685,7 +670,16 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int psc = p_scale();
+  };
+  // O^T += V^T P^T (FP8 x FP8) and L += sum(P) for chunk ch (V in vb), the one
+  // place in the loop where low-bit PV touches O: with a single update site the
+  // MFMAs accumulate in place (an update in several alternative branches makes
+  // the compiler copy O back after each).  A wave with no low-bit tile in the
+  // chunk passes pb = 0, which adds exactly nothing.  Per head_dim block: the V
+  // fragments two blocks ahead, one PV MFMA and a slice of the row maxima of the
+  // scores in S; when S holds the next hot chunk (nxt) they become its tile
+  // references.
+  auto pv_chunk = [&](const uint8_t* vb, const v8i& pb, int psc, bool nxt) {
     const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
     const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
     v8i va[NDB];
@@ -707,12 +701,14 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
-    mx0 = rowmax4(mx0);
-    mx1 = rowmax4(mx1);
-    hm0 = fmaxf(m_run, ceilf(mx0 * c));
-    hm1 = fmaxf(hm0, ceilf(mx1 * c));
-    m_run = hm1;
-    chunk_lag(hm0, hm1);
+    if (nxt) {
+      mx0 = rowmax4(mx0);
+      mx1 = rowmax4(mx1);
+      hm0 = fmaxf(m_run, ceilf(mx0 * c));
+      hm1 = fmaxf(hm0, ceilf(mx1 * c));
+      m_run = hm1;
+      chunk_lag(hm0, hm1);
+    }
   };
 
   if (a.mode != MXQ_ALL_LOWBIT || LINES) {  // bf16 Q rows of the workgroup -> LDS (rows past N are never read)
@@ -787,6 +783,10 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     ks_store(kbuf(1));
     pvs = pvs0;
     vs_store(vbuf(0));
+  } else {
+    // no low-bit operands: the V ring is never filled, yet the shared PV step
+    // runs on every chunk (with P = 0); zero codes and scales make it add 0
+    for (int i = tid; i < LY::RV * LY::V_BYTES / 16; i += NT) reinterpret_cast<v4i*>(vring)[i] = v4i{0, 0, 0, 0};
   }
   // the Q fragment is used in every chunk: wait for it here, once
   asm volatile("" ::"v"(qsc), "v"(qf4[0]), "v"(qf4[1]), "v"(qf4[2]), "v"(qf4[3]));
@@ -906,6 +906,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     issue_fence();
     const bool hot = is_hot(ch, f_cur);
     const int t_first = (f_cur & 4) ? 0 : 1;  // first tile some wave promotes
+    v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};  // P of chunk ch's low-bit PV (0: nothing to add)
+    int psc = 0;
+    bool nxt = false;                   // S now holds the next hot chunk's scores
 
     if (hot) {
       // ================= hot path: both tiles low-bit for every wave, no masks
@@ -913,17 +916,15 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         qk_lowbit(kb, S);
         chunk_refs(S, hm0, hm1);
       }
-      const bool hot_next = ch + 1 < n_chunks && is_hot(ch + 1, f_nxt);
-      if (hot_next) hot_chunk_next(vb, kbuf(ch + 1));
-      else hot_chunk(vb);
-      s_ready = hot_next;
+      nxt = ch + 1 < n_chunks && is_hot(ch + 1, f_nxt);
+      if (nxt) hot_exp_next(kbuf(ch + 1), pb);
+      else hot_exp(pb);
+      psc = p_scale();
     } else {
-      s_ready = false;
       const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
       const bool has_line = LINES && (f_cur & 64);  // line keys run in the line tile, not here
       // ================= general path: masks, FP16 tiles, line keys, a lone last tile
       const bool low_w = !(f_cur & 1) || (valid1 && !(f_cur & 2));  // this wave runs FP8 PV
-      v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};
       float m_tile0 = NEG_INF;
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
@@ -1035,19 +1036,13 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         if (m_o == NEG_INF) m_o = m_run;
         else if (__any(m_run - m_o > kMaxLag)) rebase(m_run);
         const float mt = g < 2 ? m_tile0 : m_run;
-        int psc = 0;  // a tile with no valid key for this row adds nothing
+        // a tile with no valid key for this row adds nothing (psc 0 with pb 0)
         if (mt != NEG_INF && m_o != NEG_INF)
           psc = static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + (mt - m_o), 0.0f), 254.0f));
-        const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v8i va = vfrag(vb, db);
-          const int vs = static_cast<int>(vsw[db >> 2] >> (8 * (db & 3))) & 0xFF;
-          O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vs, 0, psc);
-        }
-            L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
       }
     }
+    pv_chunk(vb, pb, psc, nxt);
+    s_ready = nxt;
     f_cur = f_nxt;
     f_nxt = f_nn;
     vslot = vslot1;
