@@ -701,6 +701,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+    // keeps the maxima here, beside the MFMAs (only the branch below reads them,
+    // so the compiler would otherwise sink them into it)
+    __asm__ volatile("" ::"v"(mx0), "v"(mx1));
     if (nxt) {
       mx0 = rowmax4(mx0);
       mx1 = rowmax4(mx1);
