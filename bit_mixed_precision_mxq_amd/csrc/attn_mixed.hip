@@ -388,9 +388,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   auto ks_fetch = [&](int ch) -> uint32_t {
     return tid < 128 * NSB ? __builtin_amdgcn_raw_buffer_load_b8(r_ks, ch * 128 * NSB + tid, 0, 0) : 0u;
   };
-  auto vs_fetch = [&](int ch) -> uint32_t {
-    return tid < D ? __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32) + ch * 4, 0, 0) : 0u;
-  };
   auto ks_load = [&](int ch) {
     if (tid < 128 * NSB) pks = __builtin_amdgcn_raw_buffer_load_b8(r_ks, ch * 128 * NSB + tid, 0, 0);
   };
@@ -441,14 +438,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   }
   // chunks 0, 1 (K) and 0 (V) in full, as iterations -3 and -2 would have
   // staged them: copies and scale loads now, scale stores before the barrier
-  uint32_t pks0 = 0, pks1 = 0, pvs0 = 0;
+  uint32_t pks0 = 0, pks1 = 0;
   if (lowbit) {
     pks0 = ks_fetch(0);
     pks1 = ks_fetch(1);
-    pvs0 = vs_fetch(0);
     k_dma(0, kbuf(0));
     k_dma(1, kbuf(1));
-    v_dma(0, vbuf(0));
   }
   issue_fence();
 
@@ -570,36 +565,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       S[beta] = qk_block(ka, sc, beta);
     }
   };
-  // running reference after an unmasked low-bit chunk: integer per-tile
-  // references m0 <= m1 and, when O's reference lags too far, a rebase
-  auto chunk_max = [&](const v4f (&S)[8], float& m0, float& m1) {
-    float mx0 = max3f(S[0][0], S[0][1], S[0][2]);
-    float mx1 = max3f(S[4][0], S[4][1], S[4][2]);
-    mx0 = max3f(mx0, S[0][3], S[1][0]);
-    mx1 = max3f(mx1, S[4][3], S[5][0]);
-#pragma unroll
-    for (int e = 5; e < 16; e += 2) {  // remaining 11 values of each tile, two per v_max3
-      const float a0 = S[e >> 2][e & 3], b0 = e + 1 < 16 ? S[(e + 1) >> 2][(e + 1) & 3] : a0;
-      const float a1 = S[4 + (e >> 2)][e & 3], b1 = e + 1 < 16 ? S[4 + ((e + 1) >> 2)][(e + 1) & 3] : a1;
-      mx0 = max3f(mx0, a0, b0);
-      mx1 = max3f(mx1, a1, b1);
-    }
-    mx0 = rowmax4(mx0);
-    mx1 = rowmax4(mx1);
-    m0 = fmaxf(m_run, ceilf(mx0 * c));
-    m1 = fmaxf(m0, ceilf(mx1 * c));
-    m_run = m1;
-  };
   auto chunk_lag = [&](float m0, float m1) {
     // O and L stay expressed against a lagging reference m_o <= m0: each
     // tile's contribution is scaled by 2^(m_t - m_o) through the E8M0 scale
     // of its P blocks, so O is only rescaled when the gap grows large
     if (m_o == NEG_INF) m_o = m0;
     if (__any(m1 - m_o > kMaxLag)) rebase(m1);
-  };
-  auto chunk_refs = [&](const v4f (&S)[8], float& m0, float& m1) {
-    chunk_max(S, m0, m1);
-    chunk_lag(m0, m1);
   };
   // P = E4M3(2^xq) of one S block (4 scores per lane -> 4 bytes)
   // (the two conversions write the low and the high half of the word, so its
@@ -615,103 +586,103 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   };
 
   // ---- main loop over 128-key chunks.
-  // Ring protocol: chunk ch+1's low-bit data (loaded into registers during
-  // iteration ch-1) is written to its ring buffer at the top of iteration ch,
-  // the loads for chunk ch+2 are issued, then one barrier.  After it, chunks ch
-  // and ch+1 are both visible, and ring buffer (ch+2)%3 may be overwritten in
-  // the next iteration (its previous chunk, ch-1, was finished by every wave
-  // before this barrier).
-  // Software pipeline for runs of unmasked all-low-bit chunks: while the
-  // exponentials of chunk ch are computed, the FP4 QK MFMAs of chunk ch+1 are
-  // issued into the score registers just consumed, and the row maxima of chunk
-  // ch+1 are taken while the PV MFMAs of chunk ch run.
-  // (zeroed: the shared PV step below also reduces S when it holds no next chunk)
-  v4f S[8] = {};
-  float hm0 = 0.0f, hm1 = 0.0f;   // tile references of the chunk whose scores S holds
-  bool s_ready = false;           // S already holds the scores of chunk ch
+  // Ring protocol: at the top of iteration ch the scale bytes of K chunk ch+2
+  // and V chunk ch (loaded into registers in iteration ch-1) are written to
+  // their buffers, each wave waits for its own copies issued up to iteration
+  // ch-2, then one barrier publishes them; after it iteration ch issues K chunk
+  // ch+3 and V chunk ch+1.  A K buffer is rewritten three iterations after the
+  // QK MFMAs of its chunk, a V buffer two iterations after its PV MFMAs, both
+  // past a barrier that every reader has passed.
+  // Software pipeline, one step per chunk: S holds chunk ch's FP4 scores (its
+  // QK MFMAs were issued in iteration ch-1).  Iteration ch turns them into P
+  // blocks while the QK MFMAs of chunk ch+1 go into the registers just read
+  // and the PV MFMAs of chunk ch-1 (the pending P) run beside them, so the
+  // vector ALU and the matrix core always have independent work.  Chunks that
+  // need masks, FP16 tiles or line keys first rewrite their S blocks (-inf where
+  // a key adds nothing to the low-bit PV) and then take the same step.
+  v4f S[8];
+  float mxa = NEG_INF, mxb = NEG_INF;  // per-lane partial row maxima of S's two tiles
+  float hm0 = 0.0f, hm1 = 0.0f;        // per-tile P references of chunk ch
+  v8i pb_p = {0, 0, 0, 0, 0, 0, 0, 0};  // pending P (chunk ch-1); 0 adds nothing
+  float hp0 = NEG_INF, hp1 = NEG_INF;  // its per-tile references
+  // chunks [0, hot_end) have both tiles valid and need no mask for this wave:
+  // no padded key, no key past the wave's first row, no padded query row
+  int hot_end = (last_tile + 1) >> 1;
+  hot_end = min(hot_end, a.n_valid >> 7);
+  if (a.causal) hot_end = min(hot_end, (wq_lo + 1) >> 7);
+  if (qe < qs + BQ - 1) hot_end = 0;
+  hot_end = __builtin_amdgcn_readfirstlane(hot_end);
   auto is_hot = [&](int ch, int fl) -> bool {
-    const int kc = ch * 128;
-    const bool valid1 = 2 * ch + 1 <= last_tile;
-    const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
-    return !((fl >> 2) & 3) && !(LINES && (fl & 64)) && valid1 && !need_mask;
+    return ch < hot_end && !((fl >> 2) & 3) && !(LINES && (fl & 64));
   };
-  // P blocks of the chunk held in S (references hm0, hm1)
-  auto p_scale = [&]() -> int {
-    // 2^-8 * 2^(m_t - m_o); below 2^-127 (after a forced rebase) the tile adds nothing visible
-    return static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + ((g < 2 ? hm0 : hm1) - m_o), 0.0f), 254.0f));
+  // E8M0 scale of the pending P: 2^-8 * 2^(m_t - m_o), taken when it is
+  // applied (after any rebase since it was formed); below 2^-127 the tile adds
+  // nothing visible, and a tile with no valid key for this row adds nothing
+  auto pend_scale = [&]() -> int {
+    const float mt = g < 2 ? hp0 : hp1;
+    if (mt == NEG_INF || m_o == NEG_INF) return 0;
+    return static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + (mt - m_o), 0.0f), 254.0f));
   };
-  // last chunk of a run: its P blocks only
-  auto hot_exp = [&](v8i& pb) {
-    const float off0 = kGridMagic + kExpOffset - hm0;  // hm0 is finite: key 0.. are valid
-    const float off1 = kGridMagic + kExpOffset - hm1;
-#pragma unroll
-    for (int beta = 0; beta < 8; ++beta) pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
+  // partial maxima of S block beta (tile beta / 4)
+  auto s_max = [&](int beta) {
+    float& mx = beta < 4 ? mxa : mxb;
+    mx = max3f(mx, S[beta][0], S[beta][1]);
+    mx = max3f(mx, S[beta][2], S[beta][3]);
   };
-  // P blocks of chunk ch (scores in S) while the FP4 QK MFMAs of the next hot
-  // chunk (K in kbn) are issued into the same registers.  Issue order, fixed
-  // with scheduling barriers: the next chunk's K fragments; per S block its
-  // exponentials and then the QK MFMA (the vector ALU and the matrix core work
-  // side by side).
-  auto hot_exp_next = [&](const uint8_t* kbn, v8i& pb) {
-    const float off0 = kGridMagic + kExpOffset - hm0;
-    const float off1 = kGridMagic + kExpOffset - hm1;
+  // One pipeline step (see above).  Issue order, fixed with scheduling
+  // barriers, per S block: the K fragment three blocks ahead, the block's
+  // exponentials, its QK MFMA for the next chunk, every 8/NDB blocks one PV
+  // MFMA of the pending chunk (V fragments two head_dim blocks ahead), and the
+  // partial maxima of the block whose QK MFMA was issued three blocks before.
+  auto pipe = [&](const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb) {
+    float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
+    float off1 = kGridMagic + kExpOffset - (hm1 == NEG_INF ? 0.0f : hm1);
+    // opaque from here on: the exponentials cannot be moved out of this step
+    // (the compiler would otherwise compute them where the references are set)
+    __asm__ volatile("" : "+v"(off0), "+v"(off1));
     const uint32_t* ksw = reinterpret_cast<const uint32_t*>(kbn + ksoff);
     const uint32_t nks0 = ksw[0], nks1 = ksw[1];
+    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vbp + vsoff);
+    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
     constexpr int KAHEAD = 3;  // K fragments in flight ahead of their MFMA
+    constexpr int SPB = 8 / NDB;  // S blocks per PV MFMA
     v4i kn[8];
+    v8i va[NDB];
 #pragma unroll
     for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(kbn + koff(beta));
+    va[0] = vfrag(vbp, 0);
+    va[1] = vfrag(vbp, 1);
+    mxa = NEG_INF;
+    mxb = NEG_INF;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) {
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
       pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
+      __asm__ volatile("" ::"v"(pb[beta]));  // formed here, not where it is next read
       const v8i ka = {kn[beta][0], kn[beta][1], kn[beta][2], kn[beta][3], 0, 0, 0, 0};
       S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // O^T += V^T P^T (FP8 x FP8) and L += sum(P) for chunk ch (V in vb), the one
-  // place in the loop where low-bit PV touches O: with a single update site the
-  // MFMAs accumulate in place (an update in several alternative branches makes
-  // the compiler copy O back after each).  A wave with no low-bit tile in the
-  // chunk passes pb = 0, which adds exactly nothing.  Per head_dim block: the V
-  // fragments two blocks ahead, one PV MFMA and a slice of the row maxima of the
-  // scores in S; when S holds the next hot chunk (nxt) they become its tile
-  // references.
-  auto pv_chunk = [&](const uint8_t* vb, const v8i& pb, int psc, bool nxt) {
-    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vb + vsoff);
-    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
-    v8i va[NDB];
-    va[0] = vfrag(vb, 0);
-    va[1] = vfrag(vb, 1);
-    constexpr int SPB = 8 / NDB;  // S blocks reduced per PV step
-    float mx0 = NEG_INF, mx1 = NEG_INF;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      if (db + 2 < NDB) va[db + 2] = vfrag(vb, db + 2);
-      O[db] = pv_block(va[db], pb, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), psc, db);
-#pragma unroll
-      for (int j = 0; j < SPB; ++j) {
-        const int beta = db * SPB + j;
-        float& mx = beta < 4 ? mx0 : mx1;
-        mx = max3f(mx, S[beta][0], S[beta][1]);
-        mx = max3f(mx, S[beta][2], S[beta][3]);
+      if (beta % SPB == SPB - 1) {
+        const int db = beta / SPB;
+        if (db + 2 < NDB) va[db + 2] = vfrag(vbp, db + 2);
+        O[db] = pv_block(va[db], pb_p, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), pscp, db);
       }
+      if (beta >= 3) s_max(beta - 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
-    // keeps the maxima here, beside the MFMAs (only the branch below reads them,
-    // so the compiler would otherwise sink them into it)
-    __asm__ volatile("" ::"v"(mx0), "v"(mx1));
-    if (nxt) {
-      mx0 = rowmax4(mx0);
-      mx1 = rowmax4(mx1);
-      hm0 = fmaxf(m_run, ceilf(mx0 * c));
-      hm1 = fmaxf(hm0, ceilf(mx1 * c));
-      m_run = hm1;
-      chunk_lag(hm0, hm1);
-    }
+    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb_p, L, 0, 0, 0, 127, 0, pscp);
+    s_max(5);
+    s_max(6);
+    s_max(7);
+  };
+  // the pending chunk's PV on its own (after the last chunk)
+  auto pv_flush = [&](const uint8_t* vbp, int pscp) {
+    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vbp + vsoff);
+    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      O[db] = pv_block(vfrag(vbp, db), pb_p, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), pscp, db);
+    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb_p, L, 0, 0, 0, 127, 0, pscp);
   };
 
   if (a.mode != MXQ_ALL_LOWBIT || LINES) {  // bf16 Q rows of the workgroup -> LDS (rows past N are never read)
@@ -784,12 +755,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     ks_store(kbuf(0));
     pks = pks1;
     ks_store(kbuf(1));
-    pvs = pvs0;
-    vs_store(vbuf(0));
   } else {
-    // no low-bit operands: the V ring is never filled, yet the shared PV step
-    // runs on every chunk (with P = 0); zero codes and scales make it add 0
-    for (int i = tid; i < LY::RV * LY::V_BYTES / 16; i += NT) reinterpret_cast<v4i*>(vring)[i] = v4i{0, 0, 0, 0};
+    // no low-bit operands: the rings are never filled, yet every chunk's
+    // pipeline step runs its QK and PV MFMAs (with P = 0); zero codes and
+    // scales keep them finite so that they add exactly 0
+    for (int i = tid; i < (LY::RK * LY::K_BYTES + LY::RV * LY::V_BYTES) / 16; i += NT)
+      reinterpret_cast<v4i*>(kring)[i] = v4i{0, 0, 0, 0};
   }
   // the Q fragment is used in every chunk: wait for it here, once
   asm volatile("" ::"v"(qsc), "v"(qf4[0]), "v"(qf4[1]), "v"(qf4[2]), "v"(qf4[3]));
@@ -828,9 +799,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   issue_fence();
   if (lowbit) {
     ks_load(2);
-    vs_load(1);
+    vs_load(0);
     k_dma(2, kbuf(2));
-    v_dma(1, vbuf(1));
+    v_dma(0, vbuf(0));
   }
   if (LINES && n_line > 0) {
     // ---- the vertical-line tile, first in the reference order: S^T[16
@@ -868,19 +839,34 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
                        static_cast<_Float16>(1.0f)};
     L = __builtin_amdgcn_mfma_f32_16x16x16f16(ones4, ph, L, 0, 0, 0);
   }
-  int vslot = 0;  // V buffer of chunk ch
+  // integer tile references of an unmasked all-low-bit chunk from the partial
+  // maxima of its scores; O's reference follows when it lags too far
+  auto hot_refs = [&]() {
+    hm0 = fmaxf(m_run, ceilf(rowmax4(mxa) * c));
+    hm1 = fmaxf(hm0, ceilf(rowmax4(mxb) * c));
+    m_run = hm1;
+    chunk_lag(hm0, hm1);
+  };
+  int vslot = 0;    // V buffer of chunk ch
+  int vslot_p = 0;  // V buffer of the pending chunk (none yet: P = 0 reads a filled buffer)
+  if (lowbit) {     // chunk 0's FP4 scores (K chunks 0 and 1 are in place)
+    qk_lowbit(kbuf(0), S);
+#pragma unroll
+    for (int beta = 0; beta < 8; ++beta) s_max(beta);
+  } else {          // every tile is FP16 and rewrites its blocks
+#pragma unroll
+    for (int beta = 0; beta < 8; ++beta) S[beta] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+  }
+  if (n_chunks > 0 && is_hot(0, f_cur)) hot_refs();
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int kc = ch * 128;
     const bool valid1 = 2 * ch + 1 <= last_tile;
     const int vslot1 = vslot == LY::RV - 1 ? 0 : vslot + 1;
-    const int vslot2 = vslot1 == LY::RV - 1 ? 0 : vslot1 + 1;
-    const uint8_t* kb = kbuf(ch);
-    const uint8_t* vb = vbuf(vslot);
     const int f_nn = ch + 2 < n_chunks ? chunk_flags(ch + 2) : 0;
     if (lowbit) {
       ks_store(kbuf(ch + 2));
-      vs_store(vbuf(vslot1));
+      vs_store(vbuf(vslot));
       __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
     } else {
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -902,32 +888,21 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     issue_fence();
     if (lowbit) {
       ks_load(ch + 3);
-      vs_load(ch + 2);
+      vs_load(ch + 1);
       k_dma(ch + 3, kbuf(ch + 3));
-      v_dma(ch + 2, vbuf(vslot2));
+      v_dma(ch + 1, vbuf(vslot1));
     }
     issue_fence();
-    const bool hot = is_hot(ch, f_cur);
-    const int t_first = (f_cur & 4) ? 0 : 1;  // first tile some wave promotes
-    v8i pb = {0, 0, 0, 0, 0, 0, 0, 0};  // P of chunk ch's low-bit PV (0: nothing to add)
-    int psc = 0;
-    bool nxt = false;                   // S now holds the next hot chunk's scores
 
-    if (hot) {
-      // ================= hot path: both tiles low-bit for every wave, no masks
-      if (!s_ready) {
-        qk_lowbit(kb, S);
-        chunk_refs(S, hm0, hm1);
-      }
-      nxt = ch + 1 < n_chunks && is_hot(ch + 1, f_nxt);
-      if (nxt) hot_exp_next(kbuf(ch + 1), pb);
-      else hot_exp(pb);
-      psc = p_scale();
-    } else {
+    if (!is_hot(ch, f_cur)) {
+      // (a chunk with both tiles low-bit for every wave and no masks had its
+      // tile references set at the end of the previous iteration)
+      // ================= masks, FP16 tiles, line keys, a lone last tile: the
+      // S blocks are rewritten tile by tile (masked keys and FP16 tiles -inf)
       const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
       const bool has_line = LINES && (f_cur & 64);  // line keys run in the line tile, not here
-      // ================= general path: masks, FP16 tiles, line keys, a lone last tile
       const bool low_w = !(f_cur & 1) || (valid1 && !(f_cur & 2));  // this wave runs FP8 PV
+      const int t_first = (f_cur & 4) ? 0 : 1;  // first tile some wave promotes
       float m_tile0 = NEG_INF;
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
@@ -948,7 +923,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
             lds_barrier();
           }
         }
-        v4f S[4];
+        v4f St[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) St[bb] = t ? S[4 + bb] : S[bb];
         if (prom) {
           v8bf qb[NSB];
 #pragma unroll
@@ -959,19 +936,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
             for (int bb = 0; bb < 4; ++bb) {
               const int key = 16 * (col >> 2) + 4 * bb + (col & 3);
               const v8bf ka = *reinterpret_cast<const v8bf*>(sm + LY::hk_off(key, 4 * st + g));
-              S[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : S[bb], 0, 0, 0);
+              St[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : St[bb], 0, 0, 0);
             }
-          }
-        } else {
-          const uint32_t kscw = reinterpret_cast<const uint32_t*>(kb + ksoff)[t];
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-            const v4i w = *reinterpret_cast<const v4i*>(kb + (t ? koff(4 + bb) : koff(bb)));
-            ka[0] = w[0]; ka[1] = w[1]; ka[2] = w[2]; ka[3] = w[3];
-            const int sc = static_cast<int>(kscw >> (8 * bb)) & 0xFF;
-            S[bb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf4, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
-                                                                       sc, 0, qsc);
           }
         }
         if (need_mask) {
@@ -981,7 +947,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
             for (int i = 0; i < 4; ++i) {
               const int key = kc + 64 * t + 16 * g + 4 * bb + i;
               const bool ok = key < a.n_valid && q < a.n_valid && (!a.causal || key <= q);
-              if (!ok) S[bb][i] = NEG_INF;
+              if (!ok) St[bb][i] = NEG_INF;
             }
         }
         if (has_line) {  // bit 4bb + i: key kc + 64t + 16g + 4bb + i is a line key
@@ -990,16 +956,15 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
           for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if ((lm >> (4 * bb + i)) & 1u) S[bb][i] = NEG_INF;
+              if ((lm >> (4 * bb + i)) & 1u) St[bb][i] = NEG_INF;
         }
         float mx = NEG_INF;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) mx = fmaxf(fmaxf(mx, fmaxf(S[bb][0], S[bb][1])), fmaxf(S[bb][2], S[bb][3]));
+        for (int bb = 0; bb < 4; ++bb) mx = fmaxf(fmaxf(mx, fmaxf(St[bb][0], St[bb][1])), fmaxf(St[bb][2], St[bb][3]));
         mx = rowmax4(mx);
         const float m_t = fmaxf(m_run, ceilf(mx * c));
         m_run = m_t;
         if (t == 0) m_tile0 = m_t;
-        const float m_safe = m_t == NEG_INF ? 0.0f : m_t;
         if (prom) {
           // P relative to O's reference m_o <= m_t: the same fp16 values scaled
           // by 2^(m_t - m_o) (exact while normal), so O needs no rescale unless
@@ -1012,7 +977,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
             v8h ph;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * st + (e >> 2)][e & 3], c, -m_ref)));
+              ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(St[2 * st + (e >> 2)][e & 3], c, -m_ref)));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
               const v8h va = *reinterpret_cast<const v8h*>(sm + LY::HV_OFF + LY::vrow_off(16 * db + col, 2 * g + st));
@@ -1021,38 +986,51 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
             const v8h ones16 = __builtin_bit_cast(v8h, v4i{kOne16, kOne16, kOne16, kOne16});
             L = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones16, ph, L, 0, 0, 0);
           }
-        } else {
-          const float off = kGridMagic + kExpOffset - m_safe;
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            float y[4];
+          for (int bb = 0; bb < 4; ++bb) St[bb] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};  // no low-bit P
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[bb][i], c, off) - kGridMagic);
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-            pb[4 * t + bb] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-          }
+        for (int bb = 0; bb < 4; ++bb) {
+          if (t) S[4 + bb] = St[bb];
+          else S[bb] = St[bb];
         }
       }
+      if (!valid1) {  // a lone last tile: the second one adds nothing
+#pragma unroll
+        for (int bb = 4; bb < 8; ++bb) S[bb] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+      }
+      // tile references of the low-bit P: each tile's running maximum
+      hm0 = m_tile0;
+      hm1 = m_run;
       if (low_w) {
-        // as in the hot path: each tile's P enters through the E8M0 scale
+        // as for unmasked chunks: each tile's P enters through the E8M0 scale
         // 2^-8 * 2^(m_t - m_o); O is rescaled only when the lag grows large
         if (m_o == NEG_INF) m_o = m_run;
         else if (__any(m_run - m_o > kMaxLag)) rebase(m_run);
-        const float mt = g < 2 ? m_tile0 : m_run;
-        // a tile with no valid key for this row adds nothing (psc 0 with pb 0)
-        if (mt != NEG_INF && m_o != NEG_INF)
-          psc = static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + (mt - m_o), 0.0f), 254.0f));
       }
     }
-    pv_chunk(vb, pb, psc, nxt);
-    s_ready = nxt;
+    // ================= the pipeline step: P of chunk ch, QK of chunk ch+1, PV of chunk ch-1
+    v8i pb;
+    pipe(kbuf(ch + 1), vbuf(vslot_p), pend_scale(), pb);
+    pb_p = pb;
+    hp0 = hm0;
+    hp1 = hm1;
+    vslot_p = vslot;
+    // next chunk unmasked and all low-bit: its integer tile references from
+    // the partial maxima of the scores just issued (after this chunk's PV, so
+    // that a rebase of O is the last update of the iteration)
+    if (ch + 1 < n_chunks && is_hot(ch + 1, f_nxt)) hot_refs();
     f_cur = f_nxt;
     f_nxt = f_nn;
     vslot = vslot1;
     hi_ready = hi_next_ready;
   }
-  // no copy may still be landing when the workgroup's LDS is handed on
+  // no copy may still be landing when the workgroup's LDS is handed on; the
+  // last chunk's V codes (copied in the previous iteration by every wave) are
+  // published by this barrier for the last PV
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  pv_flush(vbuf(vslot_p), pend_scale());
 
   // ---------------------------------------------------------------- epilogue
   // out = O / l is independent of the reference; lse uses O's reference m_o
