@@ -126,9 +126,10 @@ __device__ __forceinline__ float rowmax4(float v) {
 //  V buffer: FP8 V^T rows (one per head_dim element, 128 keys = 8 units), unit u
 //    of row d stored at u ^ ((d >> 1) & 7); then the V scales, byte
 //    [g][col][db] = scale of key block g of row 16*db+col.
-//  FP16 tile (64 keys): bf16 K rows of 2*D bytes, unit index XOR-swizzled by 4
-//    key bits; fp16 V^T rows of 128 bytes swizzled like the FP8 V rows.
-//  bf16 Q of the workgroup's 128 rows (read by the FP16 tiles' QK), loaded once.
+//  FP16 stages, one per tile of a chunk (64 keys each): bf16 K rows of 2*D
+//    bytes, unit index XOR-swizzled by 4 key bits; fp16 V^T rows of 128 bytes
+//    swizzled like the FP8 V rows.  (The bf16 Q the FP16 tiles multiply stays
+//    in registers: each lane needs only its own row's slices.)
 //  Vertical lines: bf16 K rows of the 16 line entries (swizzled like Q) and
 //    their fp16 V as [d][entry], loaded once.
 template <int D>
@@ -142,10 +143,10 @@ struct Lds {
   static constexpr int V_BYTES = VS_IN + 512;
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = K_OFF + RK * K_BYTES;
-  static constexpr int HK_OFF = V_OFF + RV * V_BYTES;     // bf16 K tile
-  static constexpr int HV_OFF = HK_OFF + 64 * 2 * D;      // fp16 V^T tile
-  static constexpr int Q_OFF = HV_OFF + D * 128;          // bf16 Q tile of the workgroup
-  static constexpr int LK_OFF = Q_OFF + 128 * 2 * D;      // bf16 K rows of the line entries
+  static constexpr int HK_OFF = V_OFF + RV * V_BYTES;     // FP16 stage 0: bf16 K tile
+  static constexpr int HV_OFF = HK_OFF + 64 * 2 * D;      //   and fp16 V^T tile
+  static constexpr int STAGE = 64 * 2 * D + D * 128;      // bytes per FP16 stage (stage t: tile t of a chunk)
+  static constexpr int LK_OFF = HK_OFF + 2 * STAGE;       // bf16 K rows of the line entries
   static constexpr int LV_OFF = LK_OFF + kMaxLines * 2 * D;  // fp16 V of the lines, [d][entry]
   static constexpr int BYTES = LV_OFF + D * kMaxLines * 2;
   // K codes of (key, 16-byte unit g) inside a K buffer
@@ -165,10 +166,6 @@ struct Lds {
   }
   __device__ static __forceinline__ int hk_off(int key, int cidx) {  // key in [0,64)
     return HK_OFF + key * 2 * D + 16 * (cidx ^ hk_swz(key));
-  }
-  // bf16 Q row r, 16-byte unit u (8 head_dim elements), XOR-swizzled by the row
-  __device__ static __forceinline__ int q_off(int r, int u) {
-    return Q_OFF + r * 2 * D + 16 * (u ^ (r & (D / 8 - 1)));
   }
   __device__ static __forceinline__ int lk_off(int e, int u) {
     return LK_OFF + e * 2 * D + 16 * (u ^ (e & (D / 8 - 1)));
@@ -409,21 +406,21 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         vb[LY::VS_IN + (kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(pvs >> (8 * kb));
     }
   };
-  // FP16 tile (64 keys from kt0) -> the stage: bf16 K rows and fp16 V^T rows
-  auto fp16_dma = [&](int kt0) {
+  // FP16 tile (64 keys from kt0) -> stage t: bf16 K rows and fp16 V^T rows
+  auto fp16_dma = [&](int kt0, int t) {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {  // bf16 K: 2*D bytes per key
       const int blk = i * 8 + wave;
       const int o = blk * 1024 + 16 * lane;
       const int key = o / (2 * D), cu = (o % (2 * D)) / 16;
-      dma16(r_hk, sm + LY::HK_OFF + 1024 * blk, (kt0 + key) * 2 * D + 16 * (cu ^ LY::hk_swz(key)));
+      dma16(r_hk, sm + LY::HK_OFF + t * LY::STAGE + 1024 * blk, (kt0 + key) * 2 * D + 16 * (cu ^ LY::hk_swz(key)));
     }
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {  // fp16 V^T: 128 bytes per row
       const int blk = i * 8 + wave;
       const int d = blk * 8 + (lane >> 3);
       const int u = (lane & 7) ^ ((d >> 1) & 7);
-      dma16(r_hv, sm + LY::HV_OFF + 1024 * blk, d * a.N * 2 + kt0 * 2 + 16 * u);
+      dma16(r_hv, sm + LY::HV_OFF + t * LY::STAGE + 1024 * blk, d * a.N * 2 + kt0 * 2 + 16 * u);
     }
   };
 
@@ -685,15 +682,15 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb_p, L, 0, 0, 0, 127, 0, pscp);
   };
 
-  if (a.mode != MXQ_ALL_LOWBIT || LINES) {  // bf16 Q rows of the workgroup -> LDS (rows past N are never read)
-    constexpr int QU = 128 * D / 8;  // 16-byte units
-    static_assert(QU % NT == 0, "Q units must divide evenly");
+  // bf16 Q of this lane's row, head_dim elements 32 st + 8 g .. +7: the B
+  // operand of the bf16 QK MFMAs of FP16 tiles and of the line tile
+  v8bf qbr[NSB];
 #pragma unroll
-    for (int i = 0; i < QU / NT; ++i) {
-      const int u = tid + i * NT;
-      *reinterpret_cast<v4i*>(sm + LY::q_off(u / (D / 8), u % (D / 8))) =
-          *reinterpret_cast<const v4i*>(a.q_bf16 + (bhq * a.N + qs + u / (D / 8)) * D + 8 * (u % (D / 8)));
-    }
+  for (int st = 0; st < NSB; ++st) qbr[st] = v8bf{};
+  if (a.mode != MXQ_ALL_LOWBIT || LINES) {
+#pragma unroll
+    for (int st = 0; st < NSB; ++st)
+      qbr[st] = *reinterpret_cast<const v8bf*>(a.q_bf16 + (bhq * a.N + q) * D + 8 * (4 * st + g));
   }
   // per chunk: bits 0-1 row ra, 2-3 row rb, 4 the chunk holds a line key,
   // 8-11 its slot in s_lm
@@ -764,6 +761,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   }
   // the Q fragment is used in every chunk: wait for it here, once
   asm volatile("" ::"v"(qsc), "v"(qf4[0]), "v"(qf4[1]), "v"(qf4[2]), "v"(qf4[3]));
+#pragma unroll
+  for (int st = 0; st < NSB; ++st) asm volatile("" ::"v"(qbr[st]));
   __syncthreads();  // s_fl and the constant LDS words are written
   int f_cur = chunk_flags(0);
   int f_nxt = n_chunks > 1 ? chunk_flags(1) : 0;
@@ -789,12 +788,16 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // FP16 tile of chunk 0, then iteration -1's regular loads
-  bool hi_ready = false;  // the FP16 stage holds chunk ch's first promoted tile
+  // FP16 tiles of chunk 0, then iteration -1's regular loads
+  int hi_rdy = 0;  // bit t: stage t holds chunk ch's tile t
   issue_fence();
-  if (hibit && ((f_cur >> 2) & 3)) {
-    fp16_dma(64 * ((f_cur & 4) ? 0 : 1));
-    hi_ready = true;
+  if (hibit) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if ((f_cur >> (2 + t)) & 1) {
+        fp16_dma(64 * t, t);
+        hi_rdy |= 1 << t;
+      }
   }
   issue_fence();
   if (lowbit) {
@@ -812,8 +815,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 #pragma unroll
     for (int st = 0; st < NSB; ++st) {
       const v8bf ka = *reinterpret_cast<const v8bf*>(sm + LY::lk_off(col, 4 * st + g));
-      const v8bf qb = *reinterpret_cast<const v8bf*>(sm + LY::q_off(wave * 16 + col, 4 * st + g));
-      SL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, SL, 0, 0, 0);
+      SL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbr[st], SL, 0, 0, 0);
     }
     float mx = NEG_INF;
 #pragma unroll
@@ -872,19 +874,20 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     lds_barrier();
-    // FP16 tile issue: chunk ch's first promoted tile if it is not staged yet
-    // (the stage's previous users finished before this barrier), else chunk
-    // ch+1's when chunk ch leaves the stage alone
-    const bool hi_cur = (f_cur >> 2) & 3;
-    const bool hi_nxt = ch + 1 < n_chunks && ((f_nxt >> 2) & 3);
-    bool hi_next_ready = false;
-    if (hibit && hi_cur && !hi_ready) {
-      fp16_dma(kc + 64 * ((f_cur & 4) ? 0 : 1));
-    } else if (hibit && !hi_cur && hi_nxt) {
-      fp16_dma(kc + 128 + 64 * ((f_nxt & 4) ? 0 : 1));
-      hi_next_ready = true;
+    // FP16 tile issue, stage t for tile t: chunk ch's promoted tiles not staged
+    // yet, and chunk ch+1's where chunk ch leaves the stage alone (a stage's
+    // previous users finished before this barrier)
+    // (f_nxt is 0 past the last chunk)
+    const int pc = hibit ? (f_cur >> 2) & 3 : 0;
+    const int hi_now = pc & ~hi_rdy;                            // issued just now: waited for before use
+    const int hi_rdy_next = hibit ? ((f_nxt >> 2) & 3) & ~pc : 0;  // prefetched for chunk ch+1
+    if (hi_now | hi_rdy_next) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if ((hi_now >> t) & 1) fp16_dma(kc + 64 * t, t);
+        else if ((hi_rdy_next >> t) & 1) fp16_dma(kc + 128 + 64 * t, t);
+      }
     }
-    const bool hi_wait = hibit && hi_cur && !hi_ready;  // issued just now
     issue_fence();
     if (lowbit) {
       ks_load(ch + 3);
@@ -902,41 +905,29 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       const bool need_mask = (kc + 127 >= a.n_valid) || (a.causal && kc + 127 > wq_lo) || (qe < qs + BQ - 1);
       const bool has_line = LINES && (f_cur & 64);  // line keys run in the line tile, not here
       const bool low_w = !(f_cur & 1) || (valid1 && !(f_cur & 2));  // this wave runs FP8 PV
-      const int t_first = (f_cur & 4) ? 0 : 1;  // first tile some wave promotes
       float m_tile0 = NEG_INF;
+      if (hi_now) {  // FP16 tiles issued after this chunk's barrier: let them land, then publish
+        // (a chunk with a promoted tile is masked-path for every wave)
+        if (lowbit) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+      }
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (t == 1 && !valid1) break;
-        const bool prom = (f_cur >> t) & 1;            // this wave's tile t is FP16
-        const bool stage_hi = (f_cur >> (2 + t)) & 1;  // some wave's tile t is FP16
-        if (stage_hi) {
-          if (t == t_first) {
-            if (hi_wait) {  // issued after this chunk's barrier: let it land, then publish
-              if (lowbit) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
-              else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-              lds_barrier();
-            }
-          } else {  // the second promoted tile: every wave is done with the first
-            lds_barrier();
-            fp16_dma(kc + 64 * t);
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
-          }
-        }
+        const bool prom = (f_cur >> t) & 1;  // this wave's tile t is FP16 (in stage t)
+        uint8_t* const stg = sm + t * LY::STAGE;
         v4f St[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) St[bb] = t ? S[4 + bb] : S[bb];
         if (prom) {
-          v8bf qb[NSB];
-#pragma unroll
-          for (int st = 0; st < NSB; ++st) qb[st] = *reinterpret_cast<const v8bf*>(sm + LY::q_off(wave * 16 + col, 4 * st + g));
 #pragma unroll
           for (int st = 0; st < NSB; ++st) {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
               const int key = 16 * (col >> 2) + 4 * bb + (col & 3);
-              const v8bf ka = *reinterpret_cast<const v8bf*>(sm + LY::hk_off(key, 4 * st + g));
-              St[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : St[bb], 0, 0, 0);
+              const v8bf ka = *reinterpret_cast<const v8bf*>(stg + LY::hk_off(key, 4 * st + g));
+              St[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbr[st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : St[bb], 0, 0, 0);
             }
           }
         }
@@ -980,7 +971,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
               ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(St[2 * st + (e >> 2)][e & 3], c, -m_ref)));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              const v8h va = *reinterpret_cast<const v8h*>(sm + LY::HV_OFF + LY::vrow_off(16 * db + col, 2 * g + st));
+              const v8h va = *reinterpret_cast<const v8h*>(stg + LY::HV_OFF + LY::vrow_off(16 * db + col, 2 * g + st));
               O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
             }
             const v8h ones16 = __builtin_bit_cast(v8h, v4i{kOne16, kOne16, kOne16, kOne16});
@@ -1023,7 +1014,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     f_cur = f_nxt;
     f_nxt = f_nn;
     vslot = vslot1;
-    hi_ready = hi_next_ready;
+    hi_rdy = hi_rdy_next;
   }
   // no copy may still be landing when the workgroup's LDS is handed on; the
   // last chunk's V codes (copied in the previous iteration by every wave) are
