@@ -330,7 +330,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // ---- staging.  Buffer resources (built above) over this (batch, kv
   // head)'s slices: reads past a slice return zeros instead of faulting.
   const bool lowbit = a.mode != MXQ_ALL_FP16;  // low-bit operands exist
-  const bool hibit = a.mode != MXQ_ALL_LOWBIT;  // FP16 operands exist
   const auto r_kc = rsrc(a.k_codes, bhk * a.N * KROW, static_cast<int64_t>(a.N) * KROW);
   const auto r_ks = rsrc(a.k_scales, bhk * a.N * NSB, static_cast<int64_t>(a.N) * NSB);
   const auto r_vc = rsrc(a.v_codes, bhk * D * a.N, static_cast<int64_t>(D) * a.N);
@@ -692,9 +691,10 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     for (int st = 0; st < NSB; ++st)
       qbr[st] = *reinterpret_cast<const v8bf*>(a.q_bf16 + (bhq * a.N + q) * D + 8 * (4 * st + g));
   }
-  // per chunk: bits 0-1 row ra, 2-3 row rb, 4 the chunk holds a line key,
-  // 8-11 its slot in s_lm
-  using FlagT = typename std::conditional<LINES, uint16_t, uint8_t>::type;
+  // per chunk, the decoded flags (see chunk_flags) of the waves on mask row ra
+  // in the low half and of those on row rb in the high half
+  using FlagT = typename std::conditional<LINES, uint32_t, uint16_t>::type;
+  constexpr int kFlShift = LINES ? 16 : 8;
   __shared__ FlagT s_fl[kMaxChunks];
   // per slot and lane group g: the group's line keys in the chunk, bit
   // 16t + (key & 15) for key = chunk start + 64t + 16g + (key & 15)
@@ -710,7 +710,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     }
     const uint32_t wa = ch == tid ? mw_a : mask_word(mrow_a, ch);
     const uint32_t wb = ch == tid ? mw_b : mask_word(mrow_b, ch);
-    s_fl[ch] = static_cast<FlagT>(row_flags(wa, ch) | (row_flags(wb, ch) << 2) | add);
+    // bits 0-1 this wave's promoted tiles, 2-3 any wave's, 4-5 every wave's,
+    // 6 a line key in the chunk, 8-11 the chunk's line slot
+    const int fa = row_flags(wa, ch), fb = row_flags(wb, ch);
+    const int common = ((fa | fb) << 2) | ((fa & fb) << 4) | ((add & 16) << 2) | (add & 0xF00);
+    s_fl[ch] = static_cast<FlagT>((fa | common) | ((fb | common) << kFlShift));
   }
   // the line tile's keys: entries 4g..4g+3 of this lane's rows
   int lkey4[4] = {-1, -1, -1, -1};
@@ -736,16 +740,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       *reinterpret_cast<uint2*>(sm + LY::LV_OFF + (vd * kMaxLines + ve0) * 2) =
           make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
   }
-  // packed: bits 0-1 this wave, 2-3 any wave, 4-5 every wave, 6 a line key
-  // in the chunk, 8-11 the chunk's line slot
-  auto chunk_flags = [&](int ch) -> int {
-    const int v = __builtin_amdgcn_readfirstlane(static_cast<int>(s_fl[ch]));
-    const int fa = v & 3, fb = (v >> 2) & 3;
-    if constexpr (LINES)
-      return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4) | ((v & 16) << 2) | (v & 0xF00);
-    else
-      return (w_in_b ? fb : fa) | ((fa | fb) << 2) | ((fa & fb) << 4);
+  // this wave's half of a chunk's flags
+  const int fl_shift = w_in_b ? kFlShift : 0;
+  auto fl_decode = [&](int raw) -> int {
+    return (__builtin_amdgcn_readfirstlane(raw) >> fl_shift) & ((1 << kFlShift) - 1);
   };
+  auto chunk_flags = [&](int ch) -> int { return fl_decode(static_cast<int>(s_fl[ch])); };
 
   if (lowbit) {
     pks = pks0;
@@ -766,6 +766,10 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   __syncthreads();  // s_fl and the constant LDS words are written
   int f_cur = chunk_flags(0);
   int f_nxt = n_chunks > 1 ? chunk_flags(1) : 0;
+  // chunk ch+2's flags word, read from LDS one iteration before it is decoded
+  // (so that no iteration waits for that read); entries past the chunks are
+  // never decoded
+  int fl_raw = static_cast<int>(s_fl[min(2, kMaxChunks - 1)]);
 
   // Staging schedule (K ring of 4, V ring of 3, one barrier per chunk).
   // Iteration ch, after its barrier, issues (in this order): the FP16 tile of
@@ -791,14 +795,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // FP16 tiles of chunk 0, then iteration -1's regular loads
   int hi_rdy = 0;  // bit t: stage t holds chunk ch's tile t
   issue_fence();
-  if (hibit) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      if ((f_cur >> (2 + t)) & 1) {
-        fp16_dma(64 * t, t);
-        hi_rdy |= 1 << t;
-      }
-  }
+  for (int t = 0; t < 2; ++t)
+    if ((f_cur >> (2 + t)) & 1) {
+      fp16_dma(64 * t, t);
+      hi_rdy |= 1 << t;
+    }
   issue_fence();
   if (lowbit) {
     ks_load(2);
@@ -865,7 +867,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     const int kc = ch * 128;
     const bool valid1 = 2 * ch + 1 <= last_tile;
     const int vslot1 = vslot == LY::RV - 1 ? 0 : vslot + 1;
-    const int f_nn = ch + 2 < n_chunks ? chunk_flags(ch + 2) : 0;
+    const int f_nn = ch + 2 < n_chunks ? fl_decode(fl_raw) : 0;
+    fl_raw = static_cast<int>(s_fl[min(ch + 3, kMaxChunks - 1)]);
     if (lowbit) {
       ks_store(kbuf(ch + 2));
       vs_store(vbuf(vslot));
@@ -877,10 +880,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     // FP16 tile issue, stage t for tile t: chunk ch's promoted tiles not staged
     // yet, and chunk ch+1's where chunk ch leaves the stage alone (a stage's
     // previous users finished before this barrier)
-    // (f_nxt is 0 past the last chunk)
-    const int pc = hibit ? (f_cur >> 2) & 3 : 0;
-    const int hi_now = pc & ~hi_rdy;                            // issued just now: waited for before use
-    const int hi_rdy_next = hibit ? ((f_nxt >> 2) & 3) & ~pc : 0;  // prefetched for chunk ch+1
+    // (the flags promote no tile when there are no FP16 operands; f_nxt is 0
+    // past the last chunk)
+    const int pc = (f_cur >> 2) & 3;
+    const int hi_now = pc & ~hi_rdy;                  // issued just now: waited for before use
+    const int hi_rdy_next = ((f_nxt >> 2) & 3) & ~pc;  // prefetched for chunk ch+1
     if (hi_now | hi_rdy_next) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
