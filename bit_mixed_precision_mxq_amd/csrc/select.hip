@@ -12,6 +12,8 @@
 //                 top-k by rank counting with ties to the lower index.
 // The fixed operation order makes the result bit-identical to a plain CPU
 // evaluation of the same formula.
+#include <algorithm>
+
 #include "mxq_internal.h"
 
 // Every product and sum in this file is rounded on its own, as written: with
@@ -64,6 +66,7 @@ struct SelectArgs {
   int Hq, Hkv, N, n_valid, D, Bq, Bk, causal, n_qt, n_kt, words;
   int topk, ratio_num, ratio_den, sink_tiles, local_tiles;
   int B;
+  int score_free;  // no tile is chosen by score and none is reported: skip the scores
 };
 
 // One wave per (batch, query head, query tile), four per workgroup, with no
@@ -90,34 +93,36 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
   float* sc = s_score[wave];
   float* sq = s_q[wave];
 
-  for (int d = lane; d < D; d += 64) sq[d] = a.qmean[(bhq * a.n_qt + i) * D + d];
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, read by every lane
+  if (!a.score_free) {
+    for (int d = lane; d < D; d += 64) sq[d] = a.qmean[(bhq * a.n_qt + i) * D + d];
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, read by every lane
 
-  // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
-  const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
-  const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
-  const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
-  const auto r_km = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
-      __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
-  // scores of every key tile (also invalid ones, for inspection)
-  for (int j = lane; j < a.n_kt; j += 64) {
-    float acc = 0.0f;
-    constexpr int C = 64;  // loads in flight per round trip
+    // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
+    const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
+    const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
+    const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
+    const auto r_km = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
+        __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
+    // scores of every key tile (also invalid ones, for inspection)
+    for (int j = lane; j < a.n_kt; j += 64) {
+      float acc = 0.0f;
+      constexpr int C = 64;  // loads in flight per round trip
 #pragma unroll
-    for (int d0 = 0; d0 < D; d0 += C) {
-      float kv[C];
+      for (int d0 = 0; d0 < D; d0 += C) {
+        float kv[C];
 #pragma unroll
-      for (int d = 0; d < C; ++d)
-        kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
+        for (int d = 0; d < C; ++d)
+          kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
 #pragma unroll
-      for (int d = 0; d < C; ++d) acc = acc + sq[d0 + d] * kv[d];  // two roundings: contraction is off here
-      __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
+        for (int d = 0; d < C; ++d) acc = acc + sq[d0 + d] * kv[d];  // two roundings: contraction is off here
+        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
+      }
+      sc[j] = acc;
+      if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
     }
-    sc[j] = acc;
-    if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
-  }
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }  // (score_free: the budget below is 0, so no score is ever read)
 
   uint32_t* mrow = a.mask + (bhq * a.n_qt + i) * a.words;
   const int qs = i * a.Bq;
@@ -188,6 +193,15 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
 // ascending order and divided once; score of key j: probe . k_j, fp32, d
 // ascending, rounded product then rounded sum.
 constexpr int kMaxLines = 16;
+
+// line lists made of the first n_first keys only: entry e = e, then -1
+__global__ void __launch_bounds__(256) k_lines_first(int32_t* __restrict__ lines, int total, int n_lines,
+                                                     int n_first) {
+  const int idx = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+  if (idx >= total) return;
+  const int e = idx % n_lines;
+  lines[idx] = e < n_first ? e : -1;
+}
 
 struct LineArgs {
   const float* qmean;   // [B*Hq][n_qt][D]
@@ -371,12 +385,17 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
   const int n_qt = s->N / s->Bq, n_kt = s->N / s->Bk;
   float* qmean = static_cast<float*>(workspace);
   float* kmean = qmean + static_cast<size_t>(s->B) * s->Hq * n_qt * s->D;
-  hipLaunchKernelGGL(k_tile_means, dim3(n_qt, s->B * s->Hq), dim3(s->D), 0, strm, q, qmean, s->N,
-                     s->D, s->Bq, s->n_valid, n_qt, 0);
-  if ((st = check_launch("k_tile_means(q)")) != MXQ_OK) return st;
-  hipLaunchKernelGGL(k_tile_means, dim3(n_kt, s->B * s->Hkv), dim3(s->D), 0, strm, k, kmean, s->N,
-                     s->D, s->Bk, s->n_valid, n_kt, 1);
-  if ((st = check_launch("k_tile_means(k)")) != MXQ_OK) return st;
+  // a zero budget chooses only the forced tiles: without a score request the
+  // scores (and the tile means behind them) are not needed
+  const bool score_free = scores == nullptr && (p->topk == 0 || (p->topk < 0 && p->ratio_num == 0));
+  if (!score_free) {
+    hipLaunchKernelGGL(k_tile_means, dim3(n_qt, s->B * s->Hq), dim3(s->D), 0, strm, q, qmean, s->N,
+                       s->D, s->Bq, s->n_valid, n_qt, 0);
+    if ((st = check_launch("k_tile_means(q)")) != MXQ_OK) return st;
+    hipLaunchKernelGGL(k_tile_means, dim3(n_kt, s->B * s->Hkv), dim3(s->D), 0, strm, k, kmean, s->N,
+                       s->D, s->Bk, s->n_valid, n_kt, 1);
+    if ((st = check_launch("k_tile_means(k)")) != MXQ_OK) return st;
+  }
   SelectArgs a;
   a.qmean = qmean; a.kmean = kmean; a.mask = mask; a.n_fp16 = n_fp16; a.scores = scores;
   a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.D = s->D; a.Bq = s->Bq;
@@ -384,6 +403,7 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
   a.topk = p->topk; a.ratio_num = p->ratio_num; a.ratio_den = p->ratio_den;
   a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
   a.B = s->B;
+  a.score_free = score_free ? 1 : 0;
   const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
   const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
   if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
@@ -415,6 +435,15 @@ extern "C" mxq_status attn_select_lines(const uint16_t* q, const uint16_t* k, co
   MXQ_REQUIRE(workspace != nullptr && ws_bytes >= attn_select_lines_workspace(s), MXQ_EINVAL,
               "attn_select_lines: workspace too small");
   hipStream_t strm = as_stream(stream);
+  // every line is a sink token when the list has no room for a scored key (or
+  // no key is left to score): without a score request, write it directly
+  const int n_first = std::min(std::min(p->sink_tokens, s->n_valid), p->n_lines);
+  if (scores == nullptr && (n_first == p->n_lines || n_first == s->n_valid)) {
+    const int total = s->B * s->Hq * p->n_lines;
+    hipLaunchKernelGGL(k_lines_first, dim3((total + 255) / 256), dim3(256), 0, strm, lines, total, p->n_lines,
+                       n_first);
+    return check_launch("k_lines_first");
+  }
   const int n_qt = s->N / s->Bq;
   float* qmean = static_cast<float*>(workspace);
   hipLaunchKernelGGL(k_tile_means, dim3(n_qt, s->B * s->Hq), dim3(s->D), 0, strm, q, qmean, s->N,

@@ -145,6 +145,9 @@ mxq_status mxq_prefill_operands(const uint16_t* q_bf16, const uint16_t* k_bf16, 
  * Outputs: mask u32 [B][Hq][N/Bq][ceil((N/Bk)/32)] (bit j%32 of word j/32 set
  * when key tile j is FP16 for that query tile); n_fp16 i32 [B][Hq][N/Bq] or
  * NULL; scores f32 [B][Hq][N/Bq][N/Bk] or NULL (every pair, for inspection).
+ * A zero budget (topk = 0, or topk < 0 with ratio_num = 0) promotes only the
+ * forced tiles; with scores NULL the scores are then not computed at all (the
+ * mask and counts are the same).
  * workspace: device memory of at least attn_select_blocks_workspace(shape)
  * bytes, caller-owned, contents undefined after the call.
  * ------------------------------------------------------------------------- */
@@ -170,6 +173,9 @@ mxq_status attn_select_blocks(const uint16_t* q_bf16, const uint16_t* k_bf16,
  * CPU evaluation of the same formula.
  * Outputs: lines i32 [B][Hq][n_lines] (rows of one kv group identical when
  * shared); scores f32 [B][Hq][N] or NULL (key scores, -inf for j >= n_valid).
+ * When no line is chosen by score (n_lines <= sink_tokens, or no valid key
+ * past the sink tokens) and scores is NULL, the list is written without
+ * computing any score (the same list).
  * n_lines in [0, 16] (0: nothing is written).  workspace: at least
  * attn_select_lines_workspace(shape) bytes, caller-owned, contents undefined
  * after the call.

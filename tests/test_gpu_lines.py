@@ -154,3 +154,28 @@ def test_llama8b_with_lines_sampled():
                                   qtiles=tiles, lines=lines[:, h:h + 1])
         rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
         _check(out[:, h:h + 1][..., rows, :], lse[:, h:h + 1][..., rows], ro[..., rows, :], rl[..., rows])
+
+
+# Lists with no room for a scored key (n_lines <= sink_tokens) or no key left to
+# score (n_valid <= sink_tokens): without a score request the library writes the
+# first keys directly; the lists must equal the oracle's and the scored path's.
+SINK_ONLY_CASES = [
+    # B, Hq, Hkv, N, D, n_valid, Bq, n_lines, sink
+    (3, 3, 3, 256, 64, 197, 64, 1, 1),      # ViT-shaped: the CLS token only
+    (2, 4, 2, 512, 128, 500, 128, 4, 6),    # more sink tokens than lines
+    (1, 2, 2, 128, 64, 3, 64, 8, 5),        # fewer valid keys than sink tokens
+]
+
+
+@pytest.mark.parametrize("case", SINK_ONLY_CASES)
+def test_select_lines_sink_only_without_scores(case):
+    mxq = gpu_or_skip()
+    B, Hq, Hkv, N, D, nv, Bq, n_lines, sink = case
+    q, k, _ = _inputs(B, Hq, Hkv, N, D, nv, seed=N + n_lines + sink)
+    shape = mxq.Shape(B, Hq, Hkv, N, nv, D, Bq, 64, False)
+    lines, scores = mxq.attn_select_lines(bf16_dev(q), bf16_dev(k), shape, n_lines, sink)
+    assert scores is None
+    rl, _ = S.select_lines(q, k, nv, Bq, n_lines, sink)
+    assert np.array_equal(lines.cpu().numpy(), rl)
+    scored, _ = mxq.attn_select_lines(bf16_dev(q), bf16_dev(k), shape, n_lines, sink, want_scores=True)
+    assert np.array_equal(scored.cpu().numpy(), rl)

@@ -76,3 +76,37 @@ def test_deterministic():
     a = _run(mxq, cfg)
     b = _run(mxq, cfg)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+# A zero budget (topk = 0, or a ratio of 0) chooses only the forced tiles: without
+# a score request the library skips the tile means and scores.  Masks and counts
+# must equal the oracle's and the scored path's.
+ZERO_BUDGET_CASES = [
+    # B, Hq, Hkv, N, D, n_valid, Bq, causal, topk, ratio_num, sink_tiles, local_tiles
+    (2, 4, 2, 1024, 128, 1000, 128, True, 0, 5, 1, 1),
+    (3, 6, 6, 256, 64, 197, 64, False, -1, 0, 0, 0),     # ViT-shaped: nothing promoted
+    (1, 4, 1, 640, 64, 577, 64, True, -1, 0, 2, 3),
+    (1, 2, 2, 512, 128, 130, 128, False, 0, 0, 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", ZERO_BUDGET_CASES)
+def test_zero_budget_without_scores(case):
+    mxq = gpu_or_skip()
+    B, Hq, Hkv, N, D, nv, Bq, causal, topk, rnum, sink, local = case
+    rng = np.random.default_rng(N + nv + Hq)
+    q = rng.standard_normal((B, Hq, N, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, N, D)).astype(np.float32)
+    q[:, :, nv:] = 0
+    k[:, :, nv:] = 0
+    cfg = dict(B=B, Hq=Hq, Hkv=Hkv, N=N, n_valid=nv, D=D, Bq=Bq, Bk=64, causal=causal, topk=topk,
+               ratio_num=rnum, ratio_den=100, sink_tiles=sink, local_tiles=local,
+               q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k))
+    mask, nfp, sc = _run(mxq, cfg, want_scores=False)
+    assert sc is None
+    rm, rn, _ = _ref(cfg)
+    assert np.array_equal(mask, rm)
+    assert np.array_equal(nfp, rn)
+    mask2, nfp2, _ = _run(mxq, cfg, want_scores=True)
+    assert np.array_equal(mask2, rm)
+    assert np.array_equal(nfp2, rn)
