@@ -653,6 +653,13 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) {
+      // wave priority falls over the step (3, 2, 1, 0 per quarter): of the two
+      // waves sharing a SIMD the one further behind wins the issue slot, so
+      // both reach the next barrier closer together
+      if (beta == 0) __builtin_amdgcn_s_setprio(3);
+      if (beta == 2) __builtin_amdgcn_s_setprio(2);
+      if (beta == 4) __builtin_amdgcn_s_setprio(1);
+      if (beta == 6) __builtin_amdgcn_s_setprio(0);
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
       pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
       __asm__ volatile("" ::"v"(pb[beta]));  // formed here, not where it is next read
