@@ -32,7 +32,8 @@ MXQ_MIXED, MXQ_ALL_LOWBIT, MXQ_ALL_FP16 = 0, 1, 2
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 
 EXPORTED = [
-    "mxq_quantize", "mxq_prefill_operands", "attn_select_blocks_workspace", "attn_select_blocks", "attn_select_lines_workspace",
+    "mxq_quantize", "mxq_prefill_operands", "mxq_prefill_operands_means", "attn_select_blocks_workspace",
+    "attn_select_blocks", "attn_select_blocks_means", "attn_select_lines_workspace",
     "attn_select_lines", "attn_mixed_fwd",
     "attn_quantkv_decode_workspace", "attn_quantkv_decode", "attn_quantkv_append", "mxq_status_string",
     "mxq_last_error", "mxq_version",
@@ -95,6 +96,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxq_quantize.restype = i32
     lib.mxq_prefill_operands.argtypes = [vp, vp, vp, ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mxq_prefill_operands.restype = i32
+    lib.mxq_prefill_operands_means.argtypes = [vp, vp, vp, ctypes.POINTER(AttnShape), vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp]
+    lib.mxq_prefill_operands_means.restype = i32
+    lib.attn_select_blocks_means.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(SelectParams), vp, vp,
+                                             vp, vp]
+    lib.attn_select_blocks_means.restype = i32
     lib.attn_select_blocks_workspace.argtypes = [ctypes.POINTER(AttnShape)]
     lib.attn_select_blocks_workspace.restype = sz
     lib.attn_select_blocks.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(SelectParams),
@@ -220,6 +227,26 @@ def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0
     return mask, nfp, scores
 
 
+def attn_select_blocks_means(q_means, k_means, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0,
+                             want_scores=False, mask=None, n_fp16=None):
+    """attn_select_blocks on tile means from prepare_prefill_means (same result)."""
+    _need_gpu(q_means, k_means)
+    n_qt, n_kt = shape.N // shape.Bq, shape.N // shape.Bk
+    words = (n_kt + 31) // 32
+    dev = q_means.device
+    assert q_means.dtype == k_means.dtype == torch.float32
+    assert q_means.numel() == shape.B * shape.Hq * n_qt * shape.D and k_means.numel() == shape.B * shape.Hkv * n_kt * shape.D
+    if mask is None:
+        mask = torch.empty((shape.B, shape.Hq, n_qt, words), dtype=torch.int32, device=dev)
+    nfp = n_fp16 if n_fp16 is not None else torch.empty((shape.B, shape.Hq, n_qt), dtype=torch.int32, device=dev)
+    scores = torch.empty((shape.B, shape.Hq, n_qt, n_kt), dtype=torch.float32, device=dev) if want_scores else None
+    sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles))
+    cs = shape.c()
+    _check(load_library().attn_select_blocks_means(_ptr(q_means), _ptr(k_means), ctypes.byref(cs), ctypes.byref(sp),
+                                                   _ptr(mask), _ptr(nfp), _ptr(scores), _stream()))
+    return mask, nfp, scores
+
+
 def lines_workspace(shape: Shape, device) -> torch.Tensor:
     n = load_library().attn_select_lines_workspace(ctypes.byref(shape.c()))
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
@@ -286,6 +313,37 @@ def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False, rotate=False)
     return ops
 
 
+def prepare_prefill_means(q, k, v, shape: Shape, out=None, means=None):
+    """prepare_prefill (no rotation) plus the tile means attn_select_blocks
+    scores with, from one read of Q and K (mxq_prefill_operands_means).
+    Returns (ops, q_means f32 [B,Hq,N/Bq,D], k_means f32 [B,Hkv,D,N/Bk]);
+    out (PrefillOperands) and means (a pair) may be passed in to be reused."""
+    _need_gpu(q, k, v)
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16 and q.dim() == k.dim() == v.dim() == 4
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    ops = out if out is not None else PrefillOperands(q_bf16=q, k_bf16=k)
+    ops.q_bf16, ops.k_bf16 = q, k
+    if ops.q_codes is None:
+        ops.q_codes = torch.empty((B, Hq, N, D // 2), dtype=torch.uint8, device=dev)
+        ops.q_scales = torch.empty((B, Hq, N, D // 32), dtype=torch.uint8, device=dev)
+        ops.k_codes = torch.empty((B, Hkv, N, D // 2), dtype=torch.uint8, device=dev)
+        ops.k_scales = torch.empty((B, Hkv, N, D // 32), dtype=torch.uint8, device=dev)
+        ops.v_codes = torch.empty((B, Hkv, D, N), dtype=torch.uint8, device=dev)
+        ops.v_scales = torch.empty((B, Hkv, D, N // 32), dtype=torch.uint8, device=dev)
+        ops.v_f16t = torch.empty((B, Hkv, D, N), dtype=torch.float16, device=dev)
+    if means is None:
+        means = (torch.empty((B, Hq, N // shape.Bq, D), dtype=torch.float32, device=dev),
+                 torch.empty((B, Hkv, D, N // shape.Bk), dtype=torch.float32, device=dev))
+    cs = shape.c()
+    _check(load_library().mxq_prefill_operands_means(
+        _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), _ptr(ops.q_codes), _ptr(ops.q_scales), _ptr(ops.k_codes),
+        _ptr(ops.k_scales), _ptr(ops.v_codes), _ptr(ops.v_scales), _ptr(ops.v_f16t), _ptr(means[0]), _ptr(means[1]),
+        _stream()))
+    return ops, means[0], means[1]
+
+
 def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, mode=MXQ_MIXED,
                    out_dtype=MXQ_OUT_F32, want_lse=True, out=None, lse=None, lines=None):
     """lines: int32 [B,Hq,n_lines] vertical-line keys (attn_select_lines) or None."""
@@ -307,14 +365,16 @@ def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, 
 
 
 class PrefillPipeline:
-    """One prefill step as a small DAG on two HIP streams (default priority).
-    Tile selection (and line selection) reads only bf16 Q and K and is bound
-    by latency, the quantisers are bound by HBM bandwidth: selection runs on
-    a second stream while Q, K and V are quantised on the caller's stream, and
-    the attention waits for both.  Workspaces and outputs are allocated once."""
+    """One prefill step.  When tiles are chosen by score (and Q/K are not
+    rotated), one chain on the caller's stream: the quantiser also writes the
+    tile means, selection scores them, then attention.  Otherwise a small DAG
+    on two HIP streams (default priority): selection (and line selection) reads
+    only bf16 Q and K and runs on a second stream while Q, K and V are
+    quantised on the caller's stream, and the attention waits for both.
+    Workspaces and outputs are allocated once."""
 
     def __init__(self, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0, n_lines=0,
-                 sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0"):
+                 sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0", fused_means=True):
         self.shape, self.topk, self.ratio = shape, topk, ratio
         self.sink_tiles, self.local_tiles = sink_tiles, local_tiles
         self.n_lines, self.sink_tokens, self.rotate, self.out_dtype = n_lines, sink_tokens, rotate, out_dtype
@@ -330,11 +390,35 @@ class PrefillPipeline:
         self.lse = torch.empty((shape.B, shape.Hq, shape.N), dtype=torch.float32, device=dev)
         self.aux = torch.cuda.Stream(device=dev)
         self.ev_in, self.ev_sel = torch.cuda.Event(), torch.cuda.Event()
+        # when tiles are chosen by score and Q/K are not rotated, the quantiser
+        # also writes the tile means and the step runs as one chain on the
+        # caller's stream (no cross-stream waits); a zero budget needs no
+        # scores, and its selection runs beside the quantisers instead
+        scored = topk > 0 or (topk < 0 and ratio[0] > 0)
+        self.fused = bool(fused_means) and not rotate and scored
+        self.ops = PrefillOperands() if self.fused else None
+        self.means = ((torch.empty((shape.B, shape.Hq, n_qt, shape.D), dtype=torch.float32, device=dev),
+                       torch.empty((shape.B, shape.Hkv, shape.D, n_kt), dtype=torch.float32, device=dev))
+                      if self.fused else None)
 
     def __call__(self, q, k, v, events=None):
         """Returns (out, lse).  events=(e0, e1) are recorded around the
         attention kernel on the caller's stream."""
         main = torch.cuda.current_stream()
+        if self.fused:
+            ops, qm, km = prepare_prefill_means(q, k, v, self.shape, out=self.ops, means=self.means)
+            attn_select_blocks_means(qm, km, self.shape, topk=self.topk, ratio=self.ratio, sink_tiles=self.sink_tiles,
+                                     local_tiles=self.local_tiles, mask=self.mask, n_fp16=self.nfp)
+            if self.n_lines:
+                attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
+                                  lines=self.lines)
+            if events is not None:
+                events[0].record(main)
+            attn_mixed_fwd(ops, self.mask, self.shape, out_dtype=self.out_dtype, out=self.out, lse=self.lse,
+                           lines=self.lines)
+            if events is not None:
+                events[1].record(main)
+            return self.out, self.lse
         self.ev_in.record(main)
         with torch.cuda.stream(self.aux):
             self.aux.wait_event(self.ev_in)

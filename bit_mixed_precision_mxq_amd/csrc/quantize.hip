@@ -5,6 +5,8 @@
 // reads each bf16 once and writes the codes once.  Rounding is done with
 // compares and integer bit operations so that every code is the exact
 // round-half-even of the exactly scaled input.
+#include <algorithm>
+
 #include "mxq_internal.h"
 
 // Every product and sum in this file is rounded on its own, as written: with
@@ -15,6 +17,33 @@
 
 namespace mxq {
 namespace {
+
+// One 32-element block of bf16 (16 words, element 2i in the low half of word
+// i) -> 16 bytes of E2M1 codes (two per byte, element 0 in the low nibble) and
+// its E8M0 scale code.
+__device__ __forceinline__ void mxfp4_block(const uint32_t (&w)[16], uint4& codes_out, uint8_t& scale_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+  }
+  int e = shared_exponent(amax, 2);
+  uint32_t packed[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t b = h ? (w[i] & 0xFFFF0000u) : (w[i] << 16);
+      float v = __builtin_ldexpf(__uint_as_float(b), -e);
+      uint32_t c = e2m1_mag_code(fabsf(v)) | ((b >> 28) & 8u);
+      int el = 2 * i + h;  // element index within the block
+      packed[el / 8] |= c << (4 * (el % 8));
+    }
+  }
+  codes_out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scale_out = static_cast<uint8_t>(e + 127);
+}
 
 // ---- MXFP4 along D: one thread per 32-element block ---------------------------
 // x [rows][D] bf16 -> codes [rows][D/2], scales [rows][D/32].  Consecutive
@@ -48,27 +77,64 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4_d(const uint16_t* __restric
     uint4 v = live ? src[i] : make_uint4(0, 0, 0, 0);
     w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
-    amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+  mxfp4_block(w, reinterpret_cast<uint4*>(codes)[blk], scales[blk]);
+}
+
+// ---- MXFP4 of Q and K plus their tile means in one pass ----------------------
+// One workgroup per (head, tile of T rows) of Q (grid x in [0, rows_q)) or K
+// (the rest): every 32-element block is quantised as in k_quant_mxfp4_d
+// and the bf16 tile is kept in LDS; then thread d sums column d over the
+// tile's valid rows in ascending order and divides once by their count, the
+// tile mean selection uses (the same operations as its own tile-mean pass, so
+// the same bits).  Q means are written [bh][tile][d], K means [bh][d][tile].
+template <int D>
+__global__ void __launch_bounds__(256) k_quant_mxfp4_tiles(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales, float* __restrict__ mean,
+                                                           int T, int n_tiles, int transposed, int rows_q,
+                                                           const uint16_t* __restrict__ x2, uint8_t* __restrict__ codes2,
+                                                           uint8_t* __restrict__ scales2, float* __restrict__ mean2,
+                                                           int T2, int n_tiles2, int transposed2, int N, int n_valid) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile_w[128 * D / 2];  // bf16 pairs, [row][D/2]
+  constexpr int BPR = D / 32;  // blocks per row
+  int64_t bh = blockIdx.x;
+  if (bh >= rows_q) {
+    bh -= rows_q;
+    x = x2;
+    codes = codes2;
+    scales = scales2;
+    mean = mean2;
+    T = T2;
+    n_tiles = n_tiles2;
+    transposed = transposed2;
   }
-  int e = shared_exponent(amax, 2);
-  uint32_t packed[4] = {0, 0, 0, 0};
+  const int tile = blockIdx.y;
+  if (tile >= n_tiles) return;  // the whole workgroup
+  const int tid = threadIdx.x;
+  const int64_t row0 = bh * N + static_cast<int64_t>(tile) * T;  // first row of the tile
+  for (int lb = tid; lb < T * BPR; lb += 256) {
+    const int r = lb / BPR, cb = lb % BPR;
+    const int64_t blk = (row0 + r) * BPR + cb;
+    const bool live = tile * T + r < n_valid;
+    const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);
+    uint32_t w[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t b = h ? (w[i] & 0xFFFF0000u) : (w[i] << 16);
-      float v = __builtin_ldexpf(__uint_as_float(b), -e);
-      uint32_t c = e2m1_mag_code(fabsf(v)) | ((b >> 28) & 8u);
-      int el = 2 * i + h;  // element index within the block
-      packed[el / 8] |= c << (4 * (el % 8));
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = live ? src[i] : make_uint4(0, 0, 0, 0);
+      w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      *reinterpret_cast<uint4*>(&tile_w[r * (D / 2) + cb * 16 + 4 * i]) = v;
     }
+    mxfp4_block(w, reinterpret_cast<uint4*>(codes)[blk], scales[blk]);
   }
-  reinterpret_cast<uint4*>(codes)[blk] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  scales[blk] = static_cast<uint8_t>(e + 127);
+  __syncthreads();
+  if (tid < D) {
+    const int rows = max(0, min(T, n_valid - tile * T));
+    const uint16_t* col = reinterpret_cast<const uint16_t*>(tile_w) + tid;
+    float acc = 0.0f;
+    for (int r = 0; r < rows; ++r) acc = acc + bf16_to_f32(col[r * D]);
+    const float m = rows > 0 ? acc / static_cast<float>(rows) : 0.0f;  // correctly rounded division
+    if (transposed) mean[(bh * D + tid) * n_tiles + tile] = m;
+    else mean[(bh * n_tiles + tile) * D + tid] = m;
+  }
 }
 
 // ---- MXFP4 of Walsh-Hadamard-rotated rows (reading R34) ---------------------
@@ -491,6 +557,47 @@ extern "C" mxq_status mxq_prefill_operands(const uint16_t* q, const uint16_t* k,
     }
     if (r != MXQ_OK) return r;
   }
+  const int64_t BH = static_cast<int64_t>(s->B) * s->Hkv;
+  if (v8 && v_f16t) return launch_vt_n<64, kVtBoth>(v, v_f16t, v_codes, v_scales, BH, N, D, nv, st);
+  if (v8) return launch_vt_n<64, kVtF8>(v, nullptr, v_codes, v_scales, BH, N, D, nv, st);
+  if (v_f16t) return launch_vt_n<64, kVtF16>(v, v_f16t, nullptr, nullptr, BH, N, D, nv, st);
+  return MXQ_OK;
+}
+
+extern "C" mxq_status mxq_prefill_operands_means(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                                 const mxq_attn_shape* s, uint8_t* q_codes, uint8_t* q_scales,
+                                                 uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                                                 uint8_t* v_scales, uint16_t* v_f16t, float* q_means,
+                                                 float* k_means, mxq_stream_t stream) {
+  MXQ_REQUIRE(s != nullptr, MXQ_EINVAL, "mxq_prefill_operands_means: shape is NULL");
+  MXQ_REQUIRE(s->B >= 1 && s->Hq >= 1 && s->Hkv >= 1 && s->N >= 1 && s->n_valid >= 1 && s->n_valid <= s->N,
+              MXQ_EINVAL, "mxq_prefill_operands_means: bad shape");
+  MXQ_REQUIRE(s->D == 64 || s->D == 128, MXQ_EUNSUPPORTED, "mxq_prefill_operands_means: D must be 64 or 128");
+  MXQ_REQUIRE(s->N % 128 == 0, MXQ_EUNSUPPORTED, "mxq_prefill_operands_means: N must be a multiple of 128");
+  MXQ_REQUIRE((s->Bq == 64 || s->Bq == 128) && (s->Bk == 64 || s->Bk == 128), MXQ_EUNSUPPORTED,
+              "mxq_prefill_operands_means: Bq and Bk must be 64 or 128");
+  MXQ_REQUIRE(q && k && q_codes && q_scales && k_codes && k_scales && q_means && k_means, MXQ_EINVAL,
+              "mxq_prefill_operands_means: q, k, the four Q/K arrays and both mean arrays are required");
+  const bool v8 = v_codes || v_scales;
+  MXQ_REQUIRE(!v8 || (v && v_codes && v_scales), MXQ_EINVAL,
+              "mxq_prefill_operands_means: V MXFP8 needs v, codes and scales");
+  MXQ_REQUIRE(!v_f16t || v, MXQ_EINVAL, "mxq_prefill_operands_means: the fp16 V^T copy needs v");
+  hipStream_t st = as_stream(stream);
+  const int64_t D = s->D, N = s->N, nv = s->n_valid;
+  const int64_t rows_q = static_cast<int64_t>(s->B) * s->Hq, rows_k = static_cast<int64_t>(s->B) * s->Hkv;
+  MXQ_REQUIRE(rows_q + rows_k <= 0x7FFFFFFF, MXQ_EUNSUPPORTED, "mxq_prefill_operands_means: too many heads");
+  const int nt_q = static_cast<int>(N / s->Bq), nt_k = static_cast<int>(N / s->Bk);
+  const dim3 grid(static_cast<unsigned>(rows_q + rows_k), static_cast<unsigned>(std::max(nt_q, nt_k)));
+  if (D == 128)
+    hipLaunchKernelGGL(k_quant_mxfp4_tiles<128>, grid, dim3(256), 0, st, q, q_codes, q_scales, q_means, s->Bq, nt_q,
+                       0, static_cast<int>(rows_q), k, k_codes, k_scales, k_means, s->Bk, nt_k, 1,
+                       static_cast<int>(N), static_cast<int>(nv));
+  else
+    hipLaunchKernelGGL(k_quant_mxfp4_tiles<64>, grid, dim3(256), 0, st, q, q_codes, q_scales, q_means, s->Bq, nt_q,
+                       0, static_cast<int>(rows_q), k, k_codes, k_scales, k_means, s->Bk, nt_k, 1,
+                       static_cast<int>(N), static_cast<int>(nv));
+  mxq_status r = check_launch("k_quant_mxfp4_tiles");
+  if (r != MXQ_OK) return r;
   const int64_t BH = static_cast<int64_t>(s->B) * s->Hkv;
   if (v8 && v_f16t) return launch_vt_n<64, kVtBoth>(v, v_f16t, v_codes, v_scales, BH, N, D, nv, st);
   if (v8) return launch_vt_n<64, kVtF8>(v, nullptr, v_codes, v_scales, BH, N, D, nv, st);

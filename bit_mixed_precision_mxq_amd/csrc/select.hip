@@ -366,6 +366,47 @@ extern "C" size_t attn_select_blocks_workspace(const mxq_attn_shape* s) {
          static_cast<size_t>(s->D) * sizeof(float);
 }
 
+// k_select over given tile means (layouts as k_tile_means writes them)
+static mxq_status launch_select(const float* qmean, const float* kmean, const mxq_attn_shape* s,
+                                const mxq_select_params* p, uint32_t* mask, int32_t* n_fp16, float* scores,
+                                bool score_free, hipStream_t strm) {
+  const int n_qt = s->N / s->Bq, n_kt = s->N / s->Bk;
+  SelectArgs a;
+  a.qmean = qmean; a.kmean = kmean; a.mask = mask; a.n_fp16 = n_fp16; a.scores = scores;
+  a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.D = s->D; a.Bq = s->Bq;
+  a.Bk = s->Bk; a.causal = s->causal; a.n_qt = n_qt; a.n_kt = n_kt; a.words = (n_kt + 31) / 32;
+  a.topk = p->topk; a.ratio_num = p->ratio_num; a.ratio_den = p->ratio_den;
+  a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
+  a.B = s->B;
+  a.score_free = score_free ? 1 : 0;
+  const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
+  const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
+  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
+  else hipLaunchKernelGGL(k_select<64>, grid, dim3(64 * kSelWaves), 0, strm, a);
+  return check_launch("k_select");
+}
+
+static mxq_status check_select_params(const mxq_select_params* p) {
+  MXQ_REQUIRE(p != nullptr, MXQ_EINVAL, "attn_select_blocks: params is NULL");
+  MXQ_REQUIRE(p->topk >= 0 || (p->ratio_num >= 0 && p->ratio_den > 0), MXQ_EINVAL,
+              "attn_select_blocks: need topk >= 0 or ratio_num >= 0 and ratio_den > 0");
+  MXQ_REQUIRE(p->sink_tiles >= 0 && p->local_tiles >= 0, MXQ_EINVAL,
+              "attn_select_blocks: sink_tiles and local_tiles must be >= 0");
+  return MXQ_OK;
+}
+
+extern "C" mxq_status attn_select_blocks_means(const float* q_means, const float* k_means,
+                                               const mxq_attn_shape* s, const mxq_select_params* p,
+                                               uint32_t* mask, int32_t* n_fp16, float* scores,
+                                               mxq_stream_t stream) {
+  mxq_status st = validate_shape(s);
+  if (st != MXQ_OK) return st;
+  if ((st = check_select_params(p)) != MXQ_OK) return st;
+  MXQ_REQUIRE(q_means != nullptr && k_means != nullptr && mask != nullptr, MXQ_EINVAL,
+              "attn_select_blocks_means: q_means, k_means and mask are required");
+  return launch_select(q_means, k_means, s, p, mask, n_fp16, scores, false, as_stream(stream));
+}
+
 extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
                                          const mxq_attn_shape* s, const mxq_select_params* p,
                                          void* workspace, size_t ws_bytes, uint32_t* mask,
@@ -396,19 +437,7 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
                        s->D, s->Bk, s->n_valid, n_kt, 1);
     if ((st = check_launch("k_tile_means(k)")) != MXQ_OK) return st;
   }
-  SelectArgs a;
-  a.qmean = qmean; a.kmean = kmean; a.mask = mask; a.n_fp16 = n_fp16; a.scores = scores;
-  a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.D = s->D; a.Bq = s->Bq;
-  a.Bk = s->Bk; a.causal = s->causal; a.n_qt = n_qt; a.n_kt = n_kt; a.words = (n_kt + 31) / 32;
-  a.topk = p->topk; a.ratio_num = p->ratio_num; a.ratio_den = p->ratio_den;
-  a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
-  a.B = s->B;
-  a.score_free = score_free ? 1 : 0;
-  const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
-  const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
-  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
-  else hipLaunchKernelGGL(k_select<64>, grid, dim3(64 * kSelWaves), 0, strm, a);
-  return check_launch("k_select");
+  return launch_select(qmean, kmean, s, p, mask, n_fp16, scores, score_free, strm);
 }
 
 extern "C" size_t attn_select_lines_workspace(const mxq_attn_shape* s) {

@@ -135,6 +135,26 @@ mxq_status mxq_prefill_operands(const uint16_t* q_bf16, const uint16_t* k_bf16, 
                                 uint8_t* v_scales, uint16_t* v_f16t, mxq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * mxq_prefill_operands_means -- mxq_prefill_operands without rotation, plus
+ * the tile means attn_select_blocks scores with (ThriftAttention, abstract:
+ * stage 1's cheap importance estimate), taken from the same single read of
+ * bf16 Q and K.  Q and K are quantised as mxq_prefill_operands does (the same
+ * codes and scales); V likewise.  Tile means, fp32: mean of the valid rows of
+ * each tile of shape->Bq query rows (Q) or shape->Bk key rows (K), summed in
+ * ascending row order and divided once, exactly as attn_select_blocks computes
+ * them, so attn_select_blocks_means on them gives attn_select_blocks's result.
+ * Layouts: q_means [B*Hq][N/Bq][D], k_means [B*Hkv][D][N/Bk] (key tiles
+ * innermost).  Needs D in {64, 128}, N a multiple of 128, Bq and Bk in
+ * {64, 128}; q, k, the four Q/K arrays and both mean arrays are required, the
+ * V outputs are optional as in mxq_prefill_operands.  Caller-owned device
+ * memory; EINVAL / EUNSUPPORTED on bad arguments, nothing launched then.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_prefill_operands_means(const uint16_t* q_bf16, const uint16_t* k_bf16, const uint16_t* v_bf16,
+                                      const mxq_attn_shape* shape, uint8_t* q_codes, uint8_t* q_scales,
+                                      uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
+                                      uint16_t* v_f16t, float* q_means, float* k_means, mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * attn_select_blocks -- stage 1 of ThriftAttention (abstract): choose the
  * query-key tiles that run in FP16.  Importance estimate (reading R8): the
  * score of tile pair (i, j) is mean(Q rows of tile i) . mean(K rows of tile j)
@@ -156,6 +176,16 @@ mxq_status attn_select_blocks(const uint16_t* q_bf16, const uint16_t* k_bf16,
                               const mxq_attn_shape* shape, const mxq_select_params* params,
                               void* workspace, size_t ws_bytes, uint32_t* mask, int32_t* n_fp16,
                               float* scores, mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_select_blocks_means -- attn_select_blocks on tile means already
+ * computed (mxq_prefill_operands_means, same layouts): the same scores, mask
+ * and counts for the same inputs.  q_means, k_means and mask are required;
+ * n_fp16 and scores may be NULL.  Same parameter rules as attn_select_blocks.
+ * ------------------------------------------------------------------------- */
+mxq_status attn_select_blocks_means(const float* q_means, const float* k_means, const mxq_attn_shape* shape,
+                                    const mxq_select_params* params, uint32_t* mask, int32_t* n_fp16,
+                                    float* scores, mxq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * attn_select_lines -- HyQuant (summary and abstract): a few "vertical-line"

@@ -129,3 +129,22 @@ def test_host_validation_rejects_before_launch(lib):
     kvl = mxq.KVCache(fake, fake, fake, fake, fake, fake, None, None, None, None, fake, 64, 0, 0, fake, None, fake, 4)
     st = so.attn_quantkv_decode(fake, ctypes.byref(kvl), 1, 8, 2, 128, 64, 0.0, 0, fake, 1 << 20, fake, None)
     assert st == mxq.MXQ_EINVAL and b"lines" in so.mxq_last_error()
+
+
+def test_fused_means_entry_points_validate_before_launch(lib):
+    mxq, so = lib
+    ok = mxq.AttnShape(1, 2, 2, 256, 256, 64, 64, 64, 0)
+    fake = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    st = so.mxq_prefill_operands_means(fake, fake, fake, ctypes.byref(ok), fake, fake, fake, fake, None, None, None,
+                                       None, fake, None)
+    assert st == mxq.MXQ_EINVAL and b"mean" in so.mxq_last_error()
+    bad_bq = mxq.AttnShape(1, 2, 2, 256, 256, 64, 32, 64, 0)
+    st = so.mxq_prefill_operands_means(fake, fake, fake, ctypes.byref(bad_bq), fake, fake, fake, fake, None, None,
+                                       None, fake, fake, None)
+    assert st == mxq.MXQ_EUNSUPPORTED
+    sp = mxq.SelectParams(-1, 5, 100, 1, 1)
+    st = so.attn_select_blocks_means(fake, None, ctypes.byref(ok), ctypes.byref(sp), fake, None, None, None)
+    assert st == mxq.MXQ_EINVAL and b"k_means" in so.mxq_last_error()
+    bad = mxq.SelectParams(-1, 5, 0, 1, 1)
+    st = so.attn_select_blocks_means(fake, fake, ctypes.byref(ok), ctypes.byref(bad), fake, None, None, None)
+    assert st == mxq.MXQ_EINVAL

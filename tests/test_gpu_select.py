@@ -1,6 +1,7 @@
 """GPU parity: attn_select_blocks masks, counts and scores are bit-exact."""
 
 import numpy as np
+import torch
 import pytest
 
 from gpu_helpers import bf16_dev, gpu_or_skip, u32
@@ -110,3 +111,58 @@ def test_zero_budget_without_scores(case):
     mask2, nfp2, _ = _run(mxq, cfg, want_scores=True)
     assert np.array_equal(mask2, rm)
     assert np.array_equal(nfp2, rn)
+
+
+# mxq_prefill_operands_means: the quantiser's tile means equal the oracle's (bit
+# for bit), and selecting from them equals attn_select_blocks on the same inputs.
+MEANS_CASES = [
+    ("llama8b", {}),
+    ("tiny", {}),
+    ("vit", {"B": 8}),
+]
+
+
+@pytest.mark.parametrize("name,over", MEANS_CASES)
+def test_select_from_fused_means(name, over):
+    mxq = gpu_or_skip()
+    cfg = mxq_inputs.make_prefill(name, **over)
+    shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"],
+                      cfg["Bk"], cfg["causal"])
+    q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    ops, qm, km = mxq.prepare_prefill_means(q, k, v, shape)
+    rqm, rkm = S.pooled_means(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"])
+    assert np.array_equal(qm.cpu().numpy().view(np.uint32), rqm.view(np.uint32))
+    assert np.array_equal(km.cpu().numpy().transpose(0, 1, 3, 2).view(np.uint32), rkm.view(np.uint32))
+    ref = mxq.prepare_prefill(q, k, v, cfg["n_valid"])
+    for f in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales", "v_f16t"):
+        assert torch.equal(getattr(ops, f), getattr(ref, f)), f
+    topk, ratio = cfg["topk"], (cfg["ratio_num"], cfg["ratio_den"])
+    if topk == 0 or (topk < 0 and ratio[0] == 0):
+        topk, ratio = -1, (5, 100)  # a budget that needs the scores
+    m1, n1, s1 = mxq.attn_select_blocks_means(qm, km, shape, topk=topk, ratio=ratio, sink_tiles=cfg["sink_tiles"],
+                                              local_tiles=cfg["local_tiles"], want_scores=True)
+    m2, n2, s2 = mxq.attn_select_blocks(q, k, shape, topk=topk, ratio=ratio, sink_tiles=cfg["sink_tiles"],
+                                        local_tiles=cfg["local_tiles"], want_scores=True)
+    assert torch.equal(m1, m2) and torch.equal(n1, n2)
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    rm, rn, rs = S.select_blocks(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"], topk,
+                                 ratio[0], ratio[1], cfg["sink_tiles"], cfg["local_tiles"])
+    assert np.array_equal(u32(m1), rm)
+
+
+def test_fused_means_ragged_gqa():
+    mxq = gpu_or_skip()
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, N, D, nv = 2, 6, 2, 640, 64, 577
+    q = rng.standard_normal((B, Hq, N, D)).astype(np.float32) * 2
+    k = rng.standard_normal((B, Hkv, N, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, N, D)).astype(np.float32)
+    for t in (q, k, v):
+        t[:, :, nv:] = 0
+    qb, kb, vb = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    for Bq in (64, 128):
+        shape = mxq.Shape(B, Hq, Hkv, N, nv, D, Bq, 64, True)
+        ops, qm, km = mxq.prepare_prefill_means(bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), shape)
+        rqm, rkm = S.pooled_means(qb, kb, nv, Bq, 64)
+        assert np.array_equal(qm.cpu().numpy().view(np.uint32), rqm.view(np.uint32))
+        assert np.array_equal(km.cpu().numpy().transpose(0, 1, 3, 2).view(np.uint32), rkm.view(np.uint32))
