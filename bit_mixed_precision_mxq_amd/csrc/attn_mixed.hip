@@ -636,7 +636,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // One pipeline step (see above).  Issue order, fixed with scheduling
   // barriers, per S block: the K fragment three blocks ahead, the block's
   // exponentials, its QK MFMA for the next chunk, every 8/NDB blocks one PV
-  // MFMA of the pending chunk (V fragments two head_dim blocks ahead), and the
+  // MFMA of the pending chunk (V fragments one head_dim block ahead), and the
   // partial maxima of the block whose QK MFMA was issued three blocks before.
   auto pipe = [&](const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb) {
     float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
@@ -655,7 +655,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 #pragma unroll
     for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(kbn + koff(beta));
     va[0] = vfrag(vbp, 0);
-    va[1] = vfrag(vbp, 1);
     mxa = NEG_INF;
     mxb = NEG_INF;
     __builtin_amdgcn_sched_barrier(0);
@@ -675,7 +674,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
       if (beta % SPB == SPB - 1) {
         const int db = beta / SPB;
-        if (db + 2 < NDB) va[db + 2] = vfrag(vbp, db + 2);
+        if (db + 1 < NDB) va[db + 1] = vfrag(vbp, db + 1);
         O[db] = pv_block(va[db], pb_p, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), pscp, db);
       }
       if (beta >= 3) s_max(beta - 3);
