@@ -77,7 +77,7 @@ struct AttnArgs {
   float c;  // fl32(softmax_scale * log2(e))
 };
 
-constexpr float kGridMagic = 6144.0f;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^13)
+constexpr float kGridMagic = kPGridMagic;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^13)
 constexpr float kExpOffset = 8.0f;     // P is stored as E4M3(2^(x + 8)) * 2^-8
 constexpr int kPScale = 119;           // E8M0 code of 2^-8
 constexpr float kMaxLag = 64.0f;       // largest gap kept between O's reference and the running one
@@ -577,17 +577,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     if (__any(m1 - m_o > kMaxLag)) rebase(m1);
   };
   // P = E4M3(2^xq) of one S block (4 scores per lane -> 4 bytes)
-  // (the two conversions write the low and the high half of the word, so its
-  // previous contents do not matter: an opaque register spares a zeroing move)
-  auto p_block = [&](const v4f& s4, float off) -> int {
-    float y[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s4[i], c, off) - kGridMagic);
-    int w;
-    __asm__ volatile("" : "=v"(w));
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w, false);
-    return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-  };
+  auto p_block = [&](const v4f& s4, float off) -> int { return p4_e4m3(s4, c, off); };
 
   // ---- main loop over 128-key chunks.
   // Ring protocol: at the top of iteration ch the scale bytes of K chunk ch+2
@@ -766,6 +756,12 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     ks_store(kbuf(0));
     pks = pks1;
     ks_store(kbuf(1));
+    // the first pipeline step runs the PV MFMAs of a pending chunk that does
+    // not exist yet (P = 0) on V buffer RV-1, which no copy fills before
+    // iteration 1: zero codes and scales there, since bytes left in LDS by an
+    // earlier kernel may be E4M3 or E8M0 NaNs, and 0 * NaN would poison O
+    for (int i = tid; i < LY::V_BYTES / 16; i += NT)
+      reinterpret_cast<v4i*>(vbuf(LY::RV - 1))[i] = v4i{0, 0, 0, 0};
   } else {
     // no low-bit operands: the rings are never filled, yet every chunk's
     // pipeline step runs its QK and PV MFMAs (with P = 0); zero codes and
@@ -866,7 +862,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     chunk_lag(hm0, hm1);
   };
   int vslot = 0;    // V buffer of chunk ch
-  int vslot_p = 0;  // V buffer of the pending chunk (none yet: P = 0 reads a filled buffer)
+  int vslot_p = LY::RV - 1;  // V buffer of the pending chunk (none yet: P = 0 over the zeroed buffer)
   if (lowbit) {     // chunk 0's FP4 scores (K chunks 0 and 1 are in place)
     qk_lowbit(kbuf(0), S);
 #pragma unroll

@@ -109,9 +109,11 @@ struct Rsrc {
   __amdgpu_buffer_rsrc_t kc, vc;
   __amdgpu_buffer_rsrc_t sz[4];
 };
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t region(const void* base, int64_t off_bytes, int bytes) {
+// (bytes is the descriptor's unsigned 32-bit record count: up to 2^31 at
+// L_cap = 2^25, so it is carried unsigned and passed as its bit pattern)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region(const void* base, int64_t off_bytes, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base) + off_bytes), 0,
-                                           bytes, 0x00020000);
+                                           __builtin_bit_cast(int, bytes), 0x00020000);
 }
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -519,13 +521,14 @@ __global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
     cx.lane = lane;
 
     const int L = a.kv.L_cap;
+    const uint32_t Lu = static_cast<uint32_t>(L);
     Rsrc rs;
-    rs.kc = region(a.kv.k_codes, bh * L * (kD / 2), L * (kD / 2));
-    rs.vc = region(a.kv.v_codes, bh * L * (kD / 2), L * (kD / 2));
-    rs.sz[0] = region(a.kv.k_scale, bh * L * 8, L * 8);
-    rs.sz[1] = region(a.kv.k_zero, bh * L * 8, L * 8);
-    rs.sz[2] = region(a.kv.v_scale, bh * L * 8, L * 8);
-    rs.sz[3] = region(a.kv.v_zero, bh * L * 8, L * 8);
+    rs.kc = region(a.kv.k_codes, bh * L * (kD / 2), Lu * (kD / 2));
+    rs.vc = region(a.kv.v_codes, bh * L * (kD / 2), Lu * (kD / 2));
+    rs.sz[0] = region(a.kv.k_scale, bh * L * 8, Lu * 8);
+    rs.sz[1] = region(a.kv.k_zero, bh * L * 8, Lu * 8);
+    rs.sz[2] = region(a.kv.v_scale, bh * L * 8, Lu * 8);
+    rs.sz[3] = region(a.kv.v_zero, bh * L * 8, Lu * 8);
     const int offk = tl * (kD / 2) + 16 * jg;
     constexpr int kStep = kBlk * kWaves;
     int t0 = beg + kBlk * wave;

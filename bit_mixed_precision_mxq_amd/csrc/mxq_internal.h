@@ -73,6 +73,30 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return code | sign;
 }
 
+// ---- P of low-bit tiles (ThriftAttention, abstract: low-bit blocks merged
+// through one online softmax; readings R14, R15, R17) --------------------------
+// 1.5 * 2^12: an fp32 in [2^12, 2^13) has a spacing of exactly 2^-11, so one
+// fused multiply-add onto it rounds the softmax exponent to the 2^-11 grid.
+constexpr float kPGridMagic = 6144.0f;
+
+// Four scores -> four E4M3 codes packed in one word (score i in byte i):
+// code_i = E4M3_RNE(2^x_i) with x_i = fl32(s_i * c + off) - 6144, where off =
+// 6144 + 8 - m puts the exponent on the grid relative to the reference m with
+// P stored as 2^8 times its value (E8M0 2^-8 restores it).  Because x_i is a
+// grid point, v_exp_f32 followed by the round-to-nearest-even conversion gives
+// the exactly rounded E4M3 code at every grid point a tile can produce.  The
+// two conversions write the low and the high half of the word, so its earlier
+// contents do not matter: an opaque register spares a zeroing move.
+__device__ __forceinline__ int p4_e4m3(const v4f& s4, float c, float off) {
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s4[i], c, off) - kPGridMagic);
+  int w;
+  __asm__ volatile("" : "=v"(w));
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+}
+
 // Asymmetric 4-bit group of 32 values (reading R19): s = fp16(fl32(max-min)/15),
 // z = fp16(min), code = clamp(rint(fl32(x - z) / s), 0, 15), all codes 0 when
 // s == 0; codes packed two per byte, element 2k in the low nibble.  Every

@@ -96,11 +96,28 @@ def _exact_lowbit_scores(q_hat, k_hat, q_exp, k_exp):
     Every product is exact in float64 and is a multiple of 2**(Eq+Ek-2) with
     |block sum| < 2**13; when the per-pair spread of Eq+Ek over the D/32
     blocks is at most 38 bits, every float64 partial sum is exact whatever the
-    summation order, so the one rounding to fp32 is the exact rounding."""
-    e = q_exp[:, None, :] + k_exp[None, :, :]
-    spread = e.max(axis=-1) - e.min(axis=-1)
-    if spread.size and int(spread.max()) > 38:
-        raise ValueError("block-scale spread too large for the exact float64 sum")
+    summation order, so the one rounding to fp32 is the exact rounding.  A
+    block whose q or k elements are all zero contributes exactly 0 whatever its
+    exponent, so it is left out of the spread."""
+    nb = q_exp.shape[-1]
+    nzq = np.any(q_hat.reshape(q_hat.shape[0], nb, -1) != 0, axis=-1)
+    nzk = np.any(k_hat.reshape(k_hat.shape[0], nb, -1) != 0, axis=-1)
+
+    def own_spread(e, nz):  # spread of one side's exponents over its nonzero blocks
+        hi = np.where(nz, e, np.iinfo(np.int64).min).max(axis=-1)
+        lo = np.where(nz, e, np.iinfo(np.int64).max).min(axis=-1)
+        return np.where(nz.any(axis=-1), hi - lo, 0)
+
+    # a pair's spread is at most the sum of both sides' own spreads; only when
+    # that bound is over 38 is the pairwise spread computed
+    if q_exp.size and k_exp.size and int(own_spread(q_exp, nzq).max()) + int(own_spread(k_exp, nzk).max()) > 38:
+        live = nzq[:, None, :] & nzk[None, :, :]
+        e = q_exp[:, None, :] + k_exp[None, :, :]
+        hi = np.where(live, e, np.iinfo(np.int64).min).max(axis=-1)
+        lo = np.where(live, e, np.iinfo(np.int64).max).min(axis=-1)
+        spread = np.where(live.any(axis=-1), hi - lo, 0)
+        if int(spread.max()) > 38:
+            raise ValueError("block-scale spread too large for the exact float64 sum")
     return (q_hat @ k_hat.T).astype(np.float32)
 
 

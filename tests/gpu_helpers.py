@@ -1,5 +1,8 @@
 """Shared helpers for the GPU parity tests (not a test module)."""
 
+import ctypes
+import os
+
 import numpy as np
 import pytest
 
@@ -52,3 +55,28 @@ def random_bf16(shape, seed, scale=1.0, specials=True):
     b = x.view(np.uint32)
     r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
+
+
+def load_test_kernels():
+    """The test-only kernel library (tests/hip/libmxq_testkernels.so, built by
+    __graft_entry__.build() or tests/hip/build_test_kernels.py)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libmxq_testkernels.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: run python tests/hip/build_test_kernels.py")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.mxqt_p_codes.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp]
+    lib.mxqt_p_codes.restype = ctypes.c_int
+    lib.mxqt_fill_lds.argtypes = [ctypes.c_uint32, ctypes.c_int, vp, vp]
+    lib.mxqt_fill_lds.restype = ctypes.c_int
+    return lib
+
+
+def poison_lds(word):
+    """Fill the LDS of every CU with a 32-bit pattern, on torch's current
+    stream, so that the next kernel starts on stale LDS contents."""
+    lib = load_test_kernels()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert lib.mxqt_fill_lds(ctypes.c_uint32(word), 4 * n_cu, ctypes.c_void_p(sink.data_ptr()), st) == 0

@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from gpu_helpers import bf16_dev, gpu_or_skip, u32
+from gpu_helpers import bf16_dev, gpu_or_skip, poison_lds, u32
 import mxq_inputs
 from oracle import attention as A
 from oracle import select as S
@@ -109,10 +109,13 @@ def test_llama8b_full_size_sampled():
     for h in (0, 13, 31):
         kv = h // G
         sub_q, sub_k, sub_v = cfg["q"][:, h:h + 1], cfg["k"][:, kv:kv + 1], cfg["v"][:, kv:kv + 1]
+        rm, _, _ = S.select_blocks(sub_q, sub_k, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True, cfg["topk"],
+                                   cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"], cfg["local_tiles"])
+        assert np.array_equal(mask[:, h:h + 1], rm), f"head {h}: mask differs"
         ops = A.prepare_operands(sub_q, sub_k, sub_v, cfg["n_valid"])
         tiles = [0, 1, 17, 40, 63]
         ro, rl = A.attn_mixed_ref(sub_q, sub_k, sub_v, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True,
-                                  mask=mask[:, h:h + 1], qtiles=tiles, ops=ops)
+                                  mask=rm, qtiles=tiles, ops=ops)
         rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
         worst = max(worst, _check(out[:, h:h + 1], lse[:, h:h + 1], ro, rl, rows=rows))
     print(f"llama8b sampled max-abs {worst:.3e}")
@@ -125,10 +128,12 @@ def test_vit_batch_sampled():
     cfg = mxq_inputs.make_prefill("vit", B=8)
     out, lse, mask, lines = _gpu_prefill(mxq, cfg, 0, with_lines=True)
     assert not mask.any() and np.all(lines[..., 0] == 0)
+    rlines, _ = S.select_lines(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["n_lines"], cfg["sink_tokens"])
+    assert np.array_equal(lines, rlines)
     for b, h in ((0, 0), (3, 7), (7, 11)):
         ro, rl = A.attn_mixed_ref(cfg["q"][b:b + 1, h:h + 1], cfg["k"][b:b + 1, h:h + 1], cfg["v"][b:b + 1, h:h + 1],
-                                  cfg["n_valid"], 64, 64, False, mask=mask[b:b + 1, h:h + 1],
-                                  lines=lines[b:b + 1, h:h + 1])
+                                  cfg["n_valid"], 64, 64, False, mask=np.zeros_like(mask[b:b + 1, h:h + 1]),
+                                  lines=rlines[b:b + 1, h:h + 1])
         _check(out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
 
 
@@ -175,8 +180,12 @@ def test_rotated_lowbit_operands(mode):
     if mode == 0:
         mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(5, 100), sink_tiles=1, local_tiles=1)
     out, lse = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode)
+    rm = None
+    if mode == 0:
+        rm, _, _ = S.select_blocks(cfg["q"], cfg["k"], cfg["n_valid"], 128, 64, True, -1, 5, 100, 1, 1)
+        assert np.array_equal(u32(mask), rm)
     ro, rl = A.attn_mixed_ref(cfg["q"], cfg["k"], cfg["v"], cfg["n_valid"], 128, 64, True,
-                              mask=u32(mask) if mask is not None else None, mode=mode, rotate=True)
+                              mask=rm, mode=mode, rotate=True)
     _check(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
 
 
@@ -202,3 +211,130 @@ def test_prefill_pipeline_matches_the_sequential_calls():
             out, lse = pipe(q, k, v)
             torch.cuda.synchronize()
             assert torch.equal(out, ref) and torch.equal(lse, ref_lse), name
+
+
+def test_long32k_full_size_sampled():
+    """The long-context causal workload at full size (N = 32768, 5% + sink +
+    4-tile window) in the launch configuration the benchmark times (the fused
+    quantiser with tile means, selection on the means, attention), with fp32
+    output for parity: masks bit-exact for sampled heads, and the first, a
+    middle and the last query tiles (256 key chunks) within 5e-3."""
+    mxq = gpu_or_skip()
+    import torch
+
+    cfg = mxq_inputs.make_prefill("long32k")
+    q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    shape = _shape(mxq, cfg)
+    pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                               sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
+                               out_dtype=mxq.MXQ_OUT_F32)
+    assert pipe.fused
+    out_t, lse_t = pipe(q, k, v)
+    torch.cuda.synchronize()
+    out, lse, mask = out_t.cpu().numpy(), lse_t.cpu().numpy(), u32(pipe.mask)
+    del q, k, v
+    G = cfg["Hq"] // cfg["Hkv"]
+    tiles = [0, 127, 200, 255]
+    rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
+    worst = 0.0
+    for h in (0, 13, 31):
+        kv = h // G
+        sub_q, sub_k, sub_v = cfg["q"][:, h:h + 1], cfg["k"][:, kv:kv + 1], cfg["v"][:, kv:kv + 1]
+        rm, _, _ = S.select_blocks(sub_q, sub_k, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True, cfg["topk"],
+                                   cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"], cfg["local_tiles"])
+        assert np.array_equal(mask[:, h:h + 1], rm), f"head {h}: mask differs"
+        ops = A.prepare_operands(sub_q, sub_k, sub_v, cfg["n_valid"])
+        ro, rl = A.attn_mixed_ref(sub_q, sub_k, sub_v, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True,
+                                  mask=rm, qtiles=tiles, ops=ops)
+        worst = max(worst, _check(out[:, h:h + 1], lse[:, h:h + 1], ro, rl, rows=rows))
+    print(f"long32k sampled max-abs {worst:.3e}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_block_exponent_spread_above_18(mode):
+    """A pair's block-exponent spread above 18 bits: K's head_dim block 1 is
+    scaled by 2^12 and Q's block 2 by 2^-8 (spread about 20), with a softmax
+    scale of 2^-13 that keeps the logits near unit size, so every block still
+    shapes P.  The FP4 MFMA's scores must still give outputs within 5e-3 of
+    the oracle's exactly rounded ones."""
+    mxq = gpu_or_skip()
+    rng = np.random.default_rng(77)
+    N, nv, Hq, Hkv, D = 512, 500, 4, 1, 128
+    q = rng.standard_normal((1, Hq, N, D)).astype(np.float32)
+    k = rng.standard_normal((1, Hkv, N, D)).astype(np.float32)
+    v = rng.standard_normal((1, Hkv, N, D)).astype(np.float32)
+    k[..., 32:64] *= np.float32(2.0 ** 12)
+    q[..., 64:96] *= np.float32(2.0 ** -8)
+    for t in (q, k, v):
+        t[:, :, nv:] = 0
+    cfg = dict(B=1, Hq=Hq, Hkv=Hkv, N=N, n_valid=nv, D=D, Bq=128, Bk=64, causal=True,
+               q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v))
+    ops_ref = A.prepare_operands(cfg["q"], cfg["k"], cfg["v"], nv)
+    e = ops_ref["q_exp"][0, 0][:nv, None, :] + ops_ref["k_exp"][0, 0][None, :nv, :]
+    assert int((e.max(-1) - e.min(-1)).max()) > 18
+    scale = 2.0 ** -13
+    qd, kd, vd = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    shape = _shape(mxq, cfg)
+    ops = mxq.prepare_prefill(qd, kd, vd, nv, mode)
+    mask = None
+    if mode == 0:
+        mask, _, _ = mxq.attn_select_blocks(qd, kd, shape, topk=1, ratio=(0, 1), sink_tiles=0, local_tiles=1)
+    out, lse = mxq.attn_mixed_fwd(ops, mask, shape, softmax_scale=scale, mode=mode)
+    rm = None
+    if mode == 0:
+        rm, _, _ = S.select_blocks(cfg["q"], cfg["k"], nv, 128, 64, True, 1, 0, 1, 0, 1)
+        assert np.array_equal(u32(mask), rm)
+    ro, rl = A.attn_mixed_ref(cfg["q"], cfg["k"], cfg["v"], nv, 128, 64, True, mask=rm, mode=mode,
+                              softmax_scale=scale, ops=ops_ref)
+    err = _check(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+    print(f"spread > 18, mode {mode}: max-abs {err:.3e}")
+
+
+@pytest.mark.parametrize("word", [0xFFFFFFFF, 0x7F7F7F7F])
+def test_stale_lds_does_not_reach_the_output(word):
+    """LDS is not cleared between kernels: fill every CU's LDS with E4M3 / E8M0
+    NaN bytes right before the attention kernel (same stream).  Buffers the
+    first pipeline step reads before any copy has filled them must not let a
+    NaN into O (0 * NaN is NaN): outputs stay finite and within 5e-3."""
+    mxq = gpu_or_skip()
+    import torch
+
+    cases = [mxq_inputs.make_prefill("tiny"),
+             mxq_inputs.make_prefill("llama8b", N=1024, n_valid=1000, Hq=4, Hkv=1),
+             mxq_inputs.make_prefill("vit", B=2)]
+    for cfg in cases:
+        lines_on = cfg["n_lines"] > 0
+        q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+        shape = _shape(mxq, cfg)
+        lines = mxq.attn_select_lines(q, k, shape, cfg["n_lines"], cfg["sink_tokens"])[0] if lines_on else None
+        rlines = None
+        if lines_on:
+            rlines, _ = S.select_lines(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["n_lines"],
+                                       cfg["sink_tokens"])
+            assert np.array_equal(lines.cpu().numpy(), rlines)
+        for mode in (0, 1):
+            ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], mode, lines=lines_on)
+            mask = None
+            if mode == 0:
+                mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=cfg["topk"],
+                                                    ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                                                    sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"])
+            rm = None
+            if mode == 0:
+                rm, _, _ = S.select_blocks(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                                           cfg["topk"], cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"],
+                                           cfg["local_tiles"])
+                assert np.array_equal(u32(mask), rm)
+            torch.cuda.synchronize()
+            poison_lds(word)
+            out, lse = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode, lines=lines)
+            torch.cuda.synchronize()
+            hs = [(0, 0), (cfg["B"] - 1, cfg["Hq"] - 1)]
+            for b, h in hs:
+                kv = h // (cfg["Hq"] // cfg["Hkv"])
+                ro, rl = A.attn_mixed_ref(cfg["q"][b:b + 1, h:h + 1], cfg["k"][b:b + 1, kv:kv + 1],
+                                          cfg["v"][b:b + 1, kv:kv + 1], cfg["n_valid"], cfg["Bq"], cfg["Bk"],
+                                          cfg["causal"], mask=rm[b:b + 1, h:h + 1] if rm is not None else None,
+                                          mode=mode, lines=rlines[b:b + 1, h:h + 1] if lines_on else None)
+                _check(out.cpu().numpy()[b:b + 1, h:h + 1], lse.cpu().numpy()[b:b + 1, h:h + 1], ro, rl)
+            assert torch.isfinite(out).all()

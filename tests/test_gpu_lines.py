@@ -149,9 +149,12 @@ def test_llama8b_with_lines_sampled():
     for h in (0, 21):
         kv = h // G
         sub_q, sub_k, sub_v = cfg["q"][:, h:h + 1], cfg["k"][:, kv:kv + 1], cfg["v"][:, kv:kv + 1]
+        rm, _, _ = S.select_blocks(sub_q, sub_k, cfg["n_valid"], 128, 64, True, -1, 5, 100, 1, 1)
+        rlines, _ = S.select_lines(sub_q, sub_k, cfg["n_valid"], 128, 16, 1)
+        assert np.array_equal(mask[:, h:h + 1], rm) and np.array_equal(lines[:, h:h + 1], rlines)
         tiles = [0, 9, 40, 63]
-        ro, rl = A.attn_mixed_ref(sub_q, sub_k, sub_v, cfg["n_valid"], 128, 64, True, mask=mask[:, h:h + 1],
-                                  qtiles=tiles, lines=lines[:, h:h + 1])
+        ro, rl = A.attn_mixed_ref(sub_q, sub_k, sub_v, cfg["n_valid"], 128, 64, True, mask=rm,
+                                  qtiles=tiles, lines=rlines)
         rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
         _check(out[:, h:h + 1][..., rows, :], lse[:, h:h + 1][..., rows], ro[..., rows, :], rl[..., rows])
 

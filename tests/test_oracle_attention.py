@@ -51,6 +51,72 @@ def test_lowbit_scores_are_exactly_rounded():
             assert s[r, c] == best
 
 
+def _fraction_score(qc, qs, kc, ks, r, c):
+    exact = Fraction(0)
+    for d in range(qc.shape[-1]):
+        a = Fraction(float(F.e2m1_value(qc[r, d]))) * Fraction(2) ** (int(qs[r, d // 32]) - 127)
+        b = Fraction(float(F.e2m1_value(kc[c, d]))) * Fraction(2) ** (int(ks[c, d // 32]) - 127)
+        exact += a * b
+    return exact
+
+
+def _is_rounding_of(z, exact):
+    f = np.float32(z)
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda w: (abs(Fraction(float(w)) - exact), int(np.array(w).view(np.uint32)) & 1))
+    return f == best
+
+
+@pytest.mark.parametrize("zero_side", ["q", "k"])
+def test_all_zero_block_is_left_out_of_the_spread(zero_side):
+    """A head_dim block whose q (or k) elements are all zero has E8M0 0 (2^-127)
+    and contributes exactly 0, so a huge exponent on the other side of that
+    block must not trip the exactness guard; the scores stay exactly rounded."""
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    if zero_side == "q":
+        q[..., 32:64] = 0.0
+        k[..., 32:64] *= np.float32(2.0 ** 60)  # spread ~187 if the zero block counted
+    else:
+        k[..., 64:96] = 0.0
+        q[..., 64:96] *= np.float32(2.0 ** 60)
+    qb, kb = F.f32_to_bf16_bits(q), F.f32_to_bf16_bits(k)
+    ops = A.prepare_operands(qb, kb, kb, 64)
+    s = A._exact_lowbit_scores(ops["q_hat"][0, 0], ops["k_hat"][0, 0], ops["q_exp"][0, 0], ops["k_exp"][0, 0])
+    qc, qs = F.quantize_mxfp4(F.bf16_bits_to_f32(qb)[0, 0])
+    kc, ks = F.quantize_mxfp4(F.bf16_bits_to_f32(kb)[0, 0])
+    for r, c in ((0, 0), (5, 17), (63, 40), (31, 2)):
+        assert _is_rounding_of(s[r, c], _fraction_score(qc, qs, kc, ks, r, c))
+
+
+def test_spread_beyond_38_raises_and_20_is_exact():
+    """Nonzero blocks whose exponents differ by more than 38 bits are refused
+    (the float64 sum could round); a spread of about 20 (K block x2^12, Q
+    block x2^-8) still gives exactly rounded scores."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    k_big = k.copy()
+    k_big[..., 32:64] *= np.float32(2.0 ** 45)
+    qb, kb = F.f32_to_bf16_bits(q), F.f32_to_bf16_bits(k_big)
+    ops = A.prepare_operands(qb, kb, kb, 64)
+    with pytest.raises(ValueError):
+        A._exact_lowbit_scores(ops["q_hat"][0, 0], ops["k_hat"][0, 0], ops["q_exp"][0, 0], ops["k_exp"][0, 0])
+    q2, k2 = q.copy(), k.copy()
+    k2[..., 32:64] *= np.float32(2.0 ** 12)
+    q2[..., 64:96] *= np.float32(2.0 ** -8)
+    qb, kb = F.f32_to_bf16_bits(q2), F.f32_to_bf16_bits(k2)
+    ops = A.prepare_operands(qb, kb, kb, 64)
+    e = ops["q_exp"][0, 0][:, None, :] + ops["k_exp"][0, 0][None, :, :]
+    assert int((e.max(-1) - e.min(-1)).max()) > 18
+    s = A._exact_lowbit_scores(ops["q_hat"][0, 0], ops["k_hat"][0, 0], ops["q_exp"][0, 0], ops["k_exp"][0, 0])
+    qc, qs = F.quantize_mxfp4(F.bf16_bits_to_f32(qb)[0, 0])
+    kc, ks = F.quantize_mxfp4(F.bf16_bits_to_f32(kb)[0, 0])
+    for r, c in ((0, 0), (7, 9), (63, 63), (20, 50)):
+        assert _is_rounding_of(s[r, c], _fraction_score(qc, qs, kc, ks, r, c))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_fp16_mode_near_exact_softmax(causal):
     """P rounded to fp16 (relative error <= 2**-11) and S rounded to fp32 bound
