@@ -1,20 +1,29 @@
 """Benchmark of the mixed-precision block-scaled attention hot path on one MI355X.
 
-One step = the whole prefill path on one batch: MXFP4 quantisation of Q and K,
-MXFP8 quantisation of V (blocks along keys) and its fp16 copy, block selection
-(5% of tiles plus the sink column and local window), and the fused
-mixed-precision attention pass.  Selection runs on a second stream beside the
-quantisers (PrefillPipeline).  Inputs are bf16 tensors already resident in
-HBM when the timed region starts.
+One step = the whole prefill path on one batch: MXFP4 quantisation of Q and K
+(with the tile means the selection scores), MXFP8 quantisation of V (blocks
+along keys) and its fp16 copy, block selection (5% of tiles plus the sink
+column and local window), and the fused mixed-precision attention pass, as one
+chain on the caller's stream (PrefillPipeline).  Inputs are bf16 tensors
+already resident in HBM when the timed region starts.
 
-The JSON line reports effective attention TFLOP/s (4*D per valid query-key
-pair per head, divided by the step time), the roofline of the dominant kernel
-(attn_mixed_fwd) against the precision-weighted MFMA peak, the CPU oracle timed
-on a bounded sample, and the decode path (quantised-KV decode, KV-read GB/s
-against HBM peak).
+The headline workload is the long-context causal prefill (B=1, Hq=32, Hkv=8,
+N=32768, D=128, 5% + sink + 4-tile window), the largest single-GPU
+configuration.  The JSON line reports effective attention TFLOP/s of the step
+(4*D per valid query-key pair per head, divided by the step time), the
+roofline of the dominant kernel (attn_mixed_fwd, timed with HIP events on the
+stream it runs on) against the precision-weighted MFMA peak, the CPU oracle
+timed on a bounded sample across the host's cores, and two extra legs: the
+Llama-8B-shaped prefill (N=8192) and the quantised-KV decode step (KV-read
+GB/s against HBM peak).
+
+Warm-up, the same rule for every leg: W untimed steps, then more until at
+least 100 ms of the same step have run, so that the GPU clocks are steady
+before timing (fewer read a few percent slow after the idle input upload).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-decode] [--only prefill|decode|copy|quality]
+                       [--no-cpu-baseline] [--no-decode] [--no-extra]
+                       [--only prefill|decode|copy|quality]
 """
 
 from __future__ import annotations
@@ -37,20 +46,40 @@ PEAK_HBM = 8000.0
 METRIC = "effective attention TFLOPS @5% FP16 tiles (prefill); KV-read GB/s (decode)"
 
 
-def recorded_traffic(kernel):
+def recorded_traffic(kernel, workload):
     """HBM bytes per launch recorded by rocprofv3 FETCH_SIZE / WRITE_SIZE passes
-    (profiles/hbm_traffic.json), or None when the kernel's sources have changed
-    since the counters were taken."""
+    (profiles/hbm_traffic.json, entry "kernel/workload"), or None when the
+    kernel's sources have changed since the counters were taken."""
     import hashlib
 
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
+        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[f"{kernel}/{workload}"]
         h = hashlib.sha256()
         for f in rec["sources"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
     except (OSError, KeyError, ValueError):
         return None
     return rec["bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
+def warm(fn, steps, min_ms=100.0):
+    """The warm-up rule of every leg: ``steps`` untimed calls, then more, in
+    rounds of ``max(steps, 1)``, until at least ``min_ms`` of them have run
+    (GPU clocks settle).  Returns the number of calls made."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(steps):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(max(steps, 1)):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def log(*a):
@@ -72,22 +101,17 @@ def pair_counts(cfg, mask_np, lines_np=None):
 
     N, nv, Bq, Bk, causal = cfg["N"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"]
     n_qt, n_kt = N // Bq, N // Bk
-    # pairs[i, j]: valid pairs inside tile (i, j)
+    # pairs[i, j]: valid pairs inside tile (i, j); per valid row r, key tile j
+    # holds min(max(r + 1 - j*Bk, 0), keys of j) valid keys when causal
     q = np.arange(nv)
+    k0 = np.arange(n_kt) * Bk
+    width = np.clip(nv - k0, 0, Bk)
+    if causal:
+        per_row = np.minimum(np.clip(q[:, None] + 1 - k0[None, :], 0, None), width[None, :])
+    else:
+        per_row = np.broadcast_to(width[None, :], (nv, n_kt))
     pairs = np.zeros((n_qt, n_kt), dtype=np.int64)
-    for i in range(n_qt):
-        rows = q[(q >= i * Bq) & (q < (i + 1) * Bq)]
-        if rows.size == 0:
-            continue
-        for j in range(n_kt):
-            k0, k1 = j * Bk, min((j + 1) * Bk, nv)
-            if k0 >= nv:
-                break
-            if causal:
-                cnt = np.clip(rows + 1 - k0, 0, k1 - k0).sum()
-            else:
-                cnt = rows.size * (k1 - k0)
-            pairs[i, j] = cnt
+    np.add.at(pairs, q // Bq, per_row.astype(np.int64))
     bits = np.unpackbits(mask_np.view(np.uint8).reshape(mask_np.shape[:-1] + (-1,)), axis=-1, bitorder="little")
     bits = bits[..., :n_kt].astype(bool)  # [B, Hq, n_qt, n_kt]
     heads = mask_np.shape[0] * mask_np.shape[1]
@@ -120,20 +144,20 @@ def roofline_peak(D, total_pairs, fp16_pairs):
     return f_all / t_roof / 1e12, t_roof
 
 
-def bench_prefill(args, dev):
+def bench_prefill(args, dev, workload):
+    """Time the prefill step (PrefillPipeline) of one workload; the attention
+    kernel is bracketed by HIP events on the stream it is launched on."""
     import numpy as np
     import torch
 
     import bit_mixed_precision_mxq_amd as mxq
     import mxq_inputs
 
-    cfg = mxq_inputs.make_prefill(args.workload)
+    cfg = mxq_inputs.make_prefill(workload)
     q, k, v = _bf16(cfg["q"], dev), _bf16(cfg["k"], dev), _bf16(cfg["v"], dev)
     shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
                       cfg["causal"])
     n_lines = cfg.get("n_lines", 0)
-    # the step's DAG: selection on a second stream beside the quantisers,
-    # attention after both (PrefillPipeline)
     pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
                                sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"], n_lines=n_lines,
                                sink_tokens=cfg.get("sink_tokens", 0), out_dtype=mxq.MXQ_OUT_BF16, device=dev)
@@ -142,33 +166,42 @@ def bench_prefill(args, dev):
 
     def step(i=None):
         pipe(q, k, v, events=None if i is None else (ev_a0[i], ev_a1[i]))
-        return pipe.mask, pipe.lines
 
-    for _ in range(args.warmup):
-        mask, lines = step()
-    torch.cuda.synchronize()
+    n_warm = warm(step, args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        mask, lines = step(i)
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     attn_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)) / args.steps
-    mask_np = mask.cpu().numpy().view(np.uint32)
-    lines_np = lines.cpu().numpy() if lines is not None else None
+    mask_np = pipe.mask.cpu().numpy().view(np.uint32)
+    lines_np = pipe.lines.cpu().numpy() if pipe.lines is not None else None
     total, fp16 = pair_counts(cfg, mask_np, lines_np)
     flops = 4.0 * cfg["D"] * total
     peak_eff, t_roof = roofline_peak(cfg["D"], total, fp16)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     res = dict(
-        cfg=cfg, ms_step=ms_step, attn_ms=attn_ms, flops=flops, total_pairs=total, fp16_pairs=fp16,
-        tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_attn=achieved, peak_eff=peak_eff,
-        t_roof_ms=t_roof * 1e3, mask=mask_np, lines=lines_np,
+        workload=workload, cfg=cfg, ms_step=ms_step, attn_ms=attn_ms, flops=flops, total_pairs=total,
+        fp16_pairs=fp16, tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_attn=achieved, peak_eff=peak_eff,
+        t_roof_ms=t_roof * 1e3, warmup_calls=n_warm,
     )
-    log(f"prefill {args.workload}: step {ms_step:.3f} ms, attn {attn_ms:.3f} ms, "
+    log(f"prefill {workload}: step {ms_step:.3f} ms, attn {attn_ms:.3f} ms, "
         f"{res['tflops_step']:.1f} TFLOP/s step, {achieved:.1f} TFLOP/s attn, "
-        f"fp16 pairs {fp16 / total:.4f}, roofline {t_roof * 1e3:.3f} ms ({peak_eff:.0f} TFLOP/s eff peak)")
+        f"fp16 pairs {fp16 / total:.4f}, roofline {t_roof * 1e3:.3f} ms ({peak_eff:.0f} TFLOP/s eff peak), "
+        f"frac {achieved / peak_eff:.4f}, {n_warm} warm-up steps")
+    del q, k, v, pipe
+    torch.cuda.empty_cache()
     return res
+
+
+def workload_text(name, cfg):
+    return (f"{name}: B={cfg['B']} Hq={cfg['Hq']} Hkv={cfg['Hkv']} N={cfg['N']} n_valid={cfg['n_valid']} "
+            f"D={cfg['D']} {'causal' if cfg['causal'] else 'non-causal'}, {cfg['Bq']}x{cfg['Bk']} tiles, FP16 = top "
+            f"{('k=' + str(cfg['topk'])) if cfg['topk'] >= 0 else str(cfg['ratio_num']) + '%'}"
+            f" + sink {cfg['sink_tiles']} + window {cfg['local_tiles']}"
+            + (f", {cfg['n_lines']} vertical-line token(s) incl. {cfg['sink_tokens']} sink/CLS"
+               if cfg.get("n_lines", 0) else ""))
 
 
 def quality_sweep(args, dev):
@@ -324,11 +357,8 @@ def bench_decode(args, dev):
     q = _bf16(d["q"], dev)
     ws = mxq.decode_workspace(B, Hq, D, 0, int(lens.max()), dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    # the cache build above keeps the GPU idle for seconds: warm the decode
-    # step to steady clocks (at least 50 steps, about 25 ms) before timing
-    for _ in range(max(args.warmup, 50)):
-        mxq.attn_quantkv_decode(q, cache, Hkv, int(lens.max()), workspace=ws, out=out)
-    torch.cuda.synchronize()
+    n_warm = warm(lambda: mxq.attn_quantkv_decode(q, cache, Hkv, int(lens.max()), workspace=ws, out=out),
+                  args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -347,9 +377,8 @@ def bench_decode(args, dev):
     log(f"decode: {ms:.4f} ms/step, {byts / 1e9:.4f} GB, {gbs:.0f} GB/s ({gbs / PEAK_HBM:.3f} of HBM peak)")
     lines_ms = None
     if line_cache is not None:
-        for _ in range(20):
-            mxq.attn_quantkv_decode(q, line_cache, Hkv, int(lens.max()), workspace=ws, out=out)
-        torch.cuda.synchronize()
+        warm(lambda: mxq.attn_quantkv_decode(q, line_cache, Hkv, int(lens.max()), workspace=ws, out=out),
+             args.warmup)
         e0.record()
         for _ in range(args.steps):
             mxq.attn_quantkv_decode(q, line_cache, Hkv, int(lens.max()), workspace=ws, out=out)
@@ -361,87 +390,159 @@ def bench_decode(args, dev):
     # window, the token leaving it is quantised.  Timed on the same arrays with
     # the lengths pulled back so that every append has room (contents differ
     # from the timed decode's from here on; nothing reads them afterwards).
-    n_app = max(args.warmup, 50) + args.steps
+    # (the warm-up rule runs at most about 100 ms of appends, far fewer than
+    # the room of 8192 tokens made here)
+    n_app = 8192
     seq = torch.from_numpy(lens - n_app).to(dev)
     app_cache = mxq.QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, seq, n_sink, n_recent)
     g = torch.Generator(device=dev).manual_seed(4)
     kn = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
     vn = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
-    for _ in range(max(args.warmup, 50)):
-        mxq.attn_quantkv_append(app_cache, kn, vn)
-    torch.cuda.synchronize()
+    n_warm_app = warm(lambda: mxq.attn_quantkv_append(app_cache, kn, vn), args.warmup)
+    assert n_warm_app + args.steps <= n_app
     e0.record()
     for _ in range(args.steps):
         mxq.attn_quantkv_append(app_cache, kn, vn)
     e1.record()
     torch.cuda.synchronize()
     app_ms = e0.elapsed_time(e1) / args.steps
-    assert int(seq[0]) == int(lens[0])
+    assert int(seq[0]) == int(lens[0]) - n_app + n_warm_app + args.steps
     # bytes per append: the window read and written (K and V), the leaving
     # token's fp16 row read and its codes, scales and zeros written, the new rows
     app_bytes = B * Hkv * 2 * (2 * n_recent * D * 2 + D * 2 + D // 2 + 2 * 2 * (D // 32) + D * 2)
     log(f"append: {app_ms * 1e3:.1f} us/step, {app_bytes / 1e6:.1f} MB, "
         f"{app_bytes / (app_ms * 1e-3) / 1e9:.0f} GB/s")
     return dict(ms=ms, bytes=byts, gbs=gbs, append_ms=app_ms, append_bytes=app_bytes, lines_ms=lines_ms,
-                n_lines=n_lines)
+                n_lines=n_lines, warmup_calls=n_warm)
 
 
-def cpu_baseline(args, pre):
-    """The oracle (test infrastructure) timed on the host on a bounded sample of
-    the same workload: per query head in turn, its block selection and the mixed
-    attention of its query tiles (heavy causal tiles first), until about
-    ``--cpu-seconds`` of CPU work."""
+# ---------------------------------------------------------------- CPU baseline
+# The oracle (test infrastructure, never tuned for speed) timed on the host's
+# cores on a bounded sample of the same workloads.  Workers come from a pool
+# forked before the GPU is initialised; each runs single-threaded numpy.
+
+
+def _pool_init():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _oracle_prefill_worker(task):
+    """One query head of a prefill workload: its tile selection, the quantised
+    operands (a1-a3), then the mixed attention of the given query tiles until
+    the time budget runs out.  Returns (valid pairs done, tiles done)."""
     import numpy as np
 
     import oracle
     from oracle import attention as A
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
+    sub, cfg, tiles, budget_s = task
+    t0 = time.perf_counter()
+    mask, _, _ = oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                                      cfg["topk"], cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"],
+                                      cfg["local_tiles"])
+    lines = None
+    if cfg.get("n_lines", 0):
+        lines, _ = oracle.select_lines(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["n_lines"],
+                                       cfg["sink_tokens"])
+    ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
+    pairs = done = 0
+    for i in tiles:
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        A.attn_mixed_ref(sub["q"], sub["k"], sub["v"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
+                         mask=mask, qtiles=[int(i)], ops=ops, lines=lines)
+        r = np.arange(i * cfg["Bq"], min((i + 1) * cfg["Bq"], cfg["n_valid"]))
+        pairs += int(np.minimum(r + 1, cfg["n_valid"]).sum()) if cfg["causal"] else r.size * cfg["n_valid"]
+        done += 1
+    return pairs, done
+
+
+def cpu_baseline_prefill(pool, n_workers, pre, seconds):
+    """Each worker takes one (batch, query head), chosen at random with a fixed
+    seed, and its query tiles in a random order; the rate is the valid pairs
+    done by all workers over the wall time of the pool, and the whole step's
+    CPU time is extrapolated linearly by valid-pair count."""
+    import numpy as np
+
     cfg = pre["cfg"]
     G = cfg["Hq"] // cfg["Hkv"]
     n_qt = cfg["N"] // cfg["Bq"]
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    tiles, pairs, heads = 0, 0, 0
-    try:
-        t0 = time.perf_counter()
-        for b, h in ((b, h) for b in range(cfg["B"]) for h in range(cfg["Hq"])):
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-            kv = slice(h // G, h // G + 1)
-            sub = dict(q=cfg["q"][b:b + 1, h:h + 1], k=cfg["k"][b:b + 1, kv], v=cfg["v"][b:b + 1, kv])
-            oracle.select_blocks(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
-                                 cfg["topk"], cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"],
-                                 cfg["local_tiles"])
-            lines = None
-            if cfg.get("n_lines", 0):
-                oracle.select_lines(sub["q"], sub["k"], cfg["n_valid"], cfg["Bq"], cfg["n_lines"],
-                                    cfg["sink_tokens"])
-                lines = pre["lines"][b:b + 1, h:h + 1]
-            ops = A.prepare_operands(sub["q"], sub["k"], sub["v"], cfg["n_valid"])
-            mask = pre["mask"][b:b + 1, h:h + 1]
-            heads += 1
-            for i in range(n_qt - 1, -1, -1):
-                if time.perf_counter() - t0 >= args.cpu_seconds:
-                    break
-                A.attn_mixed_ref(sub["q"], sub["k"], sub["v"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], cfg["causal"],
-                                 mask=mask, qtiles=[i], ops=ops, lines=lines)
-                tiles += 1
-                r = np.arange(i * cfg["Bq"], min((i + 1) * cfg["Bq"], cfg["n_valid"]))
-                pairs += int(np.clip(r + 1, 0, cfg["n_valid"]).sum()) if cfg["causal"] else r.size * cfg["n_valid"]
-        dt = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
+    rng = np.random.default_rng(1234)
+    heads = [(b, h) for b in range(cfg["B"]) for h in range(cfg["Hq"])]
+    pick = rng.permutation(len(heads))[:n_workers]
+    small = {k: v for k, v in cfg.items() if k not in ("q", "k", "v")}
+    tasks = []
+    for idx in pick:
+        b, h = heads[idx]
+        kv = slice(h // G, h // G + 1)
+        sub = dict(q=cfg["q"][b:b + 1, h:h + 1].copy(), k=cfg["k"][b:b + 1, kv].copy(),
+                   v=cfg["v"][b:b + 1, kv].copy())
+        tasks.append((sub, small, rng.permutation(n_qt), seconds))
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_prefill_worker, tasks, chunksize=1)
+    dt = time.perf_counter() - t0
+    pairs = sum(r[0] for r in res)
+    tiles = sum(r[1] for r in res)
     flops = 4.0 * cfg["D"] * pairs
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"selection plus mixed attention of {tiles} query tiles over {heads} of "
-                       f"{cfg['B'] * cfg['Hq']} (batch, query head) pairs ({pairs} valid pairs of "
-                       f"{pre['total_pairs']}), {dt:.1f} s on 1 host thread, same inputs")
+    est_s = pre["total_pairs"] / (pairs / dt)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=n_workers, kind="oracle",
+                sample=f"{pre['workload']}: {len(tasks)} (batch, query head) pairs, one per worker, each its "
+                       f"selection, quantised operands and the mixed attention of randomly ordered query tiles "
+                       f"for {seconds:.0f} s: {tiles} query tiles, {pairs} of {pre['total_pairs']} valid pairs, "
+                       f"{dt:.1f} s wall on {n_workers} single-threaded processes; the whole step extrapolated "
+                       f"linearly by valid-pair count",
+                extrapolated_step_s=round(est_s, 1))
+
+
+def _oracle_decode_worker(task):
+    """Decode step of the oracle for one sequence: the INT4 cache of each kv
+    head is built (untimed, the cache build is off the step) and the decode
+    attention over it timed, kv head by kv head, until the budget runs out.
+    Returns (cache bytes processed, timed seconds)."""
+    import mxq_inputs
+    from oracle import decode as Dd
+
+    name, b, budget_s = task
+    d = mxq_inputs.make_decode(name, seqs=[b], threads=1)
+    Hq, Hkv, D = d["Hq"], d["Hkv"], d["D"]
+    G = Hq // Hkv
+    n_sink, n_recent = d["n_sink"], d["n_recent"]
+    lens = d["seq_len"][b:b + 1]
+    n = int(lens[0])
+    per_head = (n - n_sink - n_recent) * 2 * (D // 2 + 2 * 2 * (D // 32)) + (n_sink + n_recent) * 2 * D * 2
+    t_busy = 0.0
+    byts = 0
+    for h in range(Hkv):
+        if t_busy >= budget_s:
+            break
+        cache = Dd.build_kv_cache_ref(d["k"][:, h:h + 1], d["v"][:, h:h + 1], lens, n_sink, n_recent)
+        t0 = time.perf_counter()
+        Dd.attn_decode_ref(d["q"][b:b + 1, h * G:(h + 1) * G], cache, lens, n_sink, n_recent)
+        t_busy += time.perf_counter() - t0
+        byts += per_head
+    return byts, t_busy
+
+
+def cpu_baseline_decode(pool, n_workers, dec, seconds):
+    """Each worker takes one sequence (the first n_workers) and times the
+    oracle's decode attention over its cache, kv head by kv head; the rate is
+    the sum of the workers' rates (they run at the same time)."""
+    tasks = [("decode", b, seconds) for b in range(n_workers)]
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_decode_worker, tasks, chunksize=1)
+    dt = time.perf_counter() - t0
+    rate = sum(r[0] / r[1] for r in res if r[1] > 0) / 1e9
+    byts = sum(r[0] for r in res)
+    return dict(value=round(rate, 4), unit="GB/s", cores=n_workers, kind="oracle",
+                sample=f"decode: sequences 0..{n_workers - 1}, one per worker, the oracle's decode attention "
+                       f"over the INT4 + fp16 cache of each kv head (cache build untimed): {byts / 1e9:.3f} GB "
+                       f"of cache processed, {dt:.1f} s wall on {n_workers} single-threaded processes; the "
+                       f"whole step ({dec['bytes'] / 1e9:.4f} GB) would take {dec['bytes'] / 1e9 / rate:.1f} s")
 
 
 def copy_calibration(dev, mib=256, reps=3):
@@ -459,21 +560,44 @@ def copy_calibration(dev, mib=256, reps=3):
     print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}), flush=True)
 
 
+def prefill_summary(pre, with_traffic):
+    """The prefill leg's numbers for the JSON line."""
+    cfg = pre["cfg"]
+    return {
+        "config": {
+            "workload": workload_text(pre["workload"], cfg),
+            "step": "quantize Q,K (MXFP4, with tile means), V (MXFP8 + fp16 copy) -> select tiles"
+                    + (" and lines" if cfg.get("n_lines", 0) else "") + " -> fused mixed attention",
+            "fp16_pair_fraction": round(pre["fp16_pairs"] / pre["total_pairs"], 5),
+            "attn_ms": round(pre["attn_ms"], 4),
+            "attn_tflops": round(pre["tflops_attn"], 2),
+            "warmup_calls": pre["warmup_calls"],
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "attn_mixed_fwd",
+            "achieved": round(pre["tflops_attn"], 2), "peak": round(pre["peak_eff"], 1), "unit": "TFLOP/s",
+            "frac": round(pre["tflops_attn"] / pre["peak_eff"], 4),
+            "traffic": recorded_traffic("attn_mixed_fwd", pre["workload"]) if with_traffic else None,
+            "peak_note": "precision-weighted: FP16 pairs at 2516.6, low-bit pairs half at FP4 10066.4 (QK^T) "
+                         "and half at FP8 5033.2 (PV); achieved = 4*D*valid pairs / attention kernel time",
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # 50 untimed steps (about 35 ms of prefill): fewer leave the GPU clocks
-    # short of their steady state and read a few percent slow
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "long32k", "vit"])
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long32k", choices=["tiny", "llama8b", "long32k", "vit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the Llama-8B-shaped prefill leg")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "quality"], default=None,
                     help="copy: a plain device copy of a known size, the reference for HBM byte counters; "
                          "quality: the synthetic error/speed curve over the FP16 fraction")
     ap.add_argument("--quality-n", default="8192,16384,32768", help="sequence lengths of the quality sweep")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-time budget of each CPU-baseline leg")
     ap.add_argument("--decode-lines", type=int, default=0,
                     help="also time decode with this many vertical-line tokens (fp16) per kv head, at most 16")
     args = ap.parse_args()
@@ -481,6 +605,16 @@ def main():
         print("bench.py: this build runs on exactly one GPU; each (batch, kv head) is independent, so more GPUs "
               "would shard heads with no communication, but that path is not built. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    # the CPU baseline's worker processes are forked before anything touches
+    # the GPU (they never do); at most 16 workers, the host share of one GPU
+    pool = None
+    n_workers = 0
+    want_cpu = not args.no_cpu_baseline and args.only not in ("copy", "quality")
+    if want_cpu:
+        import multiprocessing as mp
+
+        n_workers = max(1, min(len(os.sched_getaffinity(0)), 16))
+        pool = mp.get_context("fork").Pool(n_workers, initializer=_pool_init)
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -494,61 +628,58 @@ def main():
     if args.only == "quality":
         quality_sweep(args, dev)
         return
-    pre = dec = None
+    pre = extra = dec = None
     if args.only != "decode":
-        pre = bench_prefill(args, dev)
+        pre = bench_prefill(args, dev, args.workload)
+        if not args.no_extra and args.only is None and args.workload != "llama8b":
+            extra = bench_prefill(args, dev, "llama8b")
+            for key in ("q", "k", "v"):  # only the headline's inputs feed the CPU baseline
+                extra["cfg"].pop(key)
     if args.only != "prefill" and not args.no_decode:
         dec = bench_decode(args, dev)
-    cpu = None
-    if pre is not None and not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, pre)
-        log(f"cpu baseline: {cpu['value']:.6f} TFLOP/s ({cpu['sample']})")
+    cpu = cpu_dec = None
+    if pool is not None:
+        if pre is not None:
+            cpu = cpu_baseline_prefill(pool, n_workers, pre, args.cpu_seconds)
+            log(f"cpu baseline (prefill): {cpu['value']:.6f} TFLOP/s ({cpu['sample']})")
+        if dec is not None:
+            cpu_dec = cpu_baseline_decode(pool, n_workers, dec, args.cpu_seconds * 2 / 3)
+            log(f"cpu baseline (decode): {cpu_dec['value']:.4f} GB/s ({cpu_dec['sample']})")
+        pool.close()
+        pool.join()
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded N(0,1) bf16; outlier channels and "
             "sink key as in the workload recipe)"}
     if pre is not None:
-        cfg = pre["cfg"]
+        summ = prefill_summary(pre, with_traffic=True)
         line.update(value=round(pre["tflops_step"], 3), unit="TFLOP/s", ms_per_step=round(pre["ms_step"], 4),
-                    dtype="mxfp4 QK^T + fp8 PV, fp16 on selected tiles, fp32 accumulate")
-        line["config"] = {
-            "workload": f"{args.workload}: B={cfg['B']} Hq={cfg['Hq']} Hkv={cfg['Hkv']} N={cfg['N']} "
-                        f"n_valid={cfg['n_valid']} D={cfg['D']} {'causal' if cfg['causal'] else 'non-causal'}, "
-                        f"{cfg['Bq']}x{cfg['Bk']} tiles, FP16 = top "
-                        f"{('k=' + str(cfg['topk'])) if cfg['topk'] >= 0 else str(cfg['ratio_num']) + '%'}"
-                        f" + sink {cfg['sink_tiles']} + window {cfg['local_tiles']}"
-                        + (f", {cfg['n_lines']} vertical-line token(s) incl. {cfg['sink_tokens']} sink/CLS"
-                           if cfg.get("n_lines", 0) else ""),
-            "step": "quantize Q,K (MXFP4), V (MXFP8 + fp16 copy) -> select tiles"
-                    + (" and lines" if cfg.get("n_lines", 0) else "") + " -> fused mixed attention",
-            "fp16_pair_fraction": round(pre["fp16_pairs"] / pre["total_pairs"], 5),
-            "attn_ms": round(pre["attn_ms"], 4),
-            "attn_tflops": round(pre["tflops_attn"], 2),
-        }
-        line["roofline"] = {
-            "bound": "mfma", "kernel": "attn_mixed_fwd",
-            "achieved": round(pre["tflops_attn"], 2), "peak": round(pre["peak_eff"], 1), "unit": "TFLOP/s",
-            "frac": round(pre["tflops_attn"] / pre["peak_eff"], 4),
-            "traffic": recorded_traffic("attn_mixed_fwd") if args.workload == "llama8b" else None,
-            "peak_note": "precision-weighted: FP16 pairs at 2516.6, low-bit pairs half at FP4 10066.4 (QK^T) "
-                         "and half at FP8 5033.2 (PV)",
-        }
+                    dtype="mxfp4 QK^T + fp8 PV, fp16 on selected tiles, fp32 accumulate", config=summ["config"],
+                    roofline=summ["roofline"])
+    if extra is not None:
+        summ = prefill_summary(extra, with_traffic=True)
+        line["llama8b"] = dict(value=round(extra["tflops_step"], 3), unit="TFLOP/s",
+                               ms_per_step=round(extra["ms_step"], 4), **summ)
     if dec is not None:
         dline = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 5),
                  "workload": "decode: 64 seqs x 32768 cached tokens, Hq=32 Hkv=8 D=128, INT4-G32 KV + fp16 "
                              "first 64 / last 128 tokens",
-                 "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": PEAK_HBM, "unit": "GB/s",
-                              "frac": round(dec["gbs"] / PEAK_HBM, 4),
-                              "traffic": recorded_traffic("attn_quantkv_decode")},
+                 "warmup_calls": dec["warmup_calls"],
+                 "roofline": {"bound": "hbm", "kernel": "attn_quantkv_decode", "achieved": round(dec["gbs"], 1),
+                              "peak": PEAK_HBM, "unit": "GB/s", "frac": round(dec["gbs"] / PEAK_HBM, 4),
+                              "traffic": recorded_traffic("attn_quantkv_decode", "decode")},
                  "append": {"ms_per_step": round(dec["append_ms"], 5), "bytes": dec["append_bytes"],
                             "gbs": round(dec["append_bytes"] / (dec["append_ms"] * 1e-3) / 1e9, 1),
                             "what": "attn_quantkv_append: one token per sequence into the fp16 window, the "
                                     "leaving token quantised to INT4"}}
         if dec["lines_ms"] is not None:
             dline["with_lines"] = {"n_lines": dec["n_lines"], "ms_per_step": round(dec["lines_ms"], 5)}
+        if cpu_dec is not None:
+            dline["cpu_baseline"] = cpu_dec
         line["decode"] = dline
         if pre is None:
             line.update(value=dline["value"], unit="GB/s", ms_per_step=dline["ms_per_step"], dtype="int4 KV, fp32",
                         config={"workload": dline["workload"]}, roofline=dline["roofline"])
+            cpu = cpu_dec
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
