@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   attn_select_lines(q, k, shape, n_lines, ..) -> lines, scores
   attn_mixed_fwd(ops, mask, shape, ...)       -> out, lse
   attn_quantkv_decode(q, cache, ...)          -> out
+  attn_quantkv_decode_noalloc(q, cache, ...)  -> out (no workspace: a fixed per-GPU array)
   attn_quantkv_append(cache, k_new, v_new)    -> None (updates the cache in place)
 """
 
@@ -35,7 +36,8 @@ EXPORTED = [
     "mxq_quantize", "mxq_prefill_operands", "mxq_prefill_operands_means", "attn_select_blocks_workspace",
     "attn_select_blocks", "attn_select_blocks_means", "attn_select_lines_workspace",
     "attn_select_lines", "attn_mixed_fwd",
-    "attn_quantkv_decode_workspace", "attn_quantkv_decode", "attn_quantkv_append", "mxq_status_string",
+    "attn_quantkv_decode_workspace", "attn_quantkv_decode", "attn_quantkv_decode_noalloc", "attn_quantkv_append",
+    "mxq_status_string",
     "mxq_last_error", "mxq_version",
 ]
 
@@ -120,6 +122,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_quantkv_decode.argtypes = [vp, ctypes.POINTER(KVCache), i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, vp, sz, vp, vp]
     lib.attn_quantkv_decode.restype = i32
+    lib.attn_quantkv_decode_noalloc.argtypes = [vp, ctypes.POINTER(KVCache), i32, i32, i32, i32, i32,
+                                                ctypes.c_float, i32, vp, vp]
+    lib.attn_quantkv_decode_noalloc.restype = i32
     lib.attn_quantkv_append.argtypes = [vp, vp, ctypes.POINTER(KVCacheRW), i32, i32, i32, vp]
     lib.attn_quantkv_append.restype = i32
     lib.mxq_status_string.argtypes = [i32]
@@ -516,6 +521,24 @@ def attn_quantkv_decode(q, cache: QuantKVCache, Hkv, max_seq_len, softmax_scale=
     _check(load_library().attn_quantkv_decode(_ptr(q), ctypes.byref(kv), B, Hq, Hkv, D, int(max_seq_len),
                                               float(softmax_scale), int(num_splits), _ptr(ws), ws.numel(),
                                               _ptr(out), _stream()))
+    return out
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # MXQ_DECODE_SCRATCH_BYTES
+
+
+def attn_quantkv_decode_noalloc(q, cache: QuantKVCache, Hkv, max_seq_len, softmax_scale=0.0, num_splits=0, out=None):
+    """attn_quantkv_decode with the split partials in the library's fixed
+    per-GPU array: no workspace, nothing allocated by the library (out must be
+    passed in for a call that allocates nothing at all).  Calls that overlap on
+    one GPU race on that array."""
+    _need_gpu(q)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    kv = cache.c()
+    _check(load_library().attn_quantkv_decode_noalloc(_ptr(q), ctypes.byref(kv), B, Hq, Hkv, D, int(max_seq_len),
+                                                      float(softmax_scale), int(num_splits), _ptr(out), _stream()))
     return out
 
 

@@ -39,6 +39,9 @@
 // their blocks and split S adds them to its fp16 tokens.
 // k_decode_merge: (sequence, query head): merge the S+1 partials in ascending
 // split order, 16 at a time.
+#include <mutex>
+#include <string>
+
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -674,10 +677,12 @@ extern "C" size_t attn_quantkv_decode_workspace(int32_t B, int32_t Hq, int32_t D
   return static_cast<size_t>(B) * Hq * (S + 1) * (D + 2) * sizeof(float);
 }
 
-extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache* kv, int32_t B,
-                                          int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
-                                          float softmax_scale, int32_t num_splits, void* workspace,
-                                          size_t ws_bytes, float* out, mxq_stream_t stream) {
+namespace mxq {
+namespace {
+
+// Host checks shared by both decode entry points; nothing is launched on error.
+mxq_status validate_decode(const uint16_t* q, const mxq_kv_cache* kv, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out) {
   MXQ_REQUIRE(q && kv && out, MXQ_EINVAL, "attn_quantkv_decode: q, cache and out are required");
   MXQ_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, MXQ_EINVAL,
               "attn_quantkv_decode: need B, Hq, Hkv >= 1 and Hq % Hkv == 0");
@@ -704,18 +709,24 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
   MXQ_REQUIRE(num_splits >= 0 && num_splits <= 4096, MXQ_EINVAL, "attn_quantkv_decode: num_splits out of range");
   MXQ_REQUIRE(B <= 65535 && Hkv <= 65535, MXQ_EUNSUPPORTED, "attn_quantkv_decode: B, Hkv must be <= 65535");
   MXQ_REQUIRE(!(softmax_scale != softmax_scale), MXQ_EINVAL, "attn_quantkv_decode: softmax_scale is NaN");
+  return MXQ_OK;
+}
+
+// Both decode launches on `stream`, with the split partials in `ws` (device
+// memory of at least attn_quantkv_decode_workspace(...) bytes).
+mxq_status launch_decode(const uint16_t* q, const mxq_kv_cache* kv, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* ws,
+                         float* out, hipStream_t st) {
+  const int G = Hq / Hkv;
   const int S = pick_splits(max_seq_len, num_splits);
-  MXQ_REQUIRE(workspace && ws_bytes >= attn_quantkv_decode_workspace(B, Hq, D, num_splits, max_seq_len),
-              MXQ_EINVAL, "attn_quantkv_decode: workspace too small");
   DecodeArgs a;
-  a.q = q; a.kv = *kv; a.ws = static_cast<float*>(workspace); a.Hq = Hq; a.Hkv = Hkv; a.S = S;
+  a.q = q; a.kv = *kv; a.ws = ws; a.Hq = Hq; a.Hkv = Hkv; a.S = S;
   // INT4 tokens per split: at most max_seq_len in total, whole 32-token blocks per wave
   int tps = (max_seq_len + S - 1) / S;
   tps = (tps + kWaves * kBlk - 1) / (kWaves * kBlk) * (kWaves * kBlk);
   a.tokens_per_split = tps;
   const double sc = softmax_scale > 0.0f ? static_cast<double>(softmax_scale) : 1.0 / __builtin_sqrt(static_cast<double>(D));
   a.c = static_cast<float>(sc * 1.4426950408889634);
-  hipStream_t st = as_stream(stream);
   dim3 grid(S + 1, Hkv, B);
   const bool lines = kv->n_lines > 0;
   switch (G * 2 + (lines ? 1 : 0)) {
@@ -730,4 +741,74 @@ extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache*
   if (stt != MXQ_OK) return stt;
   hipLaunchKernelGGL(k_decode_merge, dim3(Hq, B), dim3(kD), 0, st, a.ws, out, Hq, S + 1);
   return check_launch("k_decode_merge");
+}
+
+}  // namespace
+}  // namespace mxq
+
+extern "C" mxq_status attn_quantkv_decode(const uint16_t* q, const mxq_kv_cache* kv, int32_t B,
+                                          int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
+                                          float softmax_scale, int32_t num_splits, void* workspace,
+                                          size_t ws_bytes, float* out, mxq_stream_t stream) {
+  mxq_status st = validate_decode(q, kv, B, Hq, Hkv, D, max_seq_len, softmax_scale, num_splits, out);
+  if (st != MXQ_OK) return st;
+  MXQ_REQUIRE(workspace && ws_bytes >= attn_quantkv_decode_workspace(B, Hq, D, num_splits, max_seq_len),
+              MXQ_EINVAL, "attn_quantkv_decode: workspace too small");
+  return launch_decode(q, kv, B, Hq, Hkv, D, max_seq_len, softmax_scale, num_splits,
+                       static_cast<float*>(workspace), out, as_stream(stream));
+}
+
+// ---- the allocation-free variant ---------------------------------------------
+// The split partials live in this file-scope device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy for the life of
+// the process.  In host code `scratch` names a host-side stand-in, not device
+// memory: the device address of the current GPU's copy comes from
+// hipGetSymbolAddress, taken once per device and kept in scratch_ptr[].
+static __device__ __align__(256) uint8_t scratch[MXQ_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (taken under a lock on the first
+// call on that device).
+mxq_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return mxq::fail(MXQ_EHIP, std::string("attn_quantkv_decode_noalloc: hipGetDevice: ") +
+                                                      hipGetErrorString(e));
+  MXQ_REQUIRE(dev >= 0 && dev < kMaxDevices, MXQ_EUNSUPPORTED,
+              "attn_quantkv_decode_noalloc: device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return mxq::fail(MXQ_EHIP, std::string("attn_quantkv_decode_noalloc: hipGetSymbolAddress: ") +
+                                     hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MXQ_OK;
+}
+}  // namespace
+
+extern "C" mxq_status attn_quantkv_decode_noalloc(const uint16_t* q, const mxq_kv_cache* kv, int32_t B,
+                                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
+                                                  float softmax_scale, int32_t num_splits, float* out,
+                                                  mxq_stream_t stream) {
+  mxq_status st = validate_decode(q, kv, B, Hq, Hkv, D, max_seq_len, softmax_scale, num_splits, out);
+  if (st != MXQ_OK) return st;
+  const size_t need = attn_quantkv_decode_workspace(B, Hq, D, num_splits, max_seq_len);
+  MXQ_REQUIRE(need <= static_cast<size_t>(MXQ_DECODE_SCRATCH_BYTES), MXQ_EINVAL,
+              "attn_quantkv_decode_noalloc: the split partials need " + std::to_string(need) +
+                  " bytes, beyond the library's fixed scratch of " +
+                  std::to_string(static_cast<size_t>(MXQ_DECODE_SCRATCH_BYTES)) +
+                  " bytes (use fewer splits or sequences, or attn_quantkv_decode with a workspace)");
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != MXQ_OK) return st;
+  return launch_decode(q, kv, B, Hq, Hkv, D, max_seq_len, softmax_scale, num_splits, static_cast<float*>(ws),
+                       out, as_stream(stream));
 }

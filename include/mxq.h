@@ -35,7 +35,8 @@
  *    pairs).  MXQ_EHIP: a HIP launch error; mxq_last_error() has the text.
  *    Faults inside kernels surface at the caller's next synchronisation.
  *  - Results are deterministic: the same inputs give the same bits.
- *  - Calls are reentrant and hold no state between calls.
+ *  - Calls are reentrant and hold no state between calls, except the one
+ *    fixed device array of attn_quantkv_decode_noalloc (see there).
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -315,6 +316,29 @@ mxq_status attn_quantkv_decode(const uint16_t* q_bf16, const mxq_kv_cache* cache
                                int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
                                float softmax_scale, int32_t num_splits, void* workspace,
                                size_t ws_bytes, float* out, mxq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_quantkv_decode_noalloc -- attn_quantkv_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and the same results, bit
+ * for bit, with the split partials held in a fixed array inside the library
+ * instead of a caller workspace.  It allocates nothing and calls no allocating
+ * routine.
+ * Limit: attn_quantkv_decode_workspace(B, Hq, D, num_splits, max_seq_len) must
+ * not exceed MXQ_DECODE_SCRATCH_BYTES (16 MiB: e.g. 64 sequences x 32 query
+ * heads at the default 8 + 1 splits of a 32768-token cache take 9.6 MB);
+ * larger requests return MXQ_EINVAL with nothing launched.
+ * Each GPU holds one copy of the array for the life of the process, shared by
+ * every call on that GPU: calls that overlap on one GPU (other streams, other
+ * host threads) race on it and must be serialised by the caller.  No contents
+ * need clearing between calls (every split writes its whole partial).
+ * Arguments, layouts and errors otherwise as attn_quantkv_decode.
+ * ------------------------------------------------------------------------- */
+#define MXQ_DECODE_SCRATCH_BYTES (16u << 20)
+mxq_status attn_quantkv_decode_noalloc(const uint16_t* q_bf16, const mxq_kv_cache* cache, int32_t B,
+                                       int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
+                                       float softmax_scale, int32_t num_splits, float* out,
+                                       mxq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * attn_quantkv_append -- one decode step's cache update (HyQuant summary and
