@@ -103,6 +103,21 @@ __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf
 
 // Row maximum over the 4 lane groups (lanes col, col+16, col+32, col+48) with
 // two cross-row swaps (v_permlane16_swap / v_permlane32_swap), no LDS traffic.
+// Row maxima of two values at once (a: tile 0, b: tile 1): one swap pairs the
+// groups of a with those of b, a second folds the halves, a third hands each
+// lane the other value.  Three swaps and two maxima instead of four and four.
+__device__ __forceinline__ void rowmax4x2(float a, float b, float& ra, float& rb) {
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  // group 0: a of groups 0/1, 1: b of 0/1, 2: a of 2/3, 3: b of 2/3
+  const uint32_t m = __float_as_uint(fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1])));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  // groups 0 and 2: max of a; groups 1 and 3: max of b
+  const uint32_t r = __float_as_uint(fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1])));
+  const auto q16 = __builtin_amdgcn_permlane16_swap(r, r, false, false);
+  ra = __uint_as_float(q16[0]);
+  rb = __uint_as_float(q16[1]);
+}
+
 __device__ __forceinline__ float rowmax4(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -512,7 +527,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // all-ones MFMA operands for the row sums (E4M3 1.0 and fp16 1.0), kept in
   // registers: an LDS read here would be made to wait for copies in flight
   constexpr int kOne8 = 0x38383838, kOne16 = 0x3C003C00;
-  const v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
+  v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
+  __asm__ volatile("" : "+v"(ones8));  // kept in registers, not rebuilt before every use
 
   // per-lane LDS byte offsets (constant over the pass)
   // K fragment of S block beta: a per-lane base plus a constant per block
@@ -628,23 +644,33 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // exponentials, its QK MFMA for the next chunk, every 8/NDB blocks one PV
   // MFMA of the pending chunk (V fragments one head_dim block ahead), and the
   // partial maxima of the block whose QK MFMA was issued three blocks before.
-  auto pipe = [&](const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb) {
+  // Variants of the step: EX, the chunk has a live tile (some row's low-bit P
+  // is nonzero, see tile_live), so its exponentials run (a dead chunk's P is
+  // zero); PV, the pending chunk had a live tile, so its PV MFMAs and their V
+  // reads run.  Each variant keeps the whole step's issue order; the choice is
+  // one scalar branch per chunk.
+  auto pipe = [&](auto EXc, auto PVc, const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb) {
+    constexpr bool EX = decltype(EXc)::value, PV = decltype(PVc)::value;
     float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
     float off1 = kGridMagic + kExpOffset - (hm1 == NEG_INF ? 0.0f : hm1);
     // opaque from here on: the exponentials cannot be moved out of this step
     // (the compiler would otherwise compute them where the references are set)
-    __asm__ volatile("" : "+v"(off0), "+v"(off1));
+    if constexpr (EX) __asm__ volatile("" : "+v"(off0), "+v"(off1));
     const uint32_t* ksw = reinterpret_cast<const uint32_t*>(kbn + ksoff);
     const uint32_t nks0 = ksw[0], nks1 = ksw[1];
-    const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vbp + vsoff);
-    const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
+    uint32_t vsc0 = 0u, vsc1 = 0u;
+    if constexpr (PV) {
+      const uint32_t* vsw = reinterpret_cast<const uint32_t*>(vbp + vsoff);
+      vsc0 = vsw[0];
+      vsc1 = NDB > 4 ? vsw[1] : 0u;
+    }
     constexpr int KAHEAD = 3;  // K fragments in flight ahead of their MFMA
     constexpr int SPB = 8 / NDB;  // S blocks per PV MFMA
     v4i kn[8];
     v8i va[NDB];
 #pragma unroll
     for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(kbn + koff(beta));
-    va[0] = vfrag(vbp, 0);
+    if constexpr (PV) va[0] = vfrag(vbp, 0);
     mxa = NEG_INF;
     mxb = NEG_INF;
     __builtin_amdgcn_sched_barrier(0);
@@ -658,19 +684,28 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       if (beta == 4) __builtin_amdgcn_s_setprio(1);
       if (beta == 6) __builtin_amdgcn_s_setprio(0);
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
-      pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
-      __asm__ volatile("" ::"v"(pb[beta]));  // formed here, not where it is next read
+      if constexpr (EX) {
+        pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
+        __asm__ volatile("" ::"v"(pb[beta]));  // formed here, not where it is next read
+      } else {
+        pb[beta] = 0;
+        // the scores this MFMA replaces are read here, as the exponentials do
+        // in the other variant, so both keep S in the same registers
+        __asm__ volatile("" ::"v"(S[beta]));
+      }
       const v8i ka = {kn[beta][0], kn[beta][1], kn[beta][2], kn[beta][3], 0, 0, 0, 0};
       S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
-      if (beta % SPB == SPB - 1) {
-        const int db = beta / SPB;
-        if (db + 1 < NDB) va[db + 1] = vfrag(vbp, db + 1);
-        O[db] = pv_block(va[db], pb_p, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), pscp, db);
+      if constexpr (PV) {
+        if (beta % SPB == SPB - 1) {
+          const int db = beta / SPB;
+          if (db + 1 < NDB) va[db + 1] = vfrag(vbp, db + 1);
+          O[db] = pv_block(va[db], pb_p, O[db], db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1), pscp, db);
+        }
       }
       if (beta >= 3) s_max(beta - 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb_p, L, 0, 0, 0, 127, 0, pscp);
+    if constexpr (PV) L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb_p, L, 0, 0, 0, 127, 0, pscp);
     s_max(5);
     s_max(6);
     s_max(7);
@@ -855,11 +890,27 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   }
   // integer tile references of an unmasked all-low-bit chunk from the partial
   // maxima of its scores; O's reference follows when it lags too far
+  // A tile is live for this wave when some row's low-bit P there can be
+  // nonzero: P = E4M3(2^x) is 0 exactly when x = fl32(S*c + off) - 6144 <= -10
+  // (2^-10 is the tie between 0 and the smallest subnormal), and the fused
+  // multiply-add is monotonic in S, so the row maximum decides for the row.
+  auto tile_live = [&](float rmax, float href) -> bool {
+    const float off = kGridMagic + kExpOffset - (href == NEG_INF ? 0.0f : href);
+    return __any(__builtin_fmaf(rmax, c, off) > kGridMagic - 10.0f);
+  };
+  bool live0 = true, live1 = true;  // tiles of chunk ch with a nonzero low-bit P (this wave)
+  bool pend_live = false;           // the pending chunk has a live tile
+  // integer tile references of an unmasked all-low-bit chunk from the partial
+  // maxima of its scores; O's reference follows when it lags too far
   auto hot_refs = [&]() {
-    hm0 = fmaxf(m_run, ceilf(rowmax4(mxa) * c));
-    hm1 = fmaxf(hm0, ceilf(rowmax4(mxb) * c));
+    float ra, rb;
+    rowmax4x2(mxa, mxb, ra, rb);
+    hm0 = fmaxf(m_run, ceilf(ra * c));
+    hm1 = fmaxf(hm0, ceilf(rb * c));
     m_run = hm1;
     chunk_lag(hm0, hm1);
+    live0 = tile_live(ra, hm0);
+    live1 = tile_live(rb, hm1);
   };
   int vslot = 0;    // V buffer of chunk ch
   int vslot_p = LY::RV - 1;  // V buffer of the pending chunk (none yet: P = 0 over the zeroed buffer)
@@ -920,6 +971,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       const bool has_line = LINES && (f_cur & 64);  // line keys run in the line tile, not here
       const bool low_w = !(f_cur & 1) || (valid1 && !(f_cur & 2));  // this wave runs FP8 PV
       float m_tile0 = NEG_INF;
+      float low0 = NEG_INF, low1 = NEG_INF;  // row maxima of the low-bit scores left in each tile
       if (hi_now) {  // FP16 tiles issued after this chunk's barrier: let them land, then publish
         // (a chunk with a promoted tile is masked-path for every wave)
         if (lowbit) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
@@ -970,6 +1022,10 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         const float m_t = fmaxf(m_run, ceilf(mx * c));
         m_run = m_t;
         if (t == 0) m_tile0 = m_t;
+        if (!prom) {
+          if (t == 0) low0 = mx;
+          else low1 = mx;
+        }
         if (prom) {
           // P relative to O's reference m_o <= m_t: the same fp16 values scaled
           // by 2^(m_t - m_o) (exact while normal), so O needs no rescale unless
@@ -1007,6 +1063,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       // tile references of the low-bit P: each tile's running maximum
       hm0 = m_tile0;
       hm1 = m_run;
+      live0 = tile_live(low0, hm0);
+      live1 = tile_live(low1, hm1);
       if (low_w) {
         // as for unmasked chunks: each tile's P enters through the E8M0 scale
         // 2^-8 * 2^(m_t - m_o); O is rescaled only when the lag grows large
@@ -1016,8 +1074,18 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     }
     // ================= the pipeline step: P of chunk ch, QK of chunk ch+1, PV of chunk ch-1
     v8i pb;
-    pipe(kbuf(ch + 1), vbuf(vslot_p), pend_scale(), pb);
+    {
+      const std::true_type T{};
+      const std::false_type F{};
+      const uint8_t* kbn = kbuf(ch + 1);
+      const uint8_t* vbp = vbuf(vslot_p);
+      // (one step with PV MFMAs, so that O has a single update site: two
+      // would make the compiler copy O between register sets every chunk)
+      if (live0 || live1 || pend_live) pipe(T, T, kbn, vbp, pend_scale(), pb);
+      else pipe(F, F, kbn, vbp, 0, pb);
+    }
     pb_p = pb;
+    pend_live = live0 || live1;
     hp0 = hm0;
     hp1 = hm1;
     vslot_p = vslot;
@@ -1035,7 +1103,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // published by this barrier for the last PV
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  pv_flush(vbuf(vslot_p), pend_scale());
+  if (pend_live) pv_flush(vbuf(vslot_p), pend_scale());
 
   // ---------------------------------------------------------------- epilogue
   // out = O / l is independent of the reference; lse uses O's reference m_o
