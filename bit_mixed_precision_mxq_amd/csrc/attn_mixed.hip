@@ -1132,6 +1132,468 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   (void)wave_live;
 }
 
+// ---------------------------------------------------------------------------
+// Short sequences (N <= 256: at most two 128-key chunks), such as ViT-shaped
+// batches.  The same arithmetic per chunk as k_attn_mixed (FP4 QK^T, the
+// integer tile references, P on the 2^-11 grid, FP8 PV with each tile's
+// reference in its E8M0 scale, FP16 tiles and vertical lines, the same
+// operand layouts), without its software pipeline: with one or two chunks a
+// workgroup's time is its prologue, so workgroups are small instead.
+//   workgroup = (batch, query head, 64 query rows), 4 waves of 16 rows; the
+//               head's MXFP4 K and MXFP8 V^T (and their scales) are staged
+//               once in LDS (26 KB at head_dim 64), so several workgroups
+//               share a CU;
+//   FP16 tiles and line keys read their bf16 K rows and fp16 V^T straight
+//   from global memory into the MFMA operand registers (bounds-checked
+//   buffer loads; unused entries read zeros).
+template <int D, bool LINES>
+__global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
+  using LY = Lds<D>;
+  constexpr int BQ = 64;   // query rows per workgroup
+  constexpr int NT = 256;  // 4 waves of 16 rows
+  constexpr int KROW = D / 2;
+  constexpr int NDB = D / 16;
+  constexpr int NSB = D / 32;
+  constexpr int NCH = 2;   // 128-key chunks
+  constexpr float NEG_INF = -__builtin_inff();
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[NCH][128 * KROW];  // K codes, Lds<D>::k_off layout
+  __shared__ __attribute__((aligned(16))) uint8_t s_ks[NCH][4 * 16 * 8];  // K scales [g][row][S block]
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[NCH][D * 128];     // V^T codes, Lds<D>::vrow_off layout
+  __shared__ __attribute__((aligned(16))) uint8_t s_vs[NCH][4 * 16 * 8];  // V scales [key block][d%16][d/16]
+  __shared__ uint32_t s_lm[NCH][4];  // line keys of a chunk per lane group: bit 16t + (key & 15)
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int it = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
+  const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + h / G;
+  const int qs = it * BQ;
+  const int q = qs + wave * 16 + col;
+
+  if (qs >= a.n_valid) {  // a tile of padding rows: output 0, lse -inf
+    for (int idx = tid; idx < BQ * D; idx += NT) {
+      const int64_t o = (bhq * a.N + qs) * D + idx;
+      if (a.out_bf16) static_cast<uint16_t*>(a.out)[o] = 0;
+      else static_cast<float*>(a.out)[o] = 0.0f;
+    }
+    if (a.lse)
+      for (int r = tid; r < BQ; r += NT) a.lse[bhq * a.N + qs + r] = NEG_INF;
+    return;
+  }
+  const int qe = min(qs + BQ, a.n_valid) - 1;
+  int last_tile = (a.n_valid - 1) / 64;
+  if (a.causal) last_tile = min(last_tile, qe / 64);
+  last_tile = __builtin_amdgcn_readfirstlane(last_tile);
+  const int n_chunks = (last_tile + 2) / 2;  // 1 or 2
+  const float c = a.c;
+
+  auto rsrc = [](const void* base, int64_t off_bytes, int64_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base) + (base ? off_bytes : 0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(base ? bytes : 0));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, n,
+                                             0x00020000);
+  };
+  const auto r_qc = rsrc(a.q_codes, bhq * a.N * KROW, static_cast<int64_t>(a.N) * KROW);
+  const auto r_qs = rsrc(a.q_scales, bhq * a.N * NSB, static_cast<int64_t>(a.N) * NSB);
+  const auto r_kc = rsrc(a.k_codes, bhk * a.N * KROW, static_cast<int64_t>(a.N) * KROW);
+  const auto r_ks = rsrc(a.k_scales, bhk * a.N * NSB, static_cast<int64_t>(a.N) * NSB);
+  const auto r_vc = rsrc(a.v_codes, bhk * D * a.N, static_cast<int64_t>(D) * a.N);
+  const auto r_vs = rsrc(a.v_scales, bhk * D * (a.N / 32), static_cast<int64_t>(D) * (a.N / 32));
+  const auto r_hk = rsrc(a.k_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2);
+  const auto r_hv = rsrc(a.v_f16t, bhk * D * a.N * 2, static_cast<int64_t>(D) * a.N * 2);
+  constexpr int kOut = 0x7FFFFFF0;  // an offset past every slice: the load returns zeros
+
+  // ---- the FP4 Q fragment (B operand of S^T = K Q^T; groups g >= D/32 read
+  // zero codes and a zero scale byte) and the bf16 Q slices of FP16 tiles
+  const v4i qw = __builtin_bit_cast(
+      v4i, __builtin_amdgcn_raw_buffer_load_b128(r_qc, g < NSB ? q * KROW + 16 * g : kOut, 0, 0));
+  const v8i qf4 = {qw[0], qw[1], qw[2], qw[3], 0, 0, 0, 0};
+  const int qsc = __builtin_amdgcn_raw_buffer_load_b8(r_qs, g < NSB ? q * NSB + g : kOut, 0, 0);
+  v8bf qbr[NSB];
+#pragma unroll
+  for (int st = 0; st < NSB; ++st) qbr[st] = v8bf{};
+  if (a.mode != MXQ_ALL_LOWBIT || LINES) {
+#pragma unroll
+    for (int st = 0; st < NSB; ++st)
+      qbr[st] = *reinterpret_cast<const v8bf*>(a.q_bf16 + (bhq * a.N + q) * D + 8 * (4 * st + g));
+  }
+
+  // ---- stage the head's low-bit K and V (both chunks) in LDS: every
+  // thread's loads go out first (a chunk past the slice reads zeros), then
+  // the LDS writes, so the staging costs one memory round trip
+  const bool lowbit = a.mode != MXQ_ALL_FP16;
+  constexpr int KU = NCH * 128 * KROW / 16;  // 16-byte K units
+  constexpr int VU = NCH * D * 8;            // 16-byte V^T units
+  constexpr int KPT = KU / NT, VPT = VU / NT;
+  static_assert(KU % NT == 0 && VU % NT == 0, "whole units per thread");
+  constexpr int KSW = NCH * 128 * NSB / 4;   // K scale words (four scale bytes each)
+  constexpr int VSW = D * (NCH * 4 / 4);     // V scale words: one per row d (4 key blocks per chunk)
+  static_assert(KSW <= NT && D <= NT, "one scale word per thread");
+  if (lowbit) {
+    v4i kw[KPT], vw[VPT];
+    uint32_t ksw = 0u, vsw0 = 0u, vsw1 = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + i * NT;
+      const int key = u / (KROW / 16), gu = u % (KROW / 16);  // key over both chunks
+      kw[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r_kc, key * KROW + 16 * gu, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * NT;
+      const int ch = u / (D * 8), r = u % (D * 8);
+      const int d = r / 8, vu = r % 8;
+      vw[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r_vc, d * a.N + ch * 128 + 16 * vu, 0, 0));
+    }
+    if (tid < KSW) ksw = __builtin_amdgcn_raw_buffer_load_b32(r_ks, 4 * tid, 0, 0);  // keys' scale bytes, in order
+    if (tid < D) {  // row d's scale bytes of key blocks 0..3 and 4..7
+      vsw0 = __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32), 0, 0);
+      vsw1 = __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32) + 4, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + i * NT;
+      const int key = u / (KROW / 16), gu = u % (KROW / 16);
+      *reinterpret_cast<v4i*>(&s_k[key >> 7][LY::k_off(key & 127, gu)]) = kw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * NT;
+      const int ch = u / (D * 8), r = u % (D * 8);
+      *reinterpret_cast<v4i*>(&s_v[ch][LY::vrow_off(r / 8, r % 8)]) = vw[i];
+    }
+    // K scale of (key, block kg) -> [kg][A row of the key][S block of the
+    // key]; blocks kg >= D/32 hold no head_dim data: 127, a finite 1.0
+    if (tid < KSW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = 4 * tid + j;  // byte index: key * NSB + kg
+        const int keyf = idx / NSB, kg = idx % NSB;
+        const int ch = keyf >> 7, key = keyf & 127;
+        const int kcol = 4 * ((key >> 4) & 3) + (key & 3);
+        const int kbeta = 4 * (key >> 6) + ((key >> 2) & 3);
+        s_ks[ch][(kg * 16 + kcol) * 8 + kbeta] = static_cast<uint8_t>(ksw >> (8 * j));
+      }
+    }
+    if constexpr (NSB < 4) {
+      constexpr int PAD = (4 - NSB) * 16 * 8;
+      for (int i = tid; i < NCH * PAD; i += NT) s_ks[i / PAD][NSB * 16 * 8 + i % PAD] = 127;
+    }
+    if (tid < D) {  // V scales of row d -> [key block][d % 16][d / 16] per chunk
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s_vs[0][(kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(vsw0 >> (8 * kb));
+        s_vs[1][(kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(vsw1 >> (8 * kb));
+      }
+    }
+  }
+  // ---- vertical-line keys (HyQuant): entry e takes part when 0 <= key <
+  // n_valid and it exceeds every earlier entry (exclusive prefix maximum by DPP
+  // row shifts); lane e < 16 of every wave holds entry e's key, else -1
+  int lkey = -1;
+  if constexpr (LINES) {
+    const int raw = (lane < 16 && lane < a.n_lines) ? a.lines[bhq * a.n_lines + lane] : -1;
+    constexpr int kMin = -2147483647 - 1;
+    int v = raw;
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    const int before = __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false);
+    if (lane < 16 && raw >= 0 && raw < a.n_valid && raw > before) lkey = raw;
+  }
+  // entry e's key, from lane e (an LDS permute: no copies are in flight here)
+  auto lane_key = [&](int e) -> int { return __shfl(lkey, e); };
+  // word (chunk, lane group) of the line-key bits, one thread each (the
+  // thread reads the entries of its own wave, which holds the same list)
+  if (tid < NCH * 4) {
+    uint32_t m = 0;
+    if constexpr (LINES) {
+#pragma unroll
+      for (int e = 0; e < kMaxLines; ++e) {
+        const int k = __builtin_amdgcn_readlane(lkey, e);
+        if (k >= 0 && (k >> 7) == (tid >> 2) && ((k >> 4) & 3) == (tid & 3))
+          m |= 1u << (16 * ((k >> 6) & 1) + (k & 15));
+      }
+    }
+    (&s_lm[0][0])[tid] = m;
+  }
+  __syncthreads();  // staged codes, scales and line bits
+
+  v4f O[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) O[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4f L = {0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF;  // running integer reference (log2 units)
+  float m_o = NEG_INF;    // reference O and L are expressed in
+  auto rebase = [&](float m) {  // rescale O and L from m_o to m >= m_o (powers of two)
+    if (__any(m != m_o)) {
+      float f = 1.0f;
+      if (m_o != NEG_INF && m != m_o) f = __builtin_ldexpf(1.0f, static_cast<int>(fmaxf(m_o - m, -256.0f)));
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) O[i] *= f;
+      L *= f;
+    }
+    m_o = m;
+  };
+
+  if constexpr (LINES) {
+    // the line tile, first in the reference order: S^T[16 entries x 16 queries]
+    // with the bf16 MFMA (entry col's K row as A), P = fp16(2^x), then V^T of
+    // the entries (fp16, [d][entry]) times P^T with the 16x16x16 fp16 MFMA
+    const int kcol_key = lane_key(col);
+    v4f SL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NSB; ++st) {
+      const v8bf ka = __builtin_bit_cast(
+          v8bf, __builtin_amdgcn_raw_buffer_load_b128(r_hk, kcol_key >= 0 ? (kcol_key * D + 32 * st + 8 * g) * 2
+                                                                            : kOut, 0, 0));
+      SL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbr[st], SL, 0, 0, 0);
+    }
+    int lk4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lk4[i] = lane_key(4 * g + i);
+    float mx = NEG_INF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = lk4[i] >= 0 && q < a.n_valid && (!a.causal || lk4[i] <= q);
+      if (!ok) SL[i] = NEG_INF;
+      mx = fmaxf(mx, SL[i]);
+    }
+    mx = rowmax4(mx);
+    m_run = ceilf(mx * c);  // -inf when the row sees no line
+    m_o = m_run;
+    const float m_ref = m_run == NEG_INF ? 0.0f : m_run;
+    v4h ph;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ph[i] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(SL[i], c, -m_ref)));
+    v4h vl[NDB];  // all the entries' values first, then the MFMAs
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(
+            r_hv, lk4[i] >= 0 ? ((16 * db + col) * a.N + lk4[i]) * 2 : kOut, 0, 0);
+        vl[db][i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(hv));
+      }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(vl[db], ph, O[db], 0, 0, 0);
+    const v4h ones4 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f),
+                       static_cast<_Float16>(1.0f)};
+    L = __builtin_amdgcn_mfma_f32_16x16x16f16(ones4, ph, L, 0, 0, 0);
+  }
+
+  // promotion flags of this workgroup's rows (one selection row: 64 rows lie
+  // in one 64- or 128-row selection tile)
+  const uint32_t* mrow = (a.mode == MXQ_MIXED && a.mask)
+                             ? a.mask + (bhq * (a.N / a.sel_bq) + qs / a.sel_bq) * a.words
+                             : nullptr;
+  constexpr int kOne8 = 0x38383838, kOne16 = 0x3C003C00;
+  const v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
+  const int kbase0 = LY::k_off(chunk_key(0, col), g);
+  const int kbase1 = LY::k_off(chunk_key(1, col), g);
+  auto koff = [&](int beta) -> int {
+    if constexpr (D == 128) {
+      return kbase0 + LY::KROW * (64 * (beta >> 2) + 4 * (beta & 3));
+    } else {
+      return (beta & 1 ? kbase1 : kbase0) + LY::KROW * (64 * (beta >> 2) + 4 * (beta & 2));
+    }
+  };
+  const int voff = LY::vrow_off(col, g);
+
+  // a wave whose 16 rows are all padding computes nothing (its rows are
+  // written as zeros); in other waves padding rows need no mask: their Q is
+  // zero, so their scores are finite, and their output is replaced by zeros
+  const int n_ch_wave = __builtin_amdgcn_readfirstlane(qs + 16 * wave) < a.n_valid ? n_chunks : 0;
+  // keys a row may see: below n_valid, and up to the row itself when causal
+  const int kmax = a.causal ? min(a.n_valid, q + 1) : a.n_valid;
+#pragma unroll 1
+  for (int ch = 0; ch < n_ch_wave; ++ch) {
+    const int kc = ch * 128;
+    const bool valid1 = 2 * ch + 1 <= last_tile;
+    v4f S[8];
+    if (lowbit) {
+      const uint32_t* ksw = reinterpret_cast<const uint32_t*>(&s_ks[ch][(g * 16 + col) * 8]);
+      const uint32_t ksc0 = ksw[0], ksc1 = ksw[1];
+#pragma unroll
+      for (int beta = 0; beta < 8; ++beta) {
+        const v4i w = *reinterpret_cast<const v4i*>(&s_k[ch][koff(beta)]);
+        const v8i ka = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+        const int sc = beta < 4 ? static_cast<int>(ksc0) : static_cast<int>(ksc1);
+        switch (beta & 3) {
+          case 0: S[beta] = MXQ_QK_BLOCK(0); break;
+          case 1: S[beta] = MXQ_QK_BLOCK(1); break;
+          case 2: S[beta] = MXQ_QK_BLOCK(2); break;
+          default: S[beta] = MXQ_QK_BLOCK(3); break;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int beta = 0; beta < 8; ++beta) S[beta] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    }
+    int fl = 0;  // bit t: tile t of the chunk is FP16 for these rows
+    if (a.mode == MXQ_ALL_FP16) {
+      fl = 1 | (valid1 ? 2 : 0);
+    } else if (a.mode == MXQ_MIXED) {
+      const uint32_t w = mrow[(2 * ch) >> 5];
+      fl = static_cast<int>((w >> ((2 * ch) & 31)) & 1u) |
+           (valid1 ? static_cast<int>(((w >> ((2 * ch + 1) & 31)) & 1u) << 1) : 0);
+    }
+    float m_tile0 = NEG_INF;
+    float low0 = NEG_INF, low1 = NEG_INF;  // row maxima of the low-bit scores left in each tile
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t == 1 && !valid1) {
+#pragma unroll
+        for (int bb = 4; bb < 8; ++bb) S[bb] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+        break;
+      }
+      const bool prom = (fl >> t) & 1;
+      const int kt0 = kc + 64 * t;
+      v4f St[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) St[bb] = S[4 * t + bb];
+      if (prom) {  // bf16 QK^T of the tile, K rows straight from global memory
+#pragma unroll
+        for (int st = 0; st < NSB; ++st) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int key = 16 * (col >> 2) + 4 * bb + (col & 3);
+            const v8bf ka = __builtin_bit_cast(
+                v8bf, __builtin_amdgcn_raw_buffer_load_b128(r_hk, ((kt0 + key) * D + 32 * st + 8 * g) * 2, 0, 0));
+            St[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbr[st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : St[bb],
+                                                             0, 0, 0);
+          }
+        }
+      }
+      // this lane's 16 keys kt0 + 16g + j, j = 4bb + i: bit j of vm set when the
+      // key is visible (below kmax and not a line key); the scores are
+      // rewritten only in tiles where some lane has a hidden key
+      const uint32_t lm = LINES ? ((s_lm[ch][g] >> (16 * t)) & 0xFFFFu) : 0u;
+      const int nvis = min(max(kmax - (kt0 + 16 * g), 0), 16);
+      const uint32_t vm = (nvis >= 16 ? 0xFFFFu : ((1u << nvis) - 1u)) & ~lm;
+      if (__any(vm != 0xFFFFu)) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((vm >> (4 * bb + i)) & 1u)) St[bb][i] = NEG_INF;
+      }
+      float mx = NEG_INF;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) mx = fmaxf(fmaxf(mx, fmaxf(St[bb][0], St[bb][1])), fmaxf(St[bb][2], St[bb][3]));
+      mx = rowmax4(mx);
+      const float m_t = fmaxf(m_run, ceilf(mx * c));
+      m_run = m_t;
+      if (t == 0) m_tile0 = m_t;
+      if (prom) {
+        // P relative to O's reference m_o <= m_t (exact scaling while fp16 is
+        // normal); O is rebased when 2^(m_t - m_o) would leave fp16's range
+        if (m_o == NEG_INF) m_o = m_t;
+        else if (__any(m_t - m_o > kMaxLag16)) rebase(m_t);
+        const float m_ref = m_o == NEG_INF ? 0.0f : m_o;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          v8h ph;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            ph[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(St[2 * st + (e >> 2)][e & 3], c, -m_ref)));
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const v8h va = __builtin_bit_cast(
+                v8h, __builtin_amdgcn_raw_buffer_load_b128(r_hv, ((16 * db + col) * a.N + kt0 + 16 * g + 8 * st) * 2,
+                                                           0, 0));
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
+          }
+          const v8h ones16 = __builtin_bit_cast(v8h, v4i{kOne16, kOne16, kOne16, kOne16});
+          L = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones16, ph, L, 0, 0, 0);
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) St[bb] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};  // no low-bit P
+      } else {
+        if (t == 0) low0 = mx;
+        else low1 = mx;
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) S[4 * t + bb] = St[bb];
+    }
+    // ---- low-bit P and PV of the chunk; each tile's reference enters through
+    // the E8M0 scale of its P blocks, 2^-8 * 2^(m_t - m_o)
+    const float hm0 = m_tile0, hm1 = m_run;
+    auto live = [&](float rmax, float href) -> bool {
+      const float off = kGridMagic + kExpOffset - (href == NEG_INF ? 0.0f : href);
+      return __any(__builtin_fmaf(rmax, c, off) > kGridMagic - 10.0f);
+    };
+    if (live(low0, hm0) || live(low1, hm1)) {
+      if (m_o == NEG_INF) m_o = m_run;
+      else if (__any(m_run - m_o > kMaxLag)) rebase(m_run);
+      const float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
+      const float off1 = kGridMagic + kExpOffset - (hm1 == NEG_INF ? 0.0f : hm1);
+      v8i pb;
+#pragma unroll
+      for (int beta = 0; beta < 8; ++beta) pb[beta] = p4_e4m3(S[beta], c, beta < 4 ? off0 : off1);
+      const float mt = g < 2 ? hm0 : hm1;
+      const int psc = (mt == NEG_INF || m_o == NEG_INF)
+                          ? 0 : static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + (mt - m_o), 0.0f), 254.0f));
+      const uint32_t* vsw = reinterpret_cast<const uint32_t*>(&s_vs[ch][(g * 16 + col) * 8]);
+      const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const v4i w0 = *reinterpret_cast<const v4i*>(&s_v[ch][2048 * db + voff]);
+        const v4i w1 = *reinterpret_cast<const v4i*>(&s_v[ch][2048 * db + (voff ^ 64)]);
+        const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        const v8i& pbb = pb;
+        const v4f& o = O[db];
+        const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
+        switch (db & 3) {
+          case 0: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 0, vs, 0, psc); break;
+          case 1: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 1, vs, 0, psc); break;
+          case 2: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 2, vs, 0, psc); break;
+          default: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 3, vs, 0, psc); break;
+        }
+      }
+      L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const bool row_ok = q < a.n_valid;
+  const float l = L[0];
+  const float inv = row_ok ? 1.0f / l : 0.0f;
+  const int64_t obase = (bhq * a.N + q) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d0 = 16 * db + 4 * g;
+    const float o0 = O[db][0] * inv, o1 = O[db][1] * inv, o2 = O[db][2] * inv, o3 = O[db][3] * inv;
+    if (a.out_bf16) {
+      auto bf = [](float x) -> uint32_t {
+        uint32_t u = __float_as_uint(x);
+        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      };
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) =
+          make_uint2(bf(o0) | (bf(o1) << 16), bf(o2) | (bf(o3) << 16));
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(o0, o1, o2, o3);
+    }
+  }
+  if (a.lse && g == 0) a.lse[bhq * a.N + q] = row_ok ? (m_o + __log2f(l)) * 0.69314718055994531f : NEG_INF;
+}
+
+template <int D>
+mxq_status launch_short(const AttnArgs& a, int Hq, int B, hipStream_t st) {
+  const dim3 grid(a.N / 64, Hq, B);
+  if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_short<D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_short<D, false>), grid, dim3(256), 0, st, a);
+  return check_launch("k_attn_short");
+}
+
 template <int D>
 mxq_status launch(const AttnArgs& a, int n_qt, int Hq, int B, hipStream_t st) {
   if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_mixed<D, true>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
@@ -1187,6 +1649,11 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
   // mask row is looked up per row block); one workgroup per CU.
   const int n_qt = s->N / 128;
   a.n_qt = n_qt;
+  // at most two 128-key chunks: small workgroups that stage the whole head
+  if (s->N <= 256) {
+    if (s->D == 128) return launch_short<128>(a, s->Hq, s->B, strm);
+    return launch_short<64>(a, s->Hq, s->B, strm);
+  }
   if (s->D == 128) return launch<128>(a, n_qt, s->Hq, s->B, strm);
   return launch<64>(a, n_qt, s->Hq, s->B, strm);
 }
