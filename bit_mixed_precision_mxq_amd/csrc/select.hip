@@ -150,32 +150,62 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
     if (a.topk >= 0) k = a.topk;
     else k = (static_cast<int64_t>(a.ratio_num) * nvt + a.ratio_den - 1) / a.ratio_den;
     if (k > n_cand) k = n_cand;
-    // forced and invalid tiles (up to a multiple of 4) become -inf: they then
-    // never outrank a candidate, whose score is finite
-    const int nvt4 = (nvt + 3) & ~3;
-    for (int j = lane; j < nvt4; j += 64)
-      if (j >= nvt || forced(j)) sc[j] = -__builtin_inff();
+    // The k best candidates by (score descending, index ascending), found as
+    // the k-th largest score by a radix search over order-preserving keys:
+    // a candidate's score becomes an unsigned key that orders as the float
+    // does (-0 first made +0, the two compare equal), a forced or invalid tile
+    // key 0, below every candidate (a finite score's key is at least
+    // 0x00800000).  Each of the 32 passes fixes one bit of the k-th largest
+    // key by counting, with ballots, the keys that match the bits fixed so
+    // far and have this bit set.
+    uint32_t* key = reinterpret_cast<uint32_t*>(sc);
+    const int nm = (nvt + 63) / 64;  // 64-tile groups holding valid tiles
+    for (int j = lane; j < nm * 64; j += 64) {
+      uint32_t u = 0u;
+      if (j < nvt && !forced(j)) {
+        const uint32_t bits = __float_as_uint(sc[j] + 0.0f);  // -0 -> +0
+        u = bits ^ ((bits >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+      }
+      key[j] = u;
+    }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const float4* s4 = reinterpret_cast<const float4*>(sc);
+    uint32_t thr = 0u;  // the k-th largest key (valid when 0 < k < n_cand)
+    int k_eq = 0;       // how many keys equal to thr are taken (lowest indices first)
+    if (k > 0 && k < n_cand) {
+      uint32_t hi_mask = 0u;
+      int need = static_cast<int>(k);
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t b = 1u << bit;
+        int cnt = 0;
+        for (int m = 0; m < nm; ++m) {
+          const uint32_t u = key[64 * m + lane];
+          cnt += __popcll(__ballot((u & hi_mask) == thr && (u & b) != 0u));
+        }
+        if (cnt >= need) thr |= b;
+        else need -= cnt;
+        hi_mask |= b;
+      }
+      k_eq = need;
+    }
+    int eq_before = 0;  // keys equal to thr at lower indices, over the groups done
     for (int j0 = 0; j0 < a.n_kt; j0 += 64) {
       const int j = j0 + lane;
       bool take = j < nvt && forced(j);
       if (j < nvt && !take && k > 0) {
-        // rank of candidate j: candidates with a higher score, or the same
-        // score and a lower index (the same tile never counts itself)
-        const float sj = sc[j];
-        int rank = 0;
-        for (int q4 = 0; q4 < nvt4 / 4; ++q4) {
-          const float4 o = s4[q4];
-          const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int jj = 4 * q4 + c;
-            rank += (ov[c] > sj || (ov[c] == sj && jj < j)) ? 1 : 0;
-          }
+        const uint32_t u = key[j];
+        if (k >= n_cand) {
+          take = true;
+        } else {
+          const bool eq = u == thr;
+          const uint64_t eqb = __ballot(eq);
+          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(eqb >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(eqb), 0));
+          take = u > thr || (eq && eq_before + below < k_eq);
         }
-        take = rank < k;
       }
+      // equal keys of this group (all lanes take part in the ballot)
+      if (k > 0 && k < n_cand)
+        eq_before += __popcll(__ballot(j < nvt && key[j < nm * 64 ? j : 0] == thr && j < nm * 64));
       const uint64_t bits = __ballot(take);
       count += __popcll(bits);
       if (lane < 2 && j0 / 32 + lane < a.words) mrow[j0 / 32 + lane] = static_cast<uint32_t>(bits >> (32 * lane));

@@ -72,6 +72,11 @@ CASES = [
     (128, 64, True, 384, 333, 4, 4),
     (128, 128, True, 512, 500, 4, 1),
     (128, 128, False, 256, 256, 2, 2),
+    # N <= 256 runs the short-sequence kernel: causal, ragged, one chunk
+    (64, 128, True, 256, 250, 4, 2),
+    (128, 64, True, 256, 130, 2, 1),
+    (64, 64, True, 128, 100, 2, 1),
+    (128, 128, False, 128, 77, 2, 2),
 ]
 
 
