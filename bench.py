@@ -160,7 +160,8 @@ def bench_prefill(args, dev, workload):
     n_lines = cfg.get("n_lines", 0)
     pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
                                sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"], n_lines=n_lines,
-                               sink_tokens=cfg.get("sink_tokens", 0), out_dtype=mxq.MXQ_OUT_BF16, device=dev)
+                               sink_tokens=cfg.get("sink_tokens", 0), out_dtype=mxq.MXQ_OUT_BF16, device=dev,
+                               group_shared=args.group_shared)
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
@@ -228,7 +229,7 @@ def quality_sweep(args, dev):
     sizes = [int(x) for x in args.quality_n.split(",")]
     recipes = {"outliers+sink": {}, "sink": dict(outliers=False), "plain": dict(outliers=False, sink=None)}
     fracs = [("lowbit", None), ("forced", 0), ("1%", 1), ("2%", 2), ("5%", 5), ("10%", 10), ("20%", 20), ("fp16", None),
-             ("lowbit+rot", None), ("5%+rot", 5)]
+             ("lowbit+rot", None), ("5%+rot", 5), ("5%+shared", 5)]
     rows_per_head = 16
     results = []
     for recipe, N in [(r, n) for r in recipes for n in sizes]:
@@ -255,7 +256,7 @@ def quality_sweep(args, dev):
         ws = mxq.select_workspace(shape, dev)
         errs = {}
         for label, pct in fracs:
-            base_label = label.replace("+rot", "")
+            base_label = label.replace("+rot", "").replace("+shared", "")
             ops_use = ops_rot if label.endswith("+rot") else ops_mixed
             mode = (mxq.MXQ_ALL_LOWBIT if base_label == "lowbit" else mxq.MXQ_ALL_FP16 if base_label == "fp16"
                     else mxq.MXQ_MIXED)
@@ -264,7 +265,7 @@ def quality_sweep(args, dev):
             if mode == mxq.MXQ_MIXED:
                 mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(pct, 100),
                                                     sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
-                                                    workspace=ws)
+                                                    workspace=ws, group_shared=label.endswith("+shared"))
                 total, fp16 = pair_counts(cfg, mask.cpu().numpy().view(np.uint32))
                 fp16_frac = fp16 / total
             out = torch.empty((B, Hq, N, D), dtype=torch.float32, device=dev)
@@ -598,6 +599,8 @@ def main():
                          "quality: the synthetic error/speed curve over the FP16 fraction")
     ap.add_argument("--quality-n", default="8192,16384,32768", help="sequence lengths of the quality sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-time budget of each CPU-baseline leg")
+    ap.add_argument("--group-shared", action="store_true",
+                    help="prefill with one tile mask per kv group (the G query heads share it)")
     ap.add_argument("--decode-lines", type=int, default=0,
                     help="also time decode with this many vertical-line tokens (fp16) per kv head, at most 16")
     args = ap.parse_args()

@@ -37,6 +37,7 @@ EXPORTED = [
     "attn_select_blocks", "attn_select_blocks_means", "attn_select_lines_workspace",
     "attn_select_lines", "attn_mixed_fwd",
     "attn_quantkv_decode_workspace", "attn_quantkv_decode", "attn_quantkv_decode_noalloc", "attn_quantkv_append",
+    "mxq_kv_lines_from_prefill",
     "mxq_status_string",
     "mxq_last_error", "mxq_version",
 ]
@@ -53,7 +54,8 @@ class AttnShape(ctypes.Structure):
 
 
 class SelectParams(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("topk", "ratio_num", "ratio_den", "sink_tiles", "local_tiles")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("topk", "ratio_num", "ratio_den", "sink_tiles", "local_tiles",
+                                              "group_shared")]
 
 
 class LineParams(ctypes.Structure):
@@ -125,6 +127,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_quantkv_decode_noalloc.argtypes = [vp, ctypes.POINTER(KVCache), i32, i32, i32, i32, i32,
                                                 ctypes.c_float, i32, vp, vp]
     lib.attn_quantkv_decode_noalloc.restype = i32
+    lib.mxq_kv_lines_from_prefill.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.mxq_kv_lines_from_prefill.restype = i32
     lib.attn_quantkv_append.argtypes = [vp, vp, ctypes.POINTER(KVCacheRW), i32, i32, i32, vp]
     lib.attn_quantkv_append.restype = i32
     lib.mxq_status_string.argtypes = [i32]
@@ -211,7 +215,7 @@ def select_workspace(shape: Shape, device) -> torch.Tensor:
 
 
 def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0,
-                       want_scores=False, workspace=None, mask=None, n_fp16=None):
+                       want_scores=False, workspace=None, mask=None, n_fp16=None, group_shared=False):
     """Returns (mask u32-as-int32 [B,Hq,n_qt,words], n_fp16 [B,Hq,n_qt], scores or None);
     mask and n_fp16 may be passed in to be reused."""
     _need_gpu(q, k)
@@ -225,7 +229,8 @@ def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0
     assert mask.numel() == shape.B * shape.Hq * n_qt * words and nfp.numel() == shape.B * shape.Hq * n_qt
     scores = torch.empty((shape.B, shape.Hq, n_qt, n_kt), dtype=torch.float32, device=dev) if want_scores else None
     ws = workspace if workspace is not None else select_workspace(shape, dev)
-    sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles))
+    sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles),
+                      int(bool(group_shared)))
     cs = shape.c()
     _check(load_library().attn_select_blocks(_ptr(q), _ptr(k), ctypes.byref(cs), ctypes.byref(sp), _ptr(ws),
                                              ws.numel(), _ptr(mask), _ptr(nfp), _ptr(scores), _stream()))
@@ -233,7 +238,7 @@ def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0
 
 
 def attn_select_blocks_means(q_means, k_means, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0,
-                             want_scores=False, mask=None, n_fp16=None):
+                             want_scores=False, mask=None, n_fp16=None, group_shared=False):
     """attn_select_blocks on tile means from prepare_prefill_means (same result)."""
     _need_gpu(q_means, k_means)
     n_qt, n_kt = shape.N // shape.Bq, shape.N // shape.Bk
@@ -245,7 +250,8 @@ def attn_select_blocks_means(q_means, k_means, shape: Shape, topk=-1, ratio=(5, 
         mask = torch.empty((shape.B, shape.Hq, n_qt, words), dtype=torch.int32, device=dev)
     nfp = n_fp16 if n_fp16 is not None else torch.empty((shape.B, shape.Hq, n_qt), dtype=torch.int32, device=dev)
     scores = torch.empty((shape.B, shape.Hq, n_qt, n_kt), dtype=torch.float32, device=dev) if want_scores else None
-    sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles))
+    sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles),
+                      int(bool(group_shared)))
     cs = shape.c()
     _check(load_library().attn_select_blocks_means(_ptr(q_means), _ptr(k_means), ctypes.byref(cs), ctypes.byref(sp),
                                                    _ptr(mask), _ptr(nfp), _ptr(scores), _stream()))
@@ -379,8 +385,10 @@ class PrefillPipeline:
     Workspaces and outputs are allocated once."""
 
     def __init__(self, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0, n_lines=0,
-                 sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0", fused_means=True):
+                 sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0", fused_means=True,
+                 group_shared=False):
         self.shape, self.topk, self.ratio = shape, topk, ratio
+        self.group_shared = bool(group_shared)
         self.sink_tiles, self.local_tiles = sink_tiles, local_tiles
         self.n_lines, self.sink_tokens, self.rotate, self.out_dtype = n_lines, sink_tokens, rotate, out_dtype
         dev = torch.device(device)
@@ -413,7 +421,8 @@ class PrefillPipeline:
         if self.fused:
             ops, qm, km = prepare_prefill_means(q, k, v, self.shape, out=self.ops, means=self.means)
             attn_select_blocks_means(qm, km, self.shape, topk=self.topk, ratio=self.ratio, sink_tiles=self.sink_tiles,
-                                     local_tiles=self.local_tiles, mask=self.mask, n_fp16=self.nfp)
+                                     local_tiles=self.local_tiles, mask=self.mask, n_fp16=self.nfp,
+                                     group_shared=self.group_shared)
             if self.n_lines:
                 attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
                                   lines=self.lines)
@@ -428,7 +437,8 @@ class PrefillPipeline:
         with torch.cuda.stream(self.aux):
             self.aux.wait_event(self.ev_in)
             attn_select_blocks(q, k, self.shape, topk=self.topk, ratio=self.ratio, sink_tiles=self.sink_tiles,
-                               local_tiles=self.local_tiles, workspace=self.ws, mask=self.mask, n_fp16=self.nfp)
+                               local_tiles=self.local_tiles, workspace=self.ws, mask=self.mask, n_fp16=self.nfp,
+                               group_shared=self.group_shared)
             if self.n_lines:
                 attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
                                   lines=self.lines)
@@ -502,6 +512,23 @@ def build_quant_kv_cache(k, v, seq_len, n_sink, n_recent, k_recent=None, v_recen
         v_ln, _, _ = mxq_quantize(v_line_rows.contiguous(), MXQ_FP16, MXQ_AXIS_D)
     return QuantKVCache(kc, vc, ks, kz, vs, vz, k_sink, v_sink, k_rec, v_rec, seq_len, n_sink, n_recent,
                         lines, k_ln, v_ln)
+
+
+def kv_lines_from_prefill(lines_hq, k, v):
+    """Decode line tokens from the prefill's group-shared vertical lines:
+    lines_hq int32 [B,Hq,n] (attn_select_lines with group_shared=True), k, v
+    the prompt's bf16 [B,Hkv,L,D].  Returns (lines int32 [B,Hkv,n], k_lines,
+    v_lines fp16 [B,Hkv,n,D]) for QuantKVCache."""
+    _need_gpu(lines_hq, k, v)
+    B, Hq, n = lines_hq.shape
+    _, Hkv, L, D = k.shape
+    dev = k.device
+    lines = torch.empty((B, Hkv, n), dtype=torch.int32, device=dev)
+    kl = torch.empty((B, Hkv, n, D), dtype=torch.float16, device=dev)
+    vl = torch.empty_like(kl)
+    _check(load_library().mxq_kv_lines_from_prefill(_ptr(lines_hq), Hq, _ptr(k), _ptr(v), B, Hkv, L, D, n,
+                                                    _ptr(lines), _ptr(kl), _ptr(vl), _stream()))
+    return lines, kl, vl
 
 
 def decode_workspace(B, Hq, D, num_splits, max_seq_len, device) -> torch.Tensor:

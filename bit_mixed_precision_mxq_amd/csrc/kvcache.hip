@@ -98,6 +98,43 @@ __global__ void k_kv_bump(int32_t* seq_len, int B, int L_cap) {
   }
 }
 
+// Decode line tokens from the prefill's vertical lines (HyQuant: the prefill's
+// principle carried over to the decode cache; reading R36).  One thread per
+// (entry, 8-element unit) of one (sequence, kv head): the list of the kv
+// group's first query head is copied, and the listed token's K and V rows are
+// converted bf16 -> fp16 (round to nearest even); an entry outside [0, L)
+// gets zero rows (such an entry never takes part, reading R33).
+struct LinesFromPrefillArgs {
+  const int32_t* lines_hq;  // [B][Hq][n]
+  const uint16_t* k;        // bf16 [B][Hkv][L][D]
+  const uint16_t* v;
+  int32_t* lines;           // [B][Hkv][n]
+  uint16_t* k_lines;        // fp16 [B][Hkv][n][D]
+  uint16_t* v_lines;
+  int Hq, Hkv, L, D, n;
+};
+
+__global__ void __launch_bounds__(256) k_kv_lines_from_prefill(LinesFromPrefillArgs a) {
+  const int hk = blockIdx.x, b = blockIdx.y;
+  const int G = a.Hq / a.Hkv;
+  const int units = a.D / 8;
+  const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + hk;
+  const int32_t* src = a.lines_hq + (static_cast<int64_t>(b) * a.Hq + hk * G) * a.n;
+  for (int idx = threadIdx.x; idx < a.n * units; idx += blockDim.x) {
+    const int e = idx / units, u = idx % units;
+    const int key = src[e];
+    if (u == 0) a.lines[bhk * a.n + e] = key;
+    const bool ok = key >= 0 && key < a.L;
+    const int64_t row = (bhk * a.L + (ok ? key : 0)) * a.D + 8 * u;
+    const int64_t dst = (bhk * a.n + e) * a.D + 8 * u;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      a.k_lines[dst + x] = ok ? f16_bits_of_bf16(a.k[row + x]) : 0;
+      a.v_lines[dst + x] = ok ? f16_bits_of_bf16(a.v[row + x]) : 0;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace mxq
 
@@ -129,4 +166,21 @@ extern "C" mxq_status attn_quantkv_append(const uint16_t* k_new, const uint16_t*
   if (s != MXQ_OK) return s;
   hipLaunchKernelGGL(k_kv_bump, dim3((B + 255) / 256), dim3(256), 0, st, c->seq_len, B, c->L_cap);
   return check_launch("k_kv_bump");
+}
+
+extern "C" mxq_status mxq_kv_lines_from_prefill(const int32_t* lines_hq, int32_t Hq, const uint16_t* k_bf16,
+                                                const uint16_t* v_bf16, int32_t B, int32_t Hkv, int32_t L,
+                                                int32_t D, int32_t n_lines, int32_t* lines, uint16_t* k_lines,
+                                                uint16_t* v_lines, mxq_stream_t stream) {
+  MXQ_REQUIRE(B >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0 && B <= 65535 && Hkv <= 65535, MXQ_EINVAL,
+              "mxq_kv_lines_from_prefill: need B, Hkv >= 1 and Hq a multiple of Hkv");
+  MXQ_REQUIRE(L >= 1 && D >= 8 && D % 8 == 0, MXQ_EINVAL, "mxq_kv_lines_from_prefill: need L >= 1, D a multiple of 8");
+  MXQ_REQUIRE(n_lines >= 1 && n_lines <= 16, MXQ_EINVAL, "mxq_kv_lines_from_prefill: n_lines must be in [1, 16]");
+  MXQ_REQUIRE(lines_hq && k_bf16 && v_bf16 && lines && k_lines && v_lines, MXQ_EINVAL,
+              "mxq_kv_lines_from_prefill: every array is required");
+  LinesFromPrefillArgs a;
+  a.lines_hq = lines_hq; a.k = k_bf16; a.v = v_bf16; a.lines = lines; a.k_lines = k_lines; a.v_lines = v_lines;
+  a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.D = D; a.n = n_lines;
+  hipLaunchKernelGGL(k_kv_lines_from_prefill, dim3(Hkv, B), dim3(256), 0, as_stream(stream), a);
+  return check_launch("k_kv_lines_from_prefill");
 }

@@ -67,6 +67,7 @@ struct SelectArgs {
   int topk, ratio_num, ratio_den, sink_tiles, local_tiles;
   int B;
   int score_free;  // no tile is chosen by score and none is reported: skip the scores
+  int shared;      // one mask per kv group: the G heads' tile means averaged (reading R35)
 };
 
 // One wave per (batch, query head, query tile), four per workgroup, with no
@@ -94,7 +95,19 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
   float* sq = s_q[wave];
 
   if (!a.score_free) {
-    for (int d = lane; d < D; d += 64) sq[d] = a.qmean[(bhq * a.n_qt + i) * D + d];
+    if (a.shared) {
+      // the kv group's shared tile mean: the G heads' means summed in head
+      // order, one division by G (every head of the group computes the same)
+      const int G = a.Hq / a.Hkv;
+      const int64_t bh0 = bhq - h % G;
+      for (int d = lane; d < D; d += 64) {
+        float acc = 0.0f;
+        for (int hh = 0; hh < G; ++hh) acc = acc + a.qmean[((bh0 + hh) * a.n_qt + i) * D + d];
+        sq[d] = acc / static_cast<float>(G);
+      }
+    } else {
+      for (int d = lane; d < D; d += 64) sq[d] = a.qmean[(bhq * a.n_qt + i) * D + d];
+    }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, read by every lane
 
     // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
@@ -409,6 +422,7 @@ static mxq_status launch_select(const float* qmean, const float* kmean, const mx
   a.sink_tiles = p->sink_tiles; a.local_tiles = p->local_tiles;
   a.B = s->B;
   a.score_free = score_free ? 1 : 0;
+  a.shared = p->group_shared ? 1 : 0;
   const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
   const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
   if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
@@ -420,6 +434,8 @@ static mxq_status check_select_params(const mxq_select_params* p) {
   MXQ_REQUIRE(p != nullptr, MXQ_EINVAL, "attn_select_blocks: params is NULL");
   MXQ_REQUIRE(p->topk >= 0 || (p->ratio_num >= 0 && p->ratio_den > 0), MXQ_EINVAL,
               "attn_select_blocks: need topk >= 0 or ratio_num >= 0 and ratio_den > 0");
+  MXQ_REQUIRE(p->group_shared == 0 || p->group_shared == 1, MXQ_EINVAL,
+              "attn_select_blocks: group_shared must be 0 or 1");
   MXQ_REQUIRE(p->sink_tiles >= 0 && p->local_tiles >= 0, MXQ_EINVAL,
               "attn_select_blocks: sink_tiles and local_tiles must be >= 0");
   return MXQ_OK;
@@ -448,6 +464,8 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
               "attn_select_blocks: q, k and mask are required");
   MXQ_REQUIRE(p->topk >= 0 || (p->ratio_num >= 0 && p->ratio_den > 0), MXQ_EINVAL,
               "attn_select_blocks: need topk >= 0 or ratio_num >= 0 and ratio_den > 0");
+  MXQ_REQUIRE(p->group_shared == 0 || p->group_shared == 1, MXQ_EINVAL,
+              "attn_select_blocks: group_shared must be 0 or 1");
   MXQ_REQUIRE(p->sink_tiles >= 0 && p->local_tiles >= 0, MXQ_EINVAL,
               "attn_select_blocks: sink_tiles and local_tiles must be >= 0");
   MXQ_REQUIRE(workspace != nullptr && ws_bytes >= attn_select_blocks_workspace(s), MXQ_EINVAL,

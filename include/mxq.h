@@ -83,9 +83,14 @@ typedef struct {
  * local_tiles == 0) plus the k_i best-scoring other valid tiles, where
  * k_i = topk if topk >= 0, else ceil(ratio_num * |valid tiles of i| / ratio_den)
  * (integer arithmetic), capped at the number of candidates.  Ties in score go
- * to the lower tile index. */
+ * to the lower tile index.  group_shared = 1 (reading R35; HyQuant's
+ * vertical-line signals shared by the heads of a group, applied to tiles):
+ * the G query heads of a kv group score with their shared tile means (the G
+ * heads' means summed in fp32 in head order, divided once by G) and so share
+ * one mask; 0: per query head. */
 typedef struct {
   int32_t topk, ratio_num, ratio_den, sink_tiles, local_tiles;
+  int32_t group_shared;
 } mxq_select_params;
 
 /* ---------------------------------------------------------------------------
@@ -294,6 +299,25 @@ typedef struct {
   const uint16_t* v_lines;
   int32_t n_lines;
 } mxq_kv_cache;
+
+/* ---------------------------------------------------------------------------
+ * mxq_kv_lines_from_prefill -- the decode cache's vertical-line tokens chosen
+ * by importance at prefill (HyQuant, abstract: the prefill's hybrid principle
+ * applied to KV-cache compression in decode; reading R36): the lists
+ * attn_select_lines wrote with group_shared = 1 (lines_hq i32 [B][Hq][n],
+ * identical for the G query heads of a kv group) become the cache's lists
+ * lines i32 [B][Hkv][n] (the group's first query head), and the listed
+ * tokens' rows of the prompt's K and V (bf16 [B][Hkv][L][D]) are written in
+ * fp16 (round to nearest even) to k_lines, v_lines [B][Hkv][n][D]; an entry
+ * outside [0, L) gets zero rows (it never takes part, reading R33).  These
+ * are the lines, k_lines, v_lines and n_lines of mxq_kv_cache.  n in [1, 16];
+ * D a multiple of 8.  Caller-owned device memory; EINVAL on bad arguments,
+ * nothing launched then.
+ * ------------------------------------------------------------------------- */
+mxq_status mxq_kv_lines_from_prefill(const int32_t* lines_hq, int32_t Hq, const uint16_t* k_bf16,
+                                     const uint16_t* v_bf16, int32_t B, int32_t Hkv, int32_t L, int32_t D,
+                                     int32_t n_lines, int32_t* lines, uint16_t* k_lines, uint16_t* v_lines,
+                                     mxq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * attn_quantkv_decode -- one decode step: for each sequence b and query head

@@ -13,7 +13,10 @@ The pages give no formula; the readings used here (R8-R11) are:
   tile (its diagonal tiles plus w-1 tiles before them);
 * budget per query tile k_i = topk, or ceil(num*|V_i|/den) in integers,
   capped at the number of non-forced candidates; candidates ordered by
-  descending score, ties to the lower tile index.
+  descending score, ties to the lower tile index;
+* optionally one mask per kv group (R35, after HyQuant's vertical-line
+  signals shared by the query heads of a group): the G heads' tile means are
+  averaged (fp32 sum in head order, one division by G) and scored as above.
 """
 
 from __future__ import annotations
@@ -100,12 +103,24 @@ def budget(topk, ratio_num, ratio_den, n_valid_tiles, n_candidates):
     return min(k, n_candidates)
 
 
+def group_tile_means(qm_heads: np.ndarray) -> np.ndarray:
+    """Shared query-tile means of one kv group (reading R35): the G heads' tile
+    means [G, n_qt, D] summed in fp32 head by head (ascending), then one fp32
+    division by G."""
+    acc = np.zeros(qm_heads.shape[1:], dtype=np.float32)
+    for h in range(qm_heads.shape[0]):
+        acc = (acc + qm_heads[h]).astype(np.float32)
+    return (acc / np.float32(qm_heads.shape[0])).astype(np.float32)
+
+
 def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, ratio_den,
-                  sink_tiles, local_tiles):
+                  sink_tiles, local_tiles, group_shared=False):
     """Return (mask u32 [B,Hq,n_qt,ceil(n_kt/32)], n_fp16 i32 [B,Hq,n_qt],
     scores f32 [B,Hq,n_qt,n_kt]).  Bit j%32 of word j//32 is set when key tile
     j runs in FP16 for that query tile.  Scores are given for every tile pair
-    (also non-candidates) for inspection."""
+    (also non-candidates) for inspection.  With ``group_shared`` (reading R35)
+    the G query heads of a kv group score with their shared tile means
+    (``group_tile_means``) and so share one mask."""
     B, Hq, N, D = q_bits.shape
     Hkv = k_bits.shape[1]
     G = Hq // Hkv
@@ -118,7 +133,9 @@ def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, rati
     scores = np.zeros((B, Hq, n_qt, n_kt), dtype=np.float32)
     for b in range(B):
         for h in range(Hq):
-            s = tile_scores(qm[b, h], km[b, h // G])
+            kv = h // G
+            qh = group_tile_means(qm[b, kv * G:(kv + 1) * G]) if group_shared else qm[b, h]
+            s = tile_scores(qh, km[b, kv])
             scores[b, h] = s
             for i in range(n_qt):
                 valid, forced = sets[i]

@@ -266,3 +266,46 @@ def test_decode_heavy_token_as_a_line():
     plain, _ = _run(mxq, d, 64, 128)
     e_line, e_plain = np.abs(out[0] - exact).max(), np.abs(plain[0] - exact).max()
     assert e_line < 0.2 * e_plain, (e_line, e_plain)
+
+
+def test_decode_lines_from_the_prefill_selection():
+    """Reading R36: the prefill's group-shared vertical lines become the
+    decode cache's fp16 line tokens (mxq_kv_lines_from_prefill): lists and
+    fp16 rows bit-exact against the oracle, decode within the bound."""
+    mxq = gpu_or_skip()
+    import torch
+    from gpu_helpers import u16
+    from oracle import select as S
+
+    B, Hq, Hkv, L, D = 2, 8, 2, 1024, 128
+    G = Hq // Hkv
+    rng = np.random.default_rng(36)
+    common = rng.standard_normal((B, Hkv, 1, D)).astype(np.float32)
+    qp = (rng.standard_normal((B, Hq, L, D)) * 0.5 + np.repeat(common, G, axis=1)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    k[:, :, 700] += 4.0 * common[:, :, 0]
+    from oracle.formats import f32_to_bf16_bits
+    qb, kb, vb = f32_to_bf16_bits(qp), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    qd_bits = f32_to_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    lens = np.array([L, 900], dtype=np.int32)
+    qg, kg, vg, qdg = bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), bf16_dev(qd_bits)
+    shape = mxq.Shape(B, Hq, Hkv, L, L, D, 64, 64, True)
+    lines_hq, _ = mxq.attn_select_lines(qg, kg, shape, 16, 1, group_shared=True)
+    lines, kl, vl = mxq.kv_lines_from_prefill(lines_hq, kg, vg)
+    r_hq, _ = S.select_lines(qb, kb, L, 64, 16, 1, group_shared=True)
+    r_lines = np.ascontiguousarray(r_hq[:, ::G])
+    assert np.array_equal(lines.cpu().numpy(), r_lines)
+    ref = Dm.build_kv_cache_ref(kb, vb, lens, 64, 128, lines=r_lines)
+    assert np.array_equal(u16(kl), ref["k_lines"].view(np.uint16))
+    assert np.array_equal(u16(vl), ref["v_lines"].view(np.uint16))
+    krec = torch.stack([kg[b, :, lens[b] - 128:lens[b]] for b in range(B)])
+    vrec = torch.stack([vg[b, :, lens[b] - 128:lens[b]] for b in range(B)])
+    base = mxq.build_quant_kv_cache(kg, vg, torch.from_numpy(lens).to("cuda:0"), 64, 128, krec, vrec)
+    cache = mxq.QuantKVCache(base.k_codes, base.v_codes, base.k_scale, base.k_zero, base.v_scale, base.v_zero,
+                             base.k_sink, base.v_sink, base.k_recent, base.v_recent, base.seq_len, 64, 128,
+                             lines, kl, vl)
+    out = mxq.attn_quantkv_decode(qdg, cache, Hkv, int(lens.max())).cpu().numpy()
+    oref = Dm.attn_decode_ref(qd_bits, ref, lens, 64, 128)
+    err = np.abs(out - oref).max()
+    assert err <= TIGHT, err

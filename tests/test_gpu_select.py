@@ -166,3 +166,40 @@ def test_fused_means_ragged_gqa():
         rqm, rkm = S.pooled_means(qb, kb, nv, Bq, 64)
         assert np.array_equal(qm.cpu().numpy().view(np.uint32), rqm.view(np.uint32))
         assert np.array_equal(km.cpu().numpy().transpose(0, 1, 3, 2).view(np.uint32), rkm.view(np.uint32))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_group_shared_masks_bit_exact(fused):
+    """One mask per kv group (reading R35), from bf16 Q/K and from the fused
+    quantiser's tile means: bit-exact against the oracle, every head of a
+    group identical; and the attention on it within 5e-3."""
+    mxq = gpu_or_skip()
+    from oracle import attention as A
+
+    cfg = mxq_inputs.make_prefill("llama8b", N=2048, n_valid=2000, Hq=8, Hkv=2)
+    q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
+                      cfg["causal"])
+    if fused:
+        ops, qm, km = mxq.prepare_prefill_means(q, k, v, shape)
+        mask, nfp, sc = mxq.attn_select_blocks_means(qm, km, shape, topk=-1, ratio=(10, 100), sink_tiles=1,
+                                                     local_tiles=1, want_scores=True, group_shared=True)
+    else:
+        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"])
+        mask, nfp, sc = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(10, 100), sink_tiles=1, local_tiles=1,
+                                               want_scores=True, group_shared=True)
+    rm, rn, rs = S.select_blocks(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], True, -1, 10, 100, 1, 1,
+                                 group_shared=True)
+    got = u32(mask)
+    assert np.array_equal(got, rm) and np.array_equal(nfp.cpu().numpy(), rn)
+    assert np.array_equal(sc.cpu().numpy(), rs)
+    for h in range(1, 4):
+        assert np.array_equal(got[:, h], got[:, 0]) and np.array_equal(got[:, 4 + h], got[:, 4])
+    out, lse = mxq.attn_mixed_fwd(ops, mask, shape)
+    for h in (0, 5):
+        kv = h // 4
+        ro, rl = A.attn_mixed_ref(cfg["q"][:, h:h + 1], cfg["k"][:, kv:kv + 1], cfg["v"][:, kv:kv + 1],
+                                  cfg["n_valid"], 128, 64, True, mask=rm[:, h:h + 1], qtiles=[0, 7, 15])
+        rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in (0, 7, 15)])
+        o = out.cpu().numpy()[:, h:h + 1][..., rows, :]
+        assert np.abs(o - ro[..., rows, :]).max() <= 5e-3

@@ -211,3 +211,37 @@ def test_a_heavy_token_kept_as_a_line_cuts_the_error():
     e_line = np.abs(Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(kb, d["v"], d["seq_len"], 16, 32, lines=lines),
                                        d["seq_len"], 16, 32)[0] - exact).max()
     assert e_line < 0.5 * e_plain, (e_line, e_plain)
+
+
+def test_prefill_lines_choose_the_decode_lines():
+    """Reading R36: the vertical lines the prefill finds for a kv group
+    (group-shared probe, R31) become the decode cache's fp16 line tokens.  A
+    key that lines up with the direction the prompt's queries share (plus a
+    head_dim outlier 4 bits cannot hold) is found by the prefill selection,
+    and decoding a query of the same kind with it as a line cuts the error."""
+    from oracle import select as S
+
+    rng = np.random.default_rng(31)
+    Hq, Hkv, L, D = 4, 1, 512, 64
+    G = Hq // Hkv
+    common = rng.standard_normal(D).astype(np.float32)
+    qp = (rng.standard_normal((1, Hq, L, D)) * 0.5 + common).astype(np.float32)   # the prompt's queries
+    k = rng.standard_normal((1, Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((1, Hkv, L, D)).astype(np.float32)
+    k[0, 0, 300] = 6.0 * common / np.linalg.norm(common) * np.sqrt(D) / 4.0
+    k[0, 0, 300, :8] += 37.0
+    qb, kb, vb = F.f32_to_bf16_bits(qp), F.f32_to_bf16_bits(k), F.f32_to_bf16_bits(v)
+    lines_hq, _ = S.select_lines(qb, kb, L, 64, 16, 1, group_shared=True)
+    assert all(np.array_equal(lines_hq[0, h], lines_hq[0, 0]) for h in range(G))
+    assert 300 in lines_hq[0, 0] and lines_hq[0, 0, 0] == 0  # the planted key, after the sink token
+    lines = lines_hq[:, ::G]  # the kv group's list
+    qd = F.f32_to_bf16_bits((rng.standard_normal((1, Hq, D)) * 0.5 + common).astype(np.float32))
+    lens = np.array([L], dtype=np.int32)
+    exact = np.stack([_softmax_attn(F.bf16_bits_to_f32(qd)[0, h].astype(np.float64),
+                                    F.bf16_bits_to_f32(kb)[0, 0].astype(np.float64),
+                                    F.bf16_bits_to_f32(vb)[0, 0].astype(np.float64), 1 / 8.0) for h in range(Hq)])
+    e_plain = np.abs(Dm.attn_decode_ref(qd, Dm.build_kv_cache_ref(kb, vb, lens, 16, 32), lens, 16, 32)[0]
+                     - exact).max()
+    e_line = np.abs(Dm.attn_decode_ref(qd, Dm.build_kv_cache_ref(kb, vb, lens, 16, 32, lines=lines), lens, 16, 32)[0]
+                    - exact).max()
+    assert e_line < 0.5 * e_plain, (e_line, e_plain)

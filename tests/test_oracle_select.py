@@ -6,6 +6,7 @@ import numpy as np
 
 import mxq_inputs
 from oracle import select as S
+from oracle import formats as F
 from oracle.formats import f32_to_bf16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -151,3 +152,55 @@ def test_zero_keys_pick_lowest_index_candidates():
     assert np.all(scores == 0)
     for i in range(N // 64):
         assert S.mask_to_sets(mask[0, 0, i], 8) == [0, 1, 2]   # sink 0 + lowest two candidates
+
+
+# ---- one mask per kv group (reading R35)
+def _small_int_bits(shape, seed, lo=-3, hi=4):
+    """bf16 bits of small integers: every fp32 sum and product of the tile
+    means below stays exact, so float64 arithmetic is the exact reference."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(lo, hi, size=shape).astype(np.float32)
+    return F.f32_to_bf16_bits(x)
+
+
+def test_group_shared_equals_per_head_when_g_is_1():
+    q = _small_int_bits((1, 3, 256, 64), 1)
+    k = _small_int_bits((1, 3, 256, 64), 2)
+    a = S.select_blocks(q, k, 250, 64, 64, True, -1, 20, 100, 1, 1)
+    b = S.select_blocks(q, k, 250, 64, 64, True, -1, 20, 100, 1, 1, group_shared=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_group_shared_brute_force_and_identical_rows():
+    """G = 4: every head of a group gets the same mask row; the shared scores
+    equal the float64 dot product of the exact mean of the G heads' tile
+    means with the key tile means (tile means of 64 rows of small integers
+    are multiples of 1/64: every fp32 step is exact), and the chosen tiles are
+    a brute-force sort by (-score, index) of the candidates."""
+    B, Hq, Hkv, N, D, Bq, Bk = 1, 8, 2, 512, 64, 64, 64
+    q = _small_int_bits((B, Hq, N, D), 3)
+    k = _small_int_bits((B, Hkv, N, D), 4)
+    mask, nfp, sc = S.select_blocks(q, k, N, Bq, Bk, False, 2, 0, 1, 0, 0, group_shared=True)
+    qf = F.bf16_bits_to_f32(q).astype(np.float64)
+    kf = F.bf16_bits_to_f32(k).astype(np.float64)
+    n_t = N // Bq
+    for g in range(Hkv):
+        for h in range(g * 4, g * 4 + 4):
+            assert np.array_equal(mask[0, h], mask[0, g * 4]) and np.array_equal(sc[0, h], sc[0, g * 4])
+        qbar = qf[0, g * 4:g * 4 + 4].reshape(4, n_t, Bq, D).mean(axis=2).mean(axis=0)  # [n_t, D]
+        kbar = kf[0, g].reshape(n_t, Bk, D).mean(axis=1)
+        exact = qbar @ kbar.T
+        assert np.array_equal(sc[0, g * 4].astype(np.float64), exact)
+        for i in range(n_t):
+            order = sorted(range(n_t), key=lambda j: (-exact[i, j], j))[:2]
+            assert S.mask_to_sets(mask[0, g * 4, i], n_t) == sorted(order)
+
+
+def test_group_shared_differs_from_per_head_in_general():
+    q = F.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((1, 4, 512, 64)).astype(np.float32))
+    k = F.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((1, 1, 512, 64)).astype(np.float32))
+    per_head, _, _ = S.select_blocks(q, k, 512, 64, 64, False, 1, 0, 1, 0, 0)
+    shared, _, _ = S.select_blocks(q, k, 512, 64, 64, False, 1, 0, 1, 0, 0, group_shared=True)
+    assert not np.array_equal(per_head, shared)
+    assert all(np.array_equal(shared[0, h], shared[0, 0]) for h in range(4))
