@@ -229,7 +229,7 @@ def quality_sweep(args, dev):
     sizes = [int(x) for x in args.quality_n.split(",")]
     recipes = {"outliers+sink": {}, "sink": dict(outliers=False), "plain": dict(outliers=False, sink=None)}
     fracs = [("lowbit", None), ("forced", 0), ("1%", 1), ("2%", 2), ("5%", 5), ("10%", 10), ("20%", 20), ("fp16", None),
-             ("lowbit+rot", None), ("5%+rot", 5), ("5%+shared", 5)]
+             ("lowbit+rot", None), ("5%+rot", 5), ("5%+shared", 5), ("5%+maxkey", 5)]
     rows_per_head = 16
     results = []
     for recipe, N in [(r, n) for r in recipes for n in sizes]:
@@ -256,7 +256,7 @@ def quality_sweep(args, dev):
         ws = mxq.select_workspace(shape, dev)
         errs = {}
         for label, pct in fracs:
-            base_label = label.replace("+rot", "").replace("+shared", "")
+            base_label = label.replace("+rot", "").replace("+shared", "").replace("+maxkey", "")
             ops_use = ops_rot if label.endswith("+rot") else ops_mixed
             mode = (mxq.MXQ_ALL_LOWBIT if base_label == "lowbit" else mxq.MXQ_ALL_FP16 if base_label == "fp16"
                     else mxq.MXQ_MIXED)
@@ -265,7 +265,8 @@ def quality_sweep(args, dev):
             if mode == mxq.MXQ_MIXED:
                 mask, _, _ = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(pct, 100),
                                                     sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
-                                                    workspace=ws, group_shared=label.endswith("+shared"))
+                                                    workspace=ws, group_shared=label.endswith("+shared"),
+                                                    heuristic=1 if label.endswith("+maxkey") else 0)
                 total, fp16 = pair_counts(cfg, mask.cpu().numpy().view(np.uint32))
                 fp16_frac = fp16 / total
             out = torch.empty((B, Hq, N, D), dtype=torch.float32, device=dev)

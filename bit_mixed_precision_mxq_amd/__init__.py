@@ -55,7 +55,7 @@ class AttnShape(ctypes.Structure):
 
 class SelectParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("topk", "ratio_num", "ratio_den", "sink_tiles", "local_tiles",
-                                              "group_shared")]
+                                              "group_shared", "heuristic")]
 
 
 class LineParams(ctypes.Structure):
@@ -215,7 +215,8 @@ def select_workspace(shape: Shape, device) -> torch.Tensor:
 
 
 def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0,
-                       want_scores=False, workspace=None, mask=None, n_fp16=None, group_shared=False):
+                       want_scores=False, workspace=None, mask=None, n_fp16=None, group_shared=False,
+                       heuristic=0):
     """Returns (mask u32-as-int32 [B,Hq,n_qt,words], n_fp16 [B,Hq,n_qt], scores or None);
     mask and n_fp16 may be passed in to be reused."""
     _need_gpu(q, k)
@@ -230,7 +231,7 @@ def attn_select_blocks(q, k, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0
     scores = torch.empty((shape.B, shape.Hq, n_qt, n_kt), dtype=torch.float32, device=dev) if want_scores else None
     ws = workspace if workspace is not None else select_workspace(shape, dev)
     sp = SelectParams(int(topk), int(ratio[0]), int(ratio[1]), int(sink_tiles), int(local_tiles),
-                      int(bool(group_shared)))
+                      int(bool(group_shared)), int(heuristic))
     cs = shape.c()
     _check(load_library().attn_select_blocks(_ptr(q), _ptr(k), ctypes.byref(cs), ctypes.byref(sp), _ptr(ws),
                                              ws.numel(), _ptr(mask), _ptr(nfp), _ptr(scores), _stream()))

@@ -8,8 +8,10 @@
 //                 ascending order, then one correctly rounded division.
 //  k_select     : one wave per (b, query head, query tile): scores of all
 //                 key tiles against the tile mean (sequential over d, rounded
-//                 product then rounded sum, never fused), forced tiles, and the
-//                 top-k by rank counting with ties to the lower index.
+//                 product then rounded sum, never fused) -- or of the group's
+//                 shared tile mean (R35), or the max-pooled key logits (R37)
+//                 --, forced tiles, and the top-k by a radix search for the
+//                 k-th largest score with ties to the lower index.
 // The fixed operation order makes the result bit-identical to a plain CPU
 // evaluation of the same formula.
 #include <algorithm>
@@ -68,15 +70,17 @@ struct SelectArgs {
   int B;
   int score_free;  // no tile is chosen by score and none is reported: skip the scores
   int shared;      // one mask per kv group: the G heads' tile means averaged (reading R35)
+  int maxkey;      // scores from the max-pooled key logits (reading R37); needs k
+  const uint16_t* k;  // bf16 [B*Hkv][N][D] (maxkey only)
 };
 
 // One wave per (batch, query head, query tile), four per workgroup, with no
 // workgroup barrier: the wave keeps its tile mean and scores in its own slice
 // of LDS.  D (64 or 128) is a compile-time constant so that a score's column
 // loads go out 64 at a time before their products; the sum still runs over d
-// in order.  Candidates are ranked by counting, against a score row in which
-// forced and invalid tiles are -inf; each group of 64 tiles' verdicts becomes
-// two mask words by one ballot.
+// in order.  The k best candidates come from a radix search over
+// order-preserving keys of the scores (forced and invalid tiles key 0); each
+// group of 64 tiles' verdicts becomes two mask words by one ballot.
 constexpr int kSelWaves = 4;
 
 template <int D>
@@ -110,29 +114,74 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, read by every lane
 
-    // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
-    const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
-    const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
-    const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
-    const auto r_km = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
-        __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
-    // scores of every key tile (also invalid ones, for inspection)
-    for (int j = lane; j < a.n_kt; j += 64) {
-      float acc = 0.0f;
-      constexpr int C = 64;  // loads in flight per round trip
-#pragma unroll
-      for (int d0 = 0; d0 < D; d0 += C) {
-        float kv[C];
-#pragma unroll
-        for (int d = 0; d < C; ++d)
-          kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
-#pragma unroll
-        for (int d = 0; d < C; ++d) acc = acc + sq[d0 + d] * kv[d];  // two roundings: contraction is off here
-        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
+    if (a.maxkey) {
+      // max-pooled key logits: for each key tile, lane l takes key 64 j + l,
+      // its dot product with the tile mean (d ascending, rounded products and
+      // sums), and the wave's maximum is the tile's score (-inf when no key of
+      // the tile is valid).  Only the row's valid tiles unless every score is
+      // reported.
+      int jmax = a.n_kt;
+      if (!a.scores) {
+        const int qs = i * a.Bq;
+        if (qs >= a.n_valid) {
+          jmax = 0;
+        } else {
+          const int qe = min(qs + a.Bq, a.n_valid) - 1;
+          int last = (a.n_valid - 1) / a.Bk;
+          if (a.causal) last = min(last, qe / a.Bk);
+          jmax = last + 1;
+        }
       }
-      sc[j] = acc;
-      if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+      const uint16_t* kb = a.k + bhk * a.N * D;
+      for (int j = 0; j < jmax; ++j) {
+        const int key = j * a.Bk + lane;
+        float acc = -__builtin_inff();
+        if (key < a.n_valid) {
+          const uint4* row = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * D);
+          acc = 0.0f;
+#pragma unroll 4
+          for (int u = 0; u < D / 8; ++u) {
+            const uint4 w = row[u];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t bits = (e & 1) ? (ww[e >> 1] & 0xFFFF0000u) : (ww[e >> 1] << 16);
+              acc = acc + sq[8 * u + e] * __uint_as_float(bits);  // two roundings: contraction is off
+            }
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc = fmaxf(acc, __shfl_xor(acc, off));
+        if (lane == 0) {
+          sc[j] = acc;
+          if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+        }
+      }
+    } else {
+      // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
+      const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
+      const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
+      const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
+      const auto r_km = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
+          __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
+      // scores of every key tile (also invalid ones, for inspection)
+      for (int j = lane; j < a.n_kt; j += 64) {
+        float acc = 0.0f;
+        constexpr int C = 64;  // loads in flight per round trip
+#pragma unroll
+        for (int d0 = 0; d0 < D; d0 += C) {
+          float kv[C];
+#pragma unroll
+          for (int d = 0; d < C; ++d)
+            kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
+#pragma unroll
+          for (int d = 0; d < C; ++d) acc = acc + sq[d0 + d] * kv[d];  // two roundings: contraction is off here
+          __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
+        }
+        sc[j] = acc;
+        if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+      }
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }  // (score_free: the budget below is 0, so no score is ever read)
@@ -410,7 +459,8 @@ extern "C" size_t attn_select_blocks_workspace(const mxq_attn_shape* s) {
 }
 
 // k_select over given tile means (layouts as k_tile_means writes them)
-static mxq_status launch_select(const float* qmean, const float* kmean, const mxq_attn_shape* s,
+static mxq_status launch_select(const float* qmean, const float* kmean, const uint16_t* k_bf16,
+                                const mxq_attn_shape* s,
                                 const mxq_select_params* p, uint32_t* mask, int32_t* n_fp16, float* scores,
                                 bool score_free, hipStream_t strm) {
   const int n_qt = s->N / s->Bq, n_kt = s->N / s->Bk;
@@ -423,6 +473,8 @@ static mxq_status launch_select(const float* qmean, const float* kmean, const mx
   a.B = s->B;
   a.score_free = score_free ? 1 : 0;
   a.shared = p->group_shared ? 1 : 0;
+  a.maxkey = p->heuristic == 1 ? 1 : 0;
+  a.k = k_bf16;
   const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
   const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
   if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
@@ -436,6 +488,8 @@ static mxq_status check_select_params(const mxq_select_params* p) {
               "attn_select_blocks: need topk >= 0 or ratio_num >= 0 and ratio_den > 0");
   MXQ_REQUIRE(p->group_shared == 0 || p->group_shared == 1, MXQ_EINVAL,
               "attn_select_blocks: group_shared must be 0 or 1");
+  MXQ_REQUIRE(p->heuristic == 0 || p->heuristic == 1, MXQ_EINVAL,
+              "attn_select_blocks: heuristic must be 0 (tile means) or 1 (max-pooled key logits)");
   MXQ_REQUIRE(p->sink_tiles >= 0 && p->local_tiles >= 0, MXQ_EINVAL,
               "attn_select_blocks: sink_tiles and local_tiles must be >= 0");
   return MXQ_OK;
@@ -450,7 +504,9 @@ extern "C" mxq_status attn_select_blocks_means(const float* q_means, const float
   if ((st = check_select_params(p)) != MXQ_OK) return st;
   MXQ_REQUIRE(q_means != nullptr && k_means != nullptr && mask != nullptr, MXQ_EINVAL,
               "attn_select_blocks_means: q_means, k_means and mask are required");
-  return launch_select(q_means, k_means, s, p, mask, n_fp16, scores, false, as_stream(stream));
+  MXQ_REQUIRE(p->heuristic == 0, MXQ_EUNSUPPORTED,
+              "attn_select_blocks_means: the max-pooled key heuristic needs the key rows (attn_select_blocks)");
+  return launch_select(q_means, k_means, nullptr, s, p, mask, n_fp16, scores, false, as_stream(stream));
 }
 
 extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
@@ -466,6 +522,8 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
               "attn_select_blocks: need topk >= 0 or ratio_num >= 0 and ratio_den > 0");
   MXQ_REQUIRE(p->group_shared == 0 || p->group_shared == 1, MXQ_EINVAL,
               "attn_select_blocks: group_shared must be 0 or 1");
+  MXQ_REQUIRE(p->heuristic == 0 || p->heuristic == 1, MXQ_EINVAL,
+              "attn_select_blocks: heuristic must be 0 (tile means) or 1 (max-pooled key logits)");
   MXQ_REQUIRE(p->sink_tiles >= 0 && p->local_tiles >= 0, MXQ_EINVAL,
               "attn_select_blocks: sink_tiles and local_tiles must be >= 0");
   MXQ_REQUIRE(workspace != nullptr && ws_bytes >= attn_select_blocks_workspace(s), MXQ_EINVAL,
@@ -485,7 +543,7 @@ extern "C" mxq_status attn_select_blocks(const uint16_t* q, const uint16_t* k,
                        s->D, s->Bk, s->n_valid, n_kt, 1);
     if ((st = check_launch("k_tile_means(k)")) != MXQ_OK) return st;
   }
-  return launch_select(qmean, kmean, s, p, mask, n_fp16, scores, score_free, strm);
+  return launch_select(qmean, kmean, k, s, p, mask, n_fp16, scores, score_free, strm);
 }
 
 extern "C" size_t attn_select_lines_workspace(const mxq_attn_shape* s) {

@@ -87,10 +87,17 @@ typedef struct {
  * vertical-line signals shared by the heads of a group, applied to tiles):
  * the G query heads of a kv group score with their shared tile means (the G
  * heads' means summed in fp32 in head order, divided once by G) and so share
- * one mask; 0: per query head. */
+ * one mask; 0: per query head.  heuristic (ThriftAttention, abstract: the
+ * importance of each query-key interaction; the pages give no formula):
+ * 0, reading R8 (mean of the query tile . mean of the key tile); 1, reading
+ * R37, max-pooled key logits: the largest, over the key tile's valid keys, of
+ * (mean of the query tile) . key, with R8's fp32 order (a tile with no valid
+ * key scores -inf); it needs the key rows, so attn_select_blocks_means takes
+ * 0 only. */
 typedef struct {
   int32_t topk, ratio_num, ratio_den, sink_tiles, local_tiles;
   int32_t group_shared;
+  int32_t heuristic;
 } mxq_select_params;
 
 /* ---------------------------------------------------------------------------

@@ -16,7 +16,9 @@ The pages give no formula; the readings used here (R8-R11) are:
   descending score, ties to the lower tile index;
 * optionally one mask per kv group (R35, after HyQuant's vertical-line
   signals shared by the query heads of a group): the G heads' tile means are
-  averaged (fp32 sum in head order, one division by G) and scored as above.
+  averaged (fp32 sum in head order, one division by G) and scored as above;
+* optionally max-pooled key logits (R37): a tile's score is the largest logit
+  of the query-tile mean against the tile's individual keys.
 """
 
 from __future__ import annotations
@@ -93,6 +95,22 @@ def tile_scores(qm: np.ndarray, km: np.ndarray) -> np.ndarray:
     return acc
 
 
+def tile_scores_maxkey(qm: np.ndarray, k_rows: np.ndarray, n_valid: int, Bk: int) -> np.ndarray:
+    """Max-pooled key logits (reading R37): s[i, j] = the largest, over the
+    valid keys of key tile j, of qm[i] . k_key with the arithmetic of
+    ``tile_scores`` (fl32 products, fl32 sums, d ascending, from +0); -inf for
+    a tile with no valid key.  Unlike the mean-pooled key tile, one strong key
+    keeps its full weight in the score of its tile."""
+    n_qt, D = qm.shape
+    N = k_rows.shape[0]
+    acc = np.zeros((n_qt, N), dtype=np.float32)
+    for d in range(D):
+        prod = (qm[:, d][:, None] * k_rows[:, d][None, :]).astype(np.float32)
+        acc = (acc + prod).astype(np.float32)
+    acc[:, n_valid:] = -np.inf
+    return acc.reshape(n_qt, N // Bk, Bk).max(axis=2)
+
+
 def budget(topk, ratio_num, ratio_den, n_valid_tiles, n_candidates):
     """k_i (reading R9): topk if topk >= 0, else ceil(num*|V_i|/den) computed
     in integers; never more than the number of candidates."""
@@ -114,13 +132,14 @@ def group_tile_means(qm_heads: np.ndarray) -> np.ndarray:
 
 
 def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, ratio_den,
-                  sink_tiles, local_tiles, group_shared=False):
+                  sink_tiles, local_tiles, group_shared=False, heuristic="mean"):
     """Return (mask u32 [B,Hq,n_qt,ceil(n_kt/32)], n_fp16 i32 [B,Hq,n_qt],
     scores f32 [B,Hq,n_qt,n_kt]).  Bit j%32 of word j//32 is set when key tile
     j runs in FP16 for that query tile.  Scores are given for every tile pair
     (also non-candidates) for inspection.  With ``group_shared`` (reading R35)
     the G query heads of a kv group score with their shared tile means
-    (``group_tile_means``) and so share one mask."""
+    (``group_tile_means``) and so share one mask.  ``heuristic`` "maxkey"
+    scores with the max-pooled key logits (R37) instead of the key tile means."""
     B, Hq, N, D = q_bits.shape
     Hkv = k_bits.shape[1]
     G = Hq // Hkv
@@ -128,6 +147,9 @@ def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, rati
     nw = (n_kt + 31) // 32
     sets = tile_sets(n_valid, N, Bq, Bk, causal, sink_tiles, local_tiles)
     qm, km = pooled_means(q_bits, k_bits, n_valid, Bq, Bk)
+    if heuristic == "maxkey":
+        kf = bf16_bits_to_f32(k_bits).copy()
+        kf[..., n_valid:, :] = 0.0
     mask = np.zeros((B, Hq, n_qt, nw), dtype=np.uint32)
     nfp = np.zeros((B, Hq, n_qt), dtype=np.int32)
     scores = np.zeros((B, Hq, n_qt, n_kt), dtype=np.float32)
@@ -135,7 +157,7 @@ def select_blocks(q_bits, k_bits, n_valid, Bq, Bk, causal, topk, ratio_num, rati
         for h in range(Hq):
             kv = h // G
             qh = group_tile_means(qm[b, kv * G:(kv + 1) * G]) if group_shared else qm[b, h]
-            s = tile_scores(qh, km[b, kv])
+            s = tile_scores(qh, km[b, kv]) if heuristic == "mean" else tile_scores_maxkey(qh, kf[b, kv], n_valid, Bk)
             scores[b, h] = s
             for i in range(n_qt):
                 valid, forced = sets[i]

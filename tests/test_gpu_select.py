@@ -203,3 +203,27 @@ def test_group_shared_masks_bit_exact(fused):
         rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in (0, 7, 15)])
         o = out.cpu().numpy()[:, h:h + 1][..., rows, :]
         assert np.abs(o - ro[..., rows, :]).max() <= 5e-3
+
+
+def test_maxkey_heuristic_bit_exact():
+    """Max-pooled key logits (reading R37): scores, masks and counts bit-exact
+    against the oracle (causal, ragged, GQA), and the means-only entry point
+    refuses the heuristic."""
+    mxq = gpu_or_skip()
+    cfg = mxq_inputs.make_prefill("llama8b", N=1024, n_valid=1000, Hq=8, Hkv=2)
+    q, k = bf16_dev(cfg["q"]), bf16_dev(cfg["k"])
+    shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
+                      cfg["causal"])
+    for want_scores in (True, False):
+        mask, nfp, sc = mxq.attn_select_blocks(q, k, shape, topk=-1, ratio=(10, 100), sink_tiles=1, local_tiles=1,
+                                               want_scores=want_scores, heuristic=1)
+        rm, rn, rs = S.select_blocks(cfg["q"], cfg["k"], cfg["n_valid"], cfg["Bq"], cfg["Bk"], True, -1, 10, 100,
+                                     1, 1, heuristic="maxkey")
+        assert np.array_equal(u32(mask), rm) and np.array_equal(nfp.cpu().numpy(), rn)
+        if want_scores:
+            assert np.array_equal(sc.cpu().numpy(), rs)
+    ops, qm, km = mxq.prepare_prefill_means(q, k, bf16_dev(cfg["v"]), shape)
+    sp = mxq.SelectParams(-1, 10, 100, 1, 1, 0, 1)
+    st = mxq.load_library().attn_select_blocks_means(mxq._ptr(qm), mxq._ptr(km), mxq.ctypes.byref(shape.c()),
+                                                     mxq.ctypes.byref(sp), mxq._ptr(mask), None, None, mxq._stream())
+    assert st == mxq.MXQ_EUNSUPPORTED

@@ -204,3 +204,44 @@ def test_group_shared_differs_from_per_head_in_general():
     shared, _, _ = S.select_blocks(q, k, 512, 64, 64, False, 1, 0, 1, 0, 0, group_shared=True)
     assert not np.array_equal(per_head, shared)
     assert all(np.array_equal(shared[0, h], shared[0, 0]) for h in range(4))
+
+
+# ---- max-pooled key logits (reading R37)
+def test_maxkey_scores_brute_force():
+    """Small-integer inputs: every fp32 step is exact, so the score is the
+    float64 maximum over each tile's valid keys of (exact query-tile mean) .
+    key; -inf for a tile with no valid key."""
+    B, Hq, Hkv, N, D, Bq, Bk, nv = 1, 2, 1, 384, 64, 64, 64, 288  # a 32-row tile: its mean is exact
+    q = _small_int_bits((B, Hq, N, D), 7)
+    k = _small_int_bits((B, Hkv, N, D), 8)
+    _, _, sc = S.select_blocks(q, k, nv, Bq, Bk, False, 1, 0, 1, 0, 0, heuristic="maxkey")
+    qf = F.bf16_bits_to_f32(q).astype(np.float64)
+    kf = F.bf16_bits_to_f32(k).astype(np.float64)
+    for h in range(Hq):
+        for i in range(N // Bq):
+            rows = [r for r in range(i * Bq, (i + 1) * Bq) if r < nv]
+            if not rows:
+                continue
+            qbar = qf[0, h, rows].mean(axis=0)
+            for j in range(N // Bk):
+                keys = [c for c in range(j * Bk, (j + 1) * Bk) if c < nv]
+                want = max(qbar @ kf[0, 0, c] for c in keys) if keys else -np.inf
+                assert sc[0, h, i, j] == want
+
+
+def test_maxkey_finds_one_strong_key_that_the_mean_dilutes():
+    """A single key aligned with the queries' shared direction, in an
+    otherwise ordinary tile: its tile tops the max-pooled scores, while the
+    mean over the tile's 64 keys dilutes it below tiles of mildly aligned keys."""
+    rng = np.random.default_rng(9)
+    N, D = 1024, 64
+    common = rng.standard_normal(D).astype(np.float32)
+    q = (rng.standard_normal((1, 1, N, D)) + common).astype(np.float32)
+    k = rng.standard_normal((1, 1, N, D)).astype(np.float32)
+    k[0, 0, 64 * 5:64 * 6] += 0.3 * common      # tile 5: every key a little aligned
+    k[0, 0, 64 * 11 + 17] = 8.0 * common        # tile 11: one strong key
+    qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
+    mean_mask, _, mean_sc = S.select_blocks(qb, kb, N, 64, 64, False, 1, 0, 1, 0, 0)
+    max_mask, _, max_sc = S.select_blocks(qb, kb, N, 64, 64, False, 1, 0, 1, 0, 0, heuristic="maxkey")
+    assert all(S.mask_to_sets(max_mask[0, 0, i], 16) == [11] for i in range(16))
+    assert all(S.mask_to_sets(mean_mask[0, 0, i], 16) == [5] for i in range(16))
