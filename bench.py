@@ -14,7 +14,8 @@ configuration.  The JSON line reports effective attention TFLOP/s of the step
 roofline of the dominant kernel (attn_mixed_fwd, timed with HIP events on the
 stream it runs on) against the precision-weighted MFMA peak, the CPU oracle
 timed on a bounded sample across the host's cores, and two extra legs: the
-Llama-8B-shaped prefill (N=8192) and the quantised-KV decode step (KV-read
+Llama-8B-shaped prefill (N=8192), the ViT-shaped batch (512 x 12 heads x 197
+tokens, the short-sequence kernel) and the quantised-KV decode step (KV-read
 GB/s against HBM peak).
 
 Warm-up, the same rule for every leg: W untimed steps, then more until at
@@ -594,7 +595,7 @@ def main():
     ap.add_argument("--workload", default="long32k", choices=["tiny", "llama8b", "long32k", "vit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the Llama-8B-shaped prefill leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the Llama-8B-shaped and ViT-shaped prefill legs")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "quality"], default=None,
                     help="copy: a plain device copy of a known size, the reference for HBM byte counters; "
                          "quality: the synthetic error/speed curve over the FP16 fraction")
@@ -632,13 +633,17 @@ def main():
     if args.only == "quality":
         quality_sweep(args, dev)
         return
-    pre = extra = dec = None
+    pre = dec = None
+    extras = {}
     if args.only != "decode":
         pre = bench_prefill(args, dev, args.workload)
-        if not args.no_extra and args.only is None and args.workload != "llama8b":
-            extra = bench_prefill(args, dev, "llama8b")
-            for key in ("q", "k", "v"):  # only the headline's inputs feed the CPU baseline
-                extra["cfg"].pop(key)
+        if not args.no_extra and args.only is None:
+            for name in ("llama8b", "vit"):
+                if name == args.workload:
+                    continue
+                extras[name] = bench_prefill(args, dev, name)
+                for key in ("q", "k", "v"):  # only the headline's inputs feed the CPU baseline
+                    extras[name]["cfg"].pop(key)
     if args.only != "prefill" and not args.no_decode:
         dec = bench_decode(args, dev)
     cpu = cpu_dec = None
@@ -659,10 +664,10 @@ def main():
         line.update(value=round(pre["tflops_step"], 3), unit="TFLOP/s", ms_per_step=round(pre["ms_step"], 4),
                     dtype="mxfp4 QK^T + fp8 PV, fp16 on selected tiles, fp32 accumulate", config=summ["config"],
                     roofline=summ["roofline"])
-    if extra is not None:
+    for name, extra in extras.items():
         summ = prefill_summary(extra, with_traffic=True)
-        line["llama8b"] = dict(value=round(extra["tflops_step"], 3), unit="TFLOP/s",
-                               ms_per_step=round(extra["ms_step"], 4), **summ)
+        line[name] = dict(value=round(extra["tflops_step"], 3), unit="TFLOP/s",
+                          ms_per_step=round(extra["ms_step"], 4), **summ)
     if dec is not None:
         dline = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 5),
                  "workload": "decode: 64 seqs x 32768 cached tokens, Hq=32 Hkv=8 D=128, INT4-G32 KV + fp16 "

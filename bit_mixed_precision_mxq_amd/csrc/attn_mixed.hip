@@ -74,6 +74,7 @@ struct AttnArgs {
   int Hq, Hkv, N, n_valid, n_qt, words, causal, mode, out_bf16;
   int sel_bq;  // query rows per selection tile (mask row = query row / sel_bq)
   int n_lines;
+  int nbh;  // B * Hq
   float c;  // fl32(softmax_scale * log2(e))
 };
 
@@ -1143,6 +1144,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 //               head's MXFP4 K and MXFP8 V^T (and their scales) are staged
 //               once in LDS (26 KB at head_dim 64), so several workgroups
 //               share a CU;
+//   work order: workgroups are dispatched round-robin over the 8 XCDs, so
+//               linear id w runs on XCD w % 8; the query tiles of one head
+//               take ids that agree mod 8 and follow one another on that XCD
+//               (head 8 (r / n_t) + w % 8, tile r % n_t with r = w / 8), and
+//               the head's K and V leave HBM for one L2 only;
 //   FP16 tiles and line keys read their bf16 K rows and fp16 V^T straight
 //   from global memory into the MFMA operand registers (bounds-checked
 //   buffer loads; unused entries read zeros).
@@ -1168,7 +1174,11 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int it = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n_t = a.N / BQ;
+  const int wr = static_cast<int>(blockIdx.x >> 3);
+  const int head = (wr / n_t) * 8 + static_cast<int>(blockIdx.x & 7);
+  if (head >= a.nbh) return;  // the whole workgroup: grid rounded up to whole groups of 8 heads
+  const int it = wr % n_t, h = head % a.Hq, b = head / a.Hq;
   const int G = a.Hq / a.Hkv;
   const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
   const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + h / G;
@@ -1587,8 +1597,8 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
 }
 
 template <int D>
-mxq_status launch_short(const AttnArgs& a, int Hq, int B, hipStream_t st) {
-  const dim3 grid(a.N / 64, Hq, B);
+mxq_status launch_short(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((a.nbh + 7) / 8 * 8 * (a.N / 64)));
   if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_short<D, true>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((k_attn_short<D, false>), grid, dim3(256), 0, st, a);
   return check_launch("k_attn_short");
@@ -1643,6 +1653,7 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
   a.words = (s->N / s->Bk + 31) / 32; a.causal = s->causal; a.mode = mode;
   a.out_bf16 = out_dtype == MXQ_OUT_BF16;
   a.sel_bq = s->Bq;
+  a.nbh = 0;
   a.c = static_cast<float>(sc * 1.4426950408889634);
   hipStream_t strm = as_stream(stream);
   // 128-row workgroups of 8 waves whatever the selection tile height (the
@@ -1651,8 +1662,12 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
   a.n_qt = n_qt;
   // at most two 128-key chunks: small workgroups that stage the whole head
   if (s->N <= 256) {
-    if (s->D == 128) return launch_short<128>(a, s->Hq, s->B, strm);
-    return launch_short<64>(a, s->Hq, s->B, strm);
+    // one-dimensional grid: at most 2^21 heads x 4 query tiles x 256 threads
+    MXQ_REQUIRE(static_cast<int64_t>(s->B) * s->Hq <= (1 << 21), MXQ_EUNSUPPORTED,
+                "attn_mixed_fwd: at most 2^21 (batch, head) pairs when N <= 256");
+    a.nbh = s->B * s->Hq;
+    if (s->D == 128) return launch_short<128>(a, strm);
+    return launch_short<64>(a, strm);
   }
   if (s->D == 128) return launch<128>(a, n_qt, s->Hq, s->B, strm);
   return launch<64>(a, n_qt, s->Hq, s->B, strm);

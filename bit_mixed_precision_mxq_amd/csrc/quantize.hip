@@ -18,36 +18,40 @@
 namespace mxq {
 namespace {
 
-// One 32-element block of bf16 (16 words, element 2i in the low half of word
-// i) -> 16 bytes of E2M1 codes (two per byte, element 0 in the low nibble) and
-// its E8M0 scale code.
-__device__ __forceinline__ void mxfp4_block(const uint32_t (&w)[16], uint4& codes_out, uint8_t& scale_out) {
+// One quarter of a 32-element block per lane: the lane's 8 bf16 (element 2i
+// in the low half of word i), the four lanes of an aligned quad holding the
+// block's quarters in order.  The block maximum is shared across the quad
+// with two DPP quad permutes (every lane of the quad must be active); returns
+// the lane's 8 E2M1 codes (element 0 in the low nibble) and sets e to the
+// block's shared exponent (OCP MX: floor(log2 amax) - 2).  Each element is
+// scaled exactly by 2^-e and rounded to the nearest E2M1 magnitude, ties to
+// the even code; the sign bit copies the input's.
+__device__ __forceinline__ uint32_t mxfp4_quarter(const uint4 w4, int& e) {
+  const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 4; ++i) {
     amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
     amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
   }
-  int e = shared_exponent(amax, 2);
-  uint32_t packed[4] = {0, 0, 0, 0};
+  const int ai = __float_as_int(amax);
+  const float a1 = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(ai, 0xB1, 0xF, 0xF, false)));  // quad [1,0,3,2]
+  const int a1i = __float_as_int(a1);
+  amax = fmaxf(a1, __int_as_float(__builtin_amdgcn_mov_dpp(a1i, 0x4E, 0xF, 0xF, false)));  // quad [2,3,0,1]
+  e = shared_exponent(amax, 2);
+  float v[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t b = h ? (w[i] & 0xFFFF0000u) : (w[i] << 16);
-      float v = __builtin_ldexpf(__uint_as_float(b), -e);
-      uint32_t c = e2m1_mag_code(fabsf(v)) | ((b >> 28) & 8u);
-      int el = 2 * i + h;  // element index within the block
-      packed[el / 8] |= c << (4 * (el % 8));
-    }
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __builtin_ldexpf(__uint_as_float(w[i] << 16), -e);
+    v[2 * i + 1] = __builtin_ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -e);
   }
-  codes_out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  scale_out = static_cast<uint8_t>(e + 127);
+  return e2m1_pack8(v);
 }
 
-// ---- MXFP4 along D: one thread per 32-element block ---------------------------
-// x [rows][D] bf16 -> codes [rows][D/2], scales [rows][D/32].  Consecutive
-// threads take consecutive blocks, so a wave reads 4 KB of contiguous input.
+// ---- MXFP4 along D: four lanes per 32-element block ---------------------------
+// x [rows][D] bf16 -> codes [rows][D/2], scales [rows][D/32].  Lane 4 blk + u
+// takes elements 8u .. 8u+7 of block blk, so each load of a wave reads 1 KB of
+// contiguous input and each code store writes 256 contiguous bytes.
 // A second tensor (x2, codes2, scales2; n_blocks2 blocks of the same row
 // length, N and n_valid) may follow the first in the same launch: blocks
 // n_blocks .. n_blocks + n_blocks2 - 1 are its blocks 0 .. n_blocks2 - 1.
@@ -60,24 +64,30 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4_d(const uint16_t* __restric
                                                        uint8_t* __restrict__ codes2 = nullptr,
                                                        uint8_t* __restrict__ scales2 = nullptr,
                                                        int64_t n_blocks2 = 0) {
-  int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (blk >= n_blocks + n_blocks2) return;
-  if (blk >= n_blocks) {
-    blk -= n_blocks;
+  // 32-bit indices: the host allows at most 2^29 blocks in one launch
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  uint32_t blk = gid >> 2;
+  const int u = static_cast<int>(gid & 3u);
+  // no early exit: the quad permutes need every lane of the quad (a quad is
+  // one block, so its lanes agree on every condition below)
+  const bool in = blk < static_cast<uint32_t>(n_blocks + n_blocks2);
+  if (blk >= static_cast<uint32_t>(n_blocks)) {
+    blk -= static_cast<uint32_t>(n_blocks);
     x = x2;
     codes = codes2;
     scales = scales2;
   }
-  int64_t row = blk / blocks_per_row;
-  bool live = (row % N) < n_valid;
-  const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 v = live ? src[i] : make_uint4(0, 0, 0, 0);
-    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  // padding rows (row % N >= n_valid) read as zeros; without padding no
+  // division is needed
+  const bool live = in && (n_valid >= N || (blk / static_cast<uint32_t>(blocks_per_row)) %
+                                                   static_cast<uint32_t>(N) < static_cast<uint32_t>(n_valid));
+  const uint4 w4 = live ? reinterpret_cast<const uint4*>(x)[blk * 4u + u] : make_uint4(0, 0, 0, 0);
+  int e;
+  const uint32_t packed = mxfp4_quarter(w4, e);
+  if (in) {
+    reinterpret_cast<uint32_t*>(codes)[blk * 4u + u] = packed;
+    if (u == 0) scales[blk] = static_cast<uint8_t>(e + 127);
   }
-  mxfp4_block(w, reinterpret_cast<uint4*>(codes)[blk], scales[blk]);
 }
 
 // ---- MXFP4 of Q and K plus their tile means in one pass ----------------------
@@ -111,26 +121,43 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4_tiles(const uint16_t* __res
   if (tile >= n_tiles) return;  // the whole workgroup
   const int tid = threadIdx.x;
   const int64_t row0 = bh * N + static_cast<int64_t>(tile) * T;  // first row of the tile
-  for (int lb = tid; lb < T * BPR; lb += 256) {
-    const int r = lb / BPR, cb = lb % BPR;
-    const int64_t blk = (row0 + r) * BPR + cb;
-    const bool live = tile * T + r < n_valid;
-    const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);
-    uint32_t w[16];
+  // 16-byte unit tid + 256 p of the tile (row-major, 8 bf16 each), four units
+  // to a 32-element block: every load of the tile goes out before any is used
+  constexpr int UPR = D / 8;                // units per row
+  constexpr int PASSES = 128 * UPR / 256;   // for the tallest tile (128 rows)
+  uint4 w4[PASSES];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = live ? src[i] : make_uint4(0, 0, 0, 0);
-      w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-      *reinterpret_cast<uint4*>(&tile_w[r * (D / 2) + cb * 16 + 4 * i]) = v;
+  for (int p = 0; p < PASSES; ++p) {
+    const int uidx = tid + 256 * p, r = uidx / UPR;
+    const bool live = r < T && tile * T + r < n_valid;
+    w4[p] = live ? reinterpret_cast<const uint4*>(x + row0 * D)[uidx] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int uidx = tid + 256 * p, r = uidx / UPR;
+    if (r < T) *reinterpret_cast<uint4*>(&tile_w[4 * uidx]) = w4[p];
+    int e;
+    const uint32_t packed = mxfp4_quarter(w4[p], e);  // whole quads agree on r < T
+    if (r < T) {
+      const int64_t blk = (row0 + r) * BPR + (uidx % UPR) / 4;
+      reinterpret_cast<uint32_t*>(codes)[(row0 * D) / 8 + uidx] = packed;
+      if ((uidx & 3) == 0) scales[blk] = static_cast<uint8_t>(e + 127);
     }
-    mxfp4_block(w, reinterpret_cast<uint4*>(codes)[blk], scales[blk]);
   }
   __syncthreads();
   if (tid < D) {
     const int rows = max(0, min(T, n_valid - tile * T));
     const uint16_t* col = reinterpret_cast<const uint16_t*>(tile_w) + tid;
     float acc = 0.0f;
-    for (int r = 0; r < rows; ++r) acc = acc + bf16_to_f32(col[r * D]);
+    int r = 0;
+    for (; r + 16 <= rows; r += 16) {  // 16 LDS reads in flight, then the sums in row order
+      uint16_t v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = col[(r + j) * D];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc = acc + bf16_to_f32(v[j]);
+    }
+    for (; r < rows; ++r) acc = acc + bf16_to_f32(col[r * D]);
     const float m = rows > 0 ? acc / static_cast<float>(rows) : 0.0f;  // correctly rounded division
     if (transposed) mean[(bh * D + tid) * n_tiles + tile] = m;
     else mean[(bh * n_tiles + tile) * D + tid] = m;
@@ -460,7 +487,8 @@ extern "C" mxq_status mxq_quantize(const uint16_t* x, int64_t B, int64_t H, int6
     MXQ_REQUIRE(scales != nullptr && zeros == nullptr, MXQ_EINVAL,
                 "mxq_quantize MXFP4: scales required, zeros must be NULL");
     int64_t nb = rows * (D / 32);
-    hipLaunchKernelGGL(k_quant_mxfp4_d, dim3(grid_for(nb, 256)), dim3(256), 0, st, x,
+    MXQ_REQUIRE(nb <= (int64_t{1} << 29), MXQ_EUNSUPPORTED, "mxq_quantize MXFP4: at most 2^29 blocks of 32");
+    hipLaunchKernelGGL(k_quant_mxfp4_d, dim3(grid_for(4 * nb, 256)), dim3(256), 0, st, x,
                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), nb, D / 32, N,
                        n_valid);
     return check_launch("k_quant_mxfp4_d");
@@ -551,7 +579,9 @@ extern "C" mxq_status mxq_prefill_operands(const uint16_t* q, const uint16_t* k,
                    : launch_had<64>(q, q_codes, q_scales, rows_q, N, nv, st, k, k_codes, k_scales, rows_k);
     } else {
       const int64_t nb_q = rows_q * (D / 32), nb_k = rows_k * (D / 32);
-      hipLaunchKernelGGL(k_quant_mxfp4_d, dim3(grid_for(nb_q + nb_k, 256)), dim3(256), 0, st, q, q_codes, q_scales,
+      MXQ_REQUIRE(nb_q + nb_k <= (int64_t{1} << 29), MXQ_EUNSUPPORTED,
+                  "mxq_prefill_operands: at most 2^29 blocks of 32 in Q and K together");
+      hipLaunchKernelGGL(k_quant_mxfp4_d, dim3(grid_for(4 * (nb_q + nb_k), 256)), dim3(256), 0, st, q, q_codes, q_scales,
                          nb_q, D / 32, N, nv, k, k_codes, k_scales, nb_k);
       r = check_launch("k_quant_mxfp4_d");
     }

@@ -6,12 +6,13 @@
 //  k_tile_means : fp32 mean of every query tile (per query head) and key tile
 //                 (per kv head); one thread per (tile, d), rows summed in
 //                 ascending order, then one correctly rounded division.
-//  k_select     : one wave per (b, query head, query tile): scores of all
-//                 key tiles against the tile mean (sequential over d, rounded
-//                 product then rounded sum, never fused) -- or of the group's
-//                 shared tile mean (R35), or the max-pooled key logits (R37)
-//                 --, forced tiles, and the top-k by a radix search for the
-//                 k-th largest score with ties to the lower index.
+//  k_select     : one workgroup per (b, query head, up to 8 query tiles):
+//                 scores of all key tiles against each tile mean (sequential
+//                 over d, rounded product then rounded sum, never fused) -- or
+//                 of the group's shared tile mean (R35), or the max-pooled key
+//                 logits (R37) --, forced tiles, and the top-k by a radix
+//                 search for the k-th largest score with ties to the lower
+//                 index.
 // The fixed operation order makes the result bit-identical to a plain CPU
 // evaluation of the same formula.
 #include <algorithm>
@@ -72,47 +73,63 @@ struct SelectArgs {
   int shared;      // one mask per kv group: the G heads' tile means averaged (reading R35)
   int maxkey;      // scores from the max-pooled key logits (reading R37); needs k
   const uint16_t* k;  // bf16 [B*Hkv][N][D] (maxkey only)
+  int qt;          // query tiles per workgroup
 };
 
-// One wave per (batch, query head, query tile), four per workgroup, with no
-// workgroup barrier: the wave keeps its tile mean and scores in its own slice
-// of LDS.  D (64 or 128) is a compile-time constant so that a score's column
-// loads go out 64 at a time before their products; the sum still runs over d
-// in order.  The k best candidates come from a radix search over
-// order-preserving keys of the scores (forced and invalid tiles key 0); each
-// group of 64 tiles' verdicts becomes two mask words by one ballot.
+// Workgroup = (batch, query head, qt consecutive query tiles), four waves:
+//  1. the qt tile means (or the kv group's shared means) go to LDS as [d][row];
+//  2. scores of every key tile.  Tile-mean heuristic: thread t takes key tiles
+//     t, t + 256, ... and accumulates the qt dot products side by side, d
+//     ascending (each still a sequential sum of rounded products), so a key
+//     tile's mean column is read once for all qt rows.  Max-pooled key logits:
+//     wave w takes rows w, w + 4, ..., a lane per key;
+//  3. wave w selects rows w, w + 4, ...: forced tiles, the k best candidates
+//     by a radix search over order-preserving keys of the scores (forced and
+//     invalid tiles key 0), and one ballot per 64 tiles for the mask words.
+// D (64 or 128) is a compile-time constant so that a column's loads go out 32
+// at a time before their products.  Scores live in dynamic LDS, [row][stride]
+// with stride = n_kt rounded up to 64.
 constexpr int kSelWaves = 4;
+constexpr int kSelMaxQT = 8;          // query tiles per workgroup
+constexpr int kSelLdsBytes = 32768;   // the score rows' LDS
 
 template <int D>
 __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_score[kSelWaves][kMaxKeyTiles];
-  __shared__ float s_q[kSelWaves][D];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kSelWaves + wave;
-  if (item >= static_cast<int64_t>(a.n_qt) * a.Hq * a.B) return;  // the whole wave
-  const int i = static_cast<int>(item % a.n_qt);
-  const int64_t bhq = item / a.n_qt;  // b * Hq + h
+  extern __shared__ __attribute__((aligned(16))) float s_dyn[];  // [qt][stride] scores, then keys
+  __shared__ __attribute__((aligned(16))) float s_q[D][kSelMaxQT];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int qt = a.qt;
+  const int nblk = (a.n_qt + qt - 1) / qt;
+  const int64_t bhq = static_cast<int64_t>(blockIdx.x) / nblk;  // b * Hq + h
+  const int i0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) % nblk) * qt;
+  const int nrows = min(qt, a.n_qt - i0);
   const int h = static_cast<int>(bhq % a.Hq);
   const int64_t bhk = (bhq / a.Hq) * a.Hkv + h / (a.Hq / a.Hkv);
-  float* sc = s_score[wave];
-  float* sq = s_q[wave];
+  const int stride = (a.n_kt + 63) & ~63;
 
   if (!a.score_free) {
-    if (a.shared) {
-      // the kv group's shared tile mean: the G heads' means summed in head
-      // order, one division by G (every head of the group computes the same)
-      const int G = a.Hq / a.Hkv;
-      const int64_t bh0 = bhq - h % G;
-      for (int d = lane; d < D; d += 64) {
-        float acc = 0.0f;
-        for (int hh = 0; hh < G; ++hh) acc = acc + a.qmean[((bh0 + hh) * a.n_qt + i) * D + d];
-        sq[d] = acc / static_cast<float>(G);
+    for (int idx = tid; idx < D * kSelMaxQT; idx += 64 * kSelWaves) {
+      const int r = idx / D, d = idx % D;
+      float v = 0.0f;
+      if (r < nrows) {
+        const int i = i0 + r;
+        if (a.shared) {
+          // the kv group's shared tile mean: the G heads' means summed in head
+          // order, one division by G (every head of the group computes the same)
+          const int G = a.Hq / a.Hkv;
+          const int64_t bh0 = bhq - h % G;
+          float acc = 0.0f;
+          for (int hh = 0; hh < G; ++hh) acc = acc + a.qmean[((bh0 + hh) * a.n_qt + i) * D + d];
+          v = acc / static_cast<float>(G);
+        } else {
+          v = a.qmean[(bhq * a.n_qt + i) * D + d];
+        }
       }
-    } else {
-      for (int d = lane; d < D; d += 64) sq[d] = a.qmean[(bhq * a.n_qt + i) * D + d];
+      s_q[d][r] = v;
     }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, read by every lane
+    __syncthreads();
 
     if (a.maxkey) {
       // max-pooled key logits: for each key tile, lane l takes key 64 j + l,
@@ -120,45 +137,49 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
       // sums), and the wave's maximum is the tile's score (-inf when no key of
       // the tile is valid).  Only the row's valid tiles unless every score is
       // reported.
-      int jmax = a.n_kt;
-      if (!a.scores) {
-        const int qs = i * a.Bq;
-        if (qs >= a.n_valid) {
-          jmax = 0;
-        } else {
-          const int qe = min(qs + a.Bq, a.n_valid) - 1;
-          int last = (a.n_valid - 1) / a.Bk;
-          if (a.causal) last = min(last, qe / a.Bk);
-          jmax = last + 1;
-        }
-      }
       const uint16_t* kb = a.k + bhk * a.N * D;
-      for (int j = 0; j < jmax; ++j) {
-        const int key = j * a.Bk + lane;
-        float acc = -__builtin_inff();
-        if (key < a.n_valid) {
-          const uint4* row = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * D);
-          acc = 0.0f;
-#pragma unroll 4
-          for (int u = 0; u < D / 8; ++u) {
-            const uint4 w = row[u];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t bits = (e & 1) ? (ww[e >> 1] & 0xFFFF0000u) : (ww[e >> 1] << 16);
-              acc = acc + sq[8 * u + e] * __uint_as_float(bits);  // two roundings: contraction is off
-            }
+      for (int r = wave; r < nrows; r += kSelWaves) {
+        const int i = i0 + r;
+        float* sc = s_dyn + r * stride;
+        int jmax = a.n_kt;
+        if (!a.scores) {
+          const int qs = i * a.Bq;
+          if (qs >= a.n_valid) {
+            jmax = 0;
+          } else {
+            const int qe = min(qs + a.Bq, a.n_valid) - 1;
+            int last = (a.n_valid - 1) / a.Bk;
+            if (a.causal) last = min(last, qe / a.Bk);
+            jmax = last + 1;
           }
         }
+        for (int j = 0; j < jmax; ++j) {
+          const int key = j * a.Bk + lane;
+          float acc = -__builtin_inff();
+          if (key < a.n_valid) {
+            const uint4* row = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * D);
+            acc = 0.0f;
+#pragma unroll 4
+            for (int u = 0; u < D / 8; ++u) {
+              const uint4 w = row[u];
+              const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc = fmaxf(acc, __shfl_xor(acc, off));
-        if (lane == 0) {
-          sc[j] = acc;
-          if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t bits = (e & 1) ? (ww[e >> 1] & 0xFFFF0000u) : (ww[e >> 1] << 16);
+                acc = acc + s_q[8 * u + e][r] * __uint_as_float(bits);  // two roundings: contraction is off
+              }
+            }
+          }
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) acc = fmaxf(acc, __shfl_xor(acc, off));
+          if (lane == 0) {
+            sc[j] = acc;
+            if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+          }
         }
       }
     } else {
-      // kmean[bhk] ([D][n_kt]) as a buffer: lane offset plus a scalar row offset
+      // kmean[bhk] ([D][n_kt]) as a buffer: thread offset plus a scalar row offset
       const uint64_t km_base = reinterpret_cast<uint64_t>(a.kmean + bhk * D * a.n_kt);
       const uint32_t km_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base));
       const uint32_t km_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(km_base >> 32));
@@ -166,9 +187,14 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
           reinterpret_cast<void*>((static_cast<uint64_t>(km_hi) << 32) | km_lo), 0,
           __builtin_amdgcn_readfirstlane(D * a.n_kt * 4), 0x00020000);
       // scores of every key tile (also invalid ones, for inspection)
-      for (int j = lane; j < a.n_kt; j += 64) {
-        float acc = 0.0f;
-        constexpr int C = 64;  // loads in flight per round trip
+      for (int j = tid; j < a.n_kt; j += 64 * kSelWaves) {
+        // the tile means are re-read from LDS for every key tile: kept in
+        // registers across iterations they would spill
+        __asm__ volatile("" ::: "memory");
+        float acc[kSelMaxQT];
+#pragma unroll
+        for (int r = 0; r < kSelMaxQT; ++r) acc[r] = 0.0f;
+        constexpr int C = 32;  // loads in flight per round trip
 #pragma unroll
         for (int d0 = 0; d0 < D; d0 += C) {
           float kv[C];
@@ -176,106 +202,129 @@ __global__ void __launch_bounds__(64 * kSelWaves) k_select(SelectArgs a) {
           for (int d = 0; d < C; ++d)
             kv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_km, 4 * j, 4 * (d0 + d) * a.n_kt, 0));
 #pragma unroll
-          for (int d = 0; d < C; ++d) acc = acc + sq[d0 + d] * kv[d];  // two roundings: contraction is off here
-          __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay behind (register budget)
+          for (int d = 0; d < C; ++d) {
+            const float4 q0 = *reinterpret_cast<const float4*>(&s_q[d0 + d][0]);
+            const float4 q1 = *reinterpret_cast<const float4*>(&s_q[d0 + d][4]);
+            const float qv[kSelMaxQT] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+            for (int r = 0; r < kSelMaxQT; ++r) acc[r] = acc[r] + qv[r] * kv[d];  // two roundings: contraction is off
+            // a few means in registers at a time: the sums so far are pinned
+            // here and later LDS reads stay below (compiler-only fences; the
+            // optimiser would otherwise hoist every read to the top)
+            if (d % 4 == 3) {
+#pragma unroll
+              for (int r = 0; r < kSelMaxQT; ++r) __asm__ volatile("" : "+v"(acc[r]));
+              __asm__ volatile("" ::: "memory");
+            }
+          }
+          __asm__ volatile("" ::: "memory");  // the next chunk's loads stay behind (register budget)
         }
-        sc[j] = acc;
-        if (a.scores) a.scores[(bhq * a.n_qt + i) * a.n_kt + j] = acc;
+#pragma unroll
+        for (int r = 0; r < kSelMaxQT; ++r) {
+          if (r < nrows) {
+            s_dyn[r * stride + j] = acc[r];
+            if (a.scores) a.scores[(bhq * a.n_qt + i0 + r) * a.n_kt + j] = acc[r];
+          }
+        }
       }
     }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }  // (score_free: the budget below is 0, so no score is ever read)
+  __syncthreads();
 
-  uint32_t* mrow = a.mask + (bhq * a.n_qt + i) * a.words;
-  const int qs = i * a.Bq;
-  int count = 0;
-  if (qs < a.n_valid) {
-    const int qe = min(qs + a.Bq, a.n_valid) - 1;
-    int last = (a.n_valid - 1) / a.Bk;
-    if (a.causal) last = min(last, qe / a.Bk);
-    const int nvt = last + 1;
-    const int lo = qs - (a.local_tiles - 1) * a.Bk;
-    auto forced = [&](int j) {
-      bool sink = j < a.sink_tiles;
-      bool local = a.local_tiles >= 1 && (j + 1) * a.Bk - 1 >= lo && j * a.Bk <= qe;
-      return sink || local;
-    };
-    // forced tiles: the sink tiles [0, ns) and the window tiles [lw, hw]
-    const int ns = min(a.sink_tiles, nvt);
-    int n_forced = ns;
-    if (a.local_tiles >= 1) {
-      const int lw = max(0, (lo >= 0 ? lo : lo - a.Bk + 1) / a.Bk), hw = min(nvt - 1, qe / a.Bk);
-      if (hw >= lw) n_forced += (hw - lw + 1) - max(0, min(hw, ns - 1) - lw + 1);
-    }
-    const int n_cand = nvt - n_forced;
-    int64_t k;
-    if (a.topk >= 0) k = a.topk;
-    else k = (static_cast<int64_t>(a.ratio_num) * nvt + a.ratio_den - 1) / a.ratio_den;
-    if (k > n_cand) k = n_cand;
-    // The k best candidates by (score descending, index ascending), found as
-    // the k-th largest score by a radix search over order-preserving keys:
-    // a candidate's score becomes an unsigned key that orders as the float
-    // does (-0 first made +0, the two compare equal), a forced or invalid tile
-    // key 0, below every candidate (a finite score's key is at least
-    // 0x00800000).  Each of the 32 passes fixes one bit of the k-th largest
-    // key by counting, with ballots, the keys that match the bits fixed so
-    // far and have this bit set.
-    uint32_t* key = reinterpret_cast<uint32_t*>(sc);
-    const int nm = (nvt + 63) / 64;  // 64-tile groups holding valid tiles
-    for (int j = lane; j < nm * 64; j += 64) {
-      uint32_t u = 0u;
-      if (j < nvt && !forced(j)) {
-        const uint32_t bits = __float_as_uint(sc[j] + 0.0f);  // -0 -> +0
-        u = bits ^ ((bits >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+  for (int r = wave; r < nrows; r += kSelWaves) {
+    const int i = i0 + r;
+    float* sc = s_dyn + r * stride;
+    uint32_t* mrow = a.mask + (bhq * a.n_qt + i) * a.words;
+    const int qs = i * a.Bq;
+    int count = 0;
+    if (qs < a.n_valid) {
+      const int qe = min(qs + a.Bq, a.n_valid) - 1;
+      int last = (a.n_valid - 1) / a.Bk;
+      if (a.causal) last = min(last, qe / a.Bk);
+      const int nvt = last + 1;
+      const int lo = qs - (a.local_tiles - 1) * a.Bk;
+      auto forced = [&](int j) {
+        bool sink = j < a.sink_tiles;
+        bool local = a.local_tiles >= 1 && (j + 1) * a.Bk - 1 >= lo && j * a.Bk <= qe;
+        return sink || local;
+      };
+      // forced tiles: the sink tiles [0, ns) and the window tiles [lw, hw]
+      const int ns = min(a.sink_tiles, nvt);
+      int n_forced = ns;
+      if (a.local_tiles >= 1) {
+        const int lw = max(0, (lo >= 0 ? lo : lo - a.Bk + 1) / a.Bk), hw = min(nvt - 1, qe / a.Bk);
+        if (hw >= lw) n_forced += (hw - lw + 1) - max(0, min(hw, ns - 1) - lw + 1);
       }
-      key[j] = u;
-    }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    uint32_t thr = 0u;  // the k-th largest key (valid when 0 < k < n_cand)
-    int k_eq = 0;       // how many keys equal to thr are taken (lowest indices first)
-    if (k > 0 && k < n_cand) {
-      uint32_t hi_mask = 0u;
-      int need = static_cast<int>(k);
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t b = 1u << bit;
-        int cnt = 0;
-        for (int m = 0; m < nm; ++m) {
-          const uint32_t u = key[64 * m + lane];
-          cnt += __popcll(__ballot((u & hi_mask) == thr && (u & b) != 0u));
+      const int n_cand = nvt - n_forced;
+      int64_t k;
+      if (a.topk >= 0) k = a.topk;
+      else k = (static_cast<int64_t>(a.ratio_num) * nvt + a.ratio_den - 1) / a.ratio_den;
+      if (k > n_cand) k = n_cand;
+      // The k best candidates by (score descending, index ascending), found as
+      // the k-th largest score by a radix search over order-preserving keys:
+      // a candidate's score becomes an unsigned key that orders as the float
+      // does (-0 first made +0, the two compare equal), a forced or invalid tile
+      // key 0, below every candidate (a finite score's key is at least
+      // 0x00800000).  Each of the 32 passes fixes one bit of the k-th largest
+      // key by counting, with ballots, the keys that match the bits fixed so
+      // far and have this bit set.
+      uint32_t* key = reinterpret_cast<uint32_t*>(sc);
+      const int nm = (nvt + 63) / 64;  // 64-tile groups holding valid tiles
+      for (int j = lane; j < nm * 64; j += 64) {
+        uint32_t u = 0u;
+        if (j < nvt && !forced(j)) {
+          const uint32_t bits = __float_as_uint(sc[j] + 0.0f);  // -0 -> +0
+          u = bits ^ ((bits >> 31) ? 0xFFFFFFFFu : 0x80000000u);
         }
-        if (cnt >= need) thr |= b;
-        else need -= cnt;
-        hi_mask |= b;
+        key[j] = u;
       }
-      k_eq = need;
-    }
-    int eq_before = 0;  // keys equal to thr at lower indices, over the groups done
-    for (int j0 = 0; j0 < a.n_kt; j0 += 64) {
-      const int j = j0 + lane;
-      bool take = j < nvt && forced(j);
-      if (j < nvt && !take && k > 0) {
-        const uint32_t u = key[j];
-        if (k >= n_cand) {
-          take = true;
-        } else {
-          const bool eq = u == thr;
-          const uint64_t eqb = __ballot(eq);
-          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(eqb >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(eqb), 0));
-          take = u > thr || (eq && eq_before + below < k_eq);
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      uint32_t thr = 0u;  // the k-th largest key (valid when 0 < k < n_cand)
+      int k_eq = 0;       // how many keys equal to thr are taken (lowest indices first)
+      if (k > 0 && k < n_cand) {
+        uint32_t hi_mask = 0u;
+        int need = static_cast<int>(k);
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t b = 1u << bit;
+          int cnt = 0;
+          for (int m = 0; m < nm; ++m) {
+            const uint32_t u = key[64 * m + lane];
+            cnt += __popcll(__ballot((u & hi_mask) == thr && (u & b) != 0u));
+          }
+          if (cnt >= need) thr |= b;
+          else need -= cnt;
+          hi_mask |= b;
         }
+        k_eq = need;
       }
-      // equal keys of this group (all lanes take part in the ballot)
-      if (k > 0 && k < n_cand)
-        eq_before += __popcll(__ballot(j < nvt && key[j < nm * 64 ? j : 0] == thr && j < nm * 64));
-      const uint64_t bits = __ballot(take);
-      count += __popcll(bits);
-      if (lane < 2 && j0 / 32 + lane < a.words) mrow[j0 / 32 + lane] = static_cast<uint32_t>(bits >> (32 * lane));
+      int eq_before = 0;  // keys equal to thr at lower indices, over the groups done
+      for (int j0 = 0; j0 < a.n_kt; j0 += 64) {
+        const int j = j0 + lane;
+        bool take = j < nvt && forced(j);
+        if (j < nvt && !take && k > 0) {
+          const uint32_t u = key[j];
+          if (k >= n_cand) {
+            take = true;
+          } else {
+            const bool eq = u == thr;
+            const uint64_t eqb = __ballot(eq);
+            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(eqb >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(eqb), 0));
+            take = u > thr || (eq && eq_before + below < k_eq);
+          }
+        }
+        // equal keys of this group (all lanes take part in the ballot)
+        if (k > 0 && k < n_cand)
+          eq_before += __popcll(__ballot(j < nvt && key[j < nm * 64 ? j : 0] == thr && j < nm * 64));
+        const uint64_t bits = __ballot(take);
+        count += __popcll(bits);
+        if (lane < 2 && j0 / 32 + lane < a.words) mrow[j0 / 32 + lane] = static_cast<uint32_t>(bits >> (32 * lane));
+      }
+    } else {
+      for (int w = lane; w < a.words; w += 64) mrow[w] = 0u;
     }
-  } else {
-    for (int w = lane; w < a.words; w += 64) mrow[w] = 0u;
+    if (lane == 0 && a.n_fp16) a.n_fp16[bhq * a.n_qt + i] = count;
   }
-  if (lane == 0 && a.n_fp16) a.n_fp16[bhq * a.n_qt + i] = count;
 }
 
 // ---- vertical-line tokens (HyQuant, summary and abstract: single key
@@ -475,10 +524,19 @@ static mxq_status launch_select(const float* qmean, const float* kmean, const ui
   a.shared = p->group_shared ? 1 : 0;
   a.maxkey = p->heuristic == 1 ? 1 : 0;
   a.k = k_bf16;
-  const int64_t items = static_cast<int64_t>(n_qt) * s->Hq * s->B;
-  const dim3 grid(static_cast<unsigned>((items + kSelWaves - 1) / kSelWaves));
-  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), 0, strm, a);
-  else hipLaunchKernelGGL(k_select<64>, grid, dim3(64 * kSelWaves), 0, strm, a);
+  const int stride = (n_kt + 63) / 64 * 64;
+  // up to 8 query tiles share a workgroup (fewer when a score row is wide),
+  // and fewer still while the launch would hold under 512 workgroups
+  int qt = std::max(1, std::min(kSelMaxQT, kSelLdsBytes / (4 * stride)));
+  const int64_t heads = static_cast<int64_t>(s->Hq) * s->B;
+  while (qt > 1 && static_cast<int64_t>((n_qt + qt - 1) / qt) * heads < 512) --qt;
+  a.qt = qt;
+  const int64_t wgs = static_cast<int64_t>((n_qt + a.qt - 1) / a.qt) * s->Hq * s->B;
+  MXQ_REQUIRE(wgs <= 0x7FFFFF, MXQ_EUNSUPPORTED, "attn_select_blocks: too many (batch, head, query tile) groups");
+  const size_t lds = static_cast<size_t>(a.qt) * stride * sizeof(float);
+  const dim3 grid(static_cast<unsigned>(wgs));
+  if (s->D == 128) hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kSelWaves), lds, strm, a);
+  else hipLaunchKernelGGL(k_select<64>, grid, dim3(64 * kSelWaves), lds, strm, a);
   return check_launch("k_select");
 }
 

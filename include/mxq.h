@@ -124,7 +124,8 @@ typedef struct {
  *     (fp16) [B][H][N][D/32]:  s = fp16(fl32(max-min)/15), z = fp16(min),
  *     code = clamp(rint(fl32(x-z)/s), 0, 15), 0 when s == 0.
  * `zeros` must be NULL except for INT4.  N must be a multiple of 32 (128 for
- * AXIS_N); D a multiple of 32.
+ * AXIS_N); D a multiple of 32.  MXFP4 takes at most 2^29 blocks of 32
+ * (MXQ_EUNSUPPORTED beyond; in mxq_prefill_operands, Q and K together).
  * ------------------------------------------------------------------------- */
 mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t B, int64_t H, int64_t N, int64_t D,
                         int64_t n_valid, mxq_format fmt, mxq_axis axis, void* codes, void* scales,
@@ -261,7 +262,8 @@ mxq_status attn_select_lines(const uint16_t* q_bf16, const uint16_t* k_bf16,
  * key tiles; causal masking applies to them as to any key.  They need q_bf16,
  * k_bf16 and v_f16t in every mode.  lines may be NULL when n_lines is 0.
  * out: [B][Hq][N][D] fp32 or bf16; lse: f32 [B][Hq][N] or NULL (natural log).
- * Rows >= n_valid: out 0, lse -inf.
+ * Rows >= n_valid: out 0, lse -inf.  With N <= 256 (at most two 128-key
+ * chunks) B * Hq may not exceed 2^21 (MXQ_EUNSUPPORTED).
  * ------------------------------------------------------------------------- */
 mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                           const uint8_t* k_codes, const uint8_t* k_scales,

@@ -67,6 +67,8 @@ def load_test_kernels():
     vp = ctypes.c_void_p
     lib.mxqt_p_codes.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp]
     lib.mxqt_p_codes.restype = ctypes.c_int
+    lib.mxqt_e2m1_codes.argtypes = [vp, ctypes.c_int, vp, vp]
+    lib.mxqt_e2m1_codes.restype = ctypes.c_int
     lib.mxqt_fill_lds.argtypes = [ctypes.c_uint32, ctypes.c_int, vp, vp]
     lib.mxqt_fill_lds.restype = ctypes.c_int
     return lib

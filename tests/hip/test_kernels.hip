@@ -3,6 +3,8 @@
 //    the library's internal header: fused multiply-add onto the 2^-11 grid,
 //    v_exp_f32, round-to-nearest-even E4M3 conversion) on given scores, so a
 //    test can compare every grid point with the exactly rounded code.
+//  - mxqt_e2m1_codes: runs the quantisers' E2M1 element conversion
+//    (e2m1_pack8) on given values, eight to a word.
 //  - mxqt_fill_lds: fills the whole LDS of every CU with one 32-bit word, so
 //    a kernel launched right after starts on garbage LDS contents (LDS is not
 //    cleared between workgroups).
@@ -23,6 +25,16 @@ __global__ void k_p_codes(const float* __restrict__ s, const float* __restrict__
   codes[i] = static_cast<uint32_t>(mxq::p4_e4m3(s4, c[i], off[i]));
 }
 
+// e2m1_pack8 (the quantisers' element conversion) on 8 consecutive values
+__global__ void k_e2m1_codes(const float* __restrict__ v, int n8, uint32_t* __restrict__ codes) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = v[8 * i + j];
+  codes[i] = mxq::e2m1_pack8(x);
+}
+
 constexpr int kLdsWords = 160 * 1024 / 4;  // all of a gfx950 CU's LDS
 
 __global__ void __launch_bounds__(1024) k_fill_lds(uint32_t word, int probe, uint32_t* __restrict__ sink) {
@@ -40,6 +52,13 @@ extern "C" int mxqt_p_codes(const float* s, const float* c, const float* off, in
   if (n4 <= 0) return 0;
   hipLaunchKernelGGL(k_p_codes, dim3((n4 + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), s, c,
                      off, n4, codes);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+extern "C" int mxqt_e2m1_codes(const float* v, int n8, uint32_t* codes, void* stream) {
+  if (n8 <= 0) return 0;
+  hipLaunchKernelGGL(k_e2m1_codes, dim3((n8 + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), v, n8,
+                     codes);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -142,6 +142,33 @@ def test_vit_batch_sampled():
         _check(out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
 
 
+def test_vit_full_batch_sampled():
+    """The ViT-shaped workload at its full batch (512 x 12 heads, 197 of 256
+    tokens, CLS as a line) in the benchmark's launch configuration: lines
+    bit-exact for sampled heads and their outputs within 5e-3."""
+    mxq = gpu_or_skip()
+    import torch
+
+    cfg = mxq_inputs.make_prefill("vit")
+    q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    shape = _shape(mxq, cfg)
+    pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                               sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"], n_lines=cfg["n_lines"],
+                               sink_tokens=cfg["sink_tokens"], out_dtype=mxq.MXQ_OUT_F32)
+    out_t, lse_t = pipe(q, k, v)
+    torch.cuda.synchronize()
+    out, lse = out_t.cpu().numpy(), lse_t.cpu().numpy()
+    lines, mask = pipe.lines.cpu().numpy(), u32(pipe.mask)
+    assert not mask.any()
+    for b, h in ((0, 0), (137, 5), (300, 11), (511, 6)):
+        sq, sk, sv = cfg["q"][b:b + 1, h:h + 1], cfg["k"][b:b + 1, h:h + 1], cfg["v"][b:b + 1, h:h + 1]
+        rl_, _ = S.select_lines(sq, sk, cfg["n_valid"], cfg["Bq"], cfg["n_lines"], cfg["sink_tokens"])
+        assert np.array_equal(lines[b:b + 1, h:h + 1], rl_)
+        ro, rl = A.attn_mixed_ref(sq, sk, sv, cfg["n_valid"], 64, 64, False, mask=np.zeros_like(mask[b:b + 1, h:h + 1]),
+                                  lines=rl_)
+        _check(out[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ro, rl)
+
+
 def test_deterministic_and_bf16_output():
     mxq = gpu_or_skip()
     cfg = mxq_inputs.make_prefill("tiny")

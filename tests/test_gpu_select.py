@@ -71,6 +71,34 @@ def test_ragged_gqa_and_constructed_ties(causal):
     assert np.array_equal(nfp, rn)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,Bq,heuristic", [(4, 64, 16, 1152, 128, 0), (1, 8, 2, 65664, 128, 0),
+                                                     (3, 64, 16, 1152, 64, 1)])
+def test_row_groups_ragged_and_wide(B, Hq, Hkv, N, Bq, heuristic):
+    """A workgroup scores and selects up to 8 query tiles of one head: 8 when a
+    score row fits 4 KB of LDS and the launch keeps at least 512 workgroups.
+    Shapes that run those groups with a partial last one: 9 query tiles (8 +
+    1), 513 tiles of 1026 key tiles each (7 per group: 73 x 7 + 2), 18 tiles
+    under the max-pooled heuristic (8 + 8 + 2).  Scores, masks and counts
+    bit-exact."""
+    mxq = gpu_or_skip()
+    rng = np.random.default_rng(N + Bq + Hq)
+    nv = N - 64 - 3
+    q = rng.standard_normal((B, Hq, N, 64)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, N, 64)).astype(np.float32)
+    q[:, :, nv:] = 0
+    k[:, :, nv:] = 0
+    qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
+    del q, k
+    shape = mxq.Shape(B, Hq, Hkv, N, nv, 64, Bq, 64, True)
+    mask, nfp, sc = mxq.attn_select_blocks(bf16_dev(qb), bf16_dev(kb), shape, topk=-1, ratio=(5, 100),
+                                           sink_tiles=1, local_tiles=2, want_scores=True, heuristic=heuristic)
+    rm, rn, rs = S.select_blocks(qb, kb, nv, Bq, 64, True, -1, 5, 100, 1, 2,
+                                 heuristic="maxkey" if heuristic else "mean")
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(u32(mask), rm)
+    assert np.array_equal(nfp.cpu().numpy(), rn)
+
+
 def test_deterministic():
     mxq = gpu_or_skip()
     cfg = mxq_inputs.make_prefill("llama8b")
