@@ -1117,12 +1117,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     const int d0 = 16 * db + 4 * g;
     const float o0 = O[db][0] * inv, o1 = O[db][1] * inv, o2 = O[db][2] * inv, o3 = O[db][3] * inv;
     if (a.out_bf16) {
-      auto bf = [](float x) -> uint32_t {
-        uint32_t u = __float_as_uint(x);
-        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-      };
-      uint2 pk2 = make_uint2(bf(o0) | (bf(o1) << 16), bf(o2) | (bf(o3) << 16));
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) = pk2;
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) =
+          make_uint2(bf16x2_rne(o0, o1), bf16x2_rne(o2, o3));
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(o0, o1, o2, o3);
     }
@@ -1583,12 +1579,8 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
     const int d0 = 16 * db + 4 * g;
     const float o0 = O[db][0] * inv, o1 = O[db][1] * inv, o2 = O[db][2] * inv, o3 = O[db][3] * inv;
     if (a.out_bf16) {
-      auto bf = [](float x) -> uint32_t {
-        uint32_t u = __float_as_uint(x);
-        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-      };
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) =
-          make_uint2(bf(o0) | (bf(o1) << 16), bf(o2) | (bf(o3) << 16));
+          make_uint2(bf16x2_rne(o0, o1), bf16x2_rne(o2, o3));
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(o0, o1, o2, o3);
     }

@@ -139,16 +139,22 @@ struct KBlk {
 // Issue one block's loads (kVmemPerBlk vector-memory instructions): K codes
 // and scale/zero spans into registers, the V codes straight into the wave's
 // LDS slot (the 16 bytes of lane l land at byte 16 l of each 1 KB half).
+// Offsets are formed in 32-bit unsigned arithmetic (the descriptors' range is
+// up to 2^31 bytes); t0 = L_cap puts every load past its range: the loads
+// still issue (and count) but return zeros without touching memory.
 __device__ __forceinline__ void issue_blk(KBlk& x, const Rsrc& r, int t0, int offk, int lane, lds_char* slot) {
-  const int ok = offk + t0 * (kD / 2);
-  x.kc[0] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, ok, 0, 0);
-  x.kc[1] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, ok + 16 * (kD / 2), 0, 0);
-  const int ov = lane * 16 + t0 * (kD / 2);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)slot, 16, ov, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)(slot + 1024), 16, ov + 1024, 0, 0, 0);
-  const int os = lane * 4 + t0 * 8;
+  const uint32_t t = static_cast<uint32_t>(t0);
+  const uint32_t ok = static_cast<uint32_t>(offk) + t * (kD / 2);
+  x.kc[0] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, __builtin_bit_cast(int, ok), 0, 0);
+  x.kc[1] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, __builtin_bit_cast(int, ok + 16u * (kD / 2)), 0, 0);
+  const uint32_t ov = static_cast<uint32_t>(lane) * 16u + t * (kD / 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)slot, 16, __builtin_bit_cast(int, ov), 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)(slot + 1024), 16, __builtin_bit_cast(int, ov + 1024u), 0,
+                                          0, 0);
+  const uint32_t os = static_cast<uint32_t>(lane) * 4u + t * 8u;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) x.sz[a] = __builtin_amdgcn_raw_buffer_load_b32(r.sz[a], os, 0, 0);
+  for (int a = 0; a < 4; ++a)
+    x.sz[a] = __builtin_amdgcn_raw_buffer_load_b32(r.sz[a], __builtin_bit_cast(int, os), 0, 0);
   // keep the block's loads together, ahead of the computation that follows,
   // so that waits for the block being computed never cover these loads
   __builtin_amdgcn_sched_barrier(0);
@@ -545,13 +551,15 @@ __global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
       // computed while the next three blocks' loads are in flight, and its
       // registers and slot are refilled with the block four ahead right after.
       // The loop runs whole groups of four steps with one exit: a step past
-      // the range computes nothing (all its tokens are masked), and loads past
-      // the range re-read the current block (cache hits), so every step
-      // issues the same loads and the wait count in process_blk holds.
+      // the range computes nothing (all its tokens are masked), and its loads
+      // are issued at token L_cap, past every descriptor's range, so they
+      // return zeros without memory traffic (re-reading a block instead went
+      // back to HBM once the L2 had moved on: 40 KB per split).  Every step
+      // issues the same loads, so the wait count in process_blk holds.
       const int n_steps = (end - t0 + kStep - 1) / kStep;
       const int n_groups = (n_steps + 3) / 4;
       KBlk k0, k1, k2, k3;
-#define MXQ_AT(d) (t0 + (d) * kStep < end ? t0 + (d) * kStep : t0)
+#define MXQ_AT(d) (t0 + (d) * kStep < end ? t0 + (d) * kStep : L)
       issue_blk(k0, rs, t0, offk, lane, sl0);
       issue_blk(k1, rs, MXQ_AT(1), offk, lane, sl1);
       issue_blk(k2, rs, MXQ_AT(2), offk, lane, sl2);
@@ -571,7 +579,7 @@ __global__ void __launch_bounds__(256, 3) k_decode_split(DecodeArgs a) {
         t0 += kStep;
       }
 #undef MXQ_AT
-      // the re-issued loads past the end still write LDS: let them land
+      // the loads past the end still write (zeros to) LDS: let them land
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     const float m_run = st_.m_run, l_run = st_.l_run;

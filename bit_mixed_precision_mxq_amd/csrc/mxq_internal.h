@@ -55,6 +55,14 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
          static_cast<uint32_t>(a > 5.0f);
 }
 
+// Two fp32 values rounded to bf16 (round to nearest, ties to even; one
+// v_cvt_pk_bf16_f32), a in the low half.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+  const v2bf16 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // E2M1 codes of eight block-scaled values (each x * 2^-e, exact), element i
 // in nibble i: the nearest of {0,.5,1,1.5,2,3,4,6} with ties to the even code,
 // saturating at 6, the sign bit copied from the value (so -0 and negatives
@@ -71,22 +79,19 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
   return w;
 }
 
-// OCP E4M3 code of x (|x| < 2^9 after block scaling, exact), round half to
-// even, saturating at 448, sign copied.
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  uint32_t bits = __float_as_uint(x);
-  uint32_t sign = (bits >> 24) & 0x80u;
-  float a = __uint_as_float(bits & 0x7FFFFFFFu);
-  uint32_t code;
-  if (a < 0.015625f) {  // below 2^-6: subnormal grid k * 2^-9, k = 0..8
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  } else {
-    uint32_t ab = bits & 0x7FFFFFFFu;
-    uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20;  // RNE to 3 mantissa bits
-    code = r - (120u << 3);                                   // rebias 127 -> 7
-    code = code > 126u ? 126u : code;                         // saturate at 448
-  }
-  return code | sign;
+// OCP E4M3 codes of four block-scaled values (x * 2^-e, exact), value i in
+// byte i: round to nearest, ties to even, saturating at 448 (the clamp takes
+// values beyond 448 to 448, which is also what rounding with saturation
+// gives), sign copied.  gfx950's packed FP8 conversion after the clamp does
+// exactly this (checked on every bf16-representable input against the
+// exactly rounded code).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  auto cl = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f); };
+  int w;
+  __asm__ volatile("" : "=v"(w));  // both halves are written below
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), w, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return static_cast<uint32_t>(w);
 }
 
 // ---- P of low-bit tiles (ThriftAttention, abstract: low-bit blocks merged

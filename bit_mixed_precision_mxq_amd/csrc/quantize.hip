@@ -283,12 +283,9 @@ __global__ void __launch_bounds__(256) k_quant_mxfp8_n(const uint16_t* __restric
   int e = shared_exponent(amax, 8);
   uint32_t out[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w |= e4m3_code(__builtin_ldexpf(v[4 * i + j], -e)) << (8 * j);
-    out[i] = w;
-  }
+  for (int i = 0; i < 8; ++i)
+    out[i] = e4m3_pack4(__builtin_ldexpf(v[4 * i], -e), __builtin_ldexpf(v[4 * i + 1], -e),
+                        __builtin_ldexpf(v[4 * i + 2], -e), __builtin_ldexpf(v[4 * i + 3], -e));
   uint4* dst = reinterpret_cast<uint4*>(codes + (bh * D + d) * N + blk * 32);
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -405,12 +402,9 @@ __global__ void __launch_bounds__(256) k_vt_n(const uint16_t* __restrict__ x, ui
       const int e = shared_exponent(amax, 8);
       uint32_t o[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w |= e4m3_code(__builtin_ldexpf(v[4 * i + j], -e)) << (8 * j);
-        o[i] = w;
-      }
+      for (int i = 0; i < 8; ++i)
+        o[i] = e4m3_pack4(__builtin_ldexpf(v[4 * i], -e), __builtin_ldexpf(v[4 * i + 1], -e),
+                          __builtin_ldexpf(v[4 * i + 2], -e), __builtin_ldexpf(v[4 * i + 3], -e));
       uint4* dst = reinterpret_cast<uint4*>(codes + (bh * D + d) * N + n0 + 32 * b);
       dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
       dst[1] = make_uint4(o[4], o[5], o[6], o[7]);

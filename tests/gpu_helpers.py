@@ -69,6 +69,8 @@ def load_test_kernels():
     lib.mxqt_p_codes.restype = ctypes.c_int
     lib.mxqt_e2m1_codes.argtypes = [vp, ctypes.c_int, vp, vp]
     lib.mxqt_e2m1_codes.restype = ctypes.c_int
+    lib.mxqt_e4m3_codes.argtypes = [vp, ctypes.c_int, vp, vp]
+    lib.mxqt_e4m3_codes.restype = ctypes.c_int
     lib.mxqt_fill_lds.argtypes = [ctypes.c_uint32, ctypes.c_int, vp, vp]
     lib.mxqt_fill_lds.restype = ctypes.c_int
     return lib

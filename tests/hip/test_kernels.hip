@@ -5,6 +5,8 @@
 //    test can compare every grid point with the exactly rounded code.
 //  - mxqt_e2m1_codes: runs the quantisers' E2M1 element conversion
 //    (e2m1_pack8) on given values, eight to a word.
+//  - mxqt_e4m3_codes: runs the V quantiser's E4M3 element conversion
+//    (e4m3_pack4) on given values, four to a word.
 //  - mxqt_fill_lds: fills the whole LDS of every CU with one 32-bit word, so
 //    a kernel launched right after starts on garbage LDS contents (LDS is not
 //    cleared between workgroups).
@@ -35,6 +37,13 @@ __global__ void k_e2m1_codes(const float* __restrict__ v, int n8, uint32_t* __re
   codes[i] = mxq::e2m1_pack8(x);
 }
 
+// e4m3_pack4 (the V quantiser's element conversion) on 4 consecutive values
+__global__ void k_e4m3_codes(const float* __restrict__ v, int n4, uint32_t* __restrict__ codes) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  codes[i] = mxq::e4m3_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
 constexpr int kLdsWords = 160 * 1024 / 4;  // all of a gfx950 CU's LDS
 
 __global__ void __launch_bounds__(1024) k_fill_lds(uint32_t word, int probe, uint32_t* __restrict__ sink) {
@@ -58,6 +67,13 @@ extern "C" int mxqt_p_codes(const float* s, const float* c, const float* off, in
 extern "C" int mxqt_e2m1_codes(const float* v, int n8, uint32_t* codes, void* stream) {
   if (n8 <= 0) return 0;
   hipLaunchKernelGGL(k_e2m1_codes, dim3((n8 + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), v, n8,
+                     codes);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+extern "C" int mxqt_e4m3_codes(const float* v, int n4, uint32_t* codes, void* stream) {
+  if (n4 <= 0) return 0;
+  hipLaunchKernelGGL(k_e4m3_codes, dim3((n4 + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), v, n4,
                      codes);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -7,7 +7,7 @@ from gpu_helpers import bf16_dev, gpu_or_skip, poison_lds, u32
 import mxq_inputs
 from oracle import attention as A
 from oracle import select as S
-from oracle.formats import f32_to_bf16_bits
+from oracle.formats import bf16_bits_to_f32, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -176,8 +176,14 @@ def test_deterministic_and_bf16_output():
     o2, l2, _ = _gpu_prefill(mxq, cfg, 0)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     ob, _, _ = _gpu_prefill(mxq, cfg, 0, out_dtype=1)
-    # bf16 store of the same fp32 result: relative error <= 2^-9
-    assert np.all(np.abs(ob - o1) <= np.abs(o1) * 2.0 ** -8 + 1e-30)
+    # the bf16 output is the fp32 result rounded to nearest, ties to even
+    assert np.array_equal(f32_to_bf16_bits(ob), f32_to_bf16_bits(o1))
+    assert np.array_equal(ob, bf16_bits_to_f32(f32_to_bf16_bits(o1)))
+    # the same for the short-sequence kernel
+    cfg = mxq_inputs.make_prefill("vit", B=2)
+    o1, _, _ = _gpu_prefill(mxq, cfg, 0)
+    ob, _, _ = _gpu_prefill(mxq, cfg, 0, out_dtype=1)
+    assert np.array_equal(ob, bf16_bits_to_f32(f32_to_bf16_bits(o1)))
 
 
 def test_error_paths():
