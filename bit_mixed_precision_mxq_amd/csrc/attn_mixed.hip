@@ -1317,19 +1317,16 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   }
   // entry e's key, from lane e (an LDS permute: no copies are in flight here)
   auto lane_key = [&](int e) -> int { return __shfl(lkey, e); };
-  // word (chunk, lane group) of the line-key bits, one thread each (the
-  // thread reads the entries of its own wave, which holds the same list)
-  if (tid < NCH * 4) {
-    uint32_t m = 0;
+  // word (chunk, lane group) of the line-key bits: wave 0 clears the words
+  // and its lanes 0..15 OR in their entries' bits (one wave's LDS operations
+  // complete in order, so the clears land first)
+  if (wave == 0) {
+    if (lane < NCH * 4) (&s_lm[0][0])[lane] = 0u;
     if constexpr (LINES) {
-#pragma unroll
-      for (int e = 0; e < kMaxLines; ++e) {
-        const int k = __builtin_amdgcn_readlane(lkey, e);
-        if (k >= 0 && (k >> 7) == (tid >> 2) && ((k >> 4) & 3) == (tid & 3))
-          m |= 1u << (16 * ((k >> 6) & 1) + (k & 15));
-      }
+      if (lkey >= 0)  // a counted entry lies below n_valid <= N <= 256
+        __hip_atomic_fetch_or(&s_lm[lkey >> 7][(lkey >> 4) & 3], 1u << (16 * ((lkey >> 6) & 1) + (lkey & 15)),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    (&s_lm[0][0])[tid] = m;
   }
   __syncthreads();  // staged codes, scales and line bits
 
@@ -1479,18 +1476,26 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
           }
         }
       }
-      // this lane's 16 keys kt0 + 16g + j, j = 4bb + i: bit j of vm set when the
-      // key is visible (below kmax and not a line key); the scores are
+      // this lane's 16 keys kt0 + 16g + j, j = 4bb + i, are visible for j below
+      // nvis (kmax) and when not a line key (bit j of lm); the scores are
       // rewritten only in tiles where some lane has a hidden key
-      const uint32_t lm = LINES ? ((s_lm[ch][g] >> (16 * t)) & 0xFFFFu) : 0u;
       const int nvis = min(max(kmax - (kt0 + 16 * g), 0), 16);
-      const uint32_t vm = (nvis >= 16 ? 0xFFFFu : ((1u << nvis) - 1u)) & ~lm;
-      if (__any(vm != 0xFFFFu)) {
+      if (__any(nvis < 16)) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (!((vm >> (4 * bb + i)) & 1u)) St[bb][i] = NEG_INF;
+            if (4 * bb + i >= nvis) St[bb][i] = NEG_INF;
+      }
+      if constexpr (LINES) {
+        const uint32_t lm = (s_lm[ch][g] >> (16 * t)) & 0xFFFFu;
+        if (__any(lm != 0u)) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if ((lm >> (4 * bb + i)) & 1u) St[bb][i] = NEG_INF;
+        }
       }
       float mx = NEG_INF;
 #pragma unroll

@@ -78,9 +78,14 @@ __global__ void __launch_bounds__(256) k_quant_mxfp4_d(const uint16_t* __restric
     scales = scales2;
   }
   // padding rows (row % N >= n_valid) read as zeros; without padding no
-  // division is needed
-  const bool live = in && (n_valid >= N || (blk / static_cast<uint32_t>(blocks_per_row)) %
-                                                   static_cast<uint32_t>(N) < static_cast<uint32_t>(n_valid));
+  // division is needed, and power-of-two row lengths and N take shifts
+  bool live = in;
+  if (n_valid < N) {
+    const uint32_t bpr = static_cast<uint32_t>(blocks_per_row), n = static_cast<uint32_t>(N);
+    const uint32_t row = (bpr & (bpr - 1)) == 0 ? blk >> __builtin_ctz(bpr) : blk / bpr;
+    const uint32_t r = (n & (n - 1)) == 0 ? row & (n - 1) : row % n;
+    live = live && r < static_cast<uint32_t>(n_valid);
+  }
   const uint4 w4 = live ? reinterpret_cast<const uint4*>(x)[blk * 4u + u] : make_uint4(0, 0, 0, 0);
   int e;
   const uint32_t packed = mxfp4_quarter(w4, e);
