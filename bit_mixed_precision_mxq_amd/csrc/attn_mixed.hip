@@ -650,7 +650,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // zero); PV, the pending chunk had a live tile, so its PV MFMAs and their V
   // reads run.  Each variant keeps the whole step's issue order; the choice is
   // one scalar branch per chunk.
-  auto pipe = [&](auto EXc, auto PVc, const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb) {
+  auto pipe = [&](auto EXc, auto PVc, const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb, auto&& copies) {
     constexpr bool EX = decltype(EXc)::value, PV = decltype(PVc)::value;
     float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
     float off1 = kGridMagic + kExpOffset - (hm1 == NEG_INF ? 0.0f : hm1);
@@ -685,6 +685,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       if (beta == 4) __builtin_amdgcn_s_setprio(1);
       if (beta == 6) __builtin_amdgcn_s_setprio(0);
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
+      if (beta == 1) copies();  // this iteration's copies, among the step's work
       if constexpr (EX) {
         pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
         __asm__ volatile("" ::"v"(pb[beta]));  // formed here, not where it is next read
@@ -818,16 +819,16 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   int fl_raw = static_cast<int>(s_fl[min(2, kMaxChunks - 1)]);
 
   // Staging schedule (K ring of 4, V ring of 3, one barrier per chunk).
-  // Iteration ch, after its barrier, issues (in this order): the FP16 tile of
-  // chunk ch or ch+1 when one is due (below), the K and V scale loads into
-  // registers, the K codes of chunk ch+3 and the V codes of chunk ch+2.  At the
-  // top of iteration ch+1 the scales are written to LDS and each wave waits
-  // until at most kRegOps of its loads are in flight, i.e. everything issued
-  // before iteration ch's scale loads has landed: the K codes of chunk ch+2,
-  // the V codes of chunk ch+1 and any FP16 tile issued in iteration ch.  The
-  // barrier then publishes them to all waves.  A K buffer is rewritten three
-  // iterations after its chunk was last read, a V buffer two, both after a
-  // barrier that every reader has passed.
+  // Iteration ch issues (in this order): after its barrier, the FP16 tile of
+  // chunk ch or ch+1 when one is due (below); from inside its step, the K and
+  // V scale loads into registers, the K codes of chunk ch+3 and the V codes of
+  // chunk ch+1.  At the top of iteration ch+1 the scales are written to LDS
+  // and each wave waits until at most kRegOps of its loads are in flight,
+  // i.e. everything issued before iteration ch's scale loads has landed: the
+  // K codes of chunk ch+2, the V codes of chunk ch and any FP16 tile issued
+  // in iteration ch.  The barrier then publishes them to all waves.  A K
+  // buffer is rewritten three iterations after its chunk was last read, a V
+  // buffer two, both after a barrier that every reader has passed.
   // Workgroup barrier without the memory fence __syncthreads() carries (that
   // fence waits for every load in flight, copies for later chunks included):
   // this wave's LDS writes are complete, then s_barrier.  Copies are waited
@@ -923,7 +924,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) S[beta] = v4f{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
   }
-  if (n_chunks > 0 && is_hot(0, f_cur)) hot_refs();
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int kc = ch * 128;
@@ -955,13 +955,22 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       }
     }
     issue_fence();
-    if (lowbit) {
-      ks_load(ch + 3);
-      vs_load(ch + 1);
-      k_dma(ch + 3, kbuf(ch + 3));
-      v_dma(ch + 1, vbuf(vslot1));
-    }
-    issue_fence();
+    // an unmasked all-low-bit chunk: its integer tile references from the
+    // partial maxima of its scores (issued in the previous step), computed
+    // after the barrier (the previous chunk's PV is done, so a rebase of O
+    // stays between two PV updates)
+    if (is_hot(ch, f_cur)) hot_refs();
+    // this iteration's copies (scale loads, K codes of chunk ch+3, V codes of
+    // chunk ch+1), issued in this order from inside the step, so that their
+    // issue overlaps its arithmetic instead of following the barrier
+    auto copies = [&]() {
+      if (lowbit) {
+        ks_load(ch + 3);
+        vs_load(ch + 1);
+        k_dma(ch + 3, kbuf(ch + 3));
+        v_dma(ch + 1, vbuf(vslot1));
+      }
+    };
 
     if (!is_hot(ch, f_cur)) {
       // (a chunk with both tiles low-bit for every wave and no masks had its
@@ -974,9 +983,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       float m_tile0 = NEG_INF;
       float low0 = NEG_INF, low1 = NEG_INF;  // row maxima of the low-bit scores left in each tile
       if (hi_now) {  // FP16 tiles issued after this chunk's barrier: let them land, then publish
-        // (a chunk with a promoted tile is masked-path for every wave)
-        if (lowbit) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kRegOps) : "memory");
-        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // (a chunk with a promoted tile is masked-path for every wave; the
+        // tiles are the last copies issued so far in this iteration)
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
       }
 #pragma unroll 1
@@ -1082,18 +1091,14 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       const uint8_t* vbp = vbuf(vslot_p);
       // (one step with PV MFMAs, so that O has a single update site: two
       // would make the compiler copy O between register sets every chunk)
-      if (live0 || live1 || pend_live) pipe(T, T, kbn, vbp, pend_scale(), pb);
-      else pipe(F, F, kbn, vbp, 0, pb);
+      if (live0 || live1 || pend_live) pipe(T, T, kbn, vbp, pend_scale(), pb, copies);
+      else pipe(F, F, kbn, vbp, 0, pb, copies);
     }
     pb_p = pb;
     pend_live = live0 || live1;
     hp0 = hm0;
     hp1 = hm1;
     vslot_p = vslot;
-    // next chunk unmasked and all low-bit: its integer tile references from
-    // the partial maxima of the scores just issued (after this chunk's PV, so
-    // that a rebase of O is the last update of the iteration)
-    if (ch + 1 < n_chunks && is_hot(ch + 1, f_nxt)) hot_refs();
     f_cur = f_nxt;
     f_nxt = f_nn;
     vslot = vslot1;
