@@ -142,19 +142,24 @@ struct KBlk {
 // Offsets are formed in 32-bit unsigned arithmetic (the descriptors' range is
 // up to 2^31 bytes); t0 = L_cap puts every load past its range: the loads
 // still issue (and count) but return zeros without touching memory.
+// The slot was last read (LDS reads of the block computed just before) by
+// this wave; those reads are waited for before the copies into the slot are
+// issued, since a copy's data can land in LDS ahead of a read still queued
+// (soon after issue for a load past the range, which never goes to memory).
 __device__ __forceinline__ void issue_blk(KBlk& x, const Rsrc& r, int t0, int offk, int lane, lds_char* slot) {
   const uint32_t t = static_cast<uint32_t>(t0);
   const uint32_t ok = static_cast<uint32_t>(offk) + t * (kD / 2);
   x.kc[0] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, __builtin_bit_cast(int, ok), 0, 0);
   x.kc[1] = __builtin_amdgcn_raw_buffer_load_b128(r.kc, __builtin_bit_cast(int, ok + 16u * (kD / 2)), 0, 0);
-  const uint32_t ov = static_cast<uint32_t>(lane) * 16u + t * (kD / 2);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)slot, 16, __builtin_bit_cast(int, ov), 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)(slot + 1024), 16, __builtin_bit_cast(int, ov + 1024u), 0,
-                                          0, 0);
   const uint32_t os = static_cast<uint32_t>(lane) * 4u + t * 8u;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
     x.sz[a] = __builtin_amdgcn_raw_buffer_load_b32(r.sz[a], __builtin_bit_cast(int, os), 0, 0);
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint32_t ov = static_cast<uint32_t>(lane) * 16u + t * (kD / 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)slot, 16, __builtin_bit_cast(int, ov), 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_void*)(slot + 1024), 16, __builtin_bit_cast(int, ov + 1024u), 0,
+                                          0, 0);
   // keep the block's loads together, ahead of the computation that follows,
   // so that waits for the block being computed never cover these loads
   __builtin_amdgcn_sched_barrier(0);
