@@ -988,7 +988,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
       }
-#pragma unroll 1
+      // (both tiles in one unrolled body: the second tile's MFMAs and loads
+      // overlap the first tile's softmax)
+#pragma unroll
       for (int t = 0; t < 2; ++t) {
         if (t == 1 && !valid1) break;
         const bool prom = (f_cur >> t) & 1;  // this wave's tile t is FP16 (in stage t)
