@@ -133,7 +133,10 @@ mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t B, int64_t H, int64_t N,
 
 /* ---------------------------------------------------------------------------
  * mxq_prefill_operands -- every quantised operand attn_mixed_fwd reads, in two
- * launches, with the values the separate mxq_quantize calls give:
+ * launches, with the values the separate mxq_quantize calls give (the
+ * block-scaled low-bit operands of the low-precision tiles, ThriftAttention,
+ * abstract, and the "Attention Quantization" topic page's MX formats; the
+ * fp16 V of the tiles kept in high precision):
  *   q_codes/q_scales, k_codes/k_scales: MXFP4 AXIS_D of Q [B][Hq][N][D] and K
  *     [B][Hkv][N][D] (MXFP4_E2M1_HADAMARD when rotate = 1), one launch;
  *   v_codes/v_scales: MXFP8 AXIS_N of V [B][Hkv][N][D], and v_f16t the fp16
