@@ -566,11 +566,15 @@ def copy_calibration(dev, mib=256, reps=3):
 def prefill_summary(pre, with_traffic):
     """The prefill leg's numbers for the JSON line."""
     cfg = pre["cfg"]
+    scored = cfg["topk"] > 0 or (cfg["topk"] < 0 and cfg["ratio_num"] > 0)
+    promoted = scored or cfg["sink_tiles"] > 0 or cfg["local_tiles"] > 0
     return {
         "config": {
             "workload": workload_text(pre["workload"], cfg),
-            "step": "quantize Q,K (MXFP4, with tile means), V (MXFP8 + fp16 copy) -> select tiles"
-                    + (" and lines" if cfg.get("n_lines", 0) else "") + " -> fused mixed attention",
+            "step": "quantize Q,K (MXFP4" + (", with tile means" if scored else "") + "), V (MXFP8"
+                    + (" + fp16 copy" if promoted else "") + ") -> select tiles"
+                    + (" and lines" if cfg.get("n_lines", 0) else "") + " -> fused mixed attention"
+                    + ("" if promoted else " (line V from bf16 V)"),
             "fp16_pair_fraction": round(pre["fp16_pairs"] / pre["total_pairs"], 5),
             "attn_ms": round(pre["attn_ms"], 4),
             "attn_tflops": round(pre["tflops_attn"], 2),

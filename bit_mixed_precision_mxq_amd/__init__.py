@@ -116,7 +116,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_select_lines.argtypes = [vp, vp, ctypes.POINTER(AttnShape), ctypes.POINTER(LineParams),
                                       vp, sz, vp, vp, vp]
     lib.attn_select_lines.restype = i32
-    lib.attn_mixed_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(AttnShape),
+    lib.attn_mixed_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(AttnShape),
                                    ctypes.c_float, i32, vp, i32, vp, vp]
     lib.attn_mixed_fwd.restype = i32
     lib.attn_quantkv_decode_workspace.argtypes = [i32, i32, i32, i32, i32]
@@ -296,19 +296,22 @@ class PrefillOperands:
     q_bf16: torch.Tensor | None = None
     k_bf16: torch.Tensor | None = None
     v_f16t: torch.Tensor | None = None
+    v_bf16: torch.Tensor | None = None   # read for line keys only when v_f16t is None
 
 
-def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False, rotate=False) -> PrefillOperands:
+def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False, rotate=False, promoted=True) -> PrefillOperands:
     """Quantise Q/K (MXFP4, optionally of the Walsh-Hadamard-rotated rows),
     V (MXFP8 along keys) and make the fp16 V^T copy (needed by FP16 tiles and
-    by vertical lines), all on the GPU in two launches (mxq_prefill_operands)."""
+    by vertical lines), all on the GPU in two launches (mxq_prefill_operands).
+    promoted=False (MIXED mode whose mask promotes no tile) skips the fp16
+    copy: the attention then takes the line keys' V from bf16 V."""
     _need_gpu(q, k, v)
     assert q.dtype == k.dtype == v.dtype == torch.bfloat16 and q.dim() == k.dim() == v.dim() == 4
     B, Hq, N, D = q.shape
     Hkv = k.shape[1]
     assert k.shape == v.shape == (B, Hkv, N, D)
     dev = q.device
-    ops = PrefillOperands(q_bf16=q, k_bf16=k)
+    ops = PrefillOperands(q_bf16=q, k_bf16=k, v_bf16=v)
     if mode != MXQ_ALL_FP16:
         ops.q_codes = torch.empty((B, Hq, N, D // 2), dtype=torch.uint8, device=dev)
         ops.q_scales = torch.empty((B, Hq, N, D // 32), dtype=torch.uint8, device=dev)
@@ -316,7 +319,7 @@ def prepare_prefill(q, k, v, n_valid, mode=MXQ_MIXED, lines=False, rotate=False)
         ops.k_scales = torch.empty((B, Hkv, N, D // 32), dtype=torch.uint8, device=dev)
         ops.v_codes = torch.empty((B, Hkv, D, N), dtype=torch.uint8, device=dev)
         ops.v_scales = torch.empty((B, Hkv, D, N // 32), dtype=torch.uint8, device=dev)
-    if mode != MXQ_ALL_LOWBIT or lines:
+    if mode == MXQ_ALL_FP16 or (mode == MXQ_MIXED and promoted) or (lines and mode != MXQ_MIXED):
         ops.v_f16t = torch.empty((B, Hkv, D, N), dtype=torch.float16, device=dev)
     cs = Shape(B, Hq, Hkv, N, int(n_valid), D, 64, 64, False).c()
     _check(load_library().mxq_prefill_operands(
@@ -335,8 +338,8 @@ def prepare_prefill_means(q, k, v, shape: Shape, out=None, means=None):
     B, Hq, N, D = q.shape
     Hkv = k.shape[1]
     dev = q.device
-    ops = out if out is not None else PrefillOperands(q_bf16=q, k_bf16=k)
-    ops.q_bf16, ops.k_bf16 = q, k
+    ops = out if out is not None else PrefillOperands(q_bf16=q, k_bf16=k, v_bf16=v)
+    ops.q_bf16, ops.k_bf16, ops.v_bf16 = q, k, v
     if ops.q_codes is None:
         ops.q_codes = torch.empty((B, Hq, N, D // 2), dtype=torch.uint8, device=dev)
         ops.q_scales = torch.empty((B, Hq, N, D // 32), dtype=torch.uint8, device=dev)
@@ -371,7 +374,7 @@ def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, 
     cs = shape.c()
     _check(load_library().attn_mixed_fwd(
         _ptr(ops.q_codes), _ptr(ops.q_scales), _ptr(ops.k_codes), _ptr(ops.k_scales), _ptr(ops.v_codes),
-        _ptr(ops.v_scales), _ptr(ops.q_bf16), _ptr(ops.k_bf16), _ptr(ops.v_f16t), _ptr(mask),
+        _ptr(ops.v_scales), _ptr(ops.q_bf16), _ptr(ops.k_bf16), _ptr(ops.v_f16t), _ptr(ops.v_bf16), _ptr(mask),
         _ptr(lines), 0 if lines is None else int(lines.shape[-1]), ctypes.byref(cs), float(softmax_scale), int(mode), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
     return out, lse
 
@@ -444,7 +447,10 @@ class PrefillPipeline:
                 attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
                                   lines=self.lines)
             self.ev_sel.record(self.aux)
-        ops = prepare_prefill(q, k, v, self.shape.n_valid, lines=bool(self.n_lines), rotate=self.rotate)
+        # a zero budget with no forced tile promotes nothing: no fp16 copy of V
+        promoted = self.sink_tiles > 0 or self.local_tiles > 0 or self.topk > 0 or (self.topk < 0 and self.ratio[0] > 0)
+        ops = prepare_prefill(q, k, v, self.shape.n_valid, lines=bool(self.n_lines), rotate=self.rotate,
+                              promoted=promoted)
         main.wait_event(self.ev_sel)
         if events is not None:
             events[0].record(main)

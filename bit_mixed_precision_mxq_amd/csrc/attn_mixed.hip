@@ -67,6 +67,7 @@ struct AttnArgs {
   const uint16_t* q_bf16;
   const uint16_t* k_bf16;
   const uint16_t* v_f16t;
+  const uint16_t* v_bf16;  // [B*Hkv][N][D]: the line keys' V when v_f16t is NULL
   const uint32_t* mask;
   const int32_t* lines;  // [B*Hq][n_lines] vertical-line keys
   void* out;
@@ -85,6 +86,13 @@ constexpr float kMaxLag = 64.0f;       // largest gap kept between O's reference
 constexpr float kMaxLag16 = 15.0f;     // the same for FP16 tiles, whose P must stay below 2^16
 constexpr int kMaxChunks = 1024;       // 128-key chunks: 2048 key tiles of 64
 constexpr int kMaxLines = 16;          // vertical-line keys per head: one 16-key MFMA block
+
+// fp16 bits of a line key's V element: the fp16 V^T copy's value, or the
+// bf16 value rounded to fp16 (to nearest, ties to even: the rounding of the
+// fp16 copy) when the values come straight from bf16 V.
+__device__ __forceinline__ uint32_t line_v_f16(uint32_t raw, bool from_bf16) {
+  return from_bf16 ? __builtin_bit_cast(uint16_t, static_cast<_Float16>(__uint_as_float(raw << 16))) : raw;
+}
 
 // Key (within the 128-key chunk) that A-operand row r of S-block beta holds.
 __device__ __forceinline__ int chunk_key(int beta, int r) {
@@ -362,6 +370,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   const auto r_vs = rsrc(a.v_scales, bhk * D * (a.N / 32), static_cast<int64_t>(D) * (a.N / 32));
   const auto r_hk = rsrc(a.k_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2);
   const auto r_hv = rsrc(a.v_f16t, bhk * D * a.N * 2, static_cast<int64_t>(D) * a.N * 2);
+  const bool lv_bf16 = a.v_f16t == nullptr;  // line V from bf16 V rows (no FP16 tile is promoted)
+  const auto r_lv = lv_bf16 ? rsrc(a.v_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2) : r_hv;
   uint8_t* const kring = sm + LY::K_OFF;
   uint8_t* const vring = sm + LY::V_OFF;
   // One wave's share of a direct global -> LDS copy: 64 lanes x 16 B land
@@ -520,7 +530,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int key = lane_key(ve0 + x);
-      hv[x] = __builtin_amdgcn_raw_buffer_load_b16(r_hv, (tid < LV && key >= 0) ? (vd * a.N + key) * 2 : kOut, 0, 0);
+      const int off = lv_bf16 ? (key * D + vd) * 2 : (vd * a.N + key) * 2;
+      hv[x] = __builtin_amdgcn_raw_buffer_load_b16(r_lv, (tid < LV && key >= 0) ? off : kOut, 0, 0);
     }
   }
   issue_fence();
@@ -779,7 +790,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     if (tid < LU) *reinterpret_cast<v4i*>(sm + LY::lk_off(ke, kcu)) = kw;
     if (tid < LV)
       *reinterpret_cast<uint2*>(sm + LY::LV_OFF + (vd * kMaxLines + ve0) * 2) =
-          make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+          make_uint2(line_v_f16(hv[0], lv_bf16) | (line_v_f16(hv[1], lv_bf16) << 16),
+                     line_v_f16(hv[2], lv_bf16) | (line_v_f16(hv[3], lv_bf16) << 16));
   }
   // this wave's half of a chunk's flags
   const int fl_shift = w_in_b ? kFlShift : 0;
@@ -1221,6 +1233,8 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   const auto r_vs = rsrc(a.v_scales, bhk * D * (a.N / 32), static_cast<int64_t>(D) * (a.N / 32));
   const auto r_hk = rsrc(a.k_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2);
   const auto r_hv = rsrc(a.v_f16t, bhk * D * a.N * 2, static_cast<int64_t>(D) * a.N * 2);
+  const bool lv_bf16 = a.v_f16t == nullptr;  // line V from bf16 V rows (no FP16 tile is promoted)
+  const auto r_lv = lv_bf16 ? rsrc(a.v_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2) : r_hv;
   constexpr int kOut = 0x7FFFFFF0;  // an offset past every slice: the load returns zeros
 
   // ---- the FP4 Q fragment (B operand of S^T = K Q^T; groups g >= D/32 read
@@ -1389,9 +1403,9 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(
-            r_hv, lk4[i] >= 0 ? ((16 * db + col) * a.N + lk4[i]) * 2 : kOut, 0, 0);
-        vl[db][i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(hv));
+        const int off = lv_bf16 ? (lk4[i] * D + 16 * db + col) * 2 : ((16 * db + col) * a.N + lk4[i]) * 2;
+        const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(r_lv, lk4[i] >= 0 ? off : kOut, 0, 0);
+        vl[db][i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(line_v_f16(hv, lv_bf16)));
       }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(vl[db], ph, O[db], 0, 0, 0);
@@ -1624,7 +1638,7 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
                                      const uint8_t* k_codes, const uint8_t* k_scales,
                                      const uint8_t* v_codes, const uint8_t* v_scales,
                                      const uint16_t* q_bf16, const uint16_t* k_bf16,
-                                     const uint16_t* v_f16t, const uint32_t* mask,
+                                     const uint16_t* v_f16t, const uint16_t* v_bf16, const uint32_t* mask,
                                      const int32_t* lines, int32_t n_lines,
                                      const mxq_attn_shape* s, float softmax_scale, mxq_mode mode,
                                      void* out, mxq_out_dtype out_dtype, float* lse,
@@ -1637,21 +1651,22 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
               "attn_mixed_fwd: bad out_dtype");
   MXQ_REQUIRE(out != nullptr, MXQ_EINVAL, "attn_mixed_fwd: out is NULL");
   const bool lowbit = mode != MXQ_ALL_FP16;
-  const bool hi = mode != MXQ_ALL_LOWBIT;
   MXQ_REQUIRE(!lowbit || (q_codes && q_scales && k_codes && k_scales && v_codes && v_scales),
               MXQ_EINVAL, "attn_mixed_fwd: low-bit operands are required in this mode");
-  MXQ_REQUIRE(!hi || (q_bf16 && k_bf16 && v_f16t), MXQ_EINVAL,
+  MXQ_REQUIRE(mode != MXQ_ALL_FP16 || (q_bf16 && k_bf16 && v_f16t), MXQ_EINVAL,
               "attn_mixed_fwd: bf16 Q/K and fp16 V^T are required in this mode");
+  MXQ_REQUIRE(mode != MXQ_MIXED || (q_bf16 && k_bf16 && (v_f16t || v_bf16)), MXQ_EINVAL,
+              "attn_mixed_fwd: bf16 Q/K and fp16 V^T (or, when no tile is promoted, bf16 V) are required in this mode");
   MXQ_REQUIRE(mode != MXQ_MIXED || mask != nullptr, MXQ_EINVAL, "attn_mixed_fwd: mask required in MIXED mode");
   MXQ_REQUIRE(n_lines >= 0 && n_lines <= kMaxLines, MXQ_EINVAL, "attn_mixed_fwd: n_lines must be in [0, 16]");
-  MXQ_REQUIRE(n_lines == 0 || (lines && q_bf16 && k_bf16 && v_f16t), MXQ_EINVAL,
-              "attn_mixed_fwd: vertical lines need lines, bf16 Q/K and fp16 V^T");
+  MXQ_REQUIRE(n_lines == 0 || (lines && q_bf16 && k_bf16 && (v_f16t || v_bf16)), MXQ_EINVAL,
+              "attn_mixed_fwd: vertical lines need lines, bf16 Q/K and fp16 V^T or bf16 V");
   MXQ_REQUIRE(!(softmax_scale != softmax_scale), MXQ_EINVAL, "attn_mixed_fwd: softmax_scale is NaN");
   double sc = softmax_scale > 0.0f ? static_cast<double>(softmax_scale) : 1.0 / __builtin_sqrt(static_cast<double>(s->D));
   AttnArgs a;
   a.q_codes = q_codes; a.q_scales = q_scales; a.k_codes = k_codes; a.k_scales = k_scales;
   a.v_codes = v_codes; a.v_scales = v_scales; a.q_bf16 = q_bf16; a.k_bf16 = k_bf16;
-  a.v_f16t = v_f16t; a.mask = mask; a.out = out; a.lse = lse;
+  a.v_f16t = v_f16t; a.v_bf16 = v_bf16; a.mask = mask; a.out = out; a.lse = lse;
   a.lines = lines; a.n_lines = n_lines;
   a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.n_valid = s->n_valid; a.n_qt = s->N / s->Bq;
   a.words = (s->N / s->Bk + 31) / 32; a.causal = s->causal; a.mode = mode;

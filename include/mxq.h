@@ -251,11 +251,16 @@ mxq_status attn_select_lines(const uint16_t* q_bf16, const uint16_t* k_bf16,
  *  ceil(fl32(rowmax(S_tile) * c)); O and l (the sum of the same quantised P)
  *  are rescaled by 2^(m_old - m_new); out = O / l, lse = ln2 * (m + log2 l).
  * Inputs (from mxq_quantize): q_codes/q_scales and k_codes/k_scales MXFP4
- * AXIS_D; v_codes/v_scales MXFP8 AXIS_N; q_bf16, k_bf16 the original bf16
- * [..][N][D]; v_f16t fp16 AXIS_N ([..][D][N]).  The bf16/fp16 operands may be
- * NULL in MXQ_ALL_LOWBIT mode; the low-bit operands may be NULL in
- * MXQ_ALL_FP16 mode.  mask (from attn_select_blocks) is needed in MXQ_MIXED
- * mode only.  softmax_scale <= 0 means 1/sqrt(D).
+ * AXIS_D; v_codes/v_scales MXFP8 AXIS_N; q_bf16, k_bf16 and v_bf16 the
+ * original bf16 [..][N][D]; v_f16t fp16 AXIS_N ([..][D][N]).  The bf16/fp16
+ * operands may be NULL in MXQ_ALL_LOWBIT mode; the low-bit operands may be
+ * NULL in MXQ_ALL_FP16 mode.  v_bf16 is read only when v_f16t is NULL: then
+ * the line keys' V values (below) are its values rounded to fp16 (to nearest,
+ * ties to even: the fp16 copy's values), and in MXQ_MIXED mode the caller
+ * guarantees that the mask promotes no tile (a promoted tile would read zero
+ * V); this spares a step that promotes nothing the fp16 copy of V.  mask
+ * (from attn_select_blocks) is needed in MXQ_MIXED mode only.
+ * softmax_scale <= 0 means 1/sqrt(D).
  * Vertical lines (HyQuant; readings R29, R30): lines i32 [B][Hq][n_lines]
  * (from attn_select_lines), n_lines in [0, 16], in every mode.  An entry takes
  * part when 0 <= key < n_valid and it exceeds every earlier entry of its row
@@ -263,7 +268,8 @@ mxq_status attn_select_lines(const uint16_t* q_bf16, const uint16_t* k_bf16,
  * ignored).  Those keys form one FP16 tile (bf16 Q and K, fp16 V, fp16 P)
  * processed first in the reference order, and they are left out of their
  * key tiles; causal masking applies to them as to any key.  They need q_bf16,
- * k_bf16 and v_f16t in every mode.  lines may be NULL when n_lines is 0.
+ * k_bf16 and v_f16t or v_bf16 in every mode.  lines may be NULL when n_lines
+ * is 0.
  * out: [B][Hq][N][D] fp32 or bf16; lse: f32 [B][Hq][N] or NULL (natural log).
  * Rows >= n_valid: out 0, lse -inf.  With N <= 256 (at most two 128-key
  * chunks) B * Hq may not exceed 2^21 (MXQ_EUNSUPPORTED).
@@ -272,7 +278,7 @@ mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                           const uint8_t* k_codes, const uint8_t* k_scales,
                           const uint8_t* v_codes, const uint8_t* v_scales,
                           const uint16_t* q_bf16, const uint16_t* k_bf16, const uint16_t* v_f16t,
-                          const uint32_t* mask, const int32_t* lines, int32_t n_lines,
+                          const uint16_t* v_bf16, const uint32_t* mask, const int32_t* lines, int32_t n_lines,
                           const mxq_attn_shape* shape, float softmax_scale,
                           mxq_mode mode, void* out, mxq_out_dtype out_dtype, float* lse,
                           mxq_stream_t stream);

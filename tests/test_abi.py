@@ -82,19 +82,23 @@ def test_host_validation_rejects_before_launch(lib):
     ok = mxq.AttnShape(1, 2, 2, 256, 256, 64, 64, 64, 0)
     st = so.attn_select_blocks(fake, fake, ctypes.byref(ok), ctypes.byref(p), fake, 16, fake, None, None, None)
     assert st == mxq.MXQ_EINVAL and b"workspace" in so.mxq_last_error()
-    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, None, 0, ctypes.byref(ok),
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, None, None, 0, ctypes.byref(ok),
                            0.0, mxq.MXQ_MIXED, fake, 0, None, None)
     assert st == mxq.MXQ_EINVAL and b"mask" in so.mxq_last_error()
-    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, fake, None, 0, ctypes.byref(ok),
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, fake, None, 0, ctypes.byref(ok),
                            0.0, mxq.MXQ_ALL_FP16, fake, 0, None, None)
     assert st == mxq.MXQ_EINVAL
     # vertical lines: at most 16, and they need the bf16/fp16 operands
-    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 17, ctypes.byref(ok),
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, fake, fake, 17, ctypes.byref(ok),
                            0.0, mxq.MXQ_MIXED, fake, 0, None, None)
     assert st == mxq.MXQ_EINVAL and b"n_lines" in so.mxq_last_error()
-    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, fake, 4, ctypes.byref(ok),
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, None, fake, 4, ctypes.byref(ok),
                            0.0, mxq.MXQ_ALL_LOWBIT, fake, 0, None, None)
     assert st == mxq.MXQ_EINVAL and b"lines" in so.mxq_last_error()
+    # MIXED needs fp16 V^T, or bf16 V when no tile is promoted
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, None, None, fake, None, 0, ctypes.byref(ok),
+                           0.0, mxq.MXQ_MIXED, fake, 0, None, None)
+    assert st == mxq.MXQ_EINVAL and b"bf16 V" in so.mxq_last_error()
     lp = mxq.LineParams(17, 1, 0)
     st = so.attn_select_lines(fake, fake, ctypes.byref(ok), ctypes.byref(lp), fake, 1 << 20, fake, None, None)
     assert st == mxq.MXQ_EINVAL and b"n_lines" in so.mxq_last_error()

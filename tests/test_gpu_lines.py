@@ -9,7 +9,7 @@ from gpu_helpers import bf16_dev, gpu_or_skip, u32
 import mxq_inputs
 from oracle import attention as A
 from oracle import select as S
-from oracle.formats import f32_to_bf16_bits
+from oracle.formats import bf16_bits_to_f32, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -182,3 +182,45 @@ def test_select_lines_sink_only_without_scores(case):
     assert np.array_equal(lines.cpu().numpy(), rl)
     scored, _ = mxq.attn_select_lines(bf16_dev(q), bf16_dev(k), shape, n_lines, sink, want_scores=True)
     assert np.array_equal(scored.cpu().numpy(), rl)
+
+
+@pytest.mark.parametrize("case", [
+    # D, Bq, causal, N, n_valid, Hq, Hkv, n_lines, sink
+    (64, 64, False, 256, 197, 3, 3, 1, 1),       # the short-sequence kernel, ViT-shaped
+    (128, 128, False, 256, 200, 2, 1, 4, 1),
+    (64, 64, True, 512, 500, 2, 1, 8, 1),        # the pipelined kernel
+    (128, 128, True, 768, 700, 4, 2, 16, 2),
+])
+def test_lines_with_bf16_v_when_nothing_is_promoted(case):
+    """A step whose mask promotes no tile needs no fp16 copy of V: the line
+    keys' V values come from bf16 V, rounded to fp16 in the kernel.  The
+    output equals the one computed with the fp16 copy bit for bit, and the
+    oracle within the tolerance (values in fp16's subnormal range included)."""
+    mxq = gpu_or_skip()
+    import torch
+
+    D, Bq, causal, N, nv, Hq, Hkv, n_lines, sink = case
+    q, k, v = _inputs(1, Hq, Hkv, N, D, nv, seed=7 * N + D, plant=(2, nv // 2))
+    # tiny values at the line keys: their fp16 rounding goes through subnormals
+    vf = bf16_bits_to_f32(v)
+    vf[:, :, 0, :4] = [3e-5, -7.1e-6, 2.9e-8, 6.0e-8]
+    vf[:, :, nv // 2, :2] = [1.3e-7, -5.5e-6]
+    v = f32_to_bf16_bits(vf)
+    shape = mxq.Shape(1, Hq, Hkv, N, nv, D, Bq, 64, causal)
+    lines, _ = S.select_lines(q, k, nv, Bq, n_lines, sink)
+    mask, _, _ = S.select_blocks(q, k, nv, Bq, 64, causal, 0, 0, 1, 0, 0)
+    assert not np.any(mask)
+    mask_t = torch.from_numpy(np.ascontiguousarray(mask).view(np.int32)).to("cuda:0")
+    lines_t = torch.from_numpy(np.ascontiguousarray(lines, dtype=np.int32)).to("cuda:0")
+    qd, kd, vd = bf16_dev(q), bf16_dev(k), bf16_dev(v)
+    outs = []
+    for promoted in (True, False):
+        ops = mxq.prepare_prefill(qd, kd, vd, nv, 0, lines=True, promoted=promoted)
+        assert (ops.v_f16t is None) == (not promoted)
+        out, lse = mxq.attn_mixed_fwd(ops, mask_t, shape, mode=0, lines=lines_t)
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+    (o1, l1), (o2, l2) = outs
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    ro, rl = A.attn_mixed_ref(q, k, v, nv, Bq, 64, causal, mask=mask, mode=0, lines=lines)
+    _check(o2, l2, ro, rl)
