@@ -656,18 +656,22 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // exponentials, its QK MFMA for the next chunk, every 8/NDB blocks one PV
   // MFMA of the pending chunk (V fragments one head_dim block ahead), and the
   // partial maxima of the block whose QK MFMA was issued three blocks before.
-  // Variants of the step: EX, the chunk has a live tile (some row's low-bit P
-  // is nonzero, see tile_live), so its exponentials run (a dead chunk's P is
-  // zero); PV, the pending chunk had a live tile, so its PV MFMAs and their V
-  // reads run.  Each variant keeps the whole step's issue order; the choice is
-  // one scalar branch per chunk.
-  auto pipe = [&](auto EXc, auto PVc, const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb, auto&& copies) {
-    constexpr bool EX = decltype(EXc)::value, PV = decltype(PVc)::value;
+  // The exponentials of a block run only where some of its P can be nonzero:
+  // in a live tile (see tile_live), and there only for the 16-key blocks whose
+  // largest score passes the same exact test (a block of zero P costs one
+  // maximum, one FMA and a compare); every other block's P is 0.
+  // Variants of the step: PV, the pending chunk had a live tile, so its PV
+  // MFMAs and their V reads run; the choice is one scalar branch per chunk.
+  // kpre: the first three K fragments, read by the caller after the barrier.
+  bool live0 = true, live1 = true;  // tiles of chunk ch with a nonzero low-bit P (this wave)
+  auto pipe = [&](auto PVc, const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb, auto&& copies,
+                  const v4i (&kpre)[3]) {
+    constexpr bool PV = decltype(PVc)::value;
     float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
     float off1 = kGridMagic + kExpOffset - (hm1 == NEG_INF ? 0.0f : hm1);
     // opaque from here on: the exponentials cannot be moved out of this step
     // (the compiler would otherwise compute them where the references are set)
-    if constexpr (EX) __asm__ volatile("" : "+v"(off0), "+v"(off1));
+    __asm__ volatile("" : "+v"(off0), "+v"(off1));
     const uint32_t* ksw = reinterpret_cast<const uint32_t*>(kbn + ksoff);
     const uint32_t nks0 = ksw[0], nks1 = ksw[1];
     uint32_t vsc0 = 0u, vsc1 = 0u;
@@ -681,7 +685,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     v4i kn[8];
     v8i va[NDB];
 #pragma unroll
-    for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = *reinterpret_cast<const v4i*>(kbn + koff(beta));
+    for (int beta = 0; beta < KAHEAD; ++beta) kn[beta] = kpre[beta];
     if constexpr (PV) va[0] = vfrag(vbp, 0);
     mxa = NEG_INF;
     mxb = NEG_INF;
@@ -697,14 +701,16 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       if (beta == 6) __builtin_amdgcn_s_setprio(0);
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
       if (beta == 1) copies();  // this iteration's copies, among the step's work
-      if constexpr (EX) {
-        pb[beta] = p_block(S[beta], beta < 4 ? off0 : off1);
+      {
+        const float offb = beta < 4 ? off0 : off1;
+        bool lvb = beta < 4 ? live0 : live1;
+        if (lvb) {  // P = 0 for the whole block when its largest score gives y <= 6134 (see tile_live)
+          const float m4 = fmaxf(max3f(S[beta][0], S[beta][1], S[beta][2]), S[beta][3]);
+          lvb = __any(__builtin_fmaf(m4, c, offb) > kGridMagic - 10.0f);
+        }
+        if (lvb) pb[beta] = p_block(S[beta], offb);
+        else pb[beta] = 0;
         __asm__ volatile("" ::"v"(pb[beta]));  // formed here, not where it is next read
-      } else {
-        pb[beta] = 0;
-        // the scores this MFMA replaces are read here, as the exponentials do
-        // in the other variant, so both keep S in the same registers
-        __asm__ volatile("" ::"v"(S[beta]));
       }
       const v8i ka = {kn[beta][0], kn[beta][1], kn[beta][2], kn[beta][3], 0, 0, 0, 0};
       S[beta] = qk_block(ka, beta < 4 ? static_cast<int>(nks0) : static_cast<int>(nks1), beta);
@@ -912,7 +918,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     const float off = kGridMagic + kExpOffset - (href == NEG_INF ? 0.0f : href);
     return __any(__builtin_fmaf(rmax, c, off) > kGridMagic - 10.0f);
   };
-  bool live0 = true, live1 = true;  // tiles of chunk ch with a nonzero low-bit P (this wave)
   bool pend_live = false;           // the pending chunk has a live tile
   // integer tile references of an unmasked all-low-bit chunk from the partial
   // maxima of its scores; O's reference follows when it lags too far
@@ -967,6 +972,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       }
     }
     issue_fence();
+    // the step's first K fragments (chunk ch+1, published by this barrier),
+    // read now so that their latency overlaps what follows
+    v4i kpre[3];
+#pragma unroll
+    for (int beta = 0; beta < 3; ++beta) kpre[beta] = *reinterpret_cast<const v4i*>(kbuf(ch + 1) + koff(beta));
     // an unmasked all-low-bit chunk: its integer tile references from the
     // partial maxima of its scores (issued in the previous step), computed
     // after the barrier (the previous chunk's PV is done, so a rebase of O
@@ -1059,6 +1069,13 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
           const float m_ref = m_o == NEG_INF ? 0.0f : m_o;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
+            // 32 keys whose fp16 P is 0 for every row add nothing: skip their
+            // exponentials and MFMAs.  fp16 rounds 2^x to 0 for x < -25, and
+            // x <= -25.5 keeps v_exp_f32's error far from that tie
+            const float m8 = fmaxf(fmaxf(max3f(St[2 * st][0], St[2 * st][1], St[2 * st][2]),
+                                         max3f(St[2 * st][3], St[2 * st + 1][0], St[2 * st + 1][1])),
+                                   fmaxf(St[2 * st + 1][2], St[2 * st + 1][3]));
+            if (!__any(__builtin_fmaf(m8, c, -m_ref) > -25.5f)) continue;
             v8h ph;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -1105,8 +1122,8 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       const uint8_t* vbp = vbuf(vslot_p);
       // (one step with PV MFMAs, so that O has a single update site: two
       // would make the compiler copy O between register sets every chunk)
-      if (live0 || live1 || pend_live) pipe(T, T, kbn, vbp, pend_scale(), pb, copies);
-      else pipe(F, F, kbn, vbp, 0, pb, copies);
+      if (pend_live) pipe(T, kbn, vbp, pend_scale(), pb, copies, kpre);
+      else pipe(F, kbn, vbp, 0, pb, copies, kpre);
     }
     pb_p = pb;
     pend_live = live0 || live1;
