@@ -652,7 +652,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     mx = max3f(mx, S[beta][2], S[beta][3]);
   };
   // One pipeline step (see above).  Issue order, fixed with scheduling
-  // barriers, per S block: the K fragment three blocks ahead, the block's
+  // barriers, per S block: the K fragment two blocks ahead, the block's
   // exponentials, its QK MFMA for the next chunk, every 8/NDB blocks one PV
   // MFMA of the pending chunk (V fragments one head_dim block ahead), and the
   // partial maxima of the block whose QK MFMA was issued three blocks before.
@@ -662,10 +662,10 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // maximum, one FMA and a compare); every other block's P is 0.
   // Variants of the step: PV, the pending chunk had a live tile, so its PV
   // MFMAs and their V reads run; the choice is one scalar branch per chunk.
-  // kpre: the first three K fragments, read by the caller after the barrier.
+  // kpre: the first two K fragments, read by the caller after the barrier.
   bool live0 = true, live1 = true;  // tiles of chunk ch with a nonzero low-bit P (this wave)
   auto pipe = [&](auto PVc, const uint8_t* kbn, const uint8_t* vbp, int pscp, v8i& pb, auto&& copies,
-                  const v4i (&kpre)[3]) {
+                  const v4i (&kpre)[2]) {
     constexpr bool PV = decltype(PVc)::value;
     float off0 = kGridMagic + kExpOffset - (hm0 == NEG_INF ? 0.0f : hm0);
     float off1 = kGridMagic + kExpOffset - (hm1 == NEG_INF ? 0.0f : hm1);
@@ -680,7 +680,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       vsc0 = vsw[0];
       vsc1 = NDB > 4 ? vsw[1] : 0u;
     }
-    constexpr int KAHEAD = 3;  // K fragments in flight ahead of their MFMA
+    constexpr int KAHEAD = 2;  // K fragments in flight ahead of their MFMA
     constexpr int SPB = 8 / NDB;  // S blocks per PV MFMA
     v4i kn[8];
     v8i va[NDB];
@@ -692,13 +692,6 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int beta = 0; beta < 8; ++beta) {
-      // wave priority falls over the step (3, 2, 1, 0 per quarter): of the two
-      // waves sharing a SIMD the one further behind wins the issue slot, so
-      // both reach the next barrier closer together
-      if (beta == 0) __builtin_amdgcn_s_setprio(3);
-      if (beta == 2) __builtin_amdgcn_s_setprio(2);
-      if (beta == 4) __builtin_amdgcn_s_setprio(1);
-      if (beta == 6) __builtin_amdgcn_s_setprio(0);
       if (beta + KAHEAD < 8) kn[beta + KAHEAD] = *reinterpret_cast<const v4i*>(kbn + koff(beta + KAHEAD));
       if (beta == 1) copies();  // this iteration's copies, among the step's work
       {
@@ -974,9 +967,9 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
     issue_fence();
     // the step's first K fragments (chunk ch+1, published by this barrier),
     // read now so that their latency overlaps what follows
-    v4i kpre[3];
+    v4i kpre[2];
 #pragma unroll
-    for (int beta = 0; beta < 3; ++beta) kpre[beta] = *reinterpret_cast<const v4i*>(kbuf(ch + 1) + koff(beta));
+    for (int beta = 0; beta < 2; ++beta) kpre[beta] = *reinterpret_cast<const v4i*>(kbuf(ch + 1) + koff(beta));
     // an unmasked all-low-bit chunk: its integer tile references from the
     // partial maxima of its scores (issued in the previous step), computed
     // after the barrier (the previous chunk's PV is done, so a rebase of O
