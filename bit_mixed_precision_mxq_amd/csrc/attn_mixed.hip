@@ -1189,9 +1189,11 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   constexpr float NEG_INF = -__builtin_inff();
 
   __shared__ __attribute__((aligned(16))) uint8_t s_k[NCH][128 * KROW];  // K codes, Lds<D>::k_off layout
-  __shared__ __attribute__((aligned(16))) uint8_t s_ks[NCH][4 * 16 * 8];  // K scales [g][row][S block]
   __shared__ __attribute__((aligned(16))) uint8_t s_v[NCH][D * 128];     // V^T codes, Lds<D>::vrow_off layout
-  __shared__ __attribute__((aligned(16))) uint8_t s_vs[NCH][4 * 16 * 8];  // V scales [key block][d%16][d/16]
+  // scales in their global order: K [key][D/32] of the N keys (then 16
+  // padding bytes), V [row d][N/32 key blocks]
+  __shared__ __attribute__((aligned(16))) uint8_t s_ks[NCH * 128 * NSB + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vs[D * NCH * 4];
   __shared__ uint32_t s_lm[NCH][4];  // line keys of a chunk per lane group: bit 16t + (key & 15)
 
   const int tid = threadIdx.x;
@@ -1246,6 +1248,9 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   const bool lv_bf16 = a.v_f16t == nullptr;  // line V from bf16 V rows (no FP16 tile is promoted)
   const auto r_lv = lv_bf16 ? rsrc(a.v_bf16, bhk * a.N * D * 2, static_cast<int64_t>(a.N) * D * 2) : r_hv;
   constexpr int kOut = 0x7FFFFFF0;  // an offset past every slice: the load returns zeros
+  // the head's line list goes out first: the line rows' loads depend on it
+  int line_raw = -1;
+  if constexpr (LINES) line_raw = (lane < 16 && lane < a.n_lines) ? a.lines[bhq * a.n_lines + lane] : -1;
 
   // ---- the FP4 Q fragment (B operand of S^T = K Q^T; groups g >= D/32 read
   // zero codes and a zero scale byte) and the bf16 Q slices of FP16 tiles
@@ -1262,81 +1267,55 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
       qbr[st] = *reinterpret_cast<const v8bf*>(a.q_bf16 + (bhq * a.N + q) * D + 8 * (4 * st + g));
   }
 
-  // ---- stage the head's low-bit K and V (both chunks) in LDS: every
-  // thread's loads go out first (a chunk past the slice reads zeros), then
-  // the LDS writes, so the staging costs one memory round trip
+  // ---- stage the head's low-bit K and V (both chunks) in LDS by direct
+  // global-to-LDS copies (64 lanes x 16 B per wave instruction, or 4 B per
+  // lane for nothing here): each LDS 16-byte unit p of a chunk's K or V^T
+  // buffer is fetched from the global unit its layout assigns to it; chunks
+  // past the slice read zeros.  The scales are copied as they lie in memory
+  // (the head's K scales and V scales are each one contiguous run of at most
+  // 1 KB); lanes read their scale bytes from there.
   const bool lowbit = a.mode != MXQ_ALL_FP16;
-  constexpr int KU = NCH * 128 * KROW / 16;  // 16-byte K units
-  constexpr int VU = NCH * D * 8;            // 16-byte V^T units
-  constexpr int KPT = KU / NT, VPT = VU / NT;
-  static_assert(KU % NT == 0 && VU % NT == 0, "whole units per thread");
-  constexpr int KSW = NCH * 128 * NSB / 4;   // K scale words (four scale bytes each)
-  constexpr int VSW = D * (NCH * 4 / 4);     // V scale words: one per row d (4 key blocks per chunk)
-  static_assert(KSW <= NT && D <= NT, "one scale word per thread");
+  constexpr int KUC = 128 * KROW / 16;  // 16-byte K units per chunk
+  constexpr int VUC = D * 8;            // 16-byte V^T units per chunk
+  static_assert((NCH * KUC) % (64 * 4) == 0 && (NCH * VUC) % (64 * 4) == 0, "whole wave copies");
+  auto lds_dma16 = [](const __amdgpu_buffer_rsrc_t& r, uint8_t* dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+  };
   if (lowbit) {
-    v4i kw[KPT], vw[VPT];
-    uint32_t ksw = 0u, vsw0 = 0u, vsw1 = 0u;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + i * NT;
-      const int key = u / (KROW / 16), gu = u % (KROW / 16);  // key over both chunks
-      kw[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r_kc, key * KROW + 16 * gu, 0, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * NT;
-      const int ch = u / (D * 8), r = u % (D * 8);
-      const int d = r / 8, vu = r % 8;
-      vw[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r_vc, d * a.N + ch * 128 + 16 * vu, 0, 0));
-    }
-    if (tid < KSW) ksw = __builtin_amdgcn_raw_buffer_load_b32(r_ks, 4 * tid, 0, 0);  // keys' scale bytes, in order
-    if (tid < D) {  // row d's scale bytes of key blocks 0..3 and 4..7
-      vsw0 = __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32), 0, 0);
-      vsw1 = __builtin_amdgcn_raw_buffer_load_b32(r_vs, tid * (a.N / 32) + 4, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + i * NT;
-      const int key = u / (KROW / 16), gu = u % (KROW / 16);
-      *reinterpret_cast<v4i*>(&s_k[key >> 7][LY::k_off(key & 127, gu)]) = kw[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * NT;
-      const int ch = u / (D * 8), r = u % (D * 8);
-      *reinterpret_cast<v4i*>(&s_v[ch][LY::vrow_off(r / 8, r % 8)]) = vw[i];
-    }
-    // K scale of (key, block kg) -> [kg][A row of the key][S block of the
-    // key]; blocks kg >= D/32 hold no head_dim data: 127, a finite 1.0
-    if (tid < KSW) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = 4 * tid + j;  // byte index: key * NSB + kg
-        const int keyf = idx / NSB, kg = idx % NSB;
-        const int ch = keyf >> 7, key = keyf & 127;
-        const int kcol = 4 * ((key >> 4) & 3) + (key & 3);
-        const int kbeta = 4 * (key >> 6) + ((key >> 2) & 3);
-        s_ks[ch][(kg * 16 + kcol) * 8 + kbeta] = static_cast<uint8_t>(ksw >> (8 * j));
+    for (int i = 0; i < NCH * KUC / 256; ++i) {  // K: LDS unit p of chunk ch
+      const int pu = (i * 4 + wave) * 64 + lane;
+      const int ch = pu / KUC, p = pu % KUC;
+      int key, gu;
+      if constexpr (D == 128) {
+        key = p >> 2;
+        gu = (p & 3) ^ (2 * ((key >> 5) & 1));
+      } else {
+        key = LY::k_row(p >> 1);
+        gu = p & 1;
       }
+      lds_dma16(r_kc, &s_k[0][0] + 1024 * (i * 4 + wave), (ch * 128 + key) * KROW + 16 * gu);
     }
-    if constexpr (NSB < 4) {
-      constexpr int PAD = (4 - NSB) * 16 * 8;
-      for (int i = tid; i < NCH * PAD; i += NT) s_ks[i / PAD][NSB * 16 * 8 + i % PAD] = 127;
-    }
-    if (tid < D) {  // V scales of row d -> [key block][d % 16][d / 16] per chunk
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s_vs[0][(kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(vsw0 >> (8 * kb));
-        s_vs[1][(kb * 16 + (tid & 15)) * 8 + (tid >> 4)] = static_cast<uint8_t>(vsw1 >> (8 * kb));
-      }
+    for (int i = 0; i < NCH * VUC / 256; ++i) {  // V^T: LDS unit p = row d, slot u
+      const int pu = (i * 4 + wave) * 64 + lane;
+      const int ch = pu / VUC, p = pu % VUC;
+      const int d = p >> 3, u = (p & 7) ^ ((d >> 1) & 7);
+      lds_dma16(r_vc, &s_v[0][0] + 1024 * (i * 4 + wave), d * a.N + ch * 128 + 16 * u);
     }
+    const int ksb = a.N * NSB, vsb = D * (a.N / 32);  // scale bytes of the head (multiples of 16)
+    if (wave == 0 && 16 * lane < ksb) lds_dma16(r_ks, s_ks, 16 * lane);
+    if (wave == 1 && 16 * lane < vsb) lds_dma16(r_vs, s_vs, 16 * lane);
+    // padding after the K scales: lane groups g >= D/32 of the last key read
+    // here (against zero Q codes); 127 is a finite E8M0
+    if (tid < 16) s_ks[ksb + tid] = 127;
   }
   // ---- vertical-line keys (HyQuant): entry e takes part when 0 <= key <
   // n_valid and it exceeds every earlier entry (exclusive prefix maximum by DPP
   // row shifts); lane e < 16 of every wave holds entry e's key, else -1
   int lkey = -1;
   if constexpr (LINES) {
-    const int raw = (lane < 16 && lane < a.n_lines) ? a.lines[bhq * a.n_lines + lane] : -1;
+    const int raw = line_raw;
     constexpr int kMin = -2147483647 - 1;
     int v = raw;
     v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false));  // row_shr:1
@@ -1346,8 +1325,40 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
     const int before = __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false);
     if (lane < 16 && raw >= 0 && raw < a.n_valid && raw > before) lkey = raw;
   }
-  // entry e's key, from lane e (an LDS permute: no copies are in flight here)
+  // entry e's key, from lane e (an LDS permute: the copies in flight are
+  // counted on the vector-memory counter, not the LDS one)
   auto lane_key = [&](int e) -> int { return __shfl(lkey, e); };
+  // the line tile's operands, loaded before the barrier so that their round
+  // trip overlaps the staging: entry col's bf16 K row (A of the bf16 MFMA)
+  // and the fp16 V of entries 4g..4g+3 for rows 16*db + col; entry slot i is
+  // loaded only where some lane group has a counted entry there (a list of
+  // one line loads one slot)
+  v8bf lka[NSB];
+  int lk4[4] = {-1, -1, -1, -1};
+  v4h vl[NDB];
+  if constexpr (LINES) {
+    const int kcol_key = lane_key(col);
+#pragma unroll
+    for (int st = 0; st < NSB; ++st)
+      lka[st] = __builtin_bit_cast(
+          v8bf, __builtin_amdgcn_raw_buffer_load_b128(r_hk, kcol_key >= 0 ? (kcol_key * D + 32 * st + 8 * g) * 2
+                                                                            : kOut, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lk4[i] = lane_key(4 * g + i);
+    const uint32_t used = static_cast<uint32_t>(__ballot(lane < 16 && lkey >= 0));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vl[db] = v4h{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!(used & (0x1111u << i))) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int off = lv_bf16 ? (lk4[i] * D + 16 * db + col) * 2 : ((16 * db + col) * a.N + lk4[i]) * 2;
+        const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(r_lv, lk4[i] >= 0 ? off : kOut, 0, 0);
+        vl[db][i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(line_v_f16(hv, lv_bf16)));
+      }
+    }
+  }
   // word (chunk, lane group) of the line-key bits: wave 0 clears the words
   // and its lanes 0..15 OR in their entries' bits (one wave's LDS operations
   // complete in order, so the clears land first)
@@ -1382,18 +1393,9 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
     // the line tile, first in the reference order: S^T[16 entries x 16 queries]
     // with the bf16 MFMA (entry col's K row as A), P = fp16(2^x), then V^T of
     // the entries (fp16, [d][entry]) times P^T with the 16x16x16 fp16 MFMA
-    const int kcol_key = lane_key(col);
     v4f SL = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < NSB; ++st) {
-      const v8bf ka = __builtin_bit_cast(
-          v8bf, __builtin_amdgcn_raw_buffer_load_b128(r_hk, kcol_key >= 0 ? (kcol_key * D + 32 * st + 8 * g) * 2
-                                                                            : kOut, 0, 0));
-      SL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbr[st], SL, 0, 0, 0);
-    }
-    int lk4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lk4[i] = lane_key(4 * g + i);
+    for (int st = 0; st < NSB; ++st) SL = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lka[st], qbr[st], SL, 0, 0, 0);
     float mx = NEG_INF;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1408,15 +1410,6 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
     v4h ph;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ph[i] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(SL[i], c, -m_ref)));
-    v4h vl[NDB];  // all the entries' values first, then the MFMAs
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int off = lv_bf16 ? (lk4[i] * D + 16 * db + col) * 2 : ((16 * db + col) * a.N + lk4[i]) * 2;
-        const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(r_lv, lk4[i] >= 0 ? off : kOut, 0, 0);
-        vl[db][i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(line_v_f16(hv, lv_bf16)));
-      }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(vl[db], ph, O[db], 0, 0, 0);
     const v4h ones4 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f),
@@ -1454,19 +1447,15 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
     const bool valid1 = 2 * ch + 1 <= last_tile;
     v4f S[8];
     if (lowbit) {
-      const uint32_t* ksw = reinterpret_cast<const uint32_t*>(&s_ks[ch][(g * 16 + col) * 8]);
-      const uint32_t ksc0 = ksw[0], ksc1 = ksw[1];
+      // K scale byte of (key ch*128 + chunk_key(beta, col), block g), one
+      // register per MFMA (op_sel 0)
+      const uint8_t* ksb = &s_ks[(ch * 128 + chunk_key(0, col)) * NSB + g];
 #pragma unroll
       for (int beta = 0; beta < 8; ++beta) {
         const v4i w = *reinterpret_cast<const v4i*>(&s_k[ch][koff(beta)]);
         const v8i ka = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
-        const int sc = beta < 4 ? static_cast<int>(ksc0) : static_cast<int>(ksc1);
-        switch (beta & 3) {
-          case 0: S[beta] = MXQ_QK_BLOCK(0); break;
-          case 1: S[beta] = MXQ_QK_BLOCK(1); break;
-          case 2: S[beta] = MXQ_QK_BLOCK(2); break;
-          default: S[beta] = MXQ_QK_BLOCK(3); break;
-        }
+        const int sc = ksb[NSB * (64 * (beta >> 2) + 4 * (beta & 3))];
+        S[beta] = MXQ_QK_BLOCK(0);
       }
     } else {
 #pragma unroll
@@ -1584,22 +1573,15 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
       const float mt = g < 2 ? hm0 : hm1;
       const int psc = (mt == NEG_INF || m_o == NEG_INF)
                           ? 0 : static_cast<int>(fminf(fmaxf(static_cast<float>(kPScale) + (mt - m_o), 0.0f), 254.0f));
-      const uint32_t* vsw = reinterpret_cast<const uint32_t*>(&s_vs[ch][(g * 16 + col) * 8]);
-      const uint32_t vsc0 = vsw[0], vsc1 = NDB > 4 ? vsw[1] : 0u;
+      // V scale byte of (row 16*db + col, key block 4*ch + g)
+      const uint8_t* vsb = &s_vs[col * (a.N / 32) + 4 * ch + g];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const v4i w0 = *reinterpret_cast<const v4i*>(&s_v[ch][2048 * db + voff]);
         const v4i w1 = *reinterpret_cast<const v4i*>(&s_v[ch][2048 * db + (voff ^ 64)]);
         const v8i va = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        const v8i& pbb = pb;
-        const v4f& o = O[db];
-        const int vs = db < 4 ? static_cast<int>(vsc0) : static_cast<int>(vsc1);
-        switch (db & 3) {
-          case 0: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 0, vs, 0, psc); break;
-          case 1: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 1, vs, 0, psc); break;
-          case 2: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 2, vs, 0, psc); break;
-          default: O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pbb, o, 0, 0, 3, vs, 0, psc); break;
-        }
+        const int vs = vsb[16 * db * (a.N / 32)];
+        O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb, O[db], 0, 0, 0, vs, 0, psc);
       }
       L = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones8, pb, L, 0, 0, 0, 127, 0, psc);
     }
