@@ -77,7 +77,15 @@ struct AttnArgs {
   int n_lines;
   int nbh;  // B * Hq
   float c;  // fl32(softmax_scale * log2(e))
+  // short-sequence kernel: exact quotients n / d by a multiply-high with
+  // ceil(2^32 / d) (0 for d = 1), valid for n * d <= 2^32, so that the
+  // workgroup's indices stay scalar (a division would run on the vector ALU)
+  uint32_t mg_nt, mg_hq, mg_g;  // for N / 64 query tiles, Hq, Hq / Hkv
+  int sel_shift;                // log2(sel_bq)
 };
+
+// floor(n / d) from m = ceil(2^32 / d) (m = 0: d = 1); exact for n * d <= 2^32
+__device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t m) { return m ? __umulhi(n, m) : n; }
 
 constexpr float kGridMagic = kPGridMagic;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^13)
 constexpr float kExpOffset = 8.0f;     // P is stored as E4M3(2^(x + 8)) * 2^-8
@@ -1202,13 +1210,14 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   const int col = lane & 15;
   const int g = lane >> 4;
   const int n_t = a.N / BQ;
-  const int wr = static_cast<int>(blockIdx.x >> 3);
-  const int head = (wr / n_t) * 8 + static_cast<int>(blockIdx.x & 7);
+  const uint32_t wr = blockIdx.x >> 3;
+  const uint32_t wq = mdiv(wr, a.mg_nt);
+  const int head = static_cast<int>(wq * 8 + (blockIdx.x & 7));
   if (head >= a.nbh) return;  // the whole workgroup: grid rounded up to whole groups of 8 heads
-  const int it = wr % n_t, h = head % a.Hq, b = head / a.Hq;
-  const int G = a.Hq / a.Hkv;
+  const int it = static_cast<int>(wr - wq * n_t);
+  const int b = static_cast<int>(mdiv(head, a.mg_hq)), h = head - b * a.Hq;
   const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
-  const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + h / G;
+  const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + static_cast<int>(mdiv(h, a.mg_g));
   const int qs = it * BQ;
   const int q = qs + wave * 16 + col;
 
@@ -1420,7 +1429,7 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   // promotion flags of this workgroup's rows (one selection row: 64 rows lie
   // in one 64- or 128-row selection tile)
   const uint32_t* mrow = (a.mode == MXQ_MIXED && a.mask)
-                             ? a.mask + (bhq * (a.N / a.sel_bq) + qs / a.sel_bq) * a.words
+                             ? a.mask + (bhq * (a.N >> a.sel_shift) + (qs >> a.sel_shift)) * a.words
                              : nullptr;
   constexpr int kOne8 = 0x38383838, kOne16 = 0x3C003C00;
   const v8i ones8 = {kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8};
@@ -1676,7 +1685,16 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
     // one-dimensional grid: at most 2^21 heads x 4 query tiles x 256 threads
     MXQ_REQUIRE(static_cast<int64_t>(s->B) * s->Hq <= (1 << 21), MXQ_EUNSUPPORTED,
                 "attn_mixed_fwd: at most 2^21 (batch, head) pairs when N <= 256");
+    MXQ_REQUIRE((static_cast<int64_t>(s->B) * s->Hq + 8) * s->Hq <= (int64_t{1} << 32), MXQ_EUNSUPPORTED,
+                "attn_mixed_fwd: (B * Hq + 8) * Hq must not exceed 2^32 when N <= 256");
     a.nbh = s->B * s->Hq;
+    auto magic = [](int d) -> uint32_t {
+      return d == 1 ? 0u : static_cast<uint32_t>(((int64_t{1} << 32) + d - 1) / d);
+    };
+    a.mg_nt = magic(s->N / 64);
+    a.mg_hq = magic(s->Hq);
+    a.mg_g = magic(s->Hq / s->Hkv);
+    a.sel_shift = s->Bq == 128 ? 7 : 6;
     if (s->D == 128) return launch_short<128>(a, strm);
     return launch_short<64>(a, strm);
   }
