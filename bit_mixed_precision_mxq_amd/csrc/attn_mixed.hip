@@ -85,7 +85,19 @@ struct AttnArgs {
 };
 
 // floor(n / d) from m = ceil(2^32 / d) (m = 0: d = 1); exact for n * d <= 2^32
-__device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t m) { return m ? __umulhi(n, m) : n; }
+__device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t m) {
+  return m ? static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 32) : n;
+}
+
+// Work-item and workgroup ids straight from the hardware registers.  This
+// file is compiled with IEEE mode off, so the device library's id helpers,
+// built with it on, are not inlined: threadIdx/blockIdx become calls, and
+// values derived from them land in vector registers.  The short-sequence
+// kernel uses these (its prologue is a large share of its time); the long
+// kernel keeps the library helpers, called once per workgroup, because its
+// main loop was measured to schedule slower with the intrinsics.
+__device__ __forceinline__ int lane_tid() { return static_cast<int>(__builtin_amdgcn_workitem_id_x()); }
+__device__ __forceinline__ uint32_t wg_x() { return __builtin_amdgcn_workgroup_id_x(); }
 
 constexpr float kGridMagic = kPGridMagic;  // 1.5 * 2^12: spacing 2^-11 in [2^12, 2^13)
 constexpr float kExpOffset = 8.0f;     // P is stored as E4M3(2^(x + 8)) * 2^-8
@@ -1204,15 +1216,15 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_vs[D * NCH * 4];
   __shared__ uint32_t s_lm[NCH][4];  // line keys of a chunk per lane group: bit 16t + (key & 15)
 
-  const int tid = threadIdx.x;
+  const int tid = lane_tid();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
   const int n_t = a.N / BQ;
-  const uint32_t wr = blockIdx.x >> 3;
+  const uint32_t wr = wg_x() >> 3;
   const uint32_t wq = mdiv(wr, a.mg_nt);
-  const int head = static_cast<int>(wq * 8 + (blockIdx.x & 7));
+  const int head = static_cast<int>(wq * 8 + (wg_x() & 7));
   if (head >= a.nbh) return;  // the whole workgroup: grid rounded up to whole groups of 8 heads
   const int it = static_cast<int>(wr - wq * n_t);
   const int b = static_cast<int>(mdiv(head, a.mg_hq)), h = head - b * a.Hq;
@@ -1273,7 +1285,7 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   if (a.mode != MXQ_ALL_LOWBIT || LINES) {
 #pragma unroll
     for (int st = 0; st < NSB; ++st)
-      qbr[st] = *reinterpret_cast<const v8bf*>(a.q_bf16 + (bhq * a.N + q) * D + 8 * (4 * st + g));
+      qbr[st] = *reinterpret_cast<const v8bf*>(a.q_bf16 + bhq * a.N * D + (q * D + 8 * (4 * st + g)));
   }
 
   // ---- stage the head's low-bit K and V (both chunks) in LDS by direct
@@ -1600,19 +1612,25 @@ __global__ void __launch_bounds__(256, 4) k_attn_short(AttnArgs a) {
   const bool row_ok = q < a.n_valid;
   const float l = L[0];
   const float inv = row_ok ? 1.0f / l : 0.0f;
-  const int64_t obase = (bhq * a.N + q) * D;
+  // the head's rows from a scalar base and a 32-bit row offset, formed here
+  // (the row index is made opaque, so no per-lane 64-bit address from the
+  // prologue stays live across the kernel)
+  int qo = q;
+  __asm__ volatile("" : "+v"(qo));
+  const int64_t obase = bhq * a.N * D;
+  const int orow = qo * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int d0 = 16 * db + 4 * g;
     const float o0 = O[db][0] * inv, o1 = O[db][1] * inv, o2 = O[db][2] * inv, o3 = O[db][3] * inv;
     if (a.out_bf16) {
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + d0) =
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + obase + (orow + d0)) =
           make_uint2(bf16x2_rne(o0, o1), bf16x2_rne(o2, o3));
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(o0, o1, o2, o3);
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + (orow + d0)) = make_float4(o0, o1, o2, o3);
     }
   }
-  if (a.lse && g == 0) a.lse[bhq * a.N + q] = row_ok ? (m_o + __log2f(l)) * 0.69314718055994531f : NEG_INF;
+  if (a.lse && g == 0) a.lse[bhq * a.N + qo] = row_ok ? (m_o + __log2f(l)) * 0.69314718055994531f : NEG_INF;
 }
 
 template <int D>
