@@ -77,6 +77,9 @@ CASES = [
     (128, 64, True, 256, 130, 2, 1),
     (64, 64, True, 128, 100, 2, 1),
     (128, 128, False, 128, 77, 2, 2),
+    # one valid row and key (the smallest input the host accepts), both kernels
+    (64, 64, False, 128, 1, 2, 1),
+    (128, 128, True, 384, 1, 2, 2),
 ]
 
 

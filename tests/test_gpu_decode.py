@@ -49,6 +49,26 @@ def test_small_ragged(num_splits, G):
     assert err <= TIGHT, f"rounding-level error expected: {err}"
 
 
+@pytest.mark.parametrize("n_sink, lens", [(0, [1, 2, 31, 33, 1024]), (64, [1, 10, 64, 65, 1024])])
+def test_degenerate_lengths(n_sink, lens):
+    """A single cached token, lengths below one 32-token block and below the
+    sink, exactly the sink, and the full cache: every split but the ones that
+    hold tokens is empty for the short sequences."""
+    mxq = gpu_or_skip()
+    d = mxq_inputs.make_decode(dict(B=len(lens), L=1024, Hq=8, Hkv=2, D=128, n_sink=n_sink, n_recent=0, seed=13,
+                                    seq_len=lens), threads=4)
+    for num_splits in (0, 16):
+        out, _ = _run(mxq, d, n_sink, 0, num_splits)
+        ref = Dm.attn_decode_ref(d["q"], Dm.build_kv_cache_ref(d["k"], d["v"], d["seq_len"], n_sink, 0),
+                                 d["seq_len"], n_sink, 0)
+        err = np.abs(out - ref).max()
+        assert np.isfinite(out).all()
+        # with a handful of tokens the fp16 roundings of p*s do not average
+        # out: one token's relative 2^-11 on a value near 4 is about 2e-3, so
+        # only the parity bar applies here, not TIGHT
+        assert err <= TOL, (num_splits, err)
+
+
 def test_all_fp16_and_no_fp16_regions():
     mxq = gpu_or_skip()
     d = mxq_inputs.make_decode(dict(B=2, L=256, Hq=8, Hkv=2, D=128, n_sink=64, n_recent=128, seed=3,
