@@ -379,3 +379,35 @@ def test_stale_lds_does_not_reach_the_output(word):
                                           mode=mode, lines=rlines[b:b + 1, h:h + 1] if lines_on else None)
                 _check(out.cpu().numpy()[b:b + 1, h:h + 1], lse.cpu().numpy()[b:b + 1, h:h + 1], ro, rl)
             assert torch.isfinite(out).all()
+
+
+def test_largest_key_axis_sampled():
+    """The largest key axis the host accepts (2048 key tiles, N = 131072) with a
+    ragged tail: 1024 chunks per row at the end, 64 mask words per row.  Masks
+    bit-exact for both heads; the first, a middle and the last query tile of
+    head 1 within 5e-3."""
+    mxq = gpu_or_skip()
+    import torch
+
+    cfg = mxq_inputs.make_prefill("long32k", N=131072, n_valid=131072 - 37, Hq=2, Hkv=1)
+    q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+    shape = _shape(mxq, cfg)
+    pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
+                               sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"],
+                               out_dtype=mxq.MXQ_OUT_F32)
+    out_t, lse_t = pipe(q, k, v)
+    torch.cuda.synchronize()
+    out, lse, mask = out_t.cpu().numpy(), lse_t.cpu().numpy(), u32(pipe.mask)
+    del q, k, v
+    last = (cfg["n_valid"] - 1) // 128
+    tiles = [0, 512, last]
+    rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
+    for h in (0, 1):
+        sub_q, sub_k, sub_v = cfg["q"][:, h:h + 1], cfg["k"], cfg["v"]
+        rm, _, _ = S.select_blocks(sub_q, sub_k, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True, cfg["topk"],
+                                   cfg["ratio_num"], cfg["ratio_den"], cfg["sink_tiles"], cfg["local_tiles"])
+        assert np.array_equal(mask[:, h:h + 1], rm), f"head {h}: mask differs"
+    ops = A.prepare_operands(sub_q, sub_k, sub_v, cfg["n_valid"])
+    ro, rl = A.attn_mixed_ref(sub_q, sub_k, sub_v, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True,
+                              mask=rm, qtiles=tiles, ops=ops)
+    _check(out[:, 1:2], lse[:, 1:2], ro, rl, rows=rows)
