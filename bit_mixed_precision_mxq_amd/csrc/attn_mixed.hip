@@ -39,11 +39,15 @@
 // the QK MFMAs of chunk c+1 are issued between the exponentials of chunk c,
 // and the row maxima of chunk c+1 between its PV MFMAs.  Masked chunks (the
 // causal diagonal, padding) and chunks holding FP16 tiles take a general path.
+// Exact skips: a 16-key block whose largest score gives P = 0 for every row
+// of the wave (the same grid FMA the exponentials use decides) gets P = 0
+// without exponentials; a chunk with no such block skips its PV; an FP16
+// tile's 32-key half whose fp16 P rounds to 0 everywhere skips its work.
 // Staging: the workgroup's K and V chunks arrive in LDS by direct
 // global-to-LDS copies, K two chunks and V one chunk before they are needed
 // (rings of four and three buffers, one barrier per chunk); a promoted tile's
 // bf16 K and fp16 V^T are copied into a stage one chunk ahead when the stage
-// is free; the bf16 Q rows of the workgroup sit in LDS for the FP16 tiles.
+// is free; each lane's bf16 Q slices for the FP16 tiles stay in registers.
 #include <type_traits>
 
 #include "mxq_internal.h"
