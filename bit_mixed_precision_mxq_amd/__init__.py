@@ -30,6 +30,7 @@ MXQ_OK, MXQ_EINVAL, MXQ_EUNSUPPORTED, MXQ_EHIP = 0, 1, 2, 3
 MXQ_MXFP4_E2M1, MXQ_MXFP8_E4M3, MXQ_INT4_ASYM_G32, MXQ_FP16, MXQ_MXFP4_E2M1_HADAMARD = 1, 2, 3, 4, 5
 MXQ_AXIS_D, MXQ_AXIS_N = 0, 1
 MXQ_MIXED, MXQ_ALL_LOWBIT, MXQ_ALL_FP16 = 0, 1, 2
+MXQ_GROUP_HEADS = 16  # mode flag: one workgroup serves the G query heads of a kv group
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 
 EXPORTED = [
@@ -360,8 +361,11 @@ def prepare_prefill_means(q, k, v, shape: Shape, out=None, means=None):
 
 
 def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, mode=MXQ_MIXED,
-                   out_dtype=MXQ_OUT_F32, want_lse=True, out=None, lse=None, lines=None):
-    """lines: int32 [B,Hq,n_lines] vertical-line keys (attn_select_lines) or None."""
+                   out_dtype=MXQ_OUT_F32, want_lse=True, out=None, lse=None, lines=None, group_heads=False):
+    """lines: int32 [B,Hq,n_lines] vertical-line keys (attn_select_lines) or None.
+    group_heads: one workgroup serves the G query heads of each kv group, and
+    the mask row and line list of the group's first head apply to all G (as
+    written by selection with group_shared)."""
     if lines is not None:
         _need_gpu(lines)
         assert lines.dtype == torch.int32 and lines.dim() == 3
@@ -375,7 +379,8 @@ def attn_mixed_fwd(ops: PrefillOperands, mask, shape: Shape, softmax_scale=0.0, 
     _check(load_library().attn_mixed_fwd(
         _ptr(ops.q_codes), _ptr(ops.q_scales), _ptr(ops.k_codes), _ptr(ops.k_scales), _ptr(ops.v_codes),
         _ptr(ops.v_scales), _ptr(ops.q_bf16), _ptr(ops.k_bf16), _ptr(ops.v_f16t), _ptr(ops.v_bf16), _ptr(mask),
-        _ptr(lines), 0 if lines is None else int(lines.shape[-1]), ctypes.byref(cs), float(softmax_scale), int(mode), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
+        _ptr(lines), 0 if lines is None else int(lines.shape[-1]), ctypes.byref(cs), float(softmax_scale),
+        int(mode) | (MXQ_GROUP_HEADS if group_heads else 0), _ptr(out), int(out_dtype), _ptr(lse), _stream()))
     return out, lse
 
 
@@ -390,9 +395,12 @@ class PrefillPipeline:
 
     def __init__(self, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0, n_lines=0,
                  sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0", fused_means=True,
-                 group_shared=False):
+                 group_shared=False, group_heads=False):
         self.shape, self.topk, self.ratio = shape, topk, ratio
         self.group_shared = bool(group_shared)
+        # one workgroup per kv group in the attention (needs the shared masks)
+        self.group_heads = bool(group_heads)
+        assert not self.group_heads or self.group_shared, "group_heads needs group_shared selection"
         self.sink_tiles, self.local_tiles = sink_tiles, local_tiles
         self.n_lines, self.sink_tokens, self.rotate, self.out_dtype = n_lines, sink_tokens, rotate, out_dtype
         dev = torch.device(device)
@@ -429,11 +437,11 @@ class PrefillPipeline:
                                      group_shared=self.group_shared)
             if self.n_lines:
                 attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
-                                  lines=self.lines)
+                                  lines=self.lines, group_shared=self.group_heads)
             if events is not None:
                 events[0].record(main)
             attn_mixed_fwd(ops, self.mask, self.shape, out_dtype=self.out_dtype, out=self.out, lse=self.lse,
-                           lines=self.lines)
+                           lines=self.lines, group_heads=self.group_heads)
             if events is not None:
                 events[1].record(main)
             return self.out, self.lse
@@ -445,7 +453,7 @@ class PrefillPipeline:
                                group_shared=self.group_shared)
             if self.n_lines:
                 attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
-                                  lines=self.lines)
+                                  lines=self.lines, group_shared=self.group_heads)
             self.ev_sel.record(self.aux)
         # a zero budget with no forced tile promotes nothing: no fp16 copy of V
         promoted = self.sink_tiles > 0 or self.local_tiles > 0 or self.topk > 0 or (self.topk < 0 and self.ratio[0] > 0)
@@ -455,7 +463,7 @@ class PrefillPipeline:
         if events is not None:
             events[0].record(main)
         attn_mixed_fwd(ops, self.mask, self.shape, out_dtype=self.out_dtype, out=self.out, lse=self.lse,
-                       lines=self.lines)
+                       lines=self.lines, group_heads=self.group_heads)
         if events is not None:
             events[1].record(main)
         return self.out, self.lse

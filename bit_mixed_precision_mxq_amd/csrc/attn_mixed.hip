@@ -240,10 +240,18 @@ struct Lds {
 
 // LINES: vertical-line tokens are present (n_lines > 0); without them the
 // kernel carries none of their code.
-template <int D, bool LINES>
+// GH: query heads per workgroup.  GH = 1: the workgroup's 8 waves take 128
+// rows of one head.  GH = G = Hq / Hkv (2 or 4): one workgroup serves the G
+// query heads of a kv group (HyQuant's signals shared by the heads of a
+// group): 8 / G waves per head, 128 / G rows of each, and the mask row and
+// line list of the group's first head apply to all of them (attn_select_blocks
+// and attn_select_lines with group_shared write identical rows for the G
+// heads, reading R35 and R31).  Each row's arithmetic is the same either way.
+template <int D, bool LINES, int GH>
 __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   using LY = Lds<D>;
-  constexpr int BQ = 128;        // query rows per workgroup
+  constexpr int BQ = 128 / GH;   // query rows per head and workgroup
+  constexpr int WPH = 8 / GH;    // waves per head
   constexpr int NT = 512;        // 8 waves of 16 rows
   constexpr int KROW = D / 2;
   constexpr int NDB = D / 16;    // 16-row head_dim blocks of O^T
@@ -262,29 +270,43 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   const int col = lane & 15;   // query column within the wave's 16 rows
   const int g = lane >> 4;     // lane group 0..3
   // Work order: workgroups are dispatched in linear id order, round-robin
-  // over the 8 XCDs.  Linear id L takes query tile n_qt-1 - L/Hq (longest
-  // causal tiles of every head first, then shorter ones fill in) and, when Hq
-  // is a multiple of 8, head (Hq/8)*(L%8) + (L%Hq)/8, so that each XCD (and
-  // its L2) serves a contiguous block of query heads, i.e. whole kv groups.
+  // over the 8 XCDs.  Linear id L takes query tile n_qt-1 - L/H (longest
+  // causal tiles of every head first, then shorter ones fill in; H = Hq, or
+  // Hkv when a workgroup serves a kv group) and, when H is a multiple of 8,
+  // head (H/8)*(L%8) + (L%H)/8, so that each XCD (and its L2) serves a
+  // contiguous block of heads, i.e. whole kv groups.
+  const int nh = GH == 1 ? a.Hq : a.Hkv;
   const int lin = static_cast<int>(blockIdx.x) + a.n_qt * static_cast<int>(blockIdx.y);
-  const int it = a.n_qt - 1 - lin / a.Hq;
-  const int hr = lin % a.Hq;
-  const int h = (a.Hq % 8 == 0) ? (a.Hq / 8) * (hr % 8) + hr / 8 : hr;
+  const int it = a.n_qt - 1 - lin / nh;
+  const int hr = lin % nh;
+  const int hs = (nh % 8 == 0) ? (nh / 8) * (hr % 8) + hr / 8 : hr;  // head, or kv head when GH > 1
   const int b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
+  const int h = GH == 1 ? hs : hs * GH + wave / WPH;  // this wave's query head
   const int64_t bhq = static_cast<int64_t>(b) * a.Hq + h;
+  const int64_t bhq0 = GH == 1 ? bhq : static_cast<int64_t>(b) * a.Hq + hs * GH;  // mask and line rows
   const int64_t bhk = static_cast<int64_t>(b) * a.Hkv + h / G;
   const int qs = it * BQ;
-  const int q = qs + wave * 16 + col;  // this lane's query row
+  const int wrow = (GH == 1 ? wave : wave % WPH) * 16;  // this wave's first row within the tile
+  const int q = qs + wrow + col;  // this lane's query row
 
   if (qs >= a.n_valid) {  // a tile of padding rows: output 0, lse -inf
-    for (int idx = tid; idx < BQ * D; idx += NT) {
-      int64_t o = (bhq * a.N + qs) * D + idx;
-      if (a.out_bf16) static_cast<uint16_t*>(a.out)[o] = 0;
-      else static_cast<float*>(a.out)[o] = 0.0f;
+    if constexpr (GH == 1) {
+      for (int idx = tid; idx < BQ * D; idx += NT) {
+        int64_t o = (bhq * a.N + qs) * D + idx;
+        if (a.out_bf16) static_cast<uint16_t*>(a.out)[o] = 0;
+        else static_cast<float*>(a.out)[o] = 0.0f;
+      }
+      if (a.lse)
+        for (int r = tid; r < BQ; r += NT) a.lse[bhq * a.N + qs + r] = NEG_INF;
+    } else {  // each wave its own head's 16 rows
+      for (int idx = lane; idx < 16 * D; idx += 64) {
+        int64_t o = (bhq * a.N + qs + wrow) * D + idx;
+        if (a.out_bf16) static_cast<uint16_t*>(a.out)[o] = 0;
+        else static_cast<float*>(a.out)[o] = 0.0f;
+      }
+      if (a.lse && lane < 16) a.lse[bhq * a.N + qs + wrow + lane] = NEG_INF;
     }
-    if (a.lse)
-      for (int r = tid; r < BQ; r += NT) a.lse[bhq * a.N + qs + r] = NEG_INF;
     return;
   }
   const int qe = min(qs + BQ, a.n_valid) - 1;
@@ -292,7 +314,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   if (a.causal) last_tile = min(last_tile, qe / 64);
   last_tile = __builtin_amdgcn_readfirstlane(last_tile);
   const int n_chunks = (last_tile + 2) / 2;
-  const int wq_lo = __builtin_amdgcn_readfirstlane(qs + wave * 16);  // this wave's first row
+  const int wq_lo = __builtin_amdgcn_readfirstlane(qs + wrow);  // this wave's first row
   const bool wave_live = wq_lo < a.n_valid;
 
   // Buffer resources over slices of the operands: reads past a slice return
@@ -336,7 +358,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // uses the union (FP16 data some wave needs) and the intersection (low-bit
   // data is needed unless every wave promotes the tile).  The two rows' bits
   // are unpacked once per workgroup into one byte per chunk in LDS.
-  const int64_t mbase = bhq * (a.N / a.sel_bq);
+  const int64_t mbase = bhq0 * (a.N / a.sel_bq);
   const uint32_t* mrow_a = a.mask ? a.mask + (mbase + qs / a.sel_bq) * a.words : nullptr;
   const uint32_t* mrow_b = a.mask ? a.mask + (mbase + (qs + BQ - 1) / a.sel_bq) * a.words : nullptr;
   const bool w_in_b = __builtin_amdgcn_readfirstlane(static_cast<int>(wq_lo / a.sel_bq != qs / a.sel_bq)) != 0;
@@ -363,7 +385,7 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
   // 16 loads with indices clamped to the row, then entry e to lane e
   int line_raw = -1;
   if constexpr (LINES) {
-    const uint64_t pa = reinterpret_cast<uint64_t>(a.lines + bhq * a.n_lines);
+    const uint64_t pa = reinterpret_cast<uint64_t>(a.lines + bhq0 * a.n_lines);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32));
     typedef const __attribute__((address_space(4))) int32_t cint;
@@ -1124,10 +1146,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_mixed(AttnArgs a) {
       live0 = tile_live(low0, hm0);
       live1 = tile_live(low1, hm1);
       if (low_w) {
-        // as for unmasked chunks: each tile's P enters through the E8M0 scale
-        // 2^-8 * 2^(m_t - m_o); O is rescaled only when the lag grows large
-        if (m_o == NEG_INF) m_o = m_run;
-        else if (__any(m_run - m_o > kMaxLag)) rebase(m_run);
+        // as for unmasked chunks (the same reference choices, so a row's
+        // result does not depend on which path its chunk took): each tile's
+        // P enters through the E8M0 scale 2^-8 * 2^(m_t - m_o); O starts at
+        // the first tile's reference and is rescaled when the lag grows large
+        chunk_lag(m_tile0 == NEG_INF ? m_run : m_tile0, m_run);
       }
     }
     // ================= the pipeline step: P of chunk ch, QK of chunk ch+1, PV of chunk ch-1
@@ -1647,8 +1670,18 @@ mxq_status launch_short(const AttnArgs& a, hipStream_t st) {
 
 template <int D>
 mxq_status launch(const AttnArgs& a, int n_qt, int Hq, int B, hipStream_t st) {
-  if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_mixed<D, true>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_mixed<D, false>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
+  if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_mixed<D, true, 1>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_mixed<D, false, 1>), dim3(n_qt, Hq, B), dim3(512), 0, st, a);
+  return check_launch("k_attn_mixed");
+}
+
+// one workgroup per (query tile of 128 / G rows, kv head, batch) serving the
+// G query heads of the group
+template <int D, int GH>
+mxq_status launch_group(const AttnArgs& a, int Hkv, int B, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.n_qt), static_cast<unsigned>(Hkv), static_cast<unsigned>(B));
+  if (a.n_lines > 0) hipLaunchKernelGGL((k_attn_mixed<D, true, GH>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_mixed<D, false, GH>), grid, dim3(512), 0, st, a);
   return check_launch("k_attn_mixed");
 }
 
@@ -1668,8 +1701,12 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
                                      mxq_stream_t stream) {
   mxq_status st = validate_attn_shape(s);
   if (st != MXQ_OK) return st;
+  const bool group_heads = (static_cast<int>(mode) & MXQ_GROUP_HEADS) != 0;
+  mode = static_cast<mxq_mode>(static_cast<int>(mode) & ~MXQ_GROUP_HEADS);
   MXQ_REQUIRE(mode == MXQ_MIXED || mode == MXQ_ALL_LOWBIT || mode == MXQ_ALL_FP16, MXQ_EINVAL,
               "attn_mixed_fwd: bad mode");
+  MXQ_REQUIRE(!group_heads || ((s->Hq / s->Hkv == 2 || s->Hq / s->Hkv == 4) && s->N > 256), MXQ_EUNSUPPORTED,
+              "attn_mixed_fwd: MXQ_GROUP_HEADS needs Hq / Hkv in {2, 4} and N > 256");
   MXQ_REQUIRE(out_dtype == MXQ_OUT_F32 || out_dtype == MXQ_OUT_BF16, MXQ_EINVAL,
               "attn_mixed_fwd: bad out_dtype");
   MXQ_REQUIRE(out != nullptr, MXQ_EINVAL, "attn_mixed_fwd: out is NULL");
@@ -1719,6 +1756,12 @@ extern "C" mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_sc
     a.sel_shift = s->Bq == 128 ? 7 : 6;
     if (s->D == 128) return launch_short<128>(a, strm);
     return launch_short<64>(a, strm);
+  }
+  if (group_heads) {
+    const int G = s->Hq / s->Hkv;
+    a.n_qt = s->N / (128 / G);
+    if (s->D == 128) return G == 2 ? launch_group<128, 2>(a, s->Hkv, s->B, strm) : launch_group<128, 4>(a, s->Hkv, s->B, strm);
+    return G == 2 ? launch_group<64, 2>(a, s->Hkv, s->B, strm) : launch_group<64, 4>(a, s->Hkv, s->B, strm);
   }
   if (s->D == 128) return launch<128>(a, n_qt, s->Hq, s->B, strm);
   return launch<64>(a, n_qt, s->Hq, s->B, strm);

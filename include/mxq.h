@@ -65,7 +65,7 @@ typedef enum {
   MXQ_AXIS_N = 1  /* blocks run along the sequence; output is [.., D, N]        */
 } mxq_axis;
 
-typedef enum { MXQ_MIXED = 0, MXQ_ALL_LOWBIT = 1, MXQ_ALL_FP16 = 2 } mxq_mode;
+typedef enum { MXQ_MIXED = 0, MXQ_ALL_LOWBIT = 1, MXQ_ALL_FP16 = 2, MXQ_GROUP_HEADS = 16 } mxq_mode;
 typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_dtype;
 
 /* Attention problem.  Q is [B][Hq][N][D], K and V are [B][Hkv][N][D].
@@ -272,7 +272,16 @@ mxq_status attn_select_lines(const uint16_t* q_bf16, const uint16_t* k_bf16,
  * is 0.
  * out: [B][Hq][N][D] fp32 or bf16; lse: f32 [B][Hq][N] or NULL (natural log).
  * Rows >= n_valid: out 0, lse -inf.  With N <= 256 (at most two 128-key
- * chunks) B * Hq may not exceed 2^21 (MXQ_EUNSUPPORTED).
+ * chunks) B * Hq may not exceed 2^21 and (B * Hq + 8) * Hq may not exceed
+ * 2^32 (MXQ_EUNSUPPORTED).
+ * mode may carry MXQ_GROUP_HEADS (ORed into one of the three modes): one
+ * workgroup serves the G = Hq / Hkv query heads of a kv group, 128 / G rows of
+ * each, and the mask row and line list of the group's first head apply to
+ * all G heads -- as attn_select_blocks and attn_select_lines with
+ * group_shared write them (HyQuant: selection signals shared across the
+ * heads of a GQA group; reading R35).  With such masks and lines the result
+ * is bit-identical to the default one-head-per-workgroup launch.  Needs
+ * G in {2, 4} and N > 256, else MXQ_EUNSUPPORTED.
  * ------------------------------------------------------------------------- */
 mxq_status attn_mixed_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                           const uint8_t* k_codes, const uint8_t* k_scales,

@@ -411,3 +411,75 @@ def test_largest_key_axis_sampled():
     ro, rl = A.attn_mixed_ref(sub_q, sub_k, sub_v, cfg["n_valid"], cfg["Bq"], cfg["Bk"], True,
                               mask=rm, qtiles=tiles, ops=ops)
     _check(out[:, 1:2], lse[:, 1:2], ro, rl, rows=rows)
+
+
+GROUP_CASES = [
+    # D, Bq, causal, N, n_valid, Hq, Hkv, n_lines
+    (128, 128, True, 768, 700, 8, 2, 0),    # G = 4, 32 rows per head and workgroup
+    (64, 64, False, 512, 450, 4, 2, 0),     # G = 2, 64 rows per head
+    (128, 64, True, 512, 333, 4, 1, 0),     # G = 4, 64-row selection tiles
+    (128, 128, True, 1024, 1024, 8, 4, 4),  # G = 2 with shared vertical lines
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES)
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_group_heads_equal_the_per_head_kernel(case, mode):
+    """One workgroup serving the G query heads of a kv group (MXQ_GROUP_HEADS)
+    under masks and line lists shared by the group (selection with
+    group_shared): outputs and lse bit-identical to the per-head kernel, whose
+    rows do the same arithmetic; then the first head against the oracle."""
+    mxq = gpu_or_skip()
+    import torch
+
+    D, Bq, causal, N, nv, Hq, Hkv, n_lines = case
+    rng = np.random.default_rng(D + N + nv + Hq)
+    q = rng.standard_normal((1, Hq, N, D)).astype(np.float32) * 1.5
+    k = rng.standard_normal((1, Hkv, N, D)).astype(np.float32)
+    v = rng.standard_normal((1, Hkv, N, D)).astype(np.float32)
+    k[:, :, 0] *= 8
+    for t in (q, k, v):
+        t[:, :, nv:] = 0
+    qb, kb, vb = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    qd, kd, vd = bf16_dev(qb), bf16_dev(kb), bf16_dev(vb)
+    shape = mxq.Shape(1, Hq, Hkv, N, nv, D, Bq, 64, causal)
+    mask = None
+    if mode == mxq.MXQ_MIXED:
+        mask, _, _ = mxq.attn_select_blocks(qd, kd, shape, topk=-1, ratio=(10, 100), sink_tiles=1, local_tiles=1,
+                                            group_shared=True)
+    lines = mxq.attn_select_lines(qd, kd, shape, n_lines, 1, group_shared=True)[0] if n_lines else None
+    ops = mxq.prepare_prefill(qd, kd, vd, nv, mode, lines=bool(n_lines))
+    o1, l1 = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode, lines=lines)
+    o2, l2 = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode, lines=lines, group_heads=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    # the first and last heads against the oracle, each with its own mask row
+    # and line list (the shared ones)
+    G = Hq // Hkv
+    for h in (0, Hq - 1):
+        hs = slice(h, h + 1)
+        ks = slice(h // G, h // G + 1)
+        rm = u32(mask)[:, hs] if mask is not None else None
+        rlines = lines.cpu().numpy()[:, hs] if lines is not None else None
+        ro, rl = A.attn_mixed_ref(qb[:, hs], kb[:, ks], vb[:, ks], nv, Bq, 64, causal, mask=rm, mode=mode,
+                                  lines=rlines)
+        _check(o2.cpu().numpy()[:, hs], l2.cpu().numpy()[:, hs], ro, rl)
+
+
+def test_group_heads_host_checks():
+    mxq = gpu_or_skip()
+    import torch
+
+    q = torch.zeros((1, 2, 512, 128), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.zeros((1, 2, 512, 128), dtype=torch.bfloat16, device="cuda:0")
+    ops = mxq.prepare_prefill(q, k, k, 512, mxq.MXQ_ALL_LOWBIT)
+    with pytest.raises(mxq.MxqError, match="GROUP_HEADS"):  # G = 1
+        mxq.attn_mixed_fwd(ops, None, mxq.Shape(1, 2, 2, 512, 512, 128, 128, 64, True), mode=mxq.MXQ_ALL_LOWBIT,
+                           group_heads=True)
+    q2 = torch.zeros((1, 4, 256, 128), dtype=torch.bfloat16, device="cuda:0")
+    k2 = torch.zeros((1, 2, 256, 128), dtype=torch.bfloat16, device="cuda:0")
+    ops2 = mxq.prepare_prefill(q2, k2, k2, 256, mxq.MXQ_ALL_LOWBIT)
+    with pytest.raises(mxq.MxqError, match="GROUP_HEADS"):  # N <= 256
+        mxq.attn_mixed_fwd(ops2, None, mxq.Shape(1, 4, 2, 256, 256, 128, 128, 64, True), mode=mxq.MXQ_ALL_LOWBIT,
+                           group_heads=True)
