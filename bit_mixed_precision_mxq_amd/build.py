@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmxq.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["api.cpp", "quantize.hip", "select.hip", "attn_mixed.hip", "decode.hip", "kvcache.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "select.hip", "attn_mixed.hip", "attn_short.hip", "decode.hip", "kvcache.hip"]
 ARCH = os.environ.get("MXQ_OFFLOAD_ARCH", "gfx950")
 
 
@@ -37,7 +37,14 @@ def _flags():
 
 # per-file flags: the attention kernel never sees NaN scores (finite or -inf),
 # so NaN semantics are relaxed there to drop canonicalising moves around fmaxf
-EXTRA = {"attn_mixed.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# The attention kernels run with IEEE mode off (scores are never NaN).  The
+# long kernel's loop is sensitive to where its branch targets fall in the
+# instruction fetch blocks (up to 6% between layouts with the same code), so
+# every block entered only by a jump starts on a 32-byte boundary (the padding
+# sits behind unconditional branches and never runs): its speed no longer
+# moves when code before the loop changes.
+_ATTN = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+EXTRA = {"attn_mixed.hip": _ATTN + ["-mllvm", "-align-all-nofallthru-blocks=5"], "attn_short.hip": _ATTN}
 
 
 def _compile(src: str) -> str:
