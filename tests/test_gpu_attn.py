@@ -414,11 +414,16 @@ def test_largest_key_axis_sampled():
 
 
 GROUP_CASES = [
-    # D, Bq, causal, N, n_valid, Hq, Hkv, n_lines
-    (128, 128, True, 768, 700, 8, 2, 0),    # G = 4, 32 rows per head and workgroup
-    (64, 64, False, 512, 450, 4, 2, 0),     # G = 2, 64 rows per head
-    (128, 64, True, 512, 333, 4, 1, 0),     # G = 4, 64-row selection tiles
-    (128, 128, True, 1024, 1024, 8, 4, 4),  # G = 2 with shared vertical lines
+    # D, Bq, causal, N, n_valid, Hq, Hkv, n_lines, sink_tiles
+    (128, 128, True, 768, 700, 8, 2, 0, 1),    # G = 4, 32 rows per head and workgroup
+    (64, 64, False, 512, 450, 4, 2, 0, 1),     # G = 2, 64 rows per head
+    (128, 64, True, 512, 333, 4, 1, 0, 1),     # G = 4, 64-row selection tiles
+    (128, 128, True, 1024, 1024, 8, 4, 4, 1),  # G = 2 with shared vertical lines
+    # 64-row selection tiles, no forced sink tile, no padding: a 128-row
+    # workgroup of the per-head launch spans two mask rows, so it can take
+    # the masked path for chunks that the grouped launch runs unmasked
+    (128, 64, True, 1024, 1024, 4, 2, 0, 0),
+    (64, 64, False, 768, 768, 8, 2, 0, 0),
 ]
 
 
@@ -432,7 +437,7 @@ def test_group_heads_equal_the_per_head_kernel(case, mode):
     mxq = gpu_or_skip()
     import torch
 
-    D, Bq, causal, N, nv, Hq, Hkv, n_lines = case
+    D, Bq, causal, N, nv, Hq, Hkv, n_lines, sink_tiles = case
     rng = np.random.default_rng(D + N + nv + Hq)
     q = rng.standard_normal((1, Hq, N, D)).astype(np.float32) * 1.5
     k = rng.standard_normal((1, Hkv, N, D)).astype(np.float32)
@@ -445,8 +450,8 @@ def test_group_heads_equal_the_per_head_kernel(case, mode):
     shape = mxq.Shape(1, Hq, Hkv, N, nv, D, Bq, 64, causal)
     mask = None
     if mode == mxq.MXQ_MIXED:
-        mask, _, _ = mxq.attn_select_blocks(qd, kd, shape, topk=-1, ratio=(10, 100), sink_tiles=1, local_tiles=1,
-                                            group_shared=True)
+        mask, _, _ = mxq.attn_select_blocks(qd, kd, shape, topk=-1, ratio=(10, 100), sink_tiles=sink_tiles,
+                                            local_tiles=1, group_shared=True)
     lines = mxq.attn_select_lines(qd, kd, shape, n_lines, 1, group_shared=True)[0] if n_lines else None
     ops = mxq.prepare_prefill(qd, kd, vd, nv, mode, lines=bool(n_lines))
     o1, l1 = mxq.attn_mixed_fwd(ops, mask, shape, mode=mode, lines=lines)
