@@ -49,10 +49,10 @@ __device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t m) {
   return m ? static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 32) : n;
 }
 
-// Work-item and workgroup ids straight from the hardware registers.  This
-// file is compiled with IEEE mode off, so the device library's id helpers,
-// built with it on, are not inlined: threadIdx/blockIdx become calls, and
-// values derived from them land in vector registers.  The short-sequence
+// Work-item and workgroup ids straight from the hardware registers.  The
+// attention files are compiled with IEEE mode off, so the device library's id
+// helpers, built with it on, are not inlined: threadIdx/blockIdx become calls,
+// and values derived from them land in vector registers.  The short-sequence
 // kernel uses these (its prologue is a large share of its time); the long
 // kernel keeps the library helpers, called once per workgroup, because its
 // main loop was measured to schedule slower with the intrinsics.
@@ -85,8 +85,8 @@ __device__ __forceinline__ float wave_rowmax(float v) {
   return v;
 }
 
-// max of three scores.  This file is compiled with NaNs not honoured and the
-// IEEE mode bit off (scores are finite or -inf, never NaN), so fmaxf needs no
+// max of three scores.  The attention files are compiled with NaNs not
+// honoured and the IEEE mode bit off (scores are finite or -inf, never NaN), so fmaxf needs no
 // canonicalising moves and maps to one v_max3_f32.
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
