@@ -99,6 +99,19 @@ def test_host_validation_rejects_before_launch(lib):
     st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, fake, fake, None, None, fake, None, 0, ctypes.byref(ok),
                            0.0, mxq.MXQ_MIXED, fake, 0, None, None)
     assert st == mxq.MXQ_EINVAL and b"bf16 V" in so.mxq_last_error()
+    # one workgroup per kv group: G = Hq / Hkv in {2, 4} and N > 256
+    gh = mxq.MXQ_ALL_LOWBIT | mxq.MXQ_GROUP_HEADS
+    long_g1 = mxq.AttnShape(1, 2, 2, 512, 512, 64, 64, 64, 0)
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, None, None, 0,
+                           ctypes.byref(long_g1), 0.0, gh, fake, 0, None, None)
+    assert st == mxq.MXQ_EUNSUPPORTED and b"GROUP_HEADS" in so.mxq_last_error()
+    short_g2 = mxq.AttnShape(1, 4, 2, 256, 256, 64, 64, 64, 0)
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, None, None, 0,
+                           ctypes.byref(short_g2), 0.0, gh, fake, 0, None, None)
+    assert st == mxq.MXQ_EUNSUPPORTED and b"GROUP_HEADS" in so.mxq_last_error()
+    st = so.attn_mixed_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, None, None, 0,
+                           ctypes.byref(ok), 0.0, 3 | mxq.MXQ_GROUP_HEADS, fake, 0, None, None)
+    assert st == mxq.MXQ_EINVAL and b"mode" in so.mxq_last_error()
     lp = mxq.LineParams(17, 1, 0)
     st = so.attn_select_lines(fake, fake, ctypes.byref(ok), ctypes.byref(lp), fake, 1 << 20, fake, None, None)
     assert st == mxq.MXQ_EINVAL and b"n_lines" in so.mxq_last_error()
