@@ -159,10 +159,12 @@ def bench_prefill(args, dev, workload):
     shape = mxq.Shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["n_valid"], cfg["D"], cfg["Bq"], cfg["Bk"],
                       cfg["causal"])
     n_lines = cfg.get("n_lines", 0)
+    # one workgroup per kv group where the launch supports it (G = 2 or 4, N > 256)
+    group_heads = args.group_heads and cfg["Hq"] // cfg["Hkv"] in (2, 4) and cfg["N"] > 256
     pipe = mxq.PrefillPipeline(shape, topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]),
                                sink_tiles=cfg["sink_tiles"], local_tiles=cfg["local_tiles"], n_lines=n_lines,
                                sink_tokens=cfg.get("sink_tokens", 0), out_dtype=mxq.MXQ_OUT_BF16, device=dev,
-                               group_shared=args.group_shared)
+                               group_shared=args.group_shared or group_heads, group_heads=group_heads)
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
@@ -187,6 +189,7 @@ def bench_prefill(args, dev, workload):
         workload=workload, cfg=cfg, ms_step=ms_step, attn_ms=attn_ms, flops=flops, total_pairs=total,
         fp16_pairs=fp16, tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_attn=achieved, peak_eff=peak_eff,
         t_roof_ms=t_roof * 1e3, warmup_calls=n_warm,
+        group="heads" if group_heads else ("shared" if args.group_shared or args.group_heads else None),
     )
     log(f"prefill {workload}: step {ms_step:.3f} ms, attn {attn_ms:.3f} ms, "
         f"{res['tflops_step']:.1f} TFLOP/s step, {achieved:.1f} TFLOP/s attn, "
@@ -573,8 +576,10 @@ def prefill_summary(pre, with_traffic):
             "workload": workload_text(pre["workload"], cfg),
             "step": "quantize Q,K (MXFP4" + (", with tile means" if scored else "") + "), V (MXFP8"
                     + (" + fp16 copy" if promoted else "") + ") -> select tiles"
-                    + (" and lines" if cfg.get("n_lines", 0) else "") + " -> fused mixed attention"
-                    + ("" if promoted else " (line V from bf16 V)"),
+                    + (" and lines" if cfg.get("n_lines", 0) else "")
+                    + (" (one mask per kv group)" if pre.get("group") else "") + " -> fused mixed attention"
+                    + ("" if promoted else " (line V from bf16 V)")
+                    + (" (one workgroup per kv group)" if pre.get("group") == "heads" else ""),
             "fp16_pair_fraction": round(pre["fp16_pairs"] / pre["total_pairs"], 5),
             "attn_ms": round(pre["attn_ms"], 4),
             "attn_tflops": round(pre["tflops_attn"], 2),
@@ -584,7 +589,9 @@ def prefill_summary(pre, with_traffic):
             "bound": "mfma", "kernel": "attn_mixed_fwd",
             "achieved": round(pre["tflops_attn"], 2), "peak": round(pre["peak_eff"], 1), "unit": "TFLOP/s",
             "frac": round(pre["tflops_attn"] / pre["peak_eff"], 4),
-            "traffic": recorded_traffic("attn_mixed_fwd", pre["workload"]) if with_traffic else None,
+            # the recorded counters are those of the default per-head launch
+            "traffic": recorded_traffic("attn_mixed_fwd", pre["workload"])
+                       if with_traffic and not pre.get("group") else None,
             "peak_note": "precision-weighted: FP16 pairs at 2516.6, low-bit pairs half at FP4 10066.4 (QK^T) "
                          "and half at FP8 5033.2 (PV); achieved = 4*D*valid pairs / attention kernel time",
         },
@@ -607,6 +614,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-time budget of each CPU-baseline leg")
     ap.add_argument("--group-shared", action="store_true",
                     help="prefill with one tile mask per kv group (the G query heads share it)")
+    ap.add_argument("--group-heads", action="store_true",
+                    help="prefill with shared masks and one attention workgroup per kv group (implies --group-shared)")
     ap.add_argument("--decode-lines", type=int, default=0,
                     help="also time decode with this many vertical-line tokens (fp16) per kv head, at most 16")
     args = ap.parse_args()

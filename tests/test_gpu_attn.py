@@ -254,6 +254,34 @@ def test_prefill_pipeline_matches_the_sequential_calls():
             assert torch.equal(out, ref) and torch.equal(lse, ref_lse), name
 
 
+def test_prefill_pipeline_group_heads():
+    """PrefillPipeline with group_heads (one mask and one line list per kv
+    group, the attention launched per kv group) equals the calls made one
+    after another with group-shared selection and the per-head launch, bit
+    for bit, over repeated steps (both chains: tiles chosen by score on one
+    stream, and lines on the two-stream step)."""
+    mxq = gpu_or_skip()
+    import torch
+
+    for over in (dict(N=2048, n_valid=2000, Hq=8, Hkv=2, n_lines=0), dict(N=1024, n_valid=1024, Hq=8, Hkv=4, n_lines=8)):
+        n_lines = over.pop("n_lines")
+        cfg = mxq_inputs.make_prefill("llama8b", **over)
+        q, k, v = bf16_dev(cfg["q"]), bf16_dev(cfg["k"]), bf16_dev(cfg["v"])
+        shape = _shape(mxq, cfg)
+        sel = dict(topk=cfg["topk"], ratio=(cfg["ratio_num"], cfg["ratio_den"]), sink_tiles=cfg["sink_tiles"],
+                   local_tiles=cfg["local_tiles"])
+        grouped = mxq.PrefillPipeline(shape, n_lines=n_lines, sink_tokens=1, out_dtype=mxq.MXQ_OUT_F32,
+                                      group_shared=True, group_heads=True, **sel)
+        mask, _, _ = mxq.attn_select_blocks(q, k, shape, group_shared=True, **sel)
+        lines = mxq.attn_select_lines(q, k, shape, n_lines, 1, group_shared=True)[0] if n_lines else None
+        ops = mxq.prepare_prefill(q, k, v, cfg["n_valid"], lines=lines is not None)
+        ref, ref_lse = mxq.attn_mixed_fwd(ops, mask, shape, lines=lines)
+        for _ in range(3):
+            out, lse = grouped(q, k, v)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref) and torch.equal(lse, ref_lse), over
+
+
 def test_long32k_full_size_sampled():
     """The long-context causal workload at full size (N = 32768, 5% + sink +
     4-tile window) in the launch configuration the benchmark times (the fused
