@@ -447,6 +447,7 @@ GROUP_CASES = [
     (64, 64, False, 512, 450, 4, 2, 0, 1),     # G = 2, 64 rows per head
     (128, 64, True, 512, 333, 4, 1, 0, 1),     # G = 4, 64-row selection tiles
     (128, 128, True, 1024, 1024, 8, 4, 4, 1),  # G = 2 with shared vertical lines
+    (64, 128, True, 1024, 1000, 8, 2, 6, 1),   # G = 4, head_dim 64, lines, ragged
     # 64-row selection tiles, no forced sink tile, no padding: a 128-row
     # workgroup of the per-head launch spans two mask rows, so it can take
     # the masked path for chunks that the grouped launch runs unmasked
