@@ -395,7 +395,7 @@ class PrefillPipeline:
 
     def __init__(self, shape: Shape, topk=-1, ratio=(5, 100), sink_tiles=0, local_tiles=0, n_lines=0,
                  sink_tokens=0, rotate=False, out_dtype=MXQ_OUT_BF16, device="cuda:0", fused_means=True,
-                 group_shared=False, group_heads=False):
+                 group_shared=False, group_heads=False, v_beside=True):
         self.shape, self.topk, self.ratio = shape, topk, ratio
         self.group_shared = bool(group_shared)
         # one workgroup per kv group in the attention (needs the shared masks)
@@ -425,6 +425,18 @@ class PrefillPipeline:
         self.means = ((torch.empty((shape.B, shape.Hq, n_qt, shape.D), dtype=torch.float32, device=dev),
                        torch.empty((shape.B, shape.Hkv, shape.D, n_kt), dtype=torch.float32, device=dev))
                       if self.fused else None)
+        # a zero budget with no forced tile promotes nothing: no fp16 copy of
+        # V, and (v_beside) V's MXFP8 quantiser runs on the second stream
+        # after selection while Q and K are quantised on the caller's stream
+        self.promoted = sink_tiles > 0 or local_tiles > 0 or scored
+        self.v_beside = bool(v_beside) and not self.fused and not self.promoted
+        if self.v_beside:
+            B, Hq, Hkv, N, D = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D
+            u8 = dict(dtype=torch.uint8, device=dev)
+            self.ops = PrefillOperands(
+                q_codes=torch.empty((B, Hq, N, D // 2), **u8), q_scales=torch.empty((B, Hq, N, D // 32), **u8),
+                k_codes=torch.empty((B, Hkv, N, D // 2), **u8), k_scales=torch.empty((B, Hkv, N, D // 32), **u8),
+                v_codes=torch.empty((B, Hkv, D, N), **u8), v_scales=torch.empty((B, Hkv, D, N // 32), **u8))
 
     def __call__(self, q, k, v, events=None):
         """Returns (out, lse).  events=(e0, e1) are recorded around the
@@ -455,10 +467,20 @@ class PrefillPipeline:
                 attn_select_lines(q, k, self.shape, self.n_lines, self.sink_tokens, workspace=self.lws,
                                   lines=self.lines, group_shared=self.group_heads)
             self.ev_sel.record(self.aux)
-        # a zero budget with no forced tile promotes nothing: no fp16 copy of V
-        promoted = self.sink_tiles > 0 or self.local_tiles > 0 or self.topk > 0 or (self.topk < 0 and self.ratio[0] > 0)
-        ops = prepare_prefill(q, k, v, self.shape.n_valid, lines=bool(self.n_lines), rotate=self.rotate,
-                              promoted=promoted)
+        if self.v_beside:
+            lib, sh, ops = load_library(), self.shape, self.ops
+            ops.q_bf16, ops.k_bf16, ops.v_bf16 = q, k, v
+            fmt = MXQ_MXFP4_E2M1_HADAMARD if self.rotate else MXQ_MXFP4_E2M1
+            with torch.cuda.stream(self.aux):
+                _check(lib.mxq_quantize(_ptr(v), sh.B, sh.Hkv, sh.N, sh.D, sh.n_valid, MXQ_MXFP8_E4M3, MXQ_AXIS_N,
+                                        _ptr(ops.v_codes), _ptr(ops.v_scales), None, _stream()))
+                self.ev_sel.record(self.aux)
+            for x, H, codes, scales in ((q, sh.Hq, ops.q_codes, ops.q_scales), (k, sh.Hkv, ops.k_codes, ops.k_scales)):
+                _check(lib.mxq_quantize(_ptr(x), sh.B, H, sh.N, sh.D, sh.n_valid, fmt, MXQ_AXIS_D, _ptr(codes),
+                                        _ptr(scales), None, _stream()))
+        else:
+            ops = prepare_prefill(q, k, v, self.shape.n_valid, lines=bool(self.n_lines), rotate=self.rotate,
+                                  promoted=self.promoted)
         main.wait_event(self.ev_sel)
         if events is not None:
             events[0].record(main)
